@@ -1,0 +1,192 @@
+"""CPU oracle for the fused RoPE + KV-cache write -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``liboracle_rkv.so`` (plain C,
+``rkv_oracle.c``) with numpy marshalling: every wrapper copies its inputs and
+returns fresh output arrays, so a caller's arrays are never modified.
+
+fp16 arrays are ``uint16`` bit patterns; tables are ``float32``; index arrays
+are ``int32``.  The wrappers derive sizes from array shapes the same way the
+pages' tensor signatures do (TensorRT-Edge-LLM, "Apply Rope Write KV" and
+"Dflash Runtime Kernels").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+OK, ERR_ARG, ERR_CAPACITY = 0, 1, 2
+NEOX, GPTJ = 0, 1
+TOKENS_PER_PAGE = 64
+
+_lib = None
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"oracle {what} returned {code}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        path = _build.LIB_PATH
+        if not os.path.exists(path):
+            _build.build()
+        _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
+
+def load_from(path: str):
+    """Load an oracle library built from another source (mutation tests)."""
+    return _declare(ctypes.CDLL(path))
+
+
+def _declare(L):
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    L.rkv_ref_half_to_double.restype = ctypes.c_double
+    L.rkv_ref_half_to_double.argtypes = [ctypes.c_uint16]
+    L.rkv_ref_double_to_half.restype = ctypes.c_uint16
+    L.rkv_ref_double_to_half.argtypes = [ctypes.c_double]
+    L.rkv_ref_rotate_row.restype = None
+    L.rkv_ref_rotate_row.argtypes = [P, P, P, i32, i32, i32]
+    L.rkv_ref_packed_qkv.restype = ctypes.c_int
+    L.rkv_ref_packed_qkv.argtypes = [P, i32, i32, i32, P, i32, i32, i32, i32, i32, P, i32, i32]
+    L.rkv_ref_continuous.restype = ctypes.c_int
+    L.rkv_ref_continuous.argtypes = [P, i32, i32, i32, P, P, i32, i32, i32, i32, i32, P, i32, P,
+                                     i32]
+    L.rkv_ref_tree.restype = ctypes.c_int
+    L.rkv_ref_tree.argtypes = [P, i32, i32, i32, P, P, P, i32, i32, i32, i32, i32, P, i32, P, i32]
+    L.rkv_ref_paged_delta.restype = ctypes.c_int
+    L.rkv_ref_paged_delta.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32]
+    L.rkv_ref_check_rope_capacity.restype = ctypes.c_int
+    L.rkv_ref_check_rope_capacity.argtypes = [i32, i32]
+    return L
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def half_to_double(h: int, L=None) -> float:
+    return (L or lib()).rkv_ref_half_to_double(int(h))
+
+
+def double_to_half(x: float, L=None) -> int:
+    return (L or lib()).rkv_ref_double_to_half(float(x))
+
+
+def rotate_row(x, cos_sin_row, rotary_dim: int, style: int, L=None) -> np.ndarray:
+    """Rotate one head row ``x`` (uint16 [D]) with one table row (f32 [R])."""
+    x = _c(x, np.uint16)
+    row = _c(cos_sin_row, np.float32)
+    y = np.empty_like(x)
+    (L or lib()).rkv_ref_rotate_row(_p(x), _p(y), _p(row), x.size, rotary_dim, style)
+    return y
+
+
+def packed_qkv(cos_sin, qkv, cache, style: int, L=None):
+    """Call 1.  Returns ``(qkv_out, cache_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    qkv = _c(qkv, np.uint16).copy()
+    cache = _c(cache, np.uint16).copy()
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache.shape[2], cache.shape[3]
+    rc = (L or lib()).rkv_ref_packed_qkv(_p(cos_sin), tb, tlen, R, _p(qkv), B, S, H - 2 * Hkv,
+                                         Hkv, D, _p(cache), cap, style)
+    if rc:
+        raise OracleError(rc, "packed_qkv")
+    return qkv, cache
+
+
+def continuous(cos_sin, end_lens, qkv, cache, q_out, style: int, L=None):
+    """Call 2.  Returns ``(cache_out, q_out_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    end_lens = _c(end_lens, np.int32)
+    qkv = _c(qkv, np.uint16)
+    cache = _c(cache, np.uint16).copy()
+    q_out = _c(q_out, np.uint16).copy()
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache.shape[2], cache.shape[3]
+    rc = (L or lib()).rkv_ref_continuous(_p(cos_sin), tb, tlen, R, _p(end_lens), _p(qkv), B, S,
+                                         H - 2 * Hkv, Hkv, D, _p(cache), cap, _p(q_out), style)
+    if rc:
+        raise OracleError(rc, "continuous")
+    return cache, q_out
+
+
+def tree(cos_sin, end_lens, pos_ids, qkv, cache, q_out, style: int, L=None):
+    """Call 3.  Returns ``(cache_out, q_out_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    end_lens = _c(end_lens, np.int32)
+    pos_ids = _c(pos_ids, np.int32)
+    qkv = _c(qkv, np.uint16)
+    cache = _c(cache, np.uint16).copy()
+    q_out = _c(q_out, np.uint16).copy()
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache.shape[2], cache.shape[3]
+    rc = (L or lib()).rkv_ref_tree(_p(cos_sin), tb, tlen, R, _p(end_lens), _p(pos_ids), _p(qkv),
+                                   B, S, H - 2 * Hkv, Hkv, D, _p(cache), cap, _p(q_out), style)
+    if rc:
+        raise OracleError(rc, "tree")
+    return cache, q_out
+
+
+def paged_delta(k_delta, v_delta, pool, token_cos_sin, positions, seq, page_table, batch: int,
+                style: int, L=None):
+    """Call 4.  Returns the updated pool ``[2, numPages, 64, Hkv, D]``."""
+    k_delta = _c(k_delta, np.uint16)
+    v_delta = _c(v_delta, np.uint16)
+    pool = _c(pool, np.uint16).copy()
+    token_cos_sin = _c(token_cos_sin, np.float32)
+    positions = _c(positions, np.int32)
+    seq = _c(seq, np.int32)
+    page_table = _c(page_table, np.int32)
+    N, Hkv, D = k_delta.shape
+    R = token_cos_sin.shape[1]
+    num_pages = pool.shape[1]
+    max_pages = page_table.shape[2]
+    rc = (L or lib()).rkv_ref_paged_delta(_p(k_delta), _p(v_delta), _p(pool), _p(token_cos_sin),
+                                          _p(positions), _p(seq), _p(page_table), N, batch, Hkv,
+                                          D, R, num_pages, max_pages, style)
+    if rc:
+        raise OracleError(rc, "paged_delta")
+    return pool
+
+
+def check_rope_capacity(cos_sin_len: int, kv_capacity: int, L=None) -> int:
+    return (L or lib()).rkv_ref_check_rope_capacity(cos_sin_len, kv_capacity)
+
+
+def run(w, L=None):
+    """Run the oracle on a ``workloads.Contig`` or ``workloads.Paged``.
+
+    Returns a dict of expected outputs keyed like the HIP binding's results:
+    ``qkv`` (call 1), ``q_out`` (calls 2, 3), ``cache`` (calls 1-3), ``pool`` (call 4).
+    """
+    if hasattr(w, "pool"):
+        return {"pool": paged_delta(w.k_delta, w.v_delta, w.pool, w.cos_sin, w.positions, w.seq,
+                                    w.page_table, w.batch, w.style, L=L)}
+    if w.call == "packed":
+        q, c = packed_qkv(w.cos_sin, w.qkv, w.cache, w.style, L=L)
+        return {"qkv": q, "cache": c}
+    if w.call == "continuous":
+        c, q = continuous(w.cos_sin, w.end_lens, w.qkv, w.cache, w.q_out, w.style, L=L)
+        return {"cache": c, "q_out": q}
+    if w.call == "tree":
+        c, q = tree(w.cos_sin, w.end_lens, w.pos_ids, w.qkv, w.cache, w.q_out, w.style, L=L)
+        return {"cache": c, "q_out": q}
+    raise ValueError(w.call)

@@ -1,0 +1,334 @@
+/* CPU oracle for the fused RoPE + KV-cache write -- TEST INFRASTRUCTURE.
+ *
+ * Only tests/, __graft_entry__.smoke() and the CPU-baseline leg of bench.py
+ * may load this library.  It is the definition written out as plain loops:
+ * no tiling, no fusion, no reordering, one (token, head) row at a time, and
+ * it shares nothing with the HIP library.
+ *
+ * Arithmetic: inputs are fp16 (Q, K, V) and fp32 (cos/sin).  Every rotated
+ * element is evaluated in binary64 as x_u*c - x_v*s (or x_v*c + x_u*s).  Both
+ * products of an 11-bit by a 24-bit significand are exact in binary64, so the
+ * only roundings are the one binary64 subtraction/addition and the final
+ * round-to-nearest-even to binary16.  Build with -ffp-contract=off.
+ *
+ * Sources (cited by page title and section):
+ *  [P1] TensorRT-Edge-LLM 0.4.0 C++ API, "Apply Rope Write KV":
+ *       launchApplyRopeWriteKVPackedQKV, launchApplyRopeWriteKVContinuousQAndKVCache,
+ *       launchApplyRopeWriteKVTreeDecoding (shapes, dtypes, in-place and
+ *       end-position semantics).
+ *  [P2] sglang kernels/ops/kvcache/rope_cache.py: _get_neox_rotated_x,
+ *       _get_gptj_rotated_x, _unit_rope, _load_cos_sin (pairing, sign,
+ *       [cos | sin] row layout), and the slot < 0 skip of the cache write.
+ *  [P3] TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels":
+ *       launchDFlashTargetKVCacheUpdate (paged pool, page table, skip rules),
+ *       checkDFlashRopeCapacity.
+ *  [P4] libmir-cuda execution.rs, Dynamic::new: the newest token of a cache
+ *       of length L sits at position L - 1.
+ *
+ * Readings where the pages are silent (same numbering as the design notes):
+ *  R1  a table row holds cos in [0, R/2) and sin in [R/2, R).
+ *  R3  with R < D, pairs are formed inside the first R dims; dims >= R are
+ *      copied bit for bit.
+ *  R4  table batch 1 broadcasts over the batch; table batch B is per batch.
+ *  R5  kvCacheEndLens is the length after the write: the S new tokens take
+ *      slots end-S .. end-1.
+ *  R6  tree call: slot = end-S+s, rotary position = tokenPosIds[b,s].
+ *  R7  call 1 rotates Q and K in place in the packed tensor; V is unchanged.
+ *  R10 calls 2/3: a token whose slot or position is out of range writes
+ *      nothing (neither qOut nor cache).
+ *  R11 call 4: a row is padding if either index array is negative.
+ *  R12 call 4: a row whose sequence index is >= batchSize is skipped.
+ *  R13 call 4: K writes iff its id is in [0, numPages); V writes iff its id
+ *      is in [numPages, 2*numPages).
+ *  R14 call 4: the rotation layout is an explicit argument.
+ *  R17 the capacity check rejects exactly cosSinSeqLen > kvCapacity.
+ *  Parity unpinned against the original system for R6 and R7: no page fixes
+ *  them; they are the plainest reading consistent with the rest.
+ */
+#include "rkv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- fp16 -- */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent field 0 encodes zero and subnormals (fraction * 2^-24),
+ * field 31 encodes infinity (fraction 0) and NaN. */
+double rkv_ref_half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+/* Round |x| to a multiple of the binary16 quantum of its binade, ties to
+ * even; the subnormal range shares the quantum 2^-24 of the smallest normal
+ * binade.  A result of 2^16 or more (i.e. |x| >= 65520) is infinity. */
+uint16_t rkv_ref_double_to_half(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return (uint16_t)(sign | 0x7e00);
+  double a = fabs(x);
+  if (isinf(a)) return (uint16_t)(sign | 0x7c00);
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);              /* a = m * 2^e2, 0.5 <= m < 1 */
+  int ue = e2 - 1;            /* 2^ue <= a < 2^(ue+1) */
+  if (ue < -14) ue = -14;
+  if (ue > 15) return (uint16_t)(sign | 0x7c00);
+  double n = ldexp(a, 10 - ue);   /* a / quantum, exact */
+  double fl = floor(n);
+  double rem = n - fl;
+  long long k = (long long)fl;
+  if (rem > 0.5 || (rem == 0.5 && (k & 1))) k += 1;
+  if (k >= 2048) {            /* carried into the next binade */
+    k >>= 1;
+    ue += 1;
+  }
+  if (k < 1024) return (uint16_t)(sign | (uint16_t)k);        /* subnormal */
+  if (ue + 15 >= 31) return (uint16_t)(sign | 0x7c00);        /* overflow */
+  return (uint16_t)(sign | (uint16_t)((ue + 15) << 10) | (uint16_t)(k - 1024));
+}
+
+/* -------------------------------------------------------------- rotate -- */
+
+/* One head row.  [P2] _unit_rope: y = x*cos + rotate(x)*sin, where rotate
+ * negates the first member of each pair and swaps it with the second
+ * (_get_neox_rotated_x: partner at +R/2; _get_gptj_rotated_x: adjacent
+ * partner).  Frequency i drives pair i; cos_i = row[i], sin_i = row[R/2+i]
+ * ([P2] _load_cos_sin with the half-width table; R1).  Written per pair:
+ *   y_u = x_u*cos_i - x_v*sin_i,  y_v = x_v*cos_i + x_u*sin_i. */
+void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* row,
+                        int32_t head_dim, int32_t rotary_dim, int32_t style) {
+  uint16_t tmp[4096];
+  int half = rotary_dim / 2;
+  for (int d = 0; d < head_dim; ++d) tmp[d] = x[d];     /* R3: passthrough */
+  for (int i = 0; i < half; ++i) {
+    int u, v;
+    if (style == RKV_REF_NEOX) {
+      u = i;
+      v = i + half;
+    } else {
+      u = 2 * i;
+      v = 2 * i + 1;
+    }
+    double c = (double)row[i];
+    double s = (double)row[half + i];
+    double xu = rkv_ref_half_to_double(x[u]);
+    double xv = rkv_ref_half_to_double(x[v]);
+    double pu_c = xu * c, pv_s = xv * s;   /* exact products */
+    double pv_c = xv * c, pu_s = xu * s;
+    tmp[u] = rkv_ref_double_to_half(pu_c - pv_s);
+    tmp[v] = rkv_ref_double_to_half(pv_c + pu_s);
+  }
+  for (int d = 0; d < head_dim; ++d) y[d] = tmp[d];
+}
+
+/* ------------------------------------------------------------ helpers -- */
+
+static int bad_common(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                      int32_t rotary_dim, const uint16_t* qkv, int32_t batch, int32_t seq_len,
+                      int32_t hq, int32_t hkv, int32_t head_dim, const uint16_t* cache,
+                      int32_t capacity, int32_t style) {
+  if (!cos_sin || !qkv || !cache) return 1;
+  if (batch < 0 || seq_len < 0 || hq < 0 || hkv < 0 || capacity < 0 || table_len < 0) return 1;
+  if (head_dim <= 0 || head_dim > 4096) return 1;
+  if (rotary_dim < 0 || rotary_dim > head_dim || (rotary_dim & 1)) return 1;
+  if (table_batch != 1 && table_batch != batch) return 1;   /* R4 */
+  if (style != RKV_REF_NEOX && style != RKV_REF_GPTJ) return 1;
+  return 0;
+}
+
+static const float* table_row(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                              int32_t rotary_dim, int32_t b, int32_t pos) {
+  int32_t tb = (table_batch == 1) ? 0 : b;   /* R4 */
+  return cos_sin + ((size_t)tb * table_len + pos) * rotary_dim;
+}
+
+/* packed [B, S, Hq+Hkv+Hkv, D]: head row (b, s, h) */
+static size_t qkv_row(int32_t b, int32_t s, int32_t h, int32_t S, int32_t H, int32_t D) {
+  return (((size_t)b * S + s) * H + h) * (size_t)D;
+}
+
+/* contiguous cache [B, 2, Hkv, cap, D]: plane 0 holds K, plane 1 holds V */
+static size_t cache_row(int32_t b, int32_t plane, int32_t h, int32_t slot, int32_t Hkv,
+                        int32_t cap, int32_t D) {
+  return ((((size_t)b * 2 + plane) * Hkv + h) * cap + slot) * (size_t)D;
+}
+
+/* One token of calls 2 and 3: rotate its Q rows into q_out, its K rows into
+ * cache plane 0 at `slot`, copy its V rows into plane 1 at `slot`. */
+static void write_token(const float* row, const uint16_t* qkv, int32_t b, int32_t s,
+                        int32_t slot, int32_t S, int32_t hq, int32_t hkv, int32_t D,
+                        int32_t R, uint16_t* cache, int32_t cap, uint16_t* q_out,
+                        int32_t style) {
+  int32_t H = hq + 2 * hkv;
+  for (int32_t h = 0; h < hq; ++h)
+    rkv_ref_rotate_row(qkv + qkv_row(b, s, h, S, H, D),
+                       q_out + (((size_t)b * S + s) * hq + h) * (size_t)D, row, D, R, style);
+  for (int32_t h = 0; h < hkv; ++h)
+    rkv_ref_rotate_row(qkv + qkv_row(b, s, hq + h, S, H, D),
+                       cache + cache_row(b, 0, h, slot, hkv, cap, D), row, D, R, style);
+  for (int32_t h = 0; h < hkv; ++h)
+    memcpy(cache + cache_row(b, 1, h, slot, hkv, cap, D),
+           qkv + qkv_row(b, s, hq + hkv + h, S, H, D), (size_t)D * sizeof(uint16_t));
+}
+
+/* ------------------------------------------------------------- call 1 -- */
+
+/* [P1] launchApplyRopeWriteKVPackedQKV: the cache is empty, so token s of
+ * every sequence takes position s and cache slot s.  Q and K heads of the
+ * packed tensor are rotated in place (R7); K also goes to cache plane 0 and
+ * V, unrotated, to plane 1.  Slots >= S are not touched. */
+int rkv_ref_packed_qkv(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                       int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
+                       int32_t hq, int32_t hkv, int32_t head_dim, uint16_t* cache,
+                       int32_t capacity, int32_t style) {
+  if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
+                 head_dim, cache, capacity, style))
+    return RKV_REF_ERR_ARG;
+  if (seq_len > capacity || seq_len > table_len) return RKV_REF_ERR_CAPACITY;
+  int32_t H = hq + 2 * hkv, D = head_dim, R = rotary_dim;
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int32_t s = 0; s < seq_len; ++s) {
+      int32_t pos = s;
+      const float* row = table_row(cos_sin, table_batch, table_len, R, b, pos);
+      for (int32_t h = 0; h < hq; ++h) {
+        uint16_t* x = qkv + qkv_row(b, s, h, seq_len, H, D);
+        rkv_ref_rotate_row(x, x, row, D, R, style);
+      }
+      for (int32_t h = 0; h < hkv; ++h) {
+        uint16_t* x = qkv + qkv_row(b, s, hq + h, seq_len, H, D);
+        rkv_ref_rotate_row(x, x, row, D, R, style);
+        memcpy(cache + cache_row(b, 0, h, pos, hkv, capacity, D), x,
+               (size_t)D * sizeof(uint16_t));
+      }
+      for (int32_t h = 0; h < hkv; ++h)
+        memcpy(cache + cache_row(b, 1, h, pos, hkv, capacity, D),
+               qkv + qkv_row(b, s, hq + hkv + h, seq_len, H, D),
+               (size_t)D * sizeof(uint16_t));
+    }
+  }
+  return RKV_REF_OK;
+}
+
+/* ------------------------------------------------------------- call 2 -- */
+
+/* [P1] launchApplyRopeWriteKVContinuousQAndKVCache: end_lens[b] is the cache
+ * length after the write (R5, and [P4]: the newest token sits at length-1),
+ * so token s takes position and slot end-S+s.  Rotated Q goes to q_out, the
+ * packed tensor is only read.  Out-of-range tokens write nothing (R10). */
+int rkv_ref_continuous(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                       int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                       int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
+                       int32_t head_dim, uint16_t* cache, int32_t capacity, uint16_t* q_out,
+                       int32_t style) {
+  if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
+                 head_dim, cache, capacity, style) ||
+      !end_lens || !q_out)
+    return RKV_REF_ERR_ARG;
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int32_t s = 0; s < seq_len; ++s) {
+      int64_t slot = (int64_t)end_lens[b] - seq_len + s;
+      int64_t pos = slot;
+      if (slot < 0 || slot >= capacity || pos >= table_len) continue;
+      const float* row = table_row(cos_sin, table_batch, table_len, rotary_dim, b, (int32_t)pos);
+      write_token(row, qkv, b, s, (int32_t)slot, seq_len, hq, hkv, head_dim, rotary_dim, cache,
+                  capacity, q_out, style);
+    }
+  }
+  return RKV_REF_OK;
+}
+
+/* ------------------------------------------------------------- call 3 -- */
+
+/* [P1] launchApplyRopeWriteKVTreeDecoding: as call 2, but the rotary
+ * position of token s is tokenPosIds[b, s]; the cache slot stays end-S+s,
+ * since tree siblings share a position (R6). */
+int rkv_ref_tree(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                 int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                 const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
+                 int32_t head_dim, uint16_t* cache, int32_t capacity, uint16_t* q_out,
+                 int32_t style) {
+  if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
+                 head_dim, cache, capacity, style) ||
+      !end_lens || !pos_ids || !q_out)
+    return RKV_REF_ERR_ARG;
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int32_t s = 0; s < seq_len; ++s) {
+      int64_t slot = (int64_t)end_lens[b] - seq_len + s;
+      int64_t pos = pos_ids[(size_t)b * seq_len + s];
+      if (slot < 0 || slot >= capacity || pos < 0 || pos >= table_len) continue;
+      const float* row = table_row(cos_sin, table_batch, table_len, rotary_dim, b, (int32_t)pos);
+      write_token(row, qkv, b, s, (int32_t)slot, seq_len, hq, hkv, head_dim, rotary_dim, cache,
+                  capacity, q_out, style);
+    }
+  }
+  return RKV_REF_OK;
+}
+
+/* ------------------------------------------------------------- call 4 -- */
+
+/* [P3] launchDFlashTargetKVCacheUpdate.  Delta row i belongs to sequence
+ * delta_to_seq[i] at absolute position delta_positions[i]; either negative
+ * marks padding (R11), a sequence >= batch is inactive (R12), and a position
+ * beyond max_pages_per_seq pages is skipped.  The position's logical page
+ * p/64 is looked up per plane in page_table[seq, plane, :]; the ids are
+ * canonical, so the pool reads as [2*numPages][64][Hkv][D] and the K (V)
+ * plane writes only ids in its own range (R13).  K is rotated with row i of
+ * token_cos_sin; V is copied bit for bit. */
+int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
+                        const float* token_cos_sin, const int32_t* delta_positions,
+                        const int32_t* delta_to_seq, const int32_t* page_table,
+                        int32_t num_delta, int32_t batch, int32_t hkv, int32_t head_dim,
+                        int32_t rotary_dim, int32_t num_pages, int32_t max_pages_per_seq,
+                        int32_t style) {
+  if (!k_delta || !v_delta || !pool || !token_cos_sin || !delta_positions || !delta_to_seq ||
+      !page_table)
+    return RKV_REF_ERR_ARG;
+  if (num_delta < 0 || batch < 0 || hkv < 0 || num_pages < 0 || max_pages_per_seq < 0)
+    return RKV_REF_ERR_ARG;
+  if (head_dim <= 0 || head_dim > 4096 || rotary_dim < 0 || rotary_dim > head_dim ||
+      (rotary_dim & 1))
+    return RKV_REF_ERR_ARG;
+  if (style != RKV_REF_NEOX && style != RKV_REF_GPTJ) return RKV_REF_ERR_ARG;
+  const int64_t TPP = RKV_REF_TOKENS_PER_PAGE;
+  int32_t D = head_dim;
+  for (int32_t i = 0; i < num_delta; ++i) {
+    int64_t p = delta_positions[i];
+    int64_t q = delta_to_seq[i];
+    if (p < 0 || q < 0) continue;                       /* padding */
+    if (q >= batch) continue;                           /* inactive sequence */
+    if (p >= (int64_t)max_pages_per_seq * TPP) continue; /* beyond capacity */
+    int64_t lp = p / TPP, off = p % TPP;
+    int64_t kid = page_table[((size_t)q * 2 + 0) * max_pages_per_seq + lp];
+    int64_t vid = page_table[((size_t)q * 2 + 1) * max_pages_per_seq + lp];
+    const float* row = token_cos_sin + (size_t)i * rotary_dim;
+    if (kid >= 0 && kid < num_pages) {
+      for (int32_t h = 0; h < hkv; ++h)
+        rkv_ref_rotate_row(k_delta + ((size_t)i * hkv + h) * D,
+                           pool + (((size_t)kid * TPP + off) * hkv + h) * D, row, D,
+                           rotary_dim, style);
+    }
+    if (vid >= num_pages && vid < 2 * (int64_t)num_pages) {
+      for (int32_t h = 0; h < hkv; ++h)
+        memcpy(pool + (((size_t)vid * TPP + off) * hkv + h) * D,
+               v_delta + ((size_t)i * hkv + h) * D, (size_t)D * sizeof(uint16_t));
+    }
+  }
+  return RKV_REF_OK;
+}
+
+/* [P3] checkDFlashRopeCapacity: the table may be shorter than the padded
+ * capacity; only a table longer than the capacity is rejected (R17). */
+int rkv_ref_check_rope_capacity(int32_t cos_sin_len, int32_t kv_capacity) {
+  return cos_sin_len > kv_capacity ? RKV_REF_ERR_CAPACITY : RKV_REF_OK;
+}

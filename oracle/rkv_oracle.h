@@ -1,0 +1,75 @@
+/* CPU oracle for the fused RoPE + KV-cache write -- TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, single-threaded C.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code, header or
+ * constant with the HIP library and the HIP library never calls it.
+ *
+ * All arrays are host memory in dense row-major order.  fp16 values are
+ * passed as uint16_t IEEE binary16 bit patterns; tables are fp32.
+ * Every function returns RKV_REF_OK (0) or a nonzero RKV_REF_ERR_* code and
+ * writes nothing when it returns an error.
+ */
+#ifndef RKV_ORACLE_H
+#define RKV_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RKV_REF_OK = 0,
+  RKV_REF_ERR_ARG = 1,      /* null pointer, negative size, bad style, inconsistent shape */
+  RKV_REF_ERR_CAPACITY = 2  /* positions do not fit the cache or the cos/sin table */
+};
+
+enum { RKV_REF_NEOX = 0, RKV_REF_GPTJ = 1 };
+
+#define RKV_REF_TOKENS_PER_PAGE 64
+
+/* exact binary16 -> binary64 */
+double rkv_ref_half_to_double(uint16_t h);
+/* binary64 -> binary16, round to nearest, ties to even, with subnormals */
+uint16_t rkv_ref_double_to_half(double x);
+
+/* Rotate one head row x[0:D] with one table row [cos(R/2) | sin(R/2)];
+ * y may equal x.  Dims d >= R are copied bit for bit. */
+void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* cos_sin_row,
+                        int32_t head_dim, int32_t rotary_dim, int32_t style);
+
+/* Call 1: empty-cache prefill on packed QKV, in place. */
+int rkv_ref_packed_qkv(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                       int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       uint16_t* kv_cache, int32_t capacity, int32_t style);
+
+/* Call 2: continuous write ending at end_lens[b]; rotated Q goes to q_out. */
+int rkv_ref_continuous(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                       int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                       int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, uint16_t* kv_cache,
+                       int32_t capacity, uint16_t* q_out, int32_t style);
+
+/* Call 3: tree-decoding write; slot from end_lens, rotary position from pos_ids. */
+int rkv_ref_tree(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                 int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                 const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, uint16_t* kv_cache,
+                 int32_t capacity, uint16_t* q_out, int32_t style);
+
+/* Call 4: paged delta update through a page table. */
+int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
+                        const float* token_cos_sin, const int32_t* delta_positions,
+                        const int32_t* delta_to_seq, const int32_t* page_table,
+                        int32_t num_delta, int32_t batch, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t rotary_dim, int32_t num_pages,
+                        int32_t max_pages_per_seq, int32_t style);
+
+/* Capacity check: RKV_REF_ERR_CAPACITY iff cos_sin_len > kv_capacity. */
+int rkv_ref_check_rope_capacity(int32_t cos_sin_len, int32_t kv_capacity);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

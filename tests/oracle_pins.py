@@ -1,0 +1,621 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes an oracle library handle ``L`` and raises
+``AssertionError`` when the oracle disagrees with an independent fact:
+
+* fp16 conversion against numpy's IEEE conversions (a library routine) and
+  against values worked out by hand;
+* the rotate-half examples printed in sglang rope_cache.py
+  (``tests/golden/rotate_half_page2.txt``);
+* the rotation against three independent formulations: the page's own
+  sign-mask-and-flip description (_get_neox_rotated_x / _get_gptj_rotated_x /
+  _unit_rope), complex multiplication ``(x_u + i x_v) * e^{i theta}``, and an
+  explicit D x D block-rotation matrix;
+* invariants: angle 0 is the identity, each pair keeps its norm, q.k after
+  rotation depends only on the position difference, rotating back undoes the
+  rotation, GPT-J is NeoX under the pair permutation;
+* layout and indexing by brute-force decoding: V payloads that encode
+  (b, s, h) are located by scanning the whole cache;
+* bit-exact copies of all 65,536 fp16 patterns, untouched-slot sentinels,
+  cross-call reductions, skip rules case by case, the capacity truth table
+  (``tests/golden/capacity_check.txt``).
+
+``tests/test_oracle_pins.py`` runs every pin against the oracle;
+``tests/test_oracle_mutations.py`` plants mistakes into a copy of the oracle
+source and checks that some pin fails for each.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NEOX, GPTJ = W.NEOX, W.GPTJ
+
+
+def f16(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def val(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _row(R, angles):
+    half = R // 2
+    row = np.empty(R, dtype=np.float32)
+    row[:half] = np.cos(angles)
+    row[half:] = np.sin(angles)
+    return row
+
+
+def _rand_angles(r, half):
+    return r.uniform(-40.0, 40.0, size=half)
+
+
+# ------------------------------------------------------------------ fp16 --
+
+def pin_half_to_double_all_patterns(L):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b), L) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_double_to_half_round_trip(L):
+    for b in range(1 << 16):
+        e = (b >> 10) & 0x1F
+        if e == 31 and (b & 0x3FF):
+            got = oracle.double_to_half(oracle.half_to_double(b, L), L)
+            assert (got & 0x7C00) == 0x7C00 and (got & 0x3FF), hex(b)
+            continue
+        got = oracle.double_to_half(val(b).item(), L)
+        assert got == b, (hex(b), hex(got))
+
+
+def pin_double_to_half_vs_numpy(L):
+    r = np.random.default_rng(7)
+    xs = [r.standard_normal(20000) * 10.0 ** r.uniform(-9, 5, 20000)]
+    # exact midpoints between neighbouring fp16 values and points just off them
+    h = np.arange(0, 0x7BFF, 7, dtype=np.uint16)
+    lo, hi = val(h), val(h + 1)
+    mid = (lo + hi) / 2.0
+    xs += [mid, -mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)]
+    xs.append(np.array([65504.0, 65519.99, 65520.0, 65536.0, 1e300, 2.0 ** -24, 2.0 ** -25,
+                        2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25,
+                        2.0 ** -14 - 2.0 ** -26, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 0.0, -0.0,
+                        1e-300, -1e-300]))
+    x = np.concatenate(xs)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.double_to_half(float(v), L) for v in x], dtype=np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(x[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def pin_double_to_half_hand_values(L):
+    # values worked out from the binary16 definition
+    cases = {1.0: 0x3C00, -2.0: 0xC000, 65504.0: 0x7BFF, 65520.0: 0x7C00, 2.0 ** -24: 0x0001,
+             2.0 ** -14: 0x0400, 1.0 + 2.0 ** -11: 0x3C00, 1.0 + 3 * 2.0 ** -11: 0x3C02,
+             2.0 ** -25: 0x0000, 3 * 2.0 ** -25: 0x0002, 0.333251953125: 0x3555}
+    for x, b in cases.items():
+        assert oracle.double_to_half(x, L) == b, (x, hex(oracle.double_to_half(x, L)), hex(b))
+
+
+# ---------------------------------------------------------------- rotate --
+
+def pin_golden_rotate_half(L):
+    path = os.path.join(GOLDEN, "rotate_half_page2.txt")
+    n = 0
+    for line in open(path):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        style = NEOX if line[0] == "neox" else GPTJ
+        c, s = float(line[1]), float(line[2])
+        x = [float(v) for v in line[3:7]]
+        want = [float(v) for v in line[7:11]]
+        row = np.array([c, c, s, s], dtype=np.float32)
+        y = oracle.rotate_row(f16(x), row, 4, style, L)
+        assert np.array_equal(val(y), np.array(want)), (line, val(y))
+        n += 1
+    assert n >= 8
+
+
+def _page2_rotate(x_bits, row, R, style):
+    """The page's formulation: y = x*cos + rotate(x)*sin, with rotate built
+    by a sign mask and flips, cos/sin expanded per element from the
+    half-width table; evaluated in float64 and rounded by numpy."""
+    x = val(x_bits)
+    D = x.size
+    xr = x[:R]
+    d = np.arange(R)
+    if style == NEOX:
+        mask = d < R // 2
+        t = np.where(mask, xr, -xr).reshape(2, R // 2)[:, ::-1].reshape(R)[::-1]
+        dc = np.where(d >= R // 2, d - R // 2, d)
+    else:
+        mask = d % 2 == 0
+        t = np.where(mask, xr, -xr).reshape(R // 2, 2)[:, ::-1].reshape(R)
+        dc = d // 2
+    cos = row[dc].astype(np.float64)
+    sin = row[dc + R // 2].astype(np.float64)
+    y = np.concatenate([xr * cos + t * sin, x[R:]]) if R < D else xr * cos + t * sin
+    out = f16(y)
+    out[R:] = x_bits[R:]
+    return out
+
+
+def pin_page2_formulation(L):
+    r = np.random.default_rng(11)
+    for D, R in [(64, 64), (128, 128), (128, 64), (256, 96), (16, 8), (4, 4)]:
+        for style in (NEOX, GPTJ):
+            for _ in range(20):
+                x = W.normal_f16(r, (D,))
+                row = _row(R, _rand_angles(r, R // 2))
+                got = oracle.rotate_row(x, row, R, style, L)
+                want = _page2_rotate(x, row, R, style)
+                assert np.array_equal(got, want), (D, R, style)
+
+
+def pin_complex_multiplication(L):
+    r = np.random.default_rng(12)
+    for D, R in [(128, 128), (64, 32)]:
+        for style in (NEOX, GPTJ):
+            x = W.normal_f16(r, (D,))
+            row = _row(R, _rand_angles(r, R // 2))
+            half = R // 2
+            xv = val(x)
+            if style == NEOX:
+                re, im = xv[:half], xv[half:R]
+            else:
+                re, im = xv[0:R:2], xv[1:R:2]
+            w = (re + 1j * im) * (row[:half].astype(np.float64) + 1j * row[half:].astype(np.float64))
+            got = val(oracle.rotate_row(x, row, R, style, L))
+            if style == NEOX:
+                g_re, g_im = got[:half], got[half:R]
+            else:
+                g_re, g_im = got[0:R:2], got[1:R:2]
+            assert np.array_equal(f16(w.real), f16(g_re))
+            assert np.array_equal(f16(w.imag), f16(g_im))
+            assert np.array_equal(oracle.rotate_row(x, row, R, style, L)[R:], x[R:])
+
+
+def _rotation_matrix(row, D, R, style):
+    half = R // 2
+    M = np.eye(D)
+    for i in range(half):
+        u, v = (i, i + half) if style == NEOX else (2 * i, 2 * i + 1)
+        c, s = float(row[i]), float(row[half + i])
+        M[u, u], M[u, v], M[v, u], M[v, v] = c, -s, s, c
+    return M
+
+
+def pin_brute_force_matrix(L):
+    """Two tokens at two positions, rotated by an explicit D x D matrix."""
+    r = np.random.default_rng(13)
+    D = 64
+    for R in (64, 48):
+        for style in (NEOX, GPTJ):
+            table = W.rope_table(1, 64, R, 10000.0)[0]
+            for pos in (5, 63):
+                x = W.normal_f16(r, (D,))
+                M = _rotation_matrix(table[pos], D, R, style)
+                want = f16(M @ val(x))
+                got = oracle.rotate_row(x, table[pos], R, style, L)
+                assert np.array_equal(got, want), (R, style, pos)
+
+
+def pin_identity_at_position_zero(L):
+    r = np.random.default_rng(14)
+    table = W.rope_table(1, 4, 128, 10000.0)[0]
+    for style in (NEOX, GPTJ):
+        x = W.normal_f16(r, (128,))
+        y = oracle.rotate_row(x, table[0], 128, style, L)
+        assert np.array_equal(val(y), val(x))   # value equality: -0 may become +0
+
+
+def pin_pair_norm(L):
+    r = np.random.default_rng(15)
+    R = 128
+    table = W.rope_table(1, 4096, R, 10000.0)[0]
+    for style in (NEOX, GPTJ):
+        for pos in (1, 17, 1000, 4095):
+            x = W.normal_f16(r, (R,))
+            y = oracle.rotate_row(x, table[pos], R, style, L)
+            xv, yv = val(x), val(y)
+            if style == NEOX:
+                nx = xv[:64] ** 2 + xv[64:] ** 2
+                ny = yv[:64] ** 2 + yv[64:] ** 2
+            else:
+                nx = xv[0::2] ** 2 + xv[1::2] ** 2
+                ny = yv[0::2] ** 2 + yv[1::2] ** 2
+            assert np.all(np.abs(ny - nx) <= 2.0 ** -9 * nx + 2.0 ** -22), (style, pos)
+
+
+def pin_relative_position(L):
+    r = np.random.default_rng(16)
+    R = 128
+    table = W.rope_table(1, 8192, R, 10000.0)[0]
+    for style in (NEOX, GPTJ):
+        for m, n, delta in [(5, 3, 100), (700, 20, 3000), (4000, 4000, 17), (1, 900, 6000)]:
+            q = W.normal_f16(r, (R,))
+            k = W.normal_f16(r, (R,))
+            a = val(oracle.rotate_row(q, table[m], R, style, L)) @ \
+                val(oracle.rotate_row(k, table[n], R, style, L))
+            b = val(oracle.rotate_row(q, table[m + delta], R, style, L)) @ \
+                val(oracle.rotate_row(k, table[n + delta], R, style, L))
+            bound = 4 * 2.0 ** -11 * np.linalg.norm(val(q)) * np.linalg.norm(val(k))
+            assert abs(a - b) <= bound, (style, m, n, delta, a, b)
+
+
+def pin_inverse_rotation(L):
+    r = np.random.default_rng(17)
+    R = 64
+    for style in (NEOX, GPTJ):
+        row = _row(R, _rand_angles(r, R // 2))
+        back = row.copy()
+        back[R // 2:] = -back[R // 2:]
+        x = W.normal_f16(r, (R,))
+        z = oracle.rotate_row(oracle.rotate_row(x, row, R, style, L), back, R, style, L)
+        xv, zv = val(x), val(z)
+        # each rounding errs by at most half an fp16 ulp of a pair member,
+        # whose size is bounded by the pair's norm
+        partner = (np.arange(R) + R // 2) % R if style == NEOX else np.arange(R) ^ 1
+        pair = np.hypot(xv, xv[partner])
+        assert np.all(np.abs(zv - xv) <= 2.0 ** -9 * pair + 2.0 ** -23), style
+
+
+def pin_gptj_is_permuted_neox(L):
+    r = np.random.default_rng(18)
+    for D, R in [(128, 128), (128, 64)]:
+        row = _row(R, _rand_angles(r, R // 2))
+        x = W.normal_f16(r, (D,))
+        half = R // 2
+        perm = np.arange(D)
+        perm[:half] = np.arange(0, R, 2)          # NeoX slot i <- GPT-J slot 2i
+        perm[half:R] = np.arange(1, R, 2)         # NeoX slot i+R/2 <- GPT-J slot 2i+1
+        y_neox = oracle.rotate_row(x[perm], row, R, NEOX, L)
+        y = np.empty_like(y_neox)
+        y[perm] = y_neox
+        assert np.array_equal(y, oracle.rotate_row(x, row, R, GPTJ, L)), (D, R)
+
+
+def pin_passthrough_bits(L):
+    """Dims >= R keep every one of the 65,536 bit patterns."""
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    D, R = 128, 64
+    rows = allbits.reshape(-1, D - R)
+    r = np.random.default_rng(19)
+    row = _row(R, _rand_angles(r, R // 2))
+    for style in (NEOX, GPTJ):
+        for k in range(0, rows.shape[0], 37):
+            x = np.concatenate([W.normal_f16(r, (R,)), rows[k]])
+            y = oracle.rotate_row(x, row, R, style, L)
+            assert np.array_equal(y[R:], rows[k])
+
+
+# ----------------------------------------------------------------- calls --
+
+def _code_rows(n, D):
+    """n distinct finite positive fp16 payload rows (all D elements equal)."""
+    codes = (0x0400 + np.arange(n)).astype(np.uint16)
+    assert codes.max() < 0x7C00
+    return np.repeat(codes[:, None], D, axis=1), codes
+
+
+def pin_v_copy_all_patterns(L):
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    B, S, Hq, Hkv, D = 1, 64, 1, 16, 64     # 64 tokens x 16 V heads x 64 dims
+    qkv = np.zeros((B, S, Hq + 2 * Hkv, D), dtype=np.uint16)
+    qkv[0, :, Hq + Hkv:, :] = allbits.reshape(S, Hkv, D)
+    table = W.rope_table(1, S, D, 10000.0)
+    cache = W.sentinel_f16((B, 2, Hkv, S, D))
+    q2, c2 = oracle.packed_qkv(table, qkv, cache, NEOX, L)
+    assert np.array_equal(c2[0, 1].transpose(1, 0, 2), allbits.reshape(S, Hkv, D))
+    assert np.array_equal(q2[0, :, Hq + Hkv:], qkv[0, :, Hq + Hkv:])   # V unchanged in place
+
+
+def pin_layout_packed(L):
+    """Call 1 with R = 0 (no rotation): decode where every K and V row landed."""
+    B, S, Hq, Hkv, D, cap = 2, 5, 3, 2, 16, 8
+    H = Hq + 2 * Hkv
+    rows, codes = _code_rows(B * S * H, D)
+    qkv = rows.reshape(B, S, H, D).copy()
+    table = np.zeros((1, cap, 0), dtype=np.float32)
+    cache = W.sentinel_f16((B, 2, Hkv, cap, D))
+    q2, c2 = oracle.packed_qkv(table, qkv, cache, NEOX, L)
+    assert np.array_equal(q2, qkv)
+    seen = set()
+    for b in range(B):
+        for plane in range(2):
+            for h in range(Hkv):
+                for slot in range(cap):
+                    v = c2[b, plane, h, slot]
+                    if slot >= S:
+                        assert np.all(v == W.SENTINEL), (b, plane, h, slot)
+                        continue
+                    assert np.all(v == v[0])
+                    idx = int(v[0]) - 0x0400
+                    bb, rest = divmod(idx, S * H)
+                    ss, hh = divmod(rest, H)
+                    assert (bb, ss) == (b, slot), (b, plane, h, slot, bb, ss)
+                    assert hh == Hq + plane * Hkv + h, (hh, plane, h)
+                    seen.add(idx)
+    assert len(seen) == B * S * 2 * Hkv
+
+
+def pin_layout_continuous_and_tree(L):
+    B, S, Hq, Hkv, D, cap = 3, 4, 2, 2, 16, 12
+    H = Hq + 2 * Hkv
+    rows, _ = _code_rows(B * S * H, D)
+    qkv = rows.reshape(B, S, H, D).copy()
+    end = np.array([4, 12, 7], dtype=np.int32)
+    table = np.zeros((1, cap, 0), dtype=np.float32)
+    for call in ("continuous", "tree"):
+        cache = W.sentinel_f16((B, 2, Hkv, cap, D))
+        q_out = W.sentinel_f16((B, S, Hq, D))
+        if call == "continuous":
+            c2, qo = oracle.continuous(table, end, qkv, cache, q_out, NEOX, L)
+        else:
+            pos = np.tile(np.array([0, 1, 1, 2], dtype=np.int32), (B, 1))
+            c2, qo = oracle.tree(table, end, pos, qkv, cache, q_out, GPTJ, L)
+        assert np.array_equal(qo, qkv[:, :, :Hq])
+        for b in range(B):
+            for plane in range(2):
+                for h in range(Hkv):
+                    for slot in range(cap):
+                        v = c2[b, plane, h, slot]
+                        if not (end[b] - S <= slot < end[b]):
+                            assert np.all(v == W.SENTINEL), (call, b, plane, h, slot)
+                            continue
+                        idx = int(v[0]) - 0x0400
+                        bb, rest = divmod(idx, S * H)
+                        ss, hh = divmod(rest, H)
+                        assert (bb, ss + end[b] - S) == (b, slot), (call, b, slot, bb, ss)
+                        assert hh == Hq + plane * Hkv + h
+
+
+def pin_layout_paged(L):
+    N, batch, Hkv, D, P, M = 6, 3, 2, 16, 5, 3
+    rows, _ = _code_rows(N * Hkv, D)
+    v_delta = rows.reshape(N, Hkv, D).copy()
+    k_delta = rows.reshape(N, Hkv, D).copy() + np.uint16(0x1000)
+    pos = np.array([0, 63, 64, 130, 5, 191], dtype=np.int32)
+    seq = np.array([0, 0, 1, 1, 2, 2], dtype=np.int32)
+    pt = np.empty((batch, 2, M), dtype=np.int32)
+    pt[:, 0, :] = np.array([[4, 0, 1], [2, 3, 0], [1, 2, 3]])
+    pt[:, 1, :] = P + np.array([[1, 2, 3], [0, 4, 2], [3, 1, 0]])
+    pool = W.sentinel_f16((2, P, 64, Hkv, D))
+    cs = np.zeros((N, 0), dtype=np.float32)
+    out = oracle.paged_delta(k_delta, v_delta, pool, cs, pos, seq, pt, batch, NEOX, L)
+    flat = out.reshape(2 * P, 64, Hkv, D)
+    written = 0
+    for pid in range(2 * P):
+        for off in range(64):
+            for h in range(Hkv):
+                v = flat[pid, off, h]
+                if np.all(v == W.SENTINEL):
+                    continue
+                written += 1
+                code = int(v[0])
+                is_k = code >= 0x1400
+                i, hh = divmod(code - (0x1400 if is_k else 0x0400), Hkv)
+                plane = 0 if is_k else 1
+                assert hh == h
+                assert pid == pt[seq[i], plane, pos[i] // 64], (i, plane, pid)
+                assert off == pos[i] % 64
+    assert written == 2 * N * Hkv
+
+
+def pin_untouched_and_in_place_k(L):
+    w = W.packed(2, 7, 3, 2, 64, 64, 16, GPTJ, 99, table_batch=2, table_len=9,
+                 offsets=np.array([0, 3]))
+    q2, c2 = oracle.packed_qkv(w.cos_sin, w.qkv, w.cache, w.style, L)
+    assert np.all(c2[:, :, :, w.S:] == W.SENTINEL)
+    # K in place == K in the cache, bitwise
+    k_inplace = q2[:, :, w.Hq:w.Hq + w.Hkv].transpose(0, 2, 1, 3)
+    assert np.array_equal(k_inplace, c2[:, 0, :, :w.S])
+    # Q and K changed, V not
+    assert not np.array_equal(q2[:, :, :w.Hq + w.Hkv], w.qkv[:, :, :w.Hq + w.Hkv])
+    assert np.array_equal(q2[:, :, w.Hq + w.Hkv:], w.qkv[:, :, w.Hq + w.Hkv:])
+    # each head row equals the row rotation at (table batch b, position s)
+    for b in range(w.B):
+        for s in range(w.S):
+            for h in range(w.Hq + w.Hkv):
+                want = oracle.rotate_row(w.qkv[b, s, h], w.cos_sin[b, s], w.R, w.style, L)
+                assert np.array_equal(q2[b, s, h], want), (b, s, h)
+
+
+def pin_cross_call_reductions(L):
+    r = np.random.default_rng(20)
+    B, S, Hq, Hkv, D, cap = 2, 6, 4, 2, 64, 10
+    for style in (NEOX, GPTJ):
+        qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+        table = W.rope_table(1, cap, D, 10000.0)
+        cache = W.sentinel_f16((B, 2, Hkv, cap, D))
+        q1, c1 = oracle.packed_qkv(table, qkv, cache, style, L)
+        end = np.full(B, S, dtype=np.int32)
+        c2, qo2 = oracle.continuous(table, end, qkv, cache, W.sentinel_f16((B, S, Hq, D)),
+                                    style, L)
+        assert np.array_equal(c1, c2)
+        assert np.array_equal(q1[:, :, :Hq], qo2)
+        # a linear chain of tree positions is the continuous write
+        end = np.array([7, 10], dtype=np.int32)
+        c2, qo2 = oracle.continuous(table, end, qkv, cache, W.sentinel_f16((B, S, Hq, D)),
+                                    style, L)
+        pos = (end[:, None] - S + np.arange(S)[None, :]).astype(np.int32)
+        c3, qo3 = oracle.tree(table, end, pos, qkv, cache, W.sentinel_f16((B, S, Hq, D)),
+                              style, L)
+        assert np.array_equal(c2, c3) and np.array_equal(qo2, qo3)
+        # the paged update through an identity page table is the continuous K/V write
+        TPP = 64
+        M = 1
+        P = B
+        pt = np.empty((B, 2, M), dtype=np.int32)
+        pt[:, 0, 0] = np.arange(B)
+        pt[:, 1, 0] = P + np.arange(B)
+        N = B * S
+        k_delta = qkv[:, :, Hq:Hq + Hkv].reshape(N, Hkv, D)
+        v_delta = qkv[:, :, Hq + Hkv:].reshape(N, Hkv, D)
+        posd = pos.reshape(-1).astype(np.int32)
+        seqd = np.repeat(np.arange(B), S).astype(np.int32)
+        rows = table[0][posd]
+        pool = W.sentinel_f16((2, P, TPP, Hkv, D))
+        pool = oracle.paged_delta(k_delta, v_delta, pool, rows, posd, seqd, pt, B, style, L)
+        for b in range(B):
+            for plane in range(2):
+                got = pool[plane, b, :cap].transpose(1, 0, 2)     # [Hkv, cap, D]
+                assert np.array_equal(got, c2[b, plane]), (style, b, plane)
+
+
+def pin_skip_rules_contiguous(L):
+    """Calls 2 and 3: a token whose slot or position is out of range writes
+    nothing; its neighbours still write."""
+    r = np.random.default_rng(21)
+    B, S, Hq, Hkv, D, cap, tlen = 4, 3, 2, 1, 16, 6, 5
+    qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+    table = W.rope_table(1, tlen, D, 10000.0)
+    end = np.array([2, 7, 6, 3], dtype=np.int32)   # slots: [-1,0,1] [4,5,6] [3,4,5] [0,1,2]
+    cache = W.sentinel_f16((B, 2, Hkv, cap, D))
+    qo0 = W.sentinel_f16((B, S, Hq, D))
+    c2, qo = oracle.continuous(table, end, qkv, cache, qo0, NEOX, L)
+    wrote = ~np.all(qo == W.SENTINEL, axis=(2, 3))
+    # call 2 requires slot in [0, cap) and position (= slot) in [0, tlen)
+    want = np.array([[0, 1, 1], [1, 0, 0], [1, 1, 0], [1, 1, 1]], dtype=bool)
+    assert np.array_equal(wrote, want), wrote
+    for b in range(B):
+        for s in range(S):
+            slot = end[b] - S + s
+            if 0 <= slot < cap:
+                assert np.all(c2[b, :, :, slot] == W.SENTINEL) != want[b, s]
+    pos = np.array([[0, 4, 5], [-1, 0, 1], [2, 2, 9], [4, 4, 4]], dtype=np.int32)
+    c3, qo = oracle.tree(table, end, pos, qkv, cache, qo0, NEOX, L)
+    wrote = ~np.all(qo == W.SENTINEL, axis=(2, 3))
+    # call 3 requires slot in [0, cap) and position in [0, tlen)
+    want = np.array([[0, 1, 0], [0, 1, 0], [1, 1, 0], [1, 1, 1]], dtype=bool)
+    assert np.array_equal(wrote, want), wrote
+
+
+def pin_skip_rules_paged(L):
+    """Call 4, one row at a time through every skip reason."""
+    batch, Hkv, D, P, M, R = 2, 1, 16, 4, 2, 16
+    r = np.random.default_rng(22)
+    k = W.normal_f16(r, (1, Hkv, D))
+    v = W.normal_f16(r, (1, Hkv, D))
+    cs = W.rope_rows([70], R, 10000.0)
+    pool0 = W.sentinel_f16((2, P, 64, Hkv, D))
+
+    def run(pos, seq, kid, vid):
+        pt = np.zeros((batch, 2, M), dtype=np.int32)
+        pt[:, 0, :] = 1
+        pt[:, 1, :] = P + 1
+        if 0 <= seq < batch and 0 <= pos < M * 64:
+            pt[seq, 0, pos // 64] = kid
+            pt[seq, 1, pos // 64] = vid
+        out = oracle.paged_delta(k, v, pool0, cs, np.array([pos], np.int32),
+                                 np.array([seq], np.int32), pt, batch, NEOX, L)
+        flat = out.reshape(2 * P, 64, Hkv, D)
+        changed = np.argwhere(~np.all(flat == pool0.reshape(2 * P, 64, Hkv, D), axis=(2, 3)))
+        return {(int(a), int(b)) for a, b in changed}
+
+    ok_k, ok_v = 2, P + 3
+    assert run(70, 1, ok_k, ok_v) == {(ok_k, 6), (ok_v, 6)}
+    assert run(-1, 1, ok_k, ok_v) == set()             # padding position
+    assert run(70, -1, ok_k, ok_v) == set()            # padding sequence
+    assert run(-5, -5, ok_k, ok_v) == set()
+    assert run(70, 2, ok_k, ok_v) == set()             # sequence beyond the active batch
+    assert run(128, 1, ok_k, ok_v) == set()            # position beyond maxPagesPerSeq pages
+    assert run(127, 1, ok_k, ok_v) == {(ok_k, 63), (ok_v, 63)}   # last writable position
+    assert run(70, 1, -1, ok_v) == {(ok_v, 6)}         # unmapped K page
+    assert run(70, 1, P, ok_v) == {(ok_v, 6)}          # K entry in the V plane
+    assert run(70, 1, 2 * P, ok_v) == {(ok_v, 6)}      # beyond both planes
+    assert run(70, 1, ok_k, -1) == {(ok_k, 6)}         # unmapped V page
+    assert run(70, 1, ok_k, P - 1) == {(ok_k, 6)}      # V entry in the K plane
+    assert run(70, 1, ok_k, 2 * P) == {(ok_k, 6)}      # beyond both planes
+    assert run(70, 1, 0, P) == {(0, 6), (P, 6)}        # lowest valid id of each plane
+    assert run(70, 1, P - 1, 2 * P - 1) == {(P - 1, 6), (2 * P - 1, 6)}   # highest
+    assert run(70, 1, -1, -1) == set()
+    # position == maxPagesPerSeq * 64 for sequence 0: the int32 entries that
+    # follow its last logical page in memory hold ids that are valid for the
+    # plane being read, so any read past the page row would show as a write
+    pt = np.zeros((batch, 2, M), dtype=np.int32)
+    pt[:, 0, :] = 1
+    pt[:, 1, :] = P + 1
+    pt[0, 1, 0] = 2          # read by K at logical page M of sequence 0
+    pt[1, 0, 0] = P + 2      # read by V at logical page M of sequence 0
+    out = oracle.paged_delta(k, v, pool0, cs, np.array([M * 64], np.int32),
+                             np.array([0], np.int32), pt, batch, NEOX, L)
+    assert np.array_equal(out, pool0)
+
+
+def pin_paged_values(L):
+    """A written K page row is the rotated delta row with its own table row;
+    a written V page row is the delta row, bit for bit."""
+    w = W.paged(64, 4, 2, 64, 32, 16, 4, GPTJ, 23, width=16, pool_fill="sentinel")
+    out = oracle.paged_delta(w.k_delta, w.v_delta, w.pool, w.cos_sin, w.positions, w.seq,
+                             w.page_table, w.batch, w.style, L)
+    flat = out.reshape(2 * w.num_pages, 64, w.Hkv, w.D)
+    n_k = n_v = 0
+    for i in range(w.N):
+        p, q = int(w.positions[i]), int(w.seq[i])
+        if p < 0 or q < 0:
+            continue
+        kid = int(w.page_table[q, 0, p // 64])
+        vid = int(w.page_table[q, 1, p // 64])
+        if 0 <= kid < w.num_pages:
+            n_k += 1
+            for h in range(w.Hkv):
+                want = oracle.rotate_row(w.k_delta[i, h], w.cos_sin[i], w.R, w.style, L)
+                assert np.array_equal(flat[kid, p % 64, h], want)
+        if w.num_pages <= vid < 2 * w.num_pages:
+            n_v += 1
+            assert np.array_equal(flat[vid, p % 64], w.v_delta[i])
+    assert n_k > 10 and n_v > 10
+
+
+def pin_capacity_truth_table(L):
+    n = 0
+    for line in open(os.path.join(GOLDEN, "capacity_check.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        a, b, want = int(line[0]), int(line[1]), line[2]
+        rc = oracle.check_rope_capacity(a, b, L)
+        assert (rc == 0) == (want == "ok"), (a, b, rc)
+        n += 1
+    assert n >= 10
+
+
+def pin_argument_errors(L):
+    t = W.rope_table(1, 8, 16, 10000.0)
+    qkv = np.zeros((1, 4, 4, 16), np.uint16)
+    cache = np.zeros((1, 2, 1, 8, 16), np.uint16)
+    # S > capacity or S > table length: capacity error
+    try:
+        oracle.packed_qkv(t, qkv, np.zeros((1, 2, 1, 3, 16), np.uint16), NEOX, L)
+        raise AssertionError("S > cap accepted")
+    except oracle.OracleError as e:
+        assert e.code == oracle.ERR_CAPACITY
+    try:
+        oracle.packed_qkv(W.rope_table(1, 3, 16, 1e4), qkv, cache, NEOX, L)
+        raise AssertionError("S > table length accepted")
+    except oracle.OracleError as e:
+        assert e.code == oracle.ERR_CAPACITY
+    for bad in [dict(t=W.rope_table(2, 8, 16, 1e4)), dict(style=2), dict(t=np.zeros((1, 8, 15), np.float32)),
+                dict(t=np.zeros((1, 8, 18), np.float32))]:
+        try:
+            oracle.packed_qkv(bad.get("t", t), qkv, cache, bad.get("style", NEOX), L)
+            raise AssertionError(f"accepted {bad}")
+        except oracle.OracleError as e:
+            assert e.code == oracle.ERR_ARG
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
