@@ -1,0 +1,270 @@
+"""Benchmark of the fused RoPE + KV-cache write on one MI355X.
+
+A step is one call of the library on the headline workload: empty-cache
+prefill of packed QKV in place, B=4, S=8192, Hq=64, Hkv=8, D=R=128, GPT-J,
+per-sequence cos/sin tables (1.43 GB of algorithmic traffic).  Inputs are
+seeded synthetic data already resident in HBM.  W warm-up steps, then K timed
+steps bracketed by device synchronisation; each launch is also bracketed by
+HIP events on its stream, which give the kernel's average duration for the
+roofline.  The other workloads (continuous write, tree write, paged delta
+update) are timed the same way and reported under "workloads"; the paged
+update's 31 MB of inputs fit the 256 MB MALL, so a 1 GiB buffer is written
+before each of its timed launches to push them back to HBM.
+
+Prints one JSON line on stdout; progress goes to stderr.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+HEADLINE = 5
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------- algorithmic bytes --
+
+def bytes_contig(w) -> int:
+    """Bytes the method must move for calls 1-3: per written token, its packed
+    Q/K/V rows read, Q (and for call 1, K in place) written, K and V cache
+    rows written; each distinct cos/sin row read once; the index arrays."""
+    D, R, Hq, Hkv = w.D, w.R, w.Hq, w.Hkv
+    H = Hq + 2 * Hkv
+    tb, tlen = w.cos_sin.shape[0], w.cos_sin.shape[1]
+    if w.call == "packed":
+        valid = np.ones((w.B, w.S), dtype=bool)
+        slot = pos = np.broadcast_to(np.arange(w.S), (w.B, w.S))
+        write_q = (Hq + Hkv) * D * 2
+        index = 0
+    else:
+        slot = w.end_lens[:, None].astype(np.int64) - w.S + np.arange(w.S)[None, :]
+        pos = slot if w.call == "continuous" else w.pos_ids.astype(np.int64)
+        valid = (slot >= 0) & (slot < w.cap) & (pos >= 0) & (pos < tlen)
+        write_q = Hq * D * 2
+        index = w.B * 4 + (w.B * w.S * 4 if w.call == "tree" else 0)
+    n = int(valid.sum())
+    rows = set()
+    for b in range(w.B):
+        t = 0 if tb == 1 else b
+        rows.update((t, int(p)) for p in np.asarray(pos[b])[valid[b]])
+    per_token = H * D * 2 + write_q + 2 * Hkv * D * 2
+    return n * per_token + len(rows) * R * 4 + index
+
+
+def bytes_paged(w) -> int:
+    """Call 4: per non-skipped row its two page-table entries; per mapped K
+    its delta row read, rotated row written and cos/sin row read; per mapped
+    V its delta row read and written; the two metadata arrays of all rows."""
+    D, R, Hkv, P = w.D, w.R, w.Hkv, w.num_pages
+    p, q = w.positions.astype(np.int64), w.seq.astype(np.int64)
+    live = (p >= 0) & (q >= 0) & (q < w.batch) & (p < w.max_pages * 64)
+    lp = np.where(live, p // 64, 0)
+    qq = np.where(live, q, 0)
+    kid = w.page_table[qq, 0, lp].astype(np.int64)
+    vid = w.page_table[qq, 1, lp].astype(np.int64)
+    k_ok = live & (kid >= 0) & (kid < P)
+    v_ok = live & (vid >= P) & (vid < 2 * P)
+    row = Hkv * D * 2
+    return int(k_ok.sum()) * (2 * row + R * 4) + int(v_ok.sum()) * 2 * row \
+        + w.N * 8 + int(live.sum()) * 8
+
+
+def algorithmic_bytes(w) -> int:
+    import workloads as W
+    return bytes_paged(w) if isinstance(w, W.Paged) else bytes_contig(w)
+
+
+# ----------------------------------------------------------------- timing --
+
+def time_launches(w, t, steps, warmup, flush=None):
+    """Average kernel duration (events around each launch, on the launch
+    stream) and wall time per step between device synchronisations."""
+    import torch
+    from harness import launch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        if flush is not None:
+            flush()
+        launch(w, t)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    wall = 0.0
+    if flush is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            starts[k].record(stream)
+            launch(w, t)
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        for k in range(steps):
+            flush()
+            starts[k].record(stream)
+            launch(w, t)
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+    kernel_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    return kernel_ms, wall
+
+
+def traffic_from_profile(kernel_name: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if the recorded
+    kernel source still matches the current one."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m or not h or h.group(1) != kernel_source_hash():
+        return None
+    return float(m.group(1))
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "rope_kv_cache_amd", "csrc")
+    hsh = hashlib.sha256()
+    for f in ("rkv_kernels.hip", "rkv_rotate.hpp", "rkv_launch.hpp", "rkv_abi.hip"):
+        hsh.update(open(os.path.join(d, f), "rb").read())
+    return hsh.hexdigest()
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The oracle as it is (single-threaded C) on a bounded sample of the
+    headline workload: sequence 0 (8192 tokens, all 80 heads), repeated
+    until the budget is spent."""
+    import oracle
+    sub_qkv = np.ascontiguousarray(w.qkv[:1])
+    sub_tab = np.ascontiguousarray(w.cos_sin[:1])
+    sub_cache = np.ascontiguousarray(w.cache[:1])
+    oracle.lib()
+    n, t_total = 0, 0.0
+    while t_total < budget_s:
+        t0 = time.perf_counter()
+        oracle.packed_qkv(sub_tab, sub_qkv, sub_cache, w.style)
+        t_total += time.perf_counter() - t0
+        n += 1
+    tokens = n * w.S
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0 of the workload ({w.S} tokens x {w.Hq + 2 * w.Hkv} heads), "
+                      f"{n} oracle calls, {t_total:.1f} s, includes the oracle's copies of its "
+                      "inputs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the step "
+              "needs no cross-GPU exchange, so each GPU would run this same kernel on its "
+              "own shard of batches, heads or pages", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from harness import upload
+    import rope_kv_cache_amd  # noqa: F401  (fails loudly if the library is missing)
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    torch.cuda.set_device(0)
+    log(f"[bench] device: {torch.cuda.get_device_name(0)}")
+
+    log("[bench] generating the headline workload")
+    w = W.config(HEADLINE)
+    nbytes = algorithmic_bytes(w)
+    t = upload(w)
+    log(f"[bench] {w.name}: {nbytes / 1e6:.1f} MB algorithmic per launch; timing "
+        f"{args.warmup} + {args.steps} steps")
+    kernel_ms, wall = time_launches(w, t, args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile("contig_packed_prefill_b4_s8192_h64_d128")
+    result = {
+        "metric": "tokens/s and achieved HBM GB/s (% of MI355X peak) for fused RoPE+KV write",
+        "value": w.tokens / (wall / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "call": "packed QKV prefill, in place", "B": w.B,
+                   "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "R": w.R, "style": "gptj",
+                   "io": "fp16 qkv/cache, fp32 cos/sin", "tokens_per_step": w.tokens},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel_us": kernel_ms * 1e3, "algorithmic_bytes": nbytes},
+    }
+    log(f"[bench] headline kernel {kernel_ms * 1e3:.1f} us, {achieved:.0f} GB/s "
+        f"({achieved / PEAK_HBM_GBS:.1%}), {result['value']:.3e} tokens/s")
+    del t
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = {}
+        flush_buf = torch.empty(1 << 29, dtype=torch.float16, device="cuda")   # 1 GiB
+
+        def flush():
+            flush_buf.fill_(1.0)
+
+        cases = [("continuous_neox", lambda: W.config(2, W.NEOX)),
+                 ("continuous_gptj", lambda: W.config(2, W.GPTJ)),
+                 ("tree", lambda: W.config(3)),
+                 ("paged_delta", lambda: W.config(4))]
+        for label, make in cases:
+            log(f"[bench] generating {label}")
+            x = make()
+            xb = algorithmic_bytes(x)
+            tx = upload(x)
+            steps = max(5, min(args.steps, 50))
+            k_ms, _ = time_launches(x, tx, steps, 3, flush=flush)
+            gbs = xb / (k_ms * 1e-3) / 1e9
+            extra[label] = {"workload": x.name, "kernel_us": k_ms * 1e3, "GB/s": gbs,
+                            "frac": gbs / PEAK_HBM_GBS, "tokens_per_s": x.tokens / (k_ms * 1e-3),
+                            "algorithmic_bytes": xb, "mall_flushed": True}
+            log(f"[bench] {label}: {k_ms * 1e3:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%})")
+            del tx, x
+            torch.cuda.empty_cache()
+        del flush_buf
+        result["workloads"] = extra
+
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+        log(f"[bench] cpu oracle {result['cpu_baseline']['value']:.3e} tokens/s")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/* rope_kv_cache.h -- fused rotary position embedding + KV-cache write for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Four device calls follow the
+ * problem statement of TensorRT-Edge-LLM's "Apply Rope Write KV" (calls 1-3)
+ * and "Dflash Runtime Kernels" (call 4) pages; a fifth, host-only call is
+ * that page's capacity check.
+ *
+ * Common conventions
+ * ------------------
+ * Ownership.  Every tensor pointer is a DEVICE pointer owned by the caller.
+ *   The library allocates no device memory, keeps no pointer after a call
+ *   returns and holds no state besides a thread-local error message.
+ * Asynchrony.  A call validates its arguments on the host, enqueues one
+ *   kernel on `stream` and returns without synchronising.  Buffers must stay
+ *   alive until the stream has executed the kernel.  A null stream is the
+ *   default stream.
+ * Layout.  Tensors are dense, row-major, with the shapes stated per call, and
+ *   every data pointer is 16-byte aligned.  fp16 is IEEE binary16.
+ * Aliasing.  Only call 1 updates a tensor in place (`qkv`).  Otherwise no
+ *   output may overlap an input or another output; overlapping buffers are
+ *   rejected with RKV_ERR_ALIAS where the host can see it.
+ * Errors.  Each call returns RKV_OK or an error status and, on error,
+ *   enqueues nothing.  rkv_last_error() describes the last error raised on
+ *   the calling thread.  Index values that live in device memory (end
+ *   lengths, position ids, delta metadata, page ids) are not read by the
+ *   host; the kernels skip rows whose indices fall out of range instead (the
+ *   rules are given per call).
+ * Supported shapes.  headDim in {64, 128, 256}; rotaryDim a multiple of 16
+ *   with 0 <= rotaryDim <= headDim.  Other values return
+ *   RKV_ERR_UNSUPPORTED.
+ * Rotation.  For frequency i < rotaryDim/2 with c = row[i] and
+ *   s = row[rotaryDim/2 + i] of the token's cos/sin row, the pair (u, v)
+ *   becomes (x_u*c - x_v*s, x_v*c + x_u*s), rounded to fp16 to nearest-even.
+ *   NeoX pairs (i, i + rotaryDim/2); GPT-J pairs (2i, 2i+1).  Dims
+ *   >= rotaryDim are copied bit for bit.  (sglang rope_cache.py,
+ *   _get_neox_rotated_x, _get_gptj_rotated_x, _unit_rope, _load_cos_sin.)
+ *   Results equal the products and sum evaluated exactly in binary64 and
+ *   rounded once to binary16.
+ */
+#ifndef ROPE_KV_CACHE_H
+#define ROPE_KV_CACHE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  RKV_OK = 0,
+  RKV_ERR_NULL = 1,         /* a required pointer is null */
+  RKV_ERR_DTYPE = 2,        /* a descriptor has the wrong element type */
+  RKV_ERR_SHAPE = 3,        /* ranks or dimensions are inconsistent */
+  RKV_ERR_UNSUPPORTED = 4,  /* valid but outside the supported shape set */
+  RKV_ERR_CAPACITY = 5,     /* positions cannot fit the cache or the cos/sin table */
+  RKV_ERR_ALIGNMENT = 6,    /* a data pointer is not 16-byte aligned */
+  RKV_ERR_ALIAS = 7,        /* an output overlaps an input or another output */
+  RKV_ERR_HIP = 8           /* the HIP runtime reported an error at launch */
+} rkv_status;
+
+typedef enum { RKV_ROPE_NEOX = 0, RKV_ROPE_GPTJ = 1 } rkv_rope_style;
+
+typedef enum { RKV_F16 = 0, RKV_F32 = 1, RKV_I32 = 2 } rkv_dtype;
+
+/* A dense row-major device tensor: element type, rank (<= 5) and extents.
+ * The descriptor itself is host memory and is read only during the call. */
+typedef struct {
+  void* data;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[5];
+} rkv_tensor;
+
+/* Call 1 -- empty-cache prefill on packed QKV, in place.
+ * (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV",
+ *  launchApplyRopeWriteKVPackedQKV.)
+ *   cosSinCache  [in]     f32 [T, L, R]: T = 1 (shared by all sequences) or B
+ *                         (one table per sequence); row p = [cos | sin] of
+ *                         position p; R = rotaryDim.
+ *   qkv          [in,out] f16 [B, S, Hq + Hkv + Hkv, D]: heads in Q, K, V
+ *                         order.  Q and K heads are rotated in place (token s
+ *                         at position s); V heads are left unchanged.
+ *   kvCache      [out]    f16 [B, 2, Hkv, cap, D]: plane 0 = K, plane 1 = V.
+ *                         Slot s of each head receives token s's rotated K and
+ *                         its V; slots >= S are not written.
+ * Errors: RKV_ERR_CAPACITY if S > cap or S > L.  Hq = qkv dim 2 - 2*Hkv must
+ * be >= 0.  B = 0 or S = 0 is a valid call that enqueues nothing. */
+rkv_status rkv_apply_rope_write_kv_packed_qkv(const rkv_tensor* cosSinCache, rkv_tensor* qkv,
+                                              rkv_tensor* kvCache, int32_t ropeStyle,
+                                              hipStream_t stream);
+
+/* Call 2 -- write into a non-empty cache, rotated Q to a separate tensor.
+ * (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV",
+ *  launchApplyRopeWriteKVContinuousQAndKVCache.)
+ *   cosSinCache     [in]  f32 [T, L, R], T in {1, B}.
+ *   kvCacheEndLens  [in]  i32 [B]: cache length of sequence b after the
+ *                         write; token s takes position and slot
+ *                         endLens[b] - S + s.
+ *   qkv             [in]  f16 [B, S, Hq + 2*Hkv, D]; never written.
+ *   kvCache         [out] f16 [B, 2, Hkv, cap, D]: rotated K and raw V at the
+ *                         token's slot; other slots are not written.
+ *   qOut            [out] f16 [B, S, Hq, D]: rotated Q.
+ * A token whose slot is outside [0, cap) or whose position is outside
+ * [0, L) writes nothing, neither qOut nor the cache. */
+rkv_status rkv_apply_rope_write_kv_continuous(const rkv_tensor* cosSinCache,
+                                              const rkv_tensor* kvCacheEndLens,
+                                              const rkv_tensor* qkv, rkv_tensor* kvCache,
+                                              rkv_tensor* qOut, int32_t ropeStyle,
+                                              hipStream_t stream);
+
+/* Call 3 -- tree-decoding write for speculative decoding.
+ * (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV",
+ *  launchApplyRopeWriteKVTreeDecoding.)
+ * As call 2, except that the rotary position of token s is
+ * tokenPosIds[b, s] (i32 [B, S]) while its cache slot stays endLens[b]-S+s,
+ * so that tree siblings at one depth keep distinct slots.  A token whose
+ * slot is outside [0, cap) or whose position is outside [0, L) writes
+ * nothing. */
+rkv_status rkv_apply_rope_write_kv_tree(const rkv_tensor* cosSinCache,
+                                        const rkv_tensor* kvCacheEndLens,
+                                        const rkv_tensor* tokenPosIds, const rkv_tensor* qkv,
+                                        rkv_tensor* kvCache, rkv_tensor* qOut,
+                                        int32_t ropeStyle, hipStream_t stream);
+
+/* Call 4 -- paged delta update.
+ * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
+ *  launchDFlashTargetKVCacheUpdate.)
+ *   kDelta, vDelta        [in]     f16 [N, Hkv, D], token-major rows.
+ *   kvCache               [in,out] f16 [2, numPages, 64, Hkv, D] paged pool;
+ *                                  canonical page id p addresses
+ *                                  pool[p / numPages][p % numPages].
+ *   tokenAlignedCosSin    [in]     f32 [N, R]: the cos/sin row of delta row i.
+ *   deltaPositions        [in]     i32 [N]: absolute position of row i.
+ *   deltaTokenToSequence  [in]     i32 [N]: owning sequence of row i.
+ *   pageTable             [in]     i32 [batchSize, 2, maxPagesPerSeq]:
+ *                                  canonical ids, K entries in [0, numPages),
+ *                                  V entries in [numPages, 2*numPages).
+ *   N = numDeltaTokens (physical rows), batchSize = active sequences.
+ * Row i is skipped if its position or sequence is negative (padding), if its
+ * sequence is >= batchSize, or if its position is >= maxPagesPerSeq*64.
+ * Otherwise, with lp = pos / 64 and off = pos % 64, K (rotated) is written
+ * to page pageTable[seq, 0, lp] at token off if that id is in [0, numPages),
+ * and V (copied) to page pageTable[seq, 1, lp] if that id is in
+ * [numPages, 2*numPages); an unmapped or out-of-plane id skips that plane.
+ * Rows must not map to the same (page, token): such writes race.
+ * The rotation layout is given by ropeStyle.  The pool may exceed 2 GiB. */
+rkv_status rkv_dflash_target_kv_cache_update(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCache,
+    const float* tokenAlignedCosSin, const int32_t* deltaPositions,
+    const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
+    int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim,
+    int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
+
+/* Host-only capacity check.
+ * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
+ *  checkDFlashRopeCapacity.)
+ * Returns RKV_ERR_CAPACITY exactly when cosSinSeqLen > kvCapacity (a table
+ * shorter than the padded capacity is accepted), else RKV_OK.  Where the
+ * original API throws, this returns the status and sets rkv_last_error(). */
+rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity);
+
+/* Tokens per page of the paged pool: 64. */
+int32_t rkv_tokens_per_page(void);
+
+/* Message for the last error raised on this thread ("" if none).  The
+ * pointer stays valid until the next call on the same thread. */
+const char* rkv_last_error(void);
+
+/* Static name of a status code. */
+const char* rkv_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROPE_KV_CACHE_H */

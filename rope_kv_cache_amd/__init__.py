@@ -1,0 +1,178 @@
+"""Python binding of ``librkv.so``: fused RoPE + KV-cache write on MI355X.
+
+Argument marshalling only.  Each function turns torch device tensors into the
+C descriptors of ``include/rope_kv_cache.h``, passes torch's current HIP
+stream of the tensors' device, and raises :class:`RkvError` with the
+library's message when the call returns an error status.  All computation
+happens in the HIP kernels of ``librkv.so``; there is no fallback: if the
+library is missing, importing this package raises.
+
+Functions (same names as the C entry points, without the ``rkv_`` prefix):
+  apply_rope_write_kv_packed_qkv(cos_sin_cache, qkv, kv_cache, rope_style)
+  apply_rope_write_kv_continuous(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out, rope_style)
+  apply_rope_write_kv_tree(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache, q_out, rope_style)
+  dflash_target_kv_cache_update(k_delta, v_delta, kv_cache, token_aligned_cos_sin, delta_positions,
+                                delta_token_to_sequence, page_table, batch_size, rope_style)
+  check_rope_capacity(cos_sin_seq_len, kv_capacity)
+  tokens_per_page()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librkv.so")
+
+ROPE_NEOX = 0
+ROPE_GPTJ = 1
+
+OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_ALIGNMENT, ERR_ALIAS, \
+    ERR_HIP = range(9)
+
+_F16, _F32, _I32 = 0, 1, 2
+_DTYPES = {torch.float16: _F16, torch.float32: _F32, torch.int32: _I32}
+
+
+class RkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+class RkvTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 5)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python rope_kv_cache_amd/_build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    T = ctypes.POINTER(RkvTensor)
+    sig = {
+        "rkv_apply_rope_write_kv_packed_qkv": [T, T, T, i32, P],
+        "rkv_apply_rope_write_kv_continuous": [T, T, T, T, T, i32, P],
+        "rkv_apply_rope_write_kv_tree": [T, T, T, T, T, T, i32, P],
+        "rkv_dflash_target_kv_cache_update": [P, P, P, P, P, P, P] + [i32] * 8 + [P],
+        "rkv_check_rope_capacity": [i32, i32],
+        "rkv_tokens_per_page": [],
+        "rkv_last_error": [],
+        "rkv_status_string": [i32],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int32
+    L.rkv_last_error.restype = ctypes.c_char_p
+    L.rkv_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.rkv_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise RkvError(status, lib.rkv_last_error().decode())
+
+
+def _device_of(*tensors) -> torch.device:
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("all tensors must be torch tensors in GPU memory")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+    return dev
+
+
+def _desc(t: torch.Tensor) -> RkvTensor:
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous (dense row-major)")
+    if t.dim() > 5:
+        raise ValueError("at most 5 dimensions")
+    d = RkvTensor()
+    d.data = t.data_ptr() if t.numel() else (t.data_ptr() or None)
+    d.dtype = _DTYPES.get(t.dtype, -1)
+    d.ndim = t.dim()
+    for k, n in enumerate(t.shape):
+        d.shape[k] = n
+    return d
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def apply_rope_write_kv_packed_qkv(cos_sin_cache, qkv, kv_cache, rope_style: int) -> None:
+    dev = _device_of(cos_sin_cache, qkv, kv_cache)
+    a, b, c = _desc(cos_sin_cache), _desc(qkv), _desc(kv_cache)
+    _check(lib.rkv_apply_rope_write_kv_packed_qkv(ctypes.byref(a), ctypes.byref(b),
+                                                  ctypes.byref(c), int(rope_style), _stream(dev)))
+
+
+def apply_rope_write_kv_continuous(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out,
+                                   rope_style: int) -> None:
+    dev = _device_of(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out)
+    d = [_desc(t) for t in (cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out)]
+    _check(lib.rkv_apply_rope_write_kv_continuous(*[ctypes.byref(x) for x in d], int(rope_style),
+                                                  _stream(dev)))
+
+
+def apply_rope_write_kv_tree(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache,
+                             q_out, rope_style: int) -> None:
+    dev = _device_of(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache, q_out)
+    d = [_desc(t) for t in (cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache,
+                            q_out)]
+    _check(lib.rkv_apply_rope_write_kv_tree(*[ctypes.byref(x) for x in d], int(rope_style),
+                                            _stream(dev)))
+
+
+def dflash_target_kv_cache_update(k_delta, v_delta, kv_cache, token_aligned_cos_sin,
+                                  delta_positions, delta_token_to_sequence, page_table,
+                                  batch_size: int, rope_style: int) -> None:
+    """Sizes come from the shapes: k_delta [N, Hkv, D], token_aligned_cos_sin
+    [N, R], kv_cache [2, numPages, 64, Hkv, D], page_table [B, 2, maxPagesPerSeq].
+    ``batch_size`` is the active batch size, which may be below B."""
+    ts = (k_delta, v_delta, kv_cache, token_aligned_cos_sin, delta_positions,
+          delta_token_to_sequence, page_table)
+    dev = _device_of(*ts)
+    for t, dt in zip(ts, (torch.float16, torch.float16, torch.float16, torch.float32, torch.int32,
+                          torch.int32, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"expected contiguous {dt}, got {t.dtype}")
+    if k_delta.dim() != 3 or v_delta.shape != k_delta.shape or kv_cache.dim() != 5 \
+            or token_aligned_cos_sin.dim() != 2 or page_table.dim() != 3:
+        raise ValueError("shapes must be k/v_delta [N,Hkv,D], kv_cache [2,P,64,Hkv,D], "
+                         "token_aligned_cos_sin [N,R], page_table [B,2,M]")
+    N, Hkv, D = k_delta.shape
+    if tuple(kv_cache.shape[::2]) != (2, 64, D) or kv_cache.shape[3] != Hkv \
+            or token_aligned_cos_sin.shape[0] != N or delta_positions.numel() != N \
+            or delta_token_to_sequence.numel() != N or page_table.shape[1] != 2 \
+            or batch_size > page_table.shape[0]:
+        raise ValueError("inconsistent shapes")
+    _check(lib.rkv_dflash_target_kv_cache_update(
+        *[t.data_ptr() for t in ts], N, int(batch_size), Hkv, D, token_aligned_cos_sin.shape[1],
+        kv_cache.shape[1], page_table.shape[2], int(rope_style), _stream(dev)))
+
+
+def check_rope_capacity(cos_sin_seq_len: int, kv_capacity: int) -> None:
+    _check(lib.rkv_check_rope_capacity(int(cos_sin_seq_len), int(kv_capacity)))
+
+
+def tokens_per_page() -> int:
+    return lib.rkv_tokens_per_page()

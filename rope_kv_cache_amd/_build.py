@@ -1,0 +1,31 @@
+"""Build ``librkv.so`` (the HIP kernels and their C ABI) for gfx950 with hipcc.
+
+The library is built in-tree, next to this file.  Packed-FP32 instructions
+are disabled for all device code (``-packed-fp32-ops``); the host pass of
+hipcc warns that it does not know that feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_PATH = os.path.join(HERE, "librkv.so")
+SOURCES = [os.path.join(CSRC, f) for f in ("rkv_abi.hip", "rkv_kernels.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def build(out: str = LIB_PATH, extra=()) -> str:
+    cmd = [HIPCC, *FLAGS, *extra, "-o", out + ".tmp", *SOURCES]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(extra=sys.argv[1:]))

@@ -1,0 +1,322 @@
+// C ABI of the fused RoPE + KV-cache write library (include/rope_kv_cache.h).
+//
+// Host side only: argument validation, launch-shape selection and the
+// launch itself.  Nothing here reads device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/rope_kv_cache.h"
+#include "rkv_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rkv_status fail(rkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+// Launch shape: keep the chip's 1024 SIMDs fed with many waves when the
+// token count is small by splitting a token's row sets over several waves.
+constexpr long long kTargetWaves = 32768;
+
+int elem_size(int32_t dtype) { return dtype == RKV_F16 ? 2 : 4; }
+
+struct Span {
+  const char* name;
+  uintptr_t lo, hi;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Checked product of non-negative extents.
+bool mul_ok(long long a, long long b, long long* out) {
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+rkv_status check_tensor(const rkv_tensor* t, const char* name, int32_t dtype, int32_t ndim,
+                        Span* span) {
+  if (!t) return fail(RKV_ERR_NULL, "%s: null descriptor", name);
+  if (t->dtype != dtype)
+    return fail(RKV_ERR_DTYPE, "%s: dtype %d, expected %d", name, t->dtype, dtype);
+  if (t->ndim != ndim)
+    return fail(RKV_ERR_SHAPE, "%s: rank %d, expected %d", name, t->ndim, ndim);
+  long long n = 1;
+  for (int d = 0; d < ndim; ++d) {
+    if (t->shape[d] < 0 || t->shape[d] > INT32_MAX)
+      return fail(RKV_ERR_SHAPE, "%s: extent %d is %lld", name, d, (long long)t->shape[d]);
+    if (!mul_ok(n, t->shape[d], &n)) return fail(RKV_ERR_SHAPE, "%s: size overflows", name);
+  }
+  long long bytes;
+  if (!mul_ok(n, elem_size(dtype), &bytes)) return fail(RKV_ERR_SHAPE, "%s: size overflows", name);
+  if (n > 0 && !t->data) return fail(RKV_ERR_NULL, "%s: null data pointer", name);
+  if (((uintptr_t)t->data & 15u) != 0)
+    return fail(RKV_ERR_ALIGNMENT, "%s: data pointer is not 16-byte aligned", name);
+  span->name = name;
+  span->lo = (uintptr_t)t->data;
+  span->hi = (uintptr_t)t->data + (uintptr_t)bytes;
+  return RKV_OK;
+}
+
+rkv_status check_no_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int a = 0; a < n_out; ++a) {
+    for (int b = a + 1; b < n_out; ++b)
+      if (overlaps(outs[a], outs[b]))
+        return fail(RKV_ERR_ALIAS, "%s overlaps %s", outs[a].name, outs[b].name);
+    for (int b = 0; b < n_in; ++b)
+      if (overlaps(outs[a], ins[b]))
+        return fail(RKV_ERR_ALIAS, "%s overlaps %s", outs[a].name, ins[b].name);
+  }
+  return RKV_OK;
+}
+
+rkv_status check_style(int32_t style) {
+  if (style != RKV_ROPE_NEOX && style != RKV_ROPE_GPTJ)
+    return fail(RKV_ERR_SHAPE, "ropeStyle %d is neither NeoX (0) nor GPT-J (1)", style);
+  return RKV_OK;
+}
+
+rkv_status check_dims(int32_t D, int32_t R) {
+  if (R < 0 || R > D || (R & 1))
+    return fail(RKV_ERR_SHAPE, "rotaryDim %d must be even and within [0, headDim=%d]", R, D);
+  if (D != 64 && D != 128 && D != 256)
+    return fail(RKV_ERR_UNSUPPORTED, "headDim %d: supported values are 64, 128, 256", D);
+  if (R % 16)
+    return fail(RKV_ERR_UNSUPPORTED, "rotaryDim %d: must be a multiple of 16", R);
+  return RKV_OK;
+}
+
+// Waves per work item: at most kUnroll row sets per wave pass, and more
+// waves (down to one row set each) while the grid is small.
+int32_t pick_split(long long items, int32_t row_sets, int unroll) {
+  long long f = (row_sets + unroll - 1) / unroll;
+  if (f < 1) f = 1;
+  if (items > 0 && items * f < kTargetWaves) {
+    long long want = (kTargetWaves + items - 1) / items;
+    f = want < row_sets ? want : row_sets;
+    if (f < 1) f = 1;
+  }
+  while (f > 1 && items * f > INT32_MAX) --f;
+  return (int32_t)f;
+}
+
+rkv_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(RKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return RKV_OK;
+}
+
+// Shared validation of calls 1-3.  `call` selects which descriptors exist.
+rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_lens,
+                  const rkv_tensor* pos_ids, const rkv_tensor* qkv, rkv_tensor* cache,
+                  rkv_tensor* q_out, int32_t style, hipStream_t stream) {
+  clear_error();
+  rkv_status st;
+  Span s_cs, s_qkv, s_cache, s_qo = {}, s_end = {}, s_pos = {};
+  if ((st = check_tensor(cos_sin, "cosSinCache", RKV_F32, 3, &s_cs))) return st;
+  if ((st = check_tensor(qkv, "qkv", RKV_F16, 4, &s_qkv))) return st;
+  if ((st = check_tensor(cache, "kvCache", RKV_F16, 5, &s_cache))) return st;
+  if ((st = check_style(style))) return st;
+
+  const long long B = qkv->shape[0], S = qkv->shape[1], H = qkv->shape[2], D = qkv->shape[3];
+  const long long Hkv = cache->shape[2], cap = cache->shape[3];
+  const long long TB = cos_sin->shape[0], TL = cos_sin->shape[1], R = cos_sin->shape[2];
+  if (cache->shape[0] != B || cache->shape[1] != 2 || cache->shape[4] != D)
+    return fail(RKV_ERR_SHAPE, "kvCache must be [B=%lld, 2, Hkv, cap, D=%lld]", B, D);
+  if (TB != 1 && TB != B)
+    return fail(RKV_ERR_SHAPE, "cosSinCache batch %lld must be 1 or B=%lld", TB, B);
+  long long Hq;
+  if (call == rkv::kCallPacked) {
+    Hq = H - 2 * Hkv;
+    if (Hq < 0)
+      return fail(RKV_ERR_SHAPE, "qkv heads %lld < 2 * Hkv (%lld)", H, Hkv);
+  } else {
+    if ((st = check_tensor(q_out, "qOut", RKV_F16, 4, &s_qo))) return st;
+    if ((st = check_tensor(end_lens, "kvCacheEndLens", RKV_I32, 1, &s_end))) return st;
+    Hq = q_out->shape[2];
+    if (q_out->shape[0] != B || q_out->shape[1] != S || q_out->shape[3] != D)
+      return fail(RKV_ERR_SHAPE, "qOut must be [B, S, Hq, D]");
+    if (H != Hq + 2 * Hkv)
+      return fail(RKV_ERR_SHAPE, "qkv heads %lld != Hq + 2*Hkv = %lld", H, Hq + 2 * Hkv);
+    if (end_lens->shape[0] != B) return fail(RKV_ERR_SHAPE, "kvCacheEndLens must be [B]");
+    if (call == rkv::kCallTree) {
+      if ((st = check_tensor(pos_ids, "tokenPosIds", RKV_I32, 2, &s_pos))) return st;
+      if (pos_ids->shape[0] != B || pos_ids->shape[1] != S)
+        return fail(RKV_ERR_SHAPE, "tokenPosIds must be [B, S]");
+    }
+  }
+  if ((st = check_dims((int32_t)D, (int32_t)R))) return st;
+  if (call == rkv::kCallPacked && (S > cap || S > TL))
+    return fail(RKV_ERR_CAPACITY, "S=%lld exceeds capacity %lld or cos/sin length %lld", S, cap,
+                TL);
+  {
+    Span outs[3], ins[4];
+    int no = 0, ni = 0;
+    outs[no++] = s_cache;
+    if (call == rkv::kCallPacked) {
+      outs[no++] = s_qkv;
+    } else {
+      outs[no++] = s_qo;
+      ins[ni++] = s_qkv;
+      ins[ni++] = s_end;
+      if (call == rkv::kCallTree) ins[ni++] = s_pos;
+    }
+    ins[ni++] = s_cs;
+    if ((st = check_no_alias(outs, no, ins, ni))) return st;
+  }
+  const long long tokens = B * S;
+  if (tokens > INT32_MAX) return fail(RKV_ERR_UNSUPPORTED, "B*S=%lld exceeds 2^31-1", tokens);
+  if (tokens == 0 || H == 0) return RKV_OK;
+
+  rkv::ContigParams p{};
+  p.cos_sin = (const float*)cos_sin->data;
+  p.qkv = (uint16_t*)qkv->data;
+  p.cache = (uint16_t*)cache->data;
+  p.q_out = q_out ? (uint16_t*)q_out->data : nullptr;
+  p.end_lens = end_lens ? (const int32_t*)end_lens->data : nullptr;
+  p.pos_ids = pos_ids ? (const int32_t*)pos_ids->data : nullptr;
+  p.B = (int32_t)B;
+  p.S = (int32_t)S;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.cap = (int32_t)cap;
+  p.table_batch = (int32_t)TB;
+  p.table_len = (int32_t)TL;
+  p.R = (int32_t)R;
+  const int rows_per_set = 64 / ((int)D / 16);
+  p.row_sets = (int32_t)((H + rows_per_set - 1) / rows_per_set);
+  p.waves_per_token = pick_split(tokens, p.row_sets, rkv::kContigUnroll);
+  p.total_waves = (int32_t)(tokens * p.waves_per_token);
+  return launched(rkv::launch_contig(p, call, (int)D, style, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+rkv_status rkv_apply_rope_write_kv_packed_qkv(const rkv_tensor* cosSinCache, rkv_tensor* qkv,
+                                              rkv_tensor* kvCache, int32_t ropeStyle,
+                                              hipStream_t stream) {
+  return contig(rkv::kCallPacked, cosSinCache, nullptr, nullptr, qkv, kvCache, nullptr, ropeStyle,
+                stream);
+}
+
+rkv_status rkv_apply_rope_write_kv_continuous(const rkv_tensor* cosSinCache,
+                                              const rkv_tensor* kvCacheEndLens,
+                                              const rkv_tensor* qkv, rkv_tensor* kvCache,
+                                              rkv_tensor* qOut, int32_t ropeStyle,
+                                              hipStream_t stream) {
+  return contig(rkv::kCallContinuous, cosSinCache, kvCacheEndLens, nullptr, qkv, kvCache, qOut,
+                ropeStyle, stream);
+}
+
+rkv_status rkv_apply_rope_write_kv_tree(const rkv_tensor* cosSinCache,
+                                        const rkv_tensor* kvCacheEndLens,
+                                        const rkv_tensor* tokenPosIds, const rkv_tensor* qkv,
+                                        rkv_tensor* kvCache, rkv_tensor* qOut,
+                                        int32_t ropeStyle, hipStream_t stream) {
+  return contig(rkv::kCallTree, cosSinCache, kvCacheEndLens, tokenPosIds, qkv, kvCache, qOut,
+                ropeStyle, stream);
+}
+
+rkv_status rkv_dflash_target_kv_cache_update(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCache,
+    const float* tokenAlignedCosSin, const int32_t* deltaPositions,
+    const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
+    int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
+    int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream) {
+  clear_error();
+  rkv_status st;
+  if (numDeltaTokens < 0 || batchSize < 0 || numKVHeads < 0 || numPages < 0 || maxPagesPerSeq < 0)
+    return fail(RKV_ERR_SHAPE, "negative size argument");
+  if ((st = check_style(ropeStyle))) return st;
+  if ((st = check_dims(headDim, rotaryDim))) return st;
+  const long long N = numDeltaTokens, Hkv = numKVHeads, D = headDim, R = rotaryDim;
+  long long delta_elems, pool_elems, pt_elems, cs_elems;
+  if (!mul_ok(N * Hkv, D, &delta_elems) ||
+      !mul_ok(2LL * numPages * rkv::kTokensPerPage, Hkv * D, &pool_elems) ||
+      !mul_ok((long long)batchSize * 2, maxPagesPerSeq, &pt_elems) ||
+      !mul_ok(N, R, &cs_elems) || pool_elems > (INT64_MAX / 2))
+    return fail(RKV_ERR_SHAPE, "sizes overflow");
+  if (N == 0 || Hkv == 0) return RKV_OK;
+  if (!kDelta || !vDelta || !tokenAlignedCosSin || !deltaPositions || !deltaTokenToSequence)
+    return fail(RKV_ERR_NULL, "null delta-row pointer");
+  if ((pool_elems > 0 && !kvCache) || (pt_elems > 0 && !pageTable))
+    return fail(RKV_ERR_NULL, "null kvCache or pageTable");
+  const void* ptrs[] = {kDelta, vDelta, kvCache, tokenAlignedCosSin, deltaPositions,
+                        deltaTokenToSequence, pageTable};
+  const char* names[] = {"kDelta", "vDelta", "kvCache", "tokenAlignedCosSin", "deltaPositions",
+                         "deltaTokenToSequence", "pageTable"};
+  for (int k = 0; k < 7; ++k)
+    if (((uintptr_t)ptrs[k] & 15u) != 0)
+      return fail(RKV_ERR_ALIGNMENT, "%s is not 16-byte aligned", names[k]);
+  auto span = [](const char* n, const void* p, long long bytes) {
+    return Span{n, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+  };
+  Span out = span("kvCache", kvCache, pool_elems * 2);
+  Span ins[] = {span("kDelta", kDelta, delta_elems * 2), span("vDelta", vDelta, delta_elems * 2),
+                span("tokenAlignedCosSin", tokenAlignedCosSin, cs_elems * 4),
+                span("deltaPositions", deltaPositions, N * 4),
+                span("deltaTokenToSequence", deltaTokenToSequence, N * 4),
+                span("pageTable", pageTable, pt_elems * 4)};
+  if ((st = check_no_alias(&out, 1, ins, 6))) return st;
+  if (pool_elems == 0 || pt_elems == 0) return RKV_OK;   // nothing can be written
+
+  rkv::PagedParams p{};
+  p.k_delta = kDelta;
+  p.v_delta = vDelta;
+  p.pool = kvCache;
+  p.cos_sin = tokenAlignedCosSin;
+  p.positions = deltaPositions;
+  p.seq = deltaTokenToSequence;
+  p.page_table = pageTable;
+  p.N = numDeltaTokens;
+  p.batch = batchSize;
+  p.Hkv = numKVHeads;
+  p.R = rotaryDim;
+  p.num_pages = numPages;
+  p.max_pages = maxPagesPerSeq;
+  const int rows_per_set = 64 / (headDim / 16);
+  p.row_sets = (int32_t)((2 * Hkv + rows_per_set - 1) / rows_per_set);
+  p.waves_per_row = pick_split(N, p.row_sets, rkv::kPagedUnroll);
+  p.total_waves = (int32_t)(N * p.waves_per_row);
+  return launched(rkv::launch_paged(p, headDim, ropeStyle, stream));
+}
+
+rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {
+  clear_error();
+  if (cosSinSeqLen > kvCapacity)
+    return fail(RKV_ERR_CAPACITY, "cos/sin cache length %d exceeds KV capacity %d", cosSinSeqLen,
+                kvCapacity);
+  return RKV_OK;
+}
+
+int32_t rkv_tokens_per_page(void) { return rkv::kTokensPerPage; }
+
+const char* rkv_last_error(void) { return g_err; }
+
+const char* rkv_status_string(int32_t status) {
+  switch (status) {
+    case RKV_OK: return "RKV_OK";
+    case RKV_ERR_NULL: return "RKV_ERR_NULL";
+    case RKV_ERR_DTYPE: return "RKV_ERR_DTYPE";
+    case RKV_ERR_SHAPE: return "RKV_ERR_SHAPE";
+    case RKV_ERR_UNSUPPORTED: return "RKV_ERR_UNSUPPORTED";
+    case RKV_ERR_CAPACITY: return "RKV_ERR_CAPACITY";
+    case RKV_ERR_ALIGNMENT: return "RKV_ERR_ALIGNMENT";
+    case RKV_ERR_ALIAS: return "RKV_ERR_ALIAS";
+    case RKV_ERR_HIP: return "RKV_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+"""Run a seeded workload through the HIP library and compare with the oracle.
+
+Used by the GPU parity tests, ``__graft_entry__.smoke()`` and ``bench.py``.
+Moving arrays to and from the device and calling the binding is all it does;
+every step of the computation runs in the library's kernels.
+
+Comparison rules:
+* every element that is not a rotated Q/K output (V copies, passthrough dims
+  >= R, untouched cache and pool bytes, untouched qOut rows) must match the
+  oracle bit for bit;
+* rotated Q/K elements must satisfy |gpu - ref| <= 2^-10*|ref| + 1e-3
+  (non-finite values must match in kind);
+* ``compare`` also counts rotated elements whose bits differ, so that a test
+  can require bit equality -- which the kernels' exact arithmetic provides.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads as W
+
+TOL_REL = 2.0 ** -10
+TOL_ABS = 1e-3
+
+
+def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def host16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def upload(w, device="cuda") -> dict:
+    if isinstance(w, W.Paged):
+        return {"k_delta": dev(w.k_delta, device), "v_delta": dev(w.v_delta, device),
+                "pool": dev(w.pool, device), "cos_sin": dev(w.cos_sin, device),
+                "positions": dev(w.positions, device), "seq": dev(w.seq, device),
+                "page_table": dev(w.page_table, device)}
+    t = {"cos_sin": dev(w.cos_sin, device), "qkv": dev(w.qkv, device),
+         "cache": dev(w.cache, device)}
+    if w.call != "packed":
+        t["q_out"] = dev(w.q_out, device)
+        t["end_lens"] = dev(w.end_lens, device)
+    if w.call == "tree":
+        t["pos_ids"] = dev(w.pos_ids, device)
+    return t
+
+
+def launch(w, t: dict) -> None:
+    import rope_kv_cache_amd as rkv
+    if isinstance(w, W.Paged):
+        rkv.dflash_target_kv_cache_update(t["k_delta"], t["v_delta"], t["pool"], t["cos_sin"],
+                                          t["positions"], t["seq"], t["page_table"], w.batch,
+                                          w.style)
+    elif w.call == "packed":
+        rkv.apply_rope_write_kv_packed_qkv(t["cos_sin"], t["qkv"], t["cache"], w.style)
+    elif w.call == "continuous":
+        rkv.apply_rope_write_kv_continuous(t["cos_sin"], t["end_lens"], t["qkv"], t["cache"],
+                                           t["q_out"], w.style)
+    else:
+        rkv.apply_rope_write_kv_tree(t["cos_sin"], t["end_lens"], t["pos_ids"], t["qkv"],
+                                     t["cache"], t["q_out"], w.style)
+
+
+def download(w, t: dict) -> dict:
+    torch.cuda.synchronize()
+    if isinstance(w, W.Paged):
+        return {"pool": host16(t["pool"])}
+    out = {"cache": host16(t["cache"])}
+    if w.call == "packed":
+        out["qkv"] = host16(t["qkv"])
+    else:
+        out["q_out"] = host16(t["q_out"])
+        out["qkv"] = host16(t["qkv"])      # must be unchanged
+    return out
+
+
+def run_gpu(w, device="cuda") -> dict:
+    t = upload(w, device)
+    launch(w, t)
+    return download(w, t)
+
+
+def expected(w, L=None) -> dict:
+    import oracle
+    want = oracle.run(w, L=L)
+    if not isinstance(w, W.Paged) and w.call != "packed":
+        want["qkv"] = w.qkv          # calls 2 and 3 never write qkv
+    return want
+
+
+def rotated_mask_parts(w, key):
+    """Index expressions (tuples of slices) covering the elements of output
+    ``key`` that may hold a rotated value."""
+    R = w.R
+    if key == "pool":
+        return [(0, Ellipsis, slice(0, R))]
+    if key == "cache":
+        return [(slice(None), 0, Ellipsis, slice(0, R))]
+    if key == "q_out":
+        return [(Ellipsis, slice(0, R))]
+    if key == "qkv":
+        if w.call == "packed":
+            return [(slice(None), slice(None), slice(0, w.Hq + w.Hkv), slice(0, R))]
+        return []
+    raise KeyError(key)
+
+
+def _within_tol(g: np.ndarray, r: np.ndarray) -> np.ndarray:
+    gv = g.view(np.float16).astype(np.float64)
+    rv = r.view(np.float16).astype(np.float64)
+    fin = np.isfinite(rv) & np.isfinite(gv)
+    ok = np.zeros(g.shape, dtype=bool)
+    ok[fin] = np.abs(gv[fin] - rv[fin]) <= TOL_REL * np.abs(rv[fin]) + TOL_ABS
+    both_nan = np.isnan(gv) & np.isnan(rv)
+    same_inf = np.isinf(gv) & np.isinf(rv) & (gv == rv)
+    return ok | both_nan | same_inf
+
+
+def _ulps(g: np.ndarray, r: np.ndarray) -> np.ndarray:
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(g) - ordered(r))
+
+
+def compare(w, got: dict, want: dict) -> dict:
+    """Assert the parity rules; return {key: n_rotated_bit_differences}."""
+    report = {}
+    for key, ref in want.items():
+        g = got[key]
+        assert g.shape == ref.shape, (key, g.shape, ref.shape)
+        diff = g != ref
+        if not diff.any():
+            report[key] = 0
+            continue
+        rot = np.zeros(ref.shape, dtype=bool)
+        for ix in rotated_mask_parts(w, key):
+            rot[ix] = True
+        bad = diff & ~rot
+        if bad.any():
+            idx = tuple(int(i) for i in np.argwhere(bad)[0])
+            raise AssertionError(
+                f"{w.name}: {key}{list(idx)} differs outside rotated Q/K: gpu {g[idx]:#06x} "
+                f"oracle {ref[idx]:#06x} ({int(bad.sum())} such elements)")
+        where = np.nonzero(diff)
+        gd, rd = g[where], ref[where]
+        tol_ok = _within_tol(gd, rd)
+        if not tol_ok.all():
+            k = int(np.argmin(tol_ok))
+            idx = tuple(int(a[k]) for a in where)
+            raise AssertionError(
+                f"{w.name}: {key}{list(idx)} outside tolerance: gpu {gd[k]:#06x} "
+                f"oracle {rd[k]:#06x}")
+        report[key] = int(diff.sum())
+        report[key + "_max_ulp"] = int(_ulps(gd, rd).max())
+    return report

@@ -1,0 +1,326 @@
+"""The C ABI on the host, without a GPU.
+
+* ``librkv.so`` loads and exports every function ``include/rope_kv_cache.h``
+  declares.
+* Host validation returns the documented status for every malformed call,
+  before any HIP call (so these run on a machine without a GPU).
+* The capacity check follows its truth table (tests/golden/capacity_check.txt).
+
+The descriptors here carry fake device addresses that are never dereferenced:
+every call below is invalid or empty, so it returns before any launch.  As a
+guard against a validation bug turning one of them into a launch, the
+fake-pointer tests are skipped when a GPU is visible.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rope_kv_cache.h")
+
+rkv = pytest.importorskip("rope_kv_cache_amd")
+L = rkv.lib
+T = rkv.RkvTensor
+F16, F32, I32 = 0, 1, 2
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run on CPU only")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for want in ["rkv_apply_rope_write_kv_packed_qkv", "rkv_apply_rope_write_kv_continuous",
+                 "rkv_apply_rope_write_kv_tree", "rkv_dflash_target_kv_cache_update",
+                 "rkv_check_rope_capacity", "rkv_tokens_per_page", "rkv_last_error",
+                 "rkv_status_string"]:
+        assert want in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports(name):
+    lib = ctypes.CDLL(rkv.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def test_status_strings_and_page_size():
+    assert rkv.tokens_per_page() == 64
+    for code, name in enumerate(["RKV_OK", "RKV_ERR_NULL", "RKV_ERR_DTYPE", "RKV_ERR_SHAPE",
+                                 "RKV_ERR_UNSUPPORTED", "RKV_ERR_CAPACITY", "RKV_ERR_ALIGNMENT",
+                                 "RKV_ERR_ALIAS", "RKV_ERR_HIP"]):
+        assert rkv.status_string(code) == name
+
+
+def test_capacity_truth_table():
+    path = os.path.join(ROOT, "tests", "golden", "capacity_check.txt")
+    for line in open(path):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        a, b, want = int(line[0]), int(line[1]), line[2]
+        st = L.rkv_check_rope_capacity(a, b)
+        assert st == (rkv.OK if want == "ok" else rkv.ERR_CAPACITY), (a, b)
+        if want != "ok":
+            assert b"exceeds" in L.rkv_last_error()
+        with pytest.raises(rkv.RkvError) if want != "ok" else _nullctx():
+            rkv.check_rope_capacity(a, b)
+
+
+class _nullctx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
+
+
+# --------------------------------------------------------------- helpers --
+
+_next = [0x7F0000000000]
+
+
+def fake(dtype, *shape, addr=None):
+    t = T()
+    if addr is None:
+        _next[0] += 1 << 36
+        addr = _next[0]
+    t.data = addr
+    t.dtype = dtype
+    t.ndim = len(shape)
+    for k, n in enumerate(shape):
+        t.shape[k] = n
+    return t
+
+
+def packed_args(B=2, S=8, Hq=4, Hkv=2, D=128, R=128, cap=16, tb=1, tl=16):
+    return [fake(F32, tb, tl, R), fake(F16, B, S, Hq + 2 * Hkv, D), fake(F16, B, 2, Hkv, cap, D)]
+
+
+def call_packed(cs, qkv, cache, style=0):
+    b = ctypes.byref
+    return L.rkv_apply_rope_write_kv_packed_qkv(b(cs) if cs else None, b(qkv) if qkv else None,
+                                                b(cache) if cache else None, style, None)
+
+
+def cont_args(B=2, S=8, Hq=4, Hkv=2, D=128, R=128, cap=16, tb=1, tl=16):
+    return [fake(F32, tb, tl, R), fake(I32, B), fake(F16, B, S, Hq + 2 * Hkv, D),
+            fake(F16, B, 2, Hkv, cap, D), fake(F16, B, S, Hq, D)]
+
+
+def call_cont(args, style=0):
+    return L.rkv_apply_rope_write_kv_continuous(*[ctypes.byref(a) if a else None for a in args],
+                                                style, None)
+
+
+def tree_args(B=2, S=8, Hq=4, Hkv=2, D=128, R=64, cap=16):
+    c = cont_args(B, S, Hq, Hkv, D, R, cap)
+    return [c[0], c[1], fake(I32, B, S), c[2], c[3], c[4]]
+
+
+def call_tree(args, style=0):
+    return L.rkv_apply_rope_write_kv_tree(*[ctypes.byref(a) if a else None for a in args], style,
+                                          None)
+
+
+# ------------------------------------------------------------ call 1 ------
+
+@no_gpu
+@pytest.mark.parametrize("case,want", [
+    ("null_cos_sin", rkv.ERR_NULL), ("null_qkv", rkv.ERR_NULL), ("null_cache", rkv.ERR_NULL),
+    ("null_data", rkv.ERR_NULL), ("qkv_f32", rkv.ERR_DTYPE), ("table_f16", rkv.ERR_DTYPE),
+    ("qkv_rank3", rkv.ERR_SHAPE), ("cache_B", rkv.ERR_SHAPE), ("cache_planes", rkv.ERR_SHAPE),
+    ("cache_D", rkv.ERR_SHAPE), ("table_batch", rkv.ERR_SHAPE), ("too_few_heads", rkv.ERR_SHAPE),
+    ("odd_R", rkv.ERR_SHAPE), ("R_gt_D", rkv.ERR_SHAPE), ("R_not_16", rkv.ERR_UNSUPPORTED),
+    ("D_96", rkv.ERR_UNSUPPORTED), ("S_gt_cap", rkv.ERR_CAPACITY),
+    ("S_gt_table", rkv.ERR_CAPACITY), ("misaligned", rkv.ERR_ALIGNMENT),
+    ("cache_aliases_qkv", rkv.ERR_ALIAS), ("table_aliases_cache", rkv.ERR_ALIAS),
+    ("bad_style", rkv.ERR_SHAPE), ("negative_extent", rkv.ERR_SHAPE),
+])
+def test_packed_validation(case, want):
+    cs, qkv, cache = packed_args()
+    style = 0
+    if case == "null_cos_sin":
+        cs = None
+    elif case == "null_qkv":
+        qkv = None
+    elif case == "null_cache":
+        cache = None
+    elif case == "null_data":
+        qkv.data = None
+    elif case == "qkv_f32":
+        qkv.dtype = F32
+    elif case == "table_f16":
+        cs.dtype = F16
+    elif case == "qkv_rank3":
+        qkv = fake(F16, 16, 8, 128)
+    elif case == "cache_B":
+        cache.shape[0] = 3
+    elif case == "cache_planes":
+        cache.shape[1] = 1
+    elif case == "cache_D":
+        cache.shape[4] = 64
+    elif case == "table_batch":
+        cs.shape[0] = 3
+    elif case == "too_few_heads":
+        qkv.shape[2] = 3
+    elif case == "odd_R":
+        cs.shape[2] = 63
+    elif case == "R_gt_D":
+        cs.shape[2] = 144
+    elif case == "R_not_16":
+        cs.shape[2] = 40
+    elif case == "D_96":
+        cs, qkv, cache = packed_args(D=96, R=96)
+    elif case == "S_gt_cap":
+        cs, qkv, cache = packed_args(S=8, cap=7)
+    elif case == "S_gt_table":
+        cs, qkv, cache = packed_args(S=8, tl=7)
+    elif case == "misaligned":
+        cache.data = cache.data + 2
+    elif case == "cache_aliases_qkv":
+        cache.data = qkv.data + 4096
+    elif case == "table_aliases_cache":
+        cs.data = cache.data
+    elif case == "bad_style":
+        style = 2
+    elif case == "negative_extent":
+        qkv.shape[1] = -1
+    st = call_packed(cs, qkv, cache, style)
+    assert st == want, (case, rkv.status_string(st), L.rkv_last_error())
+    assert L.rkv_last_error() != b""
+
+
+@no_gpu
+def test_packed_empty_is_ok_without_launch():
+    for B, S in [(0, 8), (2, 0)]:
+        cs, qkv, cache = packed_args(B=B, S=S)
+        assert call_packed(cs, qkv, cache) == rkv.OK
+    # zero heads: nothing to do
+    cs, qkv, cache = packed_args(Hq=0, Hkv=0)
+    assert call_packed(cs, qkv, cache) == rkv.OK
+
+
+# -------------------------------------------------------- calls 2 and 3 ---
+
+@no_gpu
+@pytest.mark.parametrize("case,want", [
+    ("null_end", rkv.ERR_NULL), ("null_qout", rkv.ERR_NULL), ("end_f32", rkv.ERR_DTYPE),
+    ("qout_f32", rkv.ERR_DTYPE), ("end_len_B", rkv.ERR_SHAPE), ("qout_S", rkv.ERR_SHAPE),
+    ("heads_mismatch", rkv.ERR_SHAPE), ("qout_aliases_qkv", rkv.ERR_ALIAS),
+    ("qout_aliases_cache", rkv.ERR_ALIAS), ("cache_aliases_end", rkv.ERR_ALIAS),
+])
+def test_continuous_validation(case, want):
+    a = cont_args()
+    if case == "null_end":
+        a[1] = None
+    elif case == "null_qout":
+        a[4] = None
+    elif case == "end_f32":
+        a[1].dtype = F32
+    elif case == "qout_f32":
+        a[4].dtype = F32
+    elif case == "end_len_B":
+        a[1].shape[0] = 3
+    elif case == "qout_S":
+        a[4].shape[1] = 7
+    elif case == "heads_mismatch":
+        a[4].shape[2] = 5
+    elif case == "qout_aliases_qkv":
+        a[4].data = a[2].data + 256
+    elif case == "qout_aliases_cache":
+        a[4].data = a[3].data
+    elif case == "cache_aliases_end":
+        a[3].data = a[1].data - 4096
+    st = call_cont(a)
+    assert st == want, (case, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+def test_continuous_does_not_check_capacity_on_host():
+    # the token positions live on the device; S > cap is not a host error,
+    # so the call gets past validation.  Make it fail on an unsupported D so
+    # that nothing is launched.
+    a = cont_args(S=8, cap=4, D=96, R=96)
+    assert call_cont(a) == rkv.ERR_UNSUPPORTED
+
+
+@no_gpu
+@pytest.mark.parametrize("case,want", [
+    ("null_pos", rkv.ERR_NULL), ("pos_f16", rkv.ERR_DTYPE), ("pos_shape", rkv.ERR_SHAPE),
+    ("cache_aliases_pos", rkv.ERR_ALIAS),
+])
+def test_tree_validation(case, want):
+    a = tree_args()
+    if case == "null_pos":
+        a[2] = None
+    elif case == "pos_f16":
+        a[2].dtype = F16
+    elif case == "pos_shape":
+        a[2].shape[1] = 9
+    elif case == "cache_aliases_pos":
+        a[4].data = a[2].data
+    st = call_tree(a)
+    assert st == want, (case, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+def test_continuous_and_tree_empty():
+    assert call_cont(cont_args(B=0)) == rkv.OK
+    assert call_tree(tree_args(S=0)) == rkv.OK
+
+
+# ---------------------------------------------------------------- call 4 --
+
+def paged_call(**kw):
+    base = dict(k=1 << 40, v=2 << 40, pool=3 << 40, cs=4 << 40, pos=5 << 40, seq=6 << 40,
+                pt=7 << 40, N=16, batch=2, Hkv=2, D=128, R=128, P=8, M=4, style=0)
+    base.update(kw)
+    b = base
+    return L.rkv_dflash_target_kv_cache_update(b["k"], b["v"], b["pool"], b["cs"], b["pos"],
+                                               b["seq"], b["pt"], b["N"], b["batch"], b["Hkv"],
+                                               b["D"], b["R"], b["P"], b["M"], b["style"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=-1), rkv.ERR_SHAPE), (dict(batch=-2), rkv.ERR_SHAPE), (dict(Hkv=-1), rkv.ERR_SHAPE),
+    (dict(P=-1), rkv.ERR_SHAPE), (dict(M=-1), rkv.ERR_SHAPE), (dict(style=5), rkv.ERR_SHAPE),
+    (dict(R=130), rkv.ERR_SHAPE), (dict(R=7), rkv.ERR_SHAPE), (dict(R=24), rkv.ERR_UNSUPPORTED),
+    (dict(D=32, R=32), rkv.ERR_UNSUPPORTED), (dict(k=0), rkv.ERR_NULL), (dict(pt=0), rkv.ERR_NULL),
+    (dict(pool=0), rkv.ERR_NULL), (dict(cs=(4 << 40) + 8), rkv.ERR_ALIGNMENT),
+    (dict(pool=(1 << 40) + 4096), rkv.ERR_ALIAS), (dict(pt=(3 << 40) + 64), rkv.ERR_ALIAS),
+    (dict(P=1 << 30, Hkv=1 << 20), rkv.ERR_SHAPE),
+])
+def test_paged_validation(kw, want):
+    st = paged_call(**kw)
+    assert st == want, (kw, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+def test_paged_empty():
+    assert paged_call(N=0) == rkv.OK
+    assert paged_call(Hkv=0) == rkv.OK
+    assert paged_call(P=0) == rkv.OK         # an empty pool: nothing can be written
+    assert paged_call(M=0) == rkv.OK
+    assert paged_call(batch=0, M=0) == rkv.OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    cs = torch.zeros(1, 16, 128)
+    qkv = torch.zeros(1, 8, 8, 128, dtype=torch.float16)
+    cache = torch.zeros(1, 2, 2, 16, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        rkv.apply_rope_write_kv_packed_qkv(cs, qkv, cache, rkv.ROPE_NEOX)

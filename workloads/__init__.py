@@ -252,11 +252,21 @@ def paged(N, batch, Hkv, D, R, num_pages, max_pages, style, seed, theta=10000.0,
                  cos_sin, pos, seq, page_table, name=name)
 
 
+_TILE = 1 << 24
+
+
 def _fill(r, shape, how):
     if how == "sentinel":
         return sentinel_f16(shape)
     if how == "normal":
-        return normal_f16(r, shape)
+        # Large caches and pools repeat a seeded 2^24-element block: every
+        # slot still holds an ordinary N(0,1) value that a stray write would
+        # change, and the fill stays cheap at gigabyte sizes.
+        n = int(np.prod(shape, dtype=np.int64))
+        if n <= _TILE:
+            return normal_f16(r, shape)
+        block = normal_f16(r, (_TILE,))
+        return np.resize(block, n).reshape(shape)
     if how == "bits":   # arbitrary bit patterns, NaNs included
         n = int(np.prod(shape, dtype=np.int64))
         return r.integers(0, 1 << 16, size=n, dtype=np.uint16).reshape(shape)
