@@ -178,6 +178,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--calib", action="store_true",
+                    help="also run a 1 GiB elementwise copy (1 GiB read + 1 GiB written per "
+                         "launch) to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the step "
@@ -228,6 +231,15 @@ def main():
         f"({achieved / PEAK_HBM_GBS:.1%}), {result['value']:.3e} tokens/s")
     del t
     torch.cuda.empty_cache()
+
+    if args.calib:
+        src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     if not args.no_extra:
         extra = {}

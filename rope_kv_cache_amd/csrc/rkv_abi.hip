@@ -248,7 +248,9 @@ rkv_status rkv_dflash_target_kv_cache_update(
       !mul_ok(N, R, &cs_elems) || pool_elems > (INT64_MAX / 2))
     return fail(RKV_ERR_SHAPE, "sizes overflow");
   if (N == 0 || Hkv == 0) return RKV_OK;
-  if (!kDelta || !vDelta || !tokenAlignedCosSin || !deltaPositions || !deltaTokenToSequence)
+  // An array with no elements (e.g. the cos/sin rows when rotaryDim = 0) may be null.
+  if ((delta_elems > 0 && (!kDelta || !vDelta)) || (cs_elems > 0 && !tokenAlignedCosSin) ||
+      !deltaPositions || !deltaTokenToSequence)
     return fail(RKV_ERR_NULL, "null delta-row pointer");
   if ((pool_elems > 0 && !kvCache) || (pt_elems > 0 && !pageTable))
     return fail(RKV_ERR_NULL, "null kvCache or pageTable");

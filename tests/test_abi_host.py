@@ -299,7 +299,9 @@ def paged_call(**kw):
     (dict(P=-1), rkv.ERR_SHAPE), (dict(M=-1), rkv.ERR_SHAPE), (dict(style=5), rkv.ERR_SHAPE),
     (dict(R=130), rkv.ERR_SHAPE), (dict(R=7), rkv.ERR_SHAPE), (dict(R=24), rkv.ERR_UNSUPPORTED),
     (dict(D=32, R=32), rkv.ERR_UNSUPPORTED), (dict(k=0), rkv.ERR_NULL), (dict(pt=0), rkv.ERR_NULL),
-    (dict(pool=0), rkv.ERR_NULL), (dict(cs=(4 << 40) + 8), rkv.ERR_ALIGNMENT),
+    (dict(pool=0), rkv.ERR_NULL), (dict(cs=0), rkv.ERR_NULL), (dict(pos=0), rkv.ERR_NULL),
+    (dict(cs=0, R=0, D=96), rkv.ERR_UNSUPPORTED),    # null cos/sin accepted when R = 0
+    (dict(cs=(4 << 40) + 8), rkv.ERR_ALIGNMENT),
     (dict(pool=(1 << 40) + 4096), rkv.ERR_ALIAS), (dict(pt=(3 << 40) + 64), rkv.ERR_ALIAS),
     (dict(P=1 << 30, Hkv=1 << 20), rkv.ERR_SHAPE),
 ])
