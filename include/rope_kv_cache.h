@@ -35,8 +35,14 @@
  *   NeoX pairs (i, i + rotaryDim/2); GPT-J pairs (2i, 2i+1).  Dims
  *   >= rotaryDim are copied bit for bit.  (sglang rope_cache.py,
  *   _get_neox_rotated_x, _get_gptj_rotated_x, _unit_rope, _load_cos_sin.)
- *   Results equal the products and sum evaluated exactly in binary64 and
- *   rounded once to binary16.
+ * Arithmetic.  By default each rotated element is computed in binary32,
+ *   compensated so that the value before the final rounding is within about
+ *   2^-23 relative of the exact x_u*c - x_v*s (also under cancellation); the
+ *   fp16 result is then the correctly rounded value or, rarely, its
+ *   neighbour (at most 1 fp16 ulp away).  With RKV_ROUND_EXACT OR-ed into
+ *   ropeStyle, the products and the sum are evaluated exactly in binary64
+ *   and rounded once to binary16: the correctly rounded result, bit for bit,
+ *   at some extra arithmetic cost.
  */
 #ifndef ROPE_KV_CACHE_H
 #define ROPE_KV_CACHE_H
@@ -62,7 +68,12 @@ typedef enum {
   RKV_ERR_HIP = 8           /* the HIP runtime reported an error at launch */
 } rkv_status;
 
-typedef enum { RKV_ROPE_NEOX = 0, RKV_ROPE_GPTJ = 1 } rkv_rope_style;
+/* ropeStyle: the pair layout, optionally OR-ed with RKV_ROUND_EXACT. */
+typedef enum {
+  RKV_ROPE_NEOX = 0,      /* pairs (i, i + R/2) */
+  RKV_ROPE_GPTJ = 1,      /* pairs (2i, 2i + 1) */
+  RKV_ROUND_EXACT = 0x100 /* correctly rounded results (see Rotation above) */
+} rkv_rope_style;
 
 typedef enum { RKV_F16 = 0, RKV_F32 = 1, RKV_I32 = 2 } rkv_dtype;
 

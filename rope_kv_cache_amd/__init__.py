@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(HERE, "librkv.so")
 
 ROPE_NEOX = 0
 ROPE_GPTJ = 1
+ROUND_EXACT = 0x100   # OR into rope_style for correctly rounded (binary64) arithmetic
 
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_ALIGNMENT, ERR_ALIAS, \
     ERR_HIP = range(9)
@@ -47,11 +48,11 @@ class RkvTensor(ctypes.Structure):
                 ("shape", ctypes.c_int64 * 5)]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
                           "or python rope_kv_cache_amd/_build.py")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32 = ctypes.c_int32
     T = ctypes.POINTER(RkvTensor)

@@ -24,9 +24,12 @@ rkv_status fail(rkv_status st, const char* fmt, ...) {
 
 void clear_error() { g_err[0] = '\0'; }
 
-// Launch shape: keep the chip's 1024 SIMDs fed with many waves when the
-// token count is small by splitting a token's row sets over several waves.
-constexpr long long kTargetWaves = 32768;
+// Launch shape.  A wave handles G row groups (512/D rows each) of one work
+// item.  Large launches are bandwidth-bound and run fastest with one row
+// group per wave; small ones are latency-bound, so they take G = 2 or 4
+// when that keeps every wave resident at once (256 CUs x 4 SIMDs x 8 waves).
+constexpr long long kResidentWaves = 8192;
+constexpr long long kStreamingGroups = 65536;
 
 int elem_size(int32_t dtype) { return dtype == RKV_F16 ? 2 : 4; }
 
@@ -81,10 +84,16 @@ rkv_status check_no_alias(const Span* outs, int n_out, const Span* ins, int n_in
 }
 
 rkv_status check_style(int32_t style) {
-  if (style != RKV_ROPE_NEOX && style != RKV_ROPE_GPTJ)
-    return fail(RKV_ERR_SHAPE, "ropeStyle %d is neither NeoX (0) nor GPT-J (1)", style);
+  const int32_t layout = style & ~RKV_ROUND_EXACT;
+  if (layout != RKV_ROPE_NEOX && layout != RKV_ROPE_GPTJ)
+    return fail(RKV_ERR_SHAPE,
+                "ropeStyle %d: layout must be NeoX (0) or GPT-J (1), optionally | RKV_ROUND_EXACT",
+                style);
   return RKV_OK;
 }
+
+int32_t layout_of(int32_t style) { return style & ~RKV_ROUND_EXACT; }
+bool exact_of(int32_t style) { return (style & RKV_ROUND_EXACT) != 0; }
 
 rkv_status check_dims(int32_t D, int32_t R) {
   if (R < 0 || R > D || (R & 1))
@@ -96,18 +105,21 @@ rkv_status check_dims(int32_t D, int32_t R) {
   return RKV_OK;
 }
 
-// Waves per work item: at most kUnroll row sets per wave pass, and more
-// waves (down to one row set each) while the grid is small.
-int32_t pick_split(long long items, int32_t row_sets, int unroll) {
-  long long f = (row_sets + unroll - 1) / unroll;
-  if (f < 1) f = 1;
-  if (items > 0 && items * f < kTargetWaves) {
-    long long want = (kTargetWaves + items - 1) / items;
-    f = want < row_sets ? want : row_sets;
-    if (f < 1) f = 1;
+struct Split {
+  int32_t groups_per_wave;
+  int32_t waves_per_item;
+};
+
+// Returns G = 0 when the wave count would not fit in int32.
+Split pick_split(long long items, long long groups_per_item) {
+  auto waves = [&](int g) { return items * ((groups_per_item + g - 1) / g); };
+  int g = 1;
+  if (items * groups_per_item <= kStreamingGroups) {
+    while (g < 4 && waves(g) > kResidentWaves) g *= 2;
   }
-  while (f > 1 && items * f > INT32_MAX) --f;
-  return (int32_t)f;
+  while (g < 4 && waves(g) > INT32_MAX) g *= 2;
+  if (waves(g) > INT32_MAX) return Split{0, 0};
+  return Split{g, (int32_t)((groups_per_item + g - 1) / g)};
 }
 
 rkv_status launched(hipError_t e) {
@@ -192,11 +204,16 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.table_batch = (int32_t)TB;
   p.table_len = (int32_t)TL;
   p.R = (int32_t)R;
-  const int rows_per_set = 64 / ((int)D / 16);
-  p.row_sets = (int32_t)((H + rows_per_set - 1) / rows_per_set);
-  p.waves_per_token = pick_split(tokens, p.row_sets, rkv::kContigUnroll);
+  const long long rows_per_group = 512 / D;
+  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group);
+  if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
+  p.groups_per_wave = sp.groups_per_wave;
+  p.waves_per_token = sp.waves_per_item;
   p.total_waves = (int32_t)(tokens * p.waves_per_token);
-  return launched(rkv::launch_contig(p, call, (int)D, style, stream));
+  p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_token);
+  p.div_seq = rkv::make_fastdiv((uint32_t)S);
+  return launched(
+      rkv::launch_contig(p, call, (int)D, layout_of(style), exact_of(style), stream));
 }
 
 }  // namespace
@@ -287,11 +304,15 @@ rkv_status rkv_dflash_target_kv_cache_update(
   p.R = rotaryDim;
   p.num_pages = numPages;
   p.max_pages = maxPagesPerSeq;
-  const int rows_per_set = 64 / (headDim / 16);
-  p.row_sets = (int32_t)((2 * Hkv + rows_per_set - 1) / rows_per_set);
-  p.waves_per_row = pick_split(N, p.row_sets, rkv::kPagedUnroll);
+  const long long rows_per_group = 512 / D;
+  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group);
+  if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
+  p.groups_per_wave = sp.groups_per_wave;
+  p.waves_per_row = sp.waves_per_item;
   p.total_waves = (int32_t)(N * p.waves_per_row);
-  return launched(rkv::launch_paged(p, headDim, ropeStyle, stream));
+  p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
+  return launched(
+      rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle), stream));
 }
 
 rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {

@@ -10,9 +10,25 @@ namespace rkv {
 enum Call : int { kCallPacked = 0, kCallContinuous = 1, kCallTree = 2 };
 
 constexpr int kTokensPerPage = 64;
-// Row sets a wave keeps in flight at once (two 16-byte loads per lane each).
-constexpr int kContigUnroll = 4;
-constexpr int kPagedUnroll = 2;
+
+// Division by a launch constant d >= 1 for numerators n < 2^31, by
+// multiply-high and shift (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994, round-up method):
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, l};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  return (__umulhi(f.m, n) + n) >> f.l;
+}
 
 struct ContigParams {
   const float* cos_sin;     // [table_batch, table_len, R]
@@ -23,9 +39,11 @@ struct ContigParams {
   const int32_t* pos_ids;   // [B, S]; call 3
   int32_t B, S, Hq, Hkv, cap;
   int32_t table_batch, table_len, R;
-  int32_t row_sets;         // ceil((Hq + 2*Hkv) / rows per set)
-  int32_t waves_per_token;  // waves sharing one token's row sets
+  int32_t groups_per_wave;  // G: row groups of 512/D rows handled by one wave (1, 2 or 4)
+  int32_t waves_per_token;  // ceil(row groups per token / G)
   int32_t total_waves;      // B * S * waves_per_token
+  FastDiv div_waves;        // by waves_per_token
+  FastDiv div_seq;          // by S
 };
 
 struct PagedParams {
@@ -37,12 +55,14 @@ struct PagedParams {
   const int32_t* seq;       // [N]
   const int32_t* page_table;// [batch, 2, max_pages]
   int32_t N, batch, Hkv, R, num_pages, max_pages;
-  int32_t row_sets;         // ceil(2*Hkv / rows per set)
-  int32_t waves_per_row;    // waves sharing one delta row
+  int32_t groups_per_wave;  // G: row groups of 512/D rows handled by one wave (1, 2 or 4)
+  int32_t waves_per_row;    // ceil(row groups per delta row / G)
   int32_t total_waves;      // N * waves_per_row
+  FastDiv div_waves;        // by waves_per_row
 };
 
-hipError_t launch_contig(const ContigParams& p, int call, int D, int style, hipStream_t stream);
-hipError_t launch_paged(const PagedParams& p, int D, int style, hipStream_t stream);
+hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool exact,
+                         hipStream_t stream);
+hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, hipStream_t stream);
 
 }  // namespace rkv

@@ -6,6 +6,20 @@
 // NeoX pairs element i with i + R/2, GPT-J pairs 2i with 2i+1; frequency i
 // drives pair i.
 //
+// Lane layout.  A head row of D fp16 values is D/8 chunks of 16 bytes.  In a
+// wave instruction, lane l holds chunk c = l % (D/8) of row l / (D/8), so
+// one instruction covers 512/D whole rows, i.e. 1 KB of contiguous memory
+// when the rows are adjacent.  Chunks c < R/8 are rotary, the others pass
+// through.
+//   GPT-J: chunk c holds the pairs (8c+2k, 8c+2k+1), k < 4, at frequency
+//          4c + k: no data leaves the lane.
+//   NeoX:  chunk c < R/16 holds the first members u = 8c + k of the pairs
+//          (u, u + R/2), whose second members sit in chunk c + R/16, i.e.
+//          lane l + R/16; a lane with R/16 <= c < R/8 holds second members
+//          and finds its partners in lane l - R/16.  The partner chunk is
+//          fetched with ds_bpermute, one dword at a time, by every lane of
+//          the wave at once.  Frequency of element k: 8*(c mod R/16) + k.
+//
 // Exactness.  An fp16 significand has 11 bits and an fp32 one 24, so each
 // product is exact in binary64; fma(x_u, c, -(x_v*s)) therefore rounds the
 // exact value x_u*c - x_v*s once to binary64.  The narrowing to binary16 goes
@@ -44,19 +58,28 @@ __device__ __forceinline__ uint32_t narrow_exact(double y) {
   return f2h_bits(__builtin_bit_cast(float, bits));
 }
 
-// One pair: (a, b) -> (a*c - b*s, b*c + a*s), fp16 bits in and out.
+// x*c + sign*(p*s), with sign = -1 (first pair member) or +1 (second).
+//
+// kExact: binary64 products and sum (exact up to the one binary64 rounding),
+// narrowed with round-to-odd -- bit-identical to a correctly rounded result.
+// Otherwise binary32, compensated: ps = RN(p*s) and its exact rounding error
+// e = fma(p, s, -ps) are formed first, then y = RN(RN(x*c - ps) - e) (the
+// first by one fma).  The two remaining roundings put y within about 2^-23
+// relative of the exact value, with no loss under cancellation, so the fp16
+// result is the correctly rounded one or its neighbour.
 template <bool kExact>
-__device__ __forceinline__ void rotate_pair(uint32_t a_bits, uint32_t b_bits, float c, float s,
-                                            uint32_t& ya, uint32_t& yb) {
+__device__ __forceinline__ uint32_t rot1(uint32_t x_bits, uint32_t p_bits, float c, float s,
+                                         bool first) {
   if constexpr (kExact) {
-    double a = (double)h2f(a_bits), b = (double)h2f(b_bits);
-    double cd = (double)c, sd = (double)s;
-    ya = narrow_exact(__builtin_fma(a, cd, -(b * sd)));
-    yb = narrow_exact(__builtin_fma(b, cd, a * sd));
+    double x = (double)h2f(x_bits), pv = (double)h2f(p_bits);
+    double ps = pv * (double)s;               // exact
+    return narrow_exact(__builtin_fma(x, (double)c, first ? -ps : ps));
   } else {
-    float a = h2f(a_bits), b = h2f(b_bits);
-    ya = f2h_bits(__builtin_fmaf(a, c, -(b * s)));
-    yb = f2h_bits(__builtin_fmaf(b, c, a * s));
+    const float x = h2f(x_bits), pv = h2f(p_bits);
+    const float sv = first ? -s : s;
+    const float ps = pv * sv;
+    const float e = __builtin_fmaf(pv, sv, -ps);   // exact: pv*sv - ps
+    return f2h_bits(__builtin_fmaf(x, c, ps) + e);
   }
 }
 
@@ -64,90 +87,106 @@ __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
-// Rotate the pairs held by one lane.
-//
-// A lane owns two 8-element chunks of a head row: A at element offset o and
-// B at o + R/2, with o = 8j for rotary lane j.
-//   NeoX: element k of A pairs with element k of B, frequency 8j + k;
-//         c[k], s[k] hold that frequency's cos and sin.
-//   GPT-J: elements (2k, 2k+1) of A pair with each other at frequency
-//         4j + k (c[k], s[k]), and those of B at frequency 4j + R/4 + k
-//         (c[4+k], s[4+k]).
-template <int kStyle, bool kExact>
-__device__ __forceinline__ void rotate_chunks(uint4& A, uint4& B, const float (&c)[8],
-                                              const float (&s)[8]) {
-  uint32_t a[4] = {A.x, A.y, A.z, A.w};
-  uint32_t b[4] = {B.x, B.y, B.z, B.w};
-  if constexpr (kStyle == kNeox) {
+// NeoX: the lane's 8 elements x with the partner chunk p; c[k], s[k] are
+// the cos/sin of element k's frequency; `first` for chunks c < R/16.
+template <bool kExact>
+__device__ __forceinline__ uint4 rotate_neox(uint4 x, uint4 p, const float (&c)[8],
+                                             const float (&s)[8], bool first) {
+  uint32_t xa[4] = {x.x, x.y, x.z, x.w};
+  uint32_t pa[4] = {p.x, p.y, p.z, p.w};
+  uint32_t y[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t ya0, yb0, ya1, yb1;
-      rotate_pair<kExact>(lo16(a[w]), lo16(b[w]), c[2 * w], s[2 * w], ya0, yb0);
-      rotate_pair<kExact>(hi16(a[w]), hi16(b[w]), c[2 * w + 1], s[2 * w + 1], ya1, yb1);
-      a[w] = pack2(ya0, ya1);
-      b[w] = pack2(yb0, yb1);
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t y0, y1;
-      rotate_pair<kExact>(lo16(a[w]), hi16(a[w]), c[w], s[w], y0, y1);
-      a[w] = pack2(y0, y1);
-      rotate_pair<kExact>(lo16(b[w]), hi16(b[w]), c[4 + w], s[4 + w], y0, y1);
-      b[w] = pack2(y0, y1);
-    }
+  for (int w = 0; w < 4; ++w) {
+    uint32_t y0 = rot1<kExact>(lo16(xa[w]), lo16(pa[w]), c[2 * w], s[2 * w], first);
+    uint32_t y1 = rot1<kExact>(hi16(xa[w]), hi16(pa[w]), c[2 * w + 1], s[2 * w + 1], first);
+    y[w] = pack2(y0, y1);
   }
-  A = make_uint4(a[0], a[1], a[2], a[3]);
-  B = make_uint4(b[0], b[1], b[2], b[3]);
+  return make_uint4(y[0], y[1], y[2], y[3]);
 }
 
-// Chunk placement of lane j (0 <= j < D/16) inside a head row of D elements,
-// and whether it rotates.  Rotary lanes j < R/16 own chunks 8j and 8j + R/2;
-// the remaining lanes own the passthrough dims [R, D), split the same way.
-struct LaneChunks {
-  int off_a;
-  int off_b;
-  bool rotary;
+// GPT-J: dword w of the chunk holds the pair (lo, hi) at frequency w.
+template <bool kExact>
+__device__ __forceinline__ uint4 rotate_gptj(uint4 x, const float (&c)[8], const float (&s)[8]) {
+  uint32_t xa[4] = {x.x, x.y, x.z, x.w};
+  uint32_t y[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t y0 = rot1<kExact>(lo16(xa[w]), hi16(xa[w]), c[w], s[w], true);
+    uint32_t y1 = rot1<kExact>(hi16(xa[w]), lo16(xa[w]), c[w], s[w], false);
+    y[w] = pack2(y0, y1);
+  }
+  return make_uint4(y[0], y[1], y[2], y[3]);
+}
+
+// Fetch lane `src_lane`'s chunk (all lanes of the wave must execute this).
+__device__ __forceinline__ uint4 lane_fetch(uint4 v, int src_lane) {
+  const int addr = src_lane << 2;
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
+}
+
+// Role of a lane's chunk index c in a row of D elements with rotary dim R.
+struct ChunkRole {
+  bool rotary;     // c < R/8
+  bool first;      // NeoX: holds first pair members (c < R/16)
+  int partner;     // NeoX: lane offset of the partner chunk (+R/16 or -R/16), else 0
+  int freq0;       // index of the first frequency this lane uses
 };
 
-template <int D>
-__device__ __forceinline__ LaneChunks lane_chunks(int j, int R) {
-  LaneChunks lc;
-  int rot_lanes = R >> 4;
-  if (j < rot_lanes) {
-    lc.rotary = true;
-    lc.off_a = 8 * j;
-    lc.off_b = 8 * j + (R >> 1);
+template <int kStyle>
+__device__ __forceinline__ ChunkRole chunk_role(int c, int R) {
+  ChunkRole r;
+  const int half_chunks = R >> 4;   // R/16
+  r.rotary = c < 2 * half_chunks;
+  r.first = c < half_chunks;
+  if constexpr (kStyle == kNeox) {
+    r.partner = r.rotary ? (r.first ? half_chunks : -half_chunks) : 0;
+    r.freq0 = 8 * (r.first ? c : c - half_chunks);
   } else {
-    int p = j - rot_lanes;
-    lc.rotary = false;
-    lc.off_a = R + 8 * p;
-    lc.off_b = R + 8 * p + ((D - R) >> 1);
+    r.partner = 0;
+    r.freq0 = 4 * c;
   }
-  return lc;
+  return r;
 }
 
-// The cos/sin values a rotary lane needs from one table row [cos | sin].
+// The cos/sin values a rotary lane needs from one table row [cos | sin]:
+// NeoX: 8 frequencies from freq0; GPT-J: 4 frequencies from freq0 (c[0..3]).
 template <int kStyle>
-__device__ __forceinline__ void load_cos_sin(const float* row, int j, int R, float (&c)[8],
+__device__ __forceinline__ void load_cos_sin(const float* row, int freq0, int R, float (&c)[8],
                                              float (&s)[8]) {
   const int half = R >> 1;
-  float4 c0, c1, s0, s1;
-  if constexpr (kStyle == kNeox) {
-    c0 = *reinterpret_cast<const float4*>(row + 8 * j);
-    c1 = *reinterpret_cast<const float4*>(row + 8 * j + 4);
-    s0 = *reinterpret_cast<const float4*>(row + half + 8 * j);
-    s1 = *reinterpret_cast<const float4*>(row + half + 8 * j + 4);
-  } else {
-    c0 = *reinterpret_cast<const float4*>(row + 4 * j);
-    c1 = *reinterpret_cast<const float4*>(row + 4 * j + (R >> 2));
-    s0 = *reinterpret_cast<const float4*>(row + half + 4 * j);
-    s1 = *reinterpret_cast<const float4*>(row + half + 4 * j + (R >> 2));
-  }
+  const float4 c0 = *reinterpret_cast<const float4*>(row + freq0);
+  const float4 s0 = *reinterpret_cast<const float4*>(row + half + freq0);
   c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
-  c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
   s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
-  s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+  if constexpr (kStyle == kNeox) {
+    const float4 c1 = *reinterpret_cast<const float4*>(row + freq0 + 4);
+    const float4 s1 = *reinterpret_cast<const float4*>(row + half + freq0 + 4);
+    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+    s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+  } else {
+#pragma unroll
+    for (int k = 4; k < 8; ++k) { c[k] = 0.f; s[k] = 0.f; }
+  }
+}
+
+// Rotate (or pass through) one chunk.  Must be called by every lane of the
+// wave with the same control flow (the NeoX partner fetch is a wave-wide
+// permute); lanes whose row is not rotated simply keep their value.
+template <int kStyle, bool kExact>
+__device__ __forceinline__ uint4 rotate_chunk(uint4 x, int lane, const ChunkRole& role,
+                                              bool rotate_row, const float (&c)[8],
+                                              const float (&s)[8]) {
+  if constexpr (kStyle == kNeox) {
+    const uint4 p = lane_fetch(x, lane + role.partner);
+    if (rotate_row && role.rotary) return rotate_neox<kExact>(x, p, c, s, role.first);
+    return x;
+  } else {
+    if (rotate_row && role.rotary) return rotate_gptj<kExact>(x, c, s);
+    return x;
+  }
 }
 
 }  // namespace rkv

@@ -10,8 +10,10 @@ Comparison rules:
   oracle bit for bit;
 * rotated Q/K elements must satisfy |gpu - ref| <= 2^-10*|ref| + 1e-3
   (non-finite values must match in kind);
-* ``compare`` also counts rotated elements whose bits differ, so that a test
-  can require bit equality -- which the kernels' exact arithmetic provides.
+* ``compare`` also counts rotated elements whose bits differ and their
+  largest distance in fp16 ulps, so that a test can require bit equality
+  (the library's RKV_ROUND_EXACT mode) or at most one ulp (its default
+  binary32 arithmetic).
 """
 from __future__ import annotations
 
@@ -50,20 +52,23 @@ def upload(w, device="cuda") -> dict:
     return t
 
 
-def launch(w, t: dict) -> None:
+def launch(w, t: dict, exact: bool = False) -> None:
+    """One call of the library on the uploaded workload; ``exact`` ORs
+    ROUND_EXACT into the rope style (binary64, correctly rounded)."""
     import rope_kv_cache_amd as rkv
+    style = w.style | (rkv.ROUND_EXACT if exact else 0)
     if isinstance(w, W.Paged):
         rkv.dflash_target_kv_cache_update(t["k_delta"], t["v_delta"], t["pool"], t["cos_sin"],
                                           t["positions"], t["seq"], t["page_table"], w.batch,
-                                          w.style)
+                                          style)
     elif w.call == "packed":
-        rkv.apply_rope_write_kv_packed_qkv(t["cos_sin"], t["qkv"], t["cache"], w.style)
+        rkv.apply_rope_write_kv_packed_qkv(t["cos_sin"], t["qkv"], t["cache"], style)
     elif w.call == "continuous":
         rkv.apply_rope_write_kv_continuous(t["cos_sin"], t["end_lens"], t["qkv"], t["cache"],
-                                           t["q_out"], w.style)
+                                           t["q_out"], style)
     else:
         rkv.apply_rope_write_kv_tree(t["cos_sin"], t["end_lens"], t["pos_ids"], t["qkv"],
-                                     t["cache"], t["q_out"], w.style)
+                                     t["cache"], t["q_out"], style)
 
 
 def download(w, t: dict) -> dict:
@@ -79,9 +84,9 @@ def download(w, t: dict) -> dict:
     return out
 
 
-def run_gpu(w, device="cuda") -> dict:
+def run_gpu(w, device="cuda", exact: bool = False) -> dict:
     t = upload(w, device)
-    launch(w, t)
+    launch(w, t, exact)
     return download(w, t)
 
 

@@ -2,9 +2,10 @@
 
 Every test calls the C ABI through the Python binding, on cuda:0.  Outputs
 are compared with ``tests/harness.compare``: bit-exact everywhere except
-rotated Q/K, which must meet |gpu - ref| <= 2^-10*|ref| + 1e-3; the
-``exact`` assertions additionally require rotated Q/K to be bit-identical,
-which the kernels' binary64 products with round-to-odd narrowing guarantee.
+rotated Q/K, which must meet |gpu - ref| <= 2^-10*|ref| + 1e-3.  Each case
+runs in both arithmetic modes: the default binary32 mode must also stay
+within one fp16 ulp of the oracle, and the RKV_ROUND_EXACT mode must be
+bit-identical to it.
 """
 import numpy as np
 import pytest
@@ -23,16 +24,25 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def check(w, exact=True):
+def check(w, modes=("fast", "exact")):
+    """Run the library in each arithmetic mode on fresh copies of the inputs
+    and compare with one oracle run: the default (binary32) mode must stay
+    within one fp16 ulp, the exact mode must be bit-identical."""
     _say(f"[parity] {w.name} tokens={w.tokens}")
-    got = run_gpu(w)
     want = expected(w)
-    rep = compare(w, got, want)
-    _say(f"[parity] {w.name} rotated bit differences: {rep}")
-    if exact:
-        diffs = {k: v for k, v in rep.items() if not k.endswith("_max_ulp") and v}
-        assert not diffs, f"rotated Q/K not bit-identical: {rep}"
-    return rep
+    reps = {}
+    for mode in modes:
+        got = run_gpu(w, exact=(mode == "exact"))
+        rep = compare(w, got, want)
+        _say(f"[parity] {w.name} {mode}: rotated elements differing from the oracle: {rep}")
+        if mode == "exact":
+            diffs = {k: v for k, v in rep.items() if not k.endswith("_max_ulp") and v}
+            assert not diffs, f"exact mode not bit-identical: {rep}"
+        else:
+            ulps = {k: v for k, v in rep.items() if k.endswith("_max_ulp")}
+            assert all(v <= 1 for v in ulps.values()), f"more than 1 ulp: {rep}"
+        reps[mode] = rep
+    return reps
 
 
 # ------------------------------------------------------- the five configs --
@@ -173,7 +183,8 @@ def test_paged_pool_beyond_4g_elements():
          "positions": dev(pos), "seq": dev(seq), "page_table": dev(pt)}
     import rope_kv_cache_amd as rkv
     rkv.dflash_target_kv_cache_update(t["k_delta"], t["v_delta"], pool, t["cos_sin"],
-                                      t["positions"], t["seq"], t["page_table"], batch, NEOX)
+                                      t["positions"], t["seq"], t["page_table"], batch,
+                                      NEOX | rkv.ROUND_EXACT)
     torch.cuda.synchronize()
     flat = pool.view(2 * P, 64 * Hkv * D)
     touched = (flat.view(torch.int16) != W.SENTINEL).any(dim=1).nonzero().flatten().cpu().numpy()
@@ -208,7 +219,8 @@ def test_contiguous_cache_beyond_4g_elements():
     cache.view(torch.int16).fill_(W.SENTINEL)
     import rope_kv_cache_amd as rkv
     q_out = dev(W.sentinel_f16((B, S, Hq, D)))
-    rkv.apply_rope_write_kv_continuous(dev(cs_full), dev(end), dev(qkv), cache, q_out, GPTJ)
+    rkv.apply_rope_write_kv_continuous(dev(cs_full), dev(end), dev(qkv), cache, q_out,
+                                       GPTJ | rkv.ROUND_EXACT)
     torch.cuda.synchronize()
     assert np.array_equal(host16(q_out), want["q_out"])
     tail = host16(cache[:, :, :, lo:])
@@ -233,7 +245,7 @@ def test_runs_on_the_current_stream_and_repeats():
     s.synchronize()
     got = download(w, t)
     rep = compare(w, got, want)
-    assert not {k: v for k, v in rep.items() if v and not k.endswith("ulp")}
+    assert all(v <= 1 for k, v in rep.items() if k.endswith("ulp"))
 
 
 def test_packed_twice_rotates_twice():
@@ -241,8 +253,8 @@ def test_packed_twice_rotates_twice():
     once_q, once_c = oracle.packed_qkv(w.cos_sin, w.qkv, w.cache, NEOX)
     twice_q, twice_c = oracle.packed_qkv(w.cos_sin, once_q, once_c, NEOX)
     t = upload(w)
-    launch(w, t)
-    launch(w, t)
+    launch(w, t, exact=True)
+    launch(w, t, exact=True)
     got = download(w, t)
     assert np.array_equal(got["qkv"], twice_q)
     assert np.array_equal(got["cache"], twice_c)
