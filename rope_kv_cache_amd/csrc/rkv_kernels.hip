@@ -27,12 +27,25 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
 __device__ __forceinline__ void st16(uint16_t* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Streaming (non-temporal) 16-byte accesses for data touched exactly once.
+// On the large packed prefill they lift the kernel from ~250 us to ~228 us
+// (measured on MI355X); the reused cos/sin rows keep ordinary loads.
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
+__device__ __forceinline__ void st16_stream(uint16_t* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
@@ -83,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     row[g] = (part * G + g) * kRowsPerGroup + row_in_group;
-    x[g] = row[g] < H ? ld16(tok_base + (size_t)row[g] * D + 8 * c) : make_uint4(0, 0, 0, 0);
+    x[g] = row[g] < H ? ld16_stream(tok_base + (size_t)row[g] * D + 8 * c) : make_uint4(0, 0, 0, 0);
   }
 
   int slot = s, pos = s;
@@ -112,13 +125,13 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
     if (is_q) {
       uint16_t* dst = (kCall == kCallPacked) ? tok_base + (size_t)r * D
                                              : p.q_out + ((size_t)token * p.Hq + r) * D;
-      st16(dst + 8 * c, y);
+      st16_stream(dst + 8 * c, y);
     } else {
       const int h = is_k ? r - p.Hq : r - p.Hq - p.Hkv;
       uint16_t* dst =
           p.cache + ((((size_t)b * 2 + (is_k ? 0 : 1)) * p.Hkv + h) * (size_t)p.cap + slot) * D;
-      st16(dst + 8 * c, y);
-      if (kCall == kCallPacked && is_k) st16(tok_base + (size_t)r * D + 8 * c, y);
+      st16_stream(dst + 8 * c, y);
+      if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
     }
   }
 }
