@@ -7,8 +7,9 @@ seeded synthetic data already resident in HBM.  W warm-up steps, then K timed
 steps bracketed by device synchronisation; each launch is also bracketed by
 HIP events on its stream, which give the kernel's average duration for the
 roofline.  The same workload in the library's RKV_ROUND_EXACT mode and the
-other workloads (continuous write, tree write, paged delta update) are
-reported under "workloads".  The small workloads' inputs fit the 256 MB
+other workloads (continuous write, tree write, paged delta update, and the
+paged update with the cos/sin gather fused in) are reported under
+"workloads".  The small workloads' inputs fit the 256 MB
 MALL, so a 1 GiB buffer is read before each of their timed launches to push
 them back to HBM (a read leaves clean lines, so the timed kernel inherits no
 write-back); their event-bracketed times include the events' own overhead
@@ -85,6 +86,17 @@ def bytes_paged(w) -> int:
     k_ok = live & (kid >= 0) & (kid < P)
     v_ok = live & (vid >= P) & (vid < 2 * P)
     row = Hkv * D * 2
+    if w.extra.get("gather"):
+        # cos/sin come from the rope table: each distinct (state, position) row once,
+        # for rows whose K is written; plus the state indices when given
+        rope = w.extra["rope"]
+        si = w.extra["state_indices"]
+        st = si[qq] if si is not None else (np.zeros_like(qq) if rope.shape[0] == 1 else qq)
+        has_row = (st >= 0) & (st < rope.shape[0]) & (p < rope.shape[1])
+        k_ok = k_ok & has_row
+        rows_read = len({(int(a), int(b)) for a, b in zip(st[k_ok], p[k_ok])})
+        return int(k_ok.sum()) * 2 * row + rows_read * R * 4 + int(v_ok.sum()) * 2 * row \
+            + w.N * 8 + int(live.sum()) * 8 + (0 if si is None else si.size * 4)
     return int(k_ok.sum()) * (2 * row + R * 4) + int(v_ok.sum()) * 2 * row \
         + w.N * 8 + int(live.sum()) * 8
 
@@ -267,7 +279,8 @@ def main():
         cases = [("continuous_neox", lambda: W.config(2, W.NEOX)),
                  ("continuous_gptj", lambda: W.config(2, W.GPTJ)),
                  ("tree", lambda: W.config(3)),
-                 ("paged_delta", lambda: W.config(4))]
+                 ("paged_delta", lambda: W.config(4)),
+                 ("paged_delta_gather_fused", lambda: W.config(41))]
         for label, make in cases:
             log(f"[bench] generating {label}")
             x = make()

@@ -166,6 +166,26 @@ rkv_status rkv_dflash_target_kv_cache_update(
     int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim,
     int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
 
+/* Call 4 with the cos/sin gather fused in (the page's
+ * launchDFlashGatherDeltaRope builds tokenAlignedCosSin from a rope table;
+ * only its parameter list is given, so its meaning here is a reading).
+ *   ropeCosSin    [in] f32 [ropeStates, ropeRows, R]: rope table(s), rows
+ *                      [cos | sin] by position.
+ *   stateIndices  [in] i32 [batchSize] or NULL: sequence q uses table
+ *                      stateIndices[q]; NULL means table q (table 0 when
+ *                      ropeStates == 1).
+ * Everything else is as in rkv_dflash_target_kv_cache_update.  The K row of
+ * delta row i is rotated with ropeCosSin[state(q_i), p_i] and written only
+ * if that state exists and p_i < ropeRows; V follows the page table alone.
+ * Saves the separate gather launch and its N*R*4-byte buffer. */
+rkv_status rkv_dflash_target_kv_cache_update_gather_rope(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCache, const float* ropeCosSin,
+    int32_t ropeStates, int32_t ropeRows, const int32_t* stateIndices,
+    const int32_t* deltaPositions, const int32_t* deltaTokenToSequence, const int32_t* pageTable,
+    int32_t numDeltaTokens, int32_t batchSize, int32_t numKVHeads, int32_t headDim,
+    int32_t rotaryDim, int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle,
+    hipStream_t stream);
+
 /* Host-only capacity check.
  * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
  *  checkDFlashRopeCapacity.)

@@ -65,6 +65,11 @@ def _declare(L):
     L.rkv_ref_tree.argtypes = [P, i32, i32, i32, P, P, P, i32, i32, i32, i32, i32, P, i32, P, i32]
     L.rkv_ref_paged_delta.restype = ctypes.c_int
     L.rkv_ref_paged_delta.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32]
+    L.rkv_ref_gather_delta_rope.restype = ctypes.c_int
+    L.rkv_ref_gather_delta_rope.argtypes = [P, i32, i32, P, P, P, i32, i32, i32, P]
+    L.rkv_ref_paged_delta_gather.restype = ctypes.c_int
+    L.rkv_ref_paged_delta_gather.argtypes = [P, P, P, P, i32, i32, P, P, P, P, i32, i32, i32,
+                                             i32, i32, i32, i32, i32]
     L.rkv_ref_check_rope_capacity.restype = ctypes.c_int
     L.rkv_ref_check_rope_capacity.argtypes = [i32, i32]
     return L
@@ -167,6 +172,42 @@ def paged_delta(k_delta, v_delta, pool, token_cos_sin, positions, seq, page_tabl
     return pool
 
 
+def gather_delta_rope(rope, state_indices, positions, seq, batch: int, L=None):
+    """Rows of a rope table [states, rows, R] for the delta rows; NaN where none."""
+    rope = _c(rope, np.float32)
+    si = None if state_indices is None else _c(state_indices, np.int32)
+    positions = _c(positions, np.int32)
+    seq = _c(seq, np.int32)
+    n, R = positions.size, rope.shape[2]
+    out = np.empty((n, R), dtype=np.float32)
+    rc = (L or lib()).rkv_ref_gather_delta_rope(_p(rope), rope.shape[0], rope.shape[1], _p(si),
+                                                _p(positions), _p(seq), n, batch, R, _p(out))
+    if rc:
+        raise OracleError(rc, "gather_delta_rope")
+    return out
+
+
+def paged_delta_gather(k_delta, v_delta, pool, rope, state_indices, positions, seq, page_table,
+                       batch: int, style: int, L=None):
+    """Call 4 with the rope-table gather fused in.  Returns the updated pool."""
+    k_delta = _c(k_delta, np.uint16)
+    v_delta = _c(v_delta, np.uint16)
+    pool = _c(pool, np.uint16).copy()
+    rope = _c(rope, np.float32)
+    si = None if state_indices is None else _c(state_indices, np.int32)
+    positions = _c(positions, np.int32)
+    seq = _c(seq, np.int32)
+    page_table = _c(page_table, np.int32)
+    N, Hkv, D = k_delta.shape
+    rc = (L or lib()).rkv_ref_paged_delta_gather(
+        _p(k_delta), _p(v_delta), _p(pool), _p(rope), rope.shape[0], rope.shape[1], _p(si),
+        _p(positions), _p(seq), _p(page_table), N, batch, Hkv, D, rope.shape[2], pool.shape[1],
+        page_table.shape[2], style)
+    if rc:
+        raise OracleError(rc, "paged_delta_gather")
+    return pool
+
+
 def check_rope_capacity(cos_sin_len: int, kv_capacity: int, L=None) -> int:
     return (L or lib()).rkv_ref_check_rope_capacity(cos_sin_len, kv_capacity)
 
@@ -178,6 +219,10 @@ def run(w, L=None):
     ``qkv`` (call 1), ``q_out`` (calls 2, 3), ``cache`` (calls 1-3), ``pool`` (call 4).
     """
     if hasattr(w, "pool"):
+        if w.extra.get("gather"):
+            return {"pool": paged_delta_gather(w.k_delta, w.v_delta, w.pool, w.extra["rope"],
+                                               w.extra["state_indices"], w.positions, w.seq,
+                                               w.page_table, w.batch, w.style, L=L)}
         return {"pool": paged_delta(w.k_delta, w.v_delta, w.pool, w.cos_sin, w.positions, w.seq,
                                     w.page_table, w.batch, w.style, L=L)}
     if w.call == "packed":

@@ -42,6 +42,9 @@
  *      is in [numPages, 2*numPages).
  *  R14 call 4: the rotation layout is an explicit argument.
  *  R17 the capacity check rejects exactly cosSinSeqLen > kvCapacity.
+ *  R23 fused gather: sequence q reads rope-table state stateIndices[q] (q
+ *      itself without state indices; 0 for a single-state table); a row
+ *      whose state or position has no table row writes no K (V as usual).
  *  Parity unpinned against the original system for R6 and R7: no page fixes
  *  them; they are the plainest reading consistent with the rest.
  */
@@ -283,18 +286,29 @@ int rkv_ref_tree(const float* cos_sin, int32_t table_batch, int32_t table_len,
  * beyond max_pages_per_seq pages is skipped.  The position's logical page
  * p/64 is looked up per plane in page_table[seq, plane, :]; the ids are
  * canonical, so the pool reads as [2*numPages][64][Hkv][D] and the K (V)
- * plane writes only ids in its own range (R13).  K is rotated with row i of
- * token_cos_sin; V is copied bit for bit. */
-int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
-                        const float* token_cos_sin, const int32_t* delta_positions,
-                        const int32_t* delta_to_seq, const int32_t* page_table,
-                        int32_t num_delta, int32_t batch, int32_t hkv, int32_t head_dim,
-                        int32_t rotary_dim, int32_t num_pages, int32_t max_pages_per_seq,
-                        int32_t style) {
-  if (!k_delta || !v_delta || !pool || !token_cos_sin || !delta_positions || !delta_to_seq ||
-      !page_table)
+ * plane writes only ids in its own range (R13).  K is rotated with the
+ * row's cos/sin row; V is copied bit for bit.
+ *
+ * The cos/sin row of delta row i is either row i of token_cos_sin (the
+ * page's tokenAlignedCosSin) or, when token_cos_sin is NULL, the rope-table
+ * row of rope_row_of (the fused gather below); a row without one writes no
+ * K. */
+static const float* rope_row_of(const float* rope, int32_t rope_states, int32_t rope_rows,
+                                const int32_t* state_indices, int64_t p, int64_t q,
+                                int32_t batch, int32_t rotary_dim);
+
+static int paged_update(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
+                        const float* token_cos_sin, const float* rope, int32_t rope_states,
+                        int32_t rope_rows, const int32_t* state_indices,
+                        const int32_t* delta_positions, const int32_t* delta_to_seq,
+                        const int32_t* page_table, int32_t num_delta, int32_t batch, int32_t hkv,
+                        int32_t head_dim, int32_t rotary_dim, int32_t num_pages,
+                        int32_t max_pages_per_seq, int32_t style) {
+  if (!k_delta || !v_delta || !pool || (!token_cos_sin && !rope) || !delta_positions ||
+      !delta_to_seq || !page_table)
     return RKV_REF_ERR_ARG;
-  if (num_delta < 0 || batch < 0 || hkv < 0 || num_pages < 0 || max_pages_per_seq < 0)
+  if (num_delta < 0 || batch < 0 || hkv < 0 || num_pages < 0 || max_pages_per_seq < 0 ||
+      rope_states < 0 || rope_rows < 0)
     return RKV_REF_ERR_ARG;
   if (head_dim <= 0 || head_dim > 4096 || rotary_dim < 0 || rotary_dim > head_dim ||
       (rotary_dim & 1))
@@ -311,8 +325,10 @@ int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16
     int64_t lp = p / TPP, off = p % TPP;
     int64_t kid = page_table[((size_t)q * 2 + 0) * max_pages_per_seq + lp];
     int64_t vid = page_table[((size_t)q * 2 + 1) * max_pages_per_seq + lp];
-    const float* row = token_cos_sin + (size_t)i * rotary_dim;
-    if (kid >= 0 && kid < num_pages) {
+    const float* row = token_cos_sin ? token_cos_sin + (size_t)i * rotary_dim
+                                     : rope_row_of(rope, rope_states, rope_rows, state_indices,
+                                                   p, q, batch, rotary_dim);
+    if (row && kid >= 0 && kid < num_pages) {
       for (int32_t h = 0; h < hkv; ++h)
         rkv_ref_rotate_row(k_delta + ((size_t)i * hkv + h) * D,
                            pool + (((size_t)kid * TPP + off) * hkv + h) * D, row, D,
@@ -325,6 +341,67 @@ int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16
     }
   }
   return RKV_REF_OK;
+}
+
+int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
+                        const float* token_cos_sin, const int32_t* delta_positions,
+                        const int32_t* delta_to_seq, const int32_t* page_table,
+                        int32_t num_delta, int32_t batch, int32_t hkv, int32_t head_dim,
+                        int32_t rotary_dim, int32_t num_pages, int32_t max_pages_per_seq,
+                        int32_t style) {
+  if (!token_cos_sin) return RKV_REF_ERR_ARG;
+  return paged_update(k_delta, v_delta, pool, token_cos_sin, NULL, 0, 0, NULL, delta_positions,
+                      delta_to_seq, page_table, num_delta, batch, hkv, head_dim, rotary_dim,
+                      num_pages, max_pages_per_seq, style);
+}
+
+/* ------------------------------------------------- call 4, gather fused -- */
+
+/* [P3] launchDFlashGatherDeltaRope builds tokenAlignedCosSin from a rope
+ * table (the page gives its parameters only).  Reading: the table is
+ * [rope_states, rope_rows, R]; sequence q uses state state_indices[q], or q
+ * itself when no state indices are given (state 0 when the table has a
+ * single state).  Row i gets table[state(q_i)][p_i] when p_i and q_i are
+ * not padding, q_i < batch, the state exists and p_i < rope_rows;
+ * otherwise it gets NaN (no row). */
+static const float* rope_row_of(const float* rope, int32_t rope_states, int32_t rope_rows,
+                                const int32_t* state_indices, int64_t p, int64_t q,
+                                int32_t batch, int32_t rotary_dim) {
+  if (p < 0 || q < 0 || q >= batch) return NULL;
+  int64_t st = state_indices ? state_indices[q] : (rope_states == 1 ? 0 : q);
+  if (st < 0 || st >= rope_states || p >= rope_rows) return NULL;
+  return rope + ((size_t)st * rope_rows + p) * rotary_dim;
+}
+
+int rkv_ref_gather_delta_rope(const float* rope, int32_t rope_states, int32_t rope_rows,
+                              const int32_t* state_indices, const int32_t* delta_positions,
+                              const int32_t* delta_to_seq, int32_t num_delta, int32_t batch,
+                              int32_t rotary_dim, float* out) {
+  if (!rope || !delta_positions || !delta_to_seq || !out) return RKV_REF_ERR_ARG;
+  if (rope_states < 0 || rope_rows < 0 || num_delta < 0 || batch < 0 || rotary_dim < 0)
+    return RKV_REF_ERR_ARG;
+  for (int32_t i = 0; i < num_delta; ++i) {
+    const float* row = rope_row_of(rope, rope_states, rope_rows, state_indices,
+                                   delta_positions[i], delta_to_seq[i], batch, rotary_dim);
+    for (int32_t d = 0; d < rotary_dim; ++d)
+      out[(size_t)i * rotary_dim + d] = row ? row[d] : NAN;
+  }
+  return RKV_REF_OK;
+}
+
+/* The update of call 4 with each row's cos/sin row taken from the rope
+ * table as the gather above would; a row without one writes no K. */
+int rkv_ref_paged_delta_gather(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
+                               const float* rope, int32_t rope_states, int32_t rope_rows,
+                               const int32_t* state_indices, const int32_t* delta_positions,
+                               const int32_t* delta_to_seq, const int32_t* page_table,
+                               int32_t num_delta, int32_t batch, int32_t hkv, int32_t head_dim,
+                               int32_t rotary_dim, int32_t num_pages, int32_t max_pages_per_seq,
+                               int32_t style) {
+  if (!rope) return RKV_REF_ERR_ARG;
+  return paged_update(k_delta, v_delta, pool, NULL, rope, rope_states, rope_rows, state_indices,
+                      delta_positions, delta_to_seq, page_table, num_delta, batch, hkv, head_dim,
+                      rotary_dim, num_pages, max_pages_per_seq, style);
 }
 
 /* [P3] checkDFlashRopeCapacity: the table may be shorter than the padded

@@ -66,6 +66,24 @@ int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16
                         int32_t head_dim, int32_t rotary_dim, int32_t num_pages,
                         int32_t max_pages_per_seq, int32_t style);
 
+/* Gather of the delta rows' cos/sin rows from a rope table
+ * [rope_states, rope_rows, R]: out[i] = table[state(seq_i)][pos_i] for rows that
+ * have one; other rows are set to NaN. */
+int rkv_ref_gather_delta_rope(const float* rope, int32_t rope_states, int32_t rope_rows,
+                              const int32_t* state_indices, const int32_t* delta_positions,
+                              const int32_t* delta_to_seq, int32_t num_delta, int32_t batch,
+                              int32_t rotary_dim, float* out);
+
+/* Call 4 with the gather fused in: K of row i is rotated with the rope table
+ * row of (state(seq_i), pos_i) and written only when that row exists. */
+int rkv_ref_paged_delta_gather(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
+                               const float* rope, int32_t rope_states, int32_t rope_rows,
+                               const int32_t* state_indices, const int32_t* delta_positions,
+                               const int32_t* delta_to_seq, const int32_t* page_table,
+                               int32_t num_delta, int32_t batch, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t rotary_dim, int32_t num_pages,
+                               int32_t max_pages_per_seq, int32_t style);
+
 /* Capacity check: RKV_REF_ERR_CAPACITY iff cos_sin_len > kv_capacity. */
 int rkv_ref_check_rope_capacity(int32_t cos_sin_len, int32_t kv_capacity);
 

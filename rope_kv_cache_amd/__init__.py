@@ -13,6 +13,9 @@ Functions (same names as the C entry points, without the ``rkv_`` prefix):
   apply_rope_write_kv_tree(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache, q_out, rope_style)
   dflash_target_kv_cache_update(k_delta, v_delta, kv_cache, token_aligned_cos_sin, delta_positions,
                                 delta_token_to_sequence, page_table, batch_size, rope_style)
+  dflash_target_kv_cache_update_gather_rope(k_delta, v_delta, kv_cache, rope_cos_sin, state_indices,
+                                            delta_positions, delta_token_to_sequence, page_table,
+                                            batch_size, rope_style)
   check_rope_capacity(cos_sin_seq_len, kv_capacity)
   tokens_per_page()
 """
@@ -61,6 +64,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rkv_apply_rope_write_kv_continuous": [T, T, T, T, T, i32, P],
         "rkv_apply_rope_write_kv_tree": [T, T, T, T, T, T, i32, P],
         "rkv_dflash_target_kv_cache_update": [P, P, P, P, P, P, P] + [i32] * 8 + [P],
+        "rkv_dflash_target_kv_cache_update_gather_rope": [P, P, P, P, i32, i32, P, P, P, P]
+        + [i32] * 8 + [P],
         "rkv_check_rope_capacity": [i32, i32],
         "rkv_tokens_per_page": [],
         "rkv_last_error": [],
@@ -169,6 +174,42 @@ def dflash_target_kv_cache_update(k_delta, v_delta, kv_cache, token_aligned_cos_
     _check(lib.rkv_dflash_target_kv_cache_update(
         *[t.data_ptr() for t in ts], N, int(batch_size), Hkv, D, token_aligned_cos_sin.shape[1],
         kv_cache.shape[1], page_table.shape[2], int(rope_style), _stream(dev)))
+
+
+def dflash_target_kv_cache_update_gather_rope(k_delta, v_delta, kv_cache, rope_cos_sin,
+                                              state_indices, delta_positions,
+                                              delta_token_to_sequence, page_table,
+                                              batch_size: int, rope_style: int) -> None:
+    """Call 4 with the cos/sin rows read from ``rope_cos_sin`` [states, rows, R]
+    by (state of the row's sequence, its position); ``state_indices`` is an
+    int32 [batch_size] tensor or None."""
+    ts = (k_delta, v_delta, kv_cache, rope_cos_sin, delta_positions, delta_token_to_sequence,
+          page_table)
+    dev = _device_of(*ts, state_indices)
+    for t, dt in zip(ts, (torch.float16, torch.float16, torch.float16, torch.float32, torch.int32,
+                          torch.int32, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"expected contiguous {dt}, got {t.dtype}")
+    if state_indices is not None and (state_indices.dtype != torch.int32
+                                      or not state_indices.is_contiguous()
+                                      or state_indices.numel() < batch_size):
+        raise ValueError("state_indices must be a contiguous int32 tensor of batch_size entries")
+    if k_delta.dim() != 3 or v_delta.shape != k_delta.shape or kv_cache.dim() != 5 \
+            or rope_cos_sin.dim() != 3 or page_table.dim() != 3:
+        raise ValueError("shapes must be k/v_delta [N,Hkv,D], kv_cache [2,P,64,Hkv,D], "
+                         "rope_cos_sin [states,rows,R], page_table [B,2,M]")
+    N, Hkv, D = k_delta.shape
+    if tuple(kv_cache.shape[::2]) != (2, 64, D) or kv_cache.shape[3] != Hkv \
+            or delta_positions.numel() != N or delta_token_to_sequence.numel() != N \
+            or page_table.shape[1] != 2 or batch_size > page_table.shape[0]:
+        raise ValueError("inconsistent shapes")
+    states, rows, R = rope_cos_sin.shape
+    _check(lib.rkv_dflash_target_kv_cache_update_gather_rope(
+        k_delta.data_ptr(), v_delta.data_ptr(), kv_cache.data_ptr(), rope_cos_sin.data_ptr(),
+        states, rows, state_indices.data_ptr() if state_indices is not None else None,
+        delta_positions.data_ptr(), delta_token_to_sequence.data_ptr(), page_table.data_ptr(),
+        N, int(batch_size), Hkv, D, R, kv_cache.shape[1], page_table.shape[2], int(rope_style),
+        _stream(dev)))
 
 
 def check_rope_capacity(cos_sin_seq_len: int, kv_capacity: int) -> None:

@@ -216,6 +216,87 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
       rkv::launch_contig(p, call, (int)D, layout_of(style), exact_of(style), stream));
 }
 
+// Shared validation and launch of call 4, with the cos/sin rows given per
+// delta row (tokenAlignedCosSin) or gathered from a rope table.
+rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCache,
+                 const float* tokenAlignedCosSin, const float* rope, int32_t ropeStates,
+                 int32_t ropeRows, const int32_t* stateIndices, const int32_t* deltaPositions,
+                 const int32_t* deltaTokenToSequence, const int32_t* pageTable,
+                 int32_t numDeltaTokens, int32_t batchSize, int32_t numKVHeads, int32_t headDim,
+                 int32_t rotaryDim, int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle,
+                 bool gather, hipStream_t stream) {
+  clear_error();
+  rkv_status st;
+  if (numDeltaTokens < 0 || batchSize < 0 || numKVHeads < 0 || numPages < 0 ||
+      maxPagesPerSeq < 0 || ropeStates < 0 || ropeRows < 0)
+    return fail(RKV_ERR_SHAPE, "negative size argument");
+  if ((st = check_style(ropeStyle))) return st;
+  if ((st = check_dims(headDim, rotaryDim))) return st;
+  const long long N = numDeltaTokens, Hkv = numKVHeads, D = headDim, R = rotaryDim;
+  long long delta_elems, pool_elems, pt_elems, cs_elems;
+  if (!mul_ok(N * Hkv, D, &delta_elems) ||
+      !mul_ok(2LL * numPages * rkv::kTokensPerPage, Hkv * D, &pool_elems) ||
+      !mul_ok((long long)batchSize * 2, maxPagesPerSeq, &pt_elems) ||
+      !mul_ok(gather ? (long long)ropeStates * ropeRows : N, R, &cs_elems) ||
+      pool_elems > (INT64_MAX / 2))
+    return fail(RKV_ERR_SHAPE, "sizes overflow");
+  if (N == 0 || Hkv == 0) return RKV_OK;
+  const float* cs = gather ? rope : tokenAlignedCosSin;
+  const char* cs_name = gather ? "ropeCosSin" : "tokenAlignedCosSin";
+  // An array with no elements (e.g. the cos/sin rows when rotaryDim = 0) may be null.
+  if ((delta_elems > 0 && (!kDelta || !vDelta)) || (cs_elems > 0 && !cs) || !deltaPositions ||
+      !deltaTokenToSequence)
+    return fail(RKV_ERR_NULL, "null delta-row or cos/sin pointer");
+  if ((pool_elems > 0 && !kvCache) || (pt_elems > 0 && !pageTable))
+    return fail(RKV_ERR_NULL, "null kvCache or pageTable");
+  const void* ptrs[] = {kDelta, vDelta, kvCache, cs, deltaPositions, deltaTokenToSequence,
+                        pageTable, stateIndices};
+  const char* names[] = {"kDelta", "vDelta", "kvCache", cs_name, "deltaPositions",
+                         "deltaTokenToSequence", "pageTable", "stateIndices"};
+  for (int k = 0; k < 8; ++k)
+    if (((uintptr_t)ptrs[k] & 15u) != 0)
+      return fail(RKV_ERR_ALIGNMENT, "%s is not 16-byte aligned", names[k]);
+  auto span = [](const char* n, const void* p, long long bytes) {
+    return Span{n, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+  };
+  Span out = span("kvCache", kvCache, pool_elems * 2);
+  Span ins[] = {span("kDelta", kDelta, delta_elems * 2), span("vDelta", vDelta, delta_elems * 2),
+                span(cs_name, cs, cs_elems * 4), span("deltaPositions", deltaPositions, N * 4),
+                span("deltaTokenToSequence", deltaTokenToSequence, N * 4),
+                span("pageTable", pageTable, pt_elems * 4),
+                span("stateIndices", stateIndices, stateIndices ? batchSize * 4LL : 0)};
+  if ((st = check_no_alias(&out, 1, ins, 7))) return st;
+  if (pool_elems == 0 || pt_elems == 0) return RKV_OK;   // nothing can be written
+
+  rkv::PagedParams p{};
+  p.k_delta = kDelta;
+  p.v_delta = vDelta;
+  p.pool = kvCache;
+  p.cos_sin = tokenAlignedCosSin;
+  p.rope = rope;
+  p.state_idx = stateIndices;
+  p.rope_states = ropeStates;
+  p.rope_rows = ropeRows;
+  p.positions = deltaPositions;
+  p.seq = deltaTokenToSequence;
+  p.page_table = pageTable;
+  p.N = numDeltaTokens;
+  p.batch = batchSize;
+  p.Hkv = numKVHeads;
+  p.R = rotaryDim;
+  p.num_pages = numPages;
+  p.max_pages = maxPagesPerSeq;
+  const long long rows_per_group = 512 / D;
+  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group);
+  if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
+  p.groups_per_wave = sp.groups_per_wave;
+  p.waves_per_row = sp.waves_per_item;
+  p.total_waves = (int32_t)(N * p.waves_per_row);
+  p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
+  return launched(rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle),
+                                    gather, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,68 +332,21 @@ rkv_status rkv_dflash_target_kv_cache_update(
     const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
     int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
     int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream) {
-  clear_error();
-  rkv_status st;
-  if (numDeltaTokens < 0 || batchSize < 0 || numKVHeads < 0 || numPages < 0 || maxPagesPerSeq < 0)
-    return fail(RKV_ERR_SHAPE, "negative size argument");
-  if ((st = check_style(ropeStyle))) return st;
-  if ((st = check_dims(headDim, rotaryDim))) return st;
-  const long long N = numDeltaTokens, Hkv = numKVHeads, D = headDim, R = rotaryDim;
-  long long delta_elems, pool_elems, pt_elems, cs_elems;
-  if (!mul_ok(N * Hkv, D, &delta_elems) ||
-      !mul_ok(2LL * numPages * rkv::kTokensPerPage, Hkv * D, &pool_elems) ||
-      !mul_ok((long long)batchSize * 2, maxPagesPerSeq, &pt_elems) ||
-      !mul_ok(N, R, &cs_elems) || pool_elems > (INT64_MAX / 2))
-    return fail(RKV_ERR_SHAPE, "sizes overflow");
-  if (N == 0 || Hkv == 0) return RKV_OK;
-  // An array with no elements (e.g. the cos/sin rows when rotaryDim = 0) may be null.
-  if ((delta_elems > 0 && (!kDelta || !vDelta)) || (cs_elems > 0 && !tokenAlignedCosSin) ||
-      !deltaPositions || !deltaTokenToSequence)
-    return fail(RKV_ERR_NULL, "null delta-row pointer");
-  if ((pool_elems > 0 && !kvCache) || (pt_elems > 0 && !pageTable))
-    return fail(RKV_ERR_NULL, "null kvCache or pageTable");
-  const void* ptrs[] = {kDelta, vDelta, kvCache, tokenAlignedCosSin, deltaPositions,
-                        deltaTokenToSequence, pageTable};
-  const char* names[] = {"kDelta", "vDelta", "kvCache", "tokenAlignedCosSin", "deltaPositions",
-                         "deltaTokenToSequence", "pageTable"};
-  for (int k = 0; k < 7; ++k)
-    if (((uintptr_t)ptrs[k] & 15u) != 0)
-      return fail(RKV_ERR_ALIGNMENT, "%s is not 16-byte aligned", names[k]);
-  auto span = [](const char* n, const void* p, long long bytes) {
-    return Span{n, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
-  };
-  Span out = span("kvCache", kvCache, pool_elems * 2);
-  Span ins[] = {span("kDelta", kDelta, delta_elems * 2), span("vDelta", vDelta, delta_elems * 2),
-                span("tokenAlignedCosSin", tokenAlignedCosSin, cs_elems * 4),
-                span("deltaPositions", deltaPositions, N * 4),
-                span("deltaTokenToSequence", deltaTokenToSequence, N * 4),
-                span("pageTable", pageTable, pt_elems * 4)};
-  if ((st = check_no_alias(&out, 1, ins, 6))) return st;
-  if (pool_elems == 0 || pt_elems == 0) return RKV_OK;   // nothing can be written
+  return paged(kDelta, vDelta, kvCache, tokenAlignedCosSin, nullptr, 0, 0, nullptr,
+               deltaPositions, deltaTokenToSequence, pageTable, numDeltaTokens, batchSize,
+               numKVHeads, headDim, rotaryDim, numPages, maxPagesPerSeq, ropeStyle, false, stream);
+}
 
-  rkv::PagedParams p{};
-  p.k_delta = kDelta;
-  p.v_delta = vDelta;
-  p.pool = kvCache;
-  p.cos_sin = tokenAlignedCosSin;
-  p.positions = deltaPositions;
-  p.seq = deltaTokenToSequence;
-  p.page_table = pageTable;
-  p.N = numDeltaTokens;
-  p.batch = batchSize;
-  p.Hkv = numKVHeads;
-  p.R = rotaryDim;
-  p.num_pages = numPages;
-  p.max_pages = maxPagesPerSeq;
-  const long long rows_per_group = 512 / D;
-  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group);
-  if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
-  p.groups_per_wave = sp.groups_per_wave;
-  p.waves_per_row = sp.waves_per_item;
-  p.total_waves = (int32_t)(N * p.waves_per_row);
-  p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
-  return launched(
-      rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle), stream));
+rkv_status rkv_dflash_target_kv_cache_update_gather_rope(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCache, const float* ropeCosSin,
+    int32_t ropeStates, int32_t ropeRows, const int32_t* stateIndices,
+    const int32_t* deltaPositions, const int32_t* deltaTokenToSequence, const int32_t* pageTable,
+    int32_t numDeltaTokens, int32_t batchSize, int32_t numKVHeads, int32_t headDim,
+    int32_t rotaryDim, int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle,
+    hipStream_t stream) {
+  return paged(kDelta, vDelta, kvCache, nullptr, ropeCosSin, ropeStates, ropeRows, stateIndices,
+               deltaPositions, deltaTokenToSequence, pageTable, numDeltaTokens, batchSize,
+               numKVHeads, headDim, rotaryDim, numPages, maxPagesPerSeq, ropeStyle, true, stream);
 }
 
 rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {

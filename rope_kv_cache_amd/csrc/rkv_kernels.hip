@@ -146,7 +146,13 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
 // the index metadata, so they are requested first; the position/sequence
 // loads and then the page-table loads overlap with them, and only the
 // stores wait for the page ids.
-template <int D, int kStyle, bool kExact, int G>
+//
+// kGather fuses the page's cos/sin gather (launchDFlashGatherDeltaRope)
+// into the update: the row's cos/sin values come from the rope table row of
+// (state of its sequence, its position), read once the position and
+// sequence are known (in parallel with the page-table lookup); a row with
+// no such table row writes no K.
+template <int D, int kStyle, bool kExact, int G, bool kGather>
 __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
@@ -178,8 +184,10 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   }
   float cs[8], sn[8];
   const bool has_k = part * G * kRowsPerGroup < p.Hkv;   // wave-uniform
-  if (has_k && role.rotary)
-    load_cos_sin<kStyle>(p.cos_sin + (size_t)i * p.R, role.freq0, p.R, cs, sn);
+  if constexpr (!kGather) {
+    if (has_k && role.rotary)
+      load_cos_sin<kStyle>(p.cos_sin + (size_t)i * p.R, role.freq0, p.R, cs, sn);
+  }
 
   const int pos = p.positions[i];
   const int seq = p.seq[i];
@@ -190,8 +198,18 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   const int* pt = p.page_table + (size_t)seq * 2 * p.max_pages;
   const int kid = pt[lp];
   const int vid = pt[p.max_pages + lp];
-  const bool k_ok = kid >= 0 && kid < p.num_pages;
+  bool k_ok = kid >= 0 && kid < p.num_pages;
   const bool v_ok = vid >= p.num_pages && (long long)vid < 2LL * p.num_pages;
+  if constexpr (kGather) {
+    if (has_k) {
+      const int st = p.state_idx ? p.state_idx[seq] : (p.rope_states == 1 ? 0 : seq);
+      const bool rope_ok = st >= 0 && st < p.rope_states && pos < p.rope_rows;
+      k_ok = k_ok && rope_ok;
+      if (rope_ok && role.rotary)
+        load_cos_sin<kStyle>(p.rope + ((size_t)st * p.rope_rows + pos) * p.R, role.freq0, p.R, cs,
+                             sn);
+    }
+  }
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -271,17 +289,29 @@ hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool
   }
 }
 
-hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, hipStream_t stream) {
+namespace {
+
+template <bool kGather>
+hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
+                          hipStream_t stream) {
   return with_d(D, [&](auto d) {
     return with_style_exact(style, exact, [&](auto st, auto ex) {
       return with_groups(p.groups_per_wave, [&](auto g) {
         hipLaunchKernelGGL((paged_kernel<decltype(d)::value, decltype(st)::value,
-                                         decltype(ex)::value != 0, decltype(g)::value>),
+                                         decltype(ex)::value != 0, decltype(g)::value, kGather>),
                            dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p);
         return hipGetLastError();
       });
     });
   });
+}
+
+}  // namespace
+
+hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool gather,
+                        hipStream_t stream) {
+  return gather ? launch_paged_g<true>(p, D, style, exact, stream)
+                : launch_paged_g<false>(p, D, style, exact, stream);
 }
 
 }  // namespace rkv

@@ -54,6 +54,9 @@ struct PagedParams {
   const int32_t* positions; // [N]
   const int32_t* seq;       // [N]
   const int32_t* page_table;// [batch, 2, max_pages]
+  const float* rope;        // fused gather: [rope_states, rope_rows, R]; else unused
+  const int32_t* state_idx; // fused gather: [batch] state of each sequence, or null
+  int32_t rope_states, rope_rows;
   int32_t N, batch, Hkv, R, num_pages, max_pages;
   int32_t groups_per_wave;  // G: row groups of 512/D rows handled by one wave (1, 2 or 4)
   int32_t waves_per_row;    // ceil(row groups per delta row / G)
@@ -63,6 +66,7 @@ struct PagedParams {
 
 hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool exact,
                          hipStream_t stream);
-hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, hipStream_t stream);
+hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool gather,
+                        hipStream_t stream);
 
 }  // namespace rkv

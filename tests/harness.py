@@ -38,10 +38,15 @@ def host16(t: torch.Tensor) -> np.ndarray:
 
 def upload(w, device="cuda") -> dict:
     if isinstance(w, W.Paged):
-        return {"k_delta": dev(w.k_delta, device), "v_delta": dev(w.v_delta, device),
-                "pool": dev(w.pool, device), "cos_sin": dev(w.cos_sin, device),
-                "positions": dev(w.positions, device), "seq": dev(w.seq, device),
-                "page_table": dev(w.page_table, device)}
+        t = {"k_delta": dev(w.k_delta, device), "v_delta": dev(w.v_delta, device),
+             "pool": dev(w.pool, device), "cos_sin": dev(w.cos_sin, device),
+             "positions": dev(w.positions, device), "seq": dev(w.seq, device),
+             "page_table": dev(w.page_table, device)}
+        if w.extra.get("gather"):
+            t["rope"] = dev(w.extra["rope"], device)
+            si = w.extra["state_indices"]
+            t["state_indices"] = None if si is None else dev(si, device)
+        return t
     t = {"cos_sin": dev(w.cos_sin, device), "qkv": dev(w.qkv, device),
          "cache": dev(w.cache, device)}
     if w.call != "packed":
@@ -57,7 +62,12 @@ def launch(w, t: dict, exact: bool = False) -> None:
     ROUND_EXACT into the rope style (binary64, correctly rounded)."""
     import rope_kv_cache_amd as rkv
     style = w.style | (rkv.ROUND_EXACT if exact else 0)
-    if isinstance(w, W.Paged):
+    if isinstance(w, W.Paged) and w.extra.get("gather"):
+        rkv.dflash_target_kv_cache_update_gather_rope(t["k_delta"], t["v_delta"], t["pool"],
+                                                      t["rope"], t["state_indices"],
+                                                      t["positions"], t["seq"], t["page_table"],
+                                                      w.batch, style)
+    elif isinstance(w, W.Paged):
         rkv.dflash_target_kv_cache_update(t["k_delta"], t["v_delta"], t["pool"], t["cos_sin"],
                                           t["positions"], t["seq"], t["page_table"], w.batch,
                                           style)

@@ -618,4 +618,60 @@ def pin_argument_errors(L):
             assert e.code == oracle.ERR_ARG
 
 
+def pin_gather_delta_rope(L):
+    """The gather picks table[state(seq)][pos] row by row; rows without one
+    (padding, inactive sequence, missing state, position past the table)
+    come back as NaN."""
+    r = np.random.default_rng(24)
+    states, rows, R, batch = 3, 40, 16, 4
+    rope = r.standard_normal((states, rows, R)).astype(np.float32)
+    pos = np.array([0, 39, 40, -1, 5, 7, 7, 12, 3], dtype=np.int32)
+    seq = np.array([0, 1, 2, 0, -1, 4, 3, 3, 2], dtype=np.int32)
+    si = np.array([2, 0, 1, 7], dtype=np.int32)          # sequence 3 maps to a missing state
+    got = oracle.gather_delta_rope(rope, si, pos, seq, batch, L)
+    for i in range(pos.size):
+        p, q = int(pos[i]), int(seq[i])
+        ok = p >= 0 and 0 <= q < batch and 0 <= si[q] < states and p < rows
+        if ok:
+            assert np.array_equal(got[i], rope[si[q], p]), i
+        else:
+            assert np.all(np.isnan(got[i])), i
+    # without state indices: sequence q uses state q (or 0 for a one-state table)
+    got = oracle.gather_delta_rope(rope, None, np.array([4, 4, 4], np.int32),
+                                   np.array([0, 1, 2], np.int32), 3, L)
+    assert np.array_equal(got, rope[[0, 1, 2], 4])
+    got = oracle.gather_delta_rope(rope[:1], None, np.array([4, 9], np.int32),
+                                   np.array([1, 2], np.int32), 3, L)
+    assert np.array_equal(got, rope[[0, 0], [4, 9]])
+
+
+def pin_fused_gather_is_gather_then_update(L):
+    """With every live row covered by the table, the fused call equals the
+    gather followed by the paged update, bit for bit; a row without a rope
+    row leaves its K slot untouched but still writes V."""
+    for style in (NEOX, GPTJ):
+        w = W.paged(128, 4, 2, 64, 64, 16, 4, style, 25 + style, width=32, pool_fill="sentinel")
+        rope = W.rope_table(4, 256, w.R, 10000.0, offsets=np.array([0, 3, 9, 27]))
+        si = np.array([3, 1, 0, 2], dtype=np.int32)
+        rows = oracle.gather_delta_rope(rope, si, w.positions, w.seq, w.batch, L)
+        want = oracle.paged_delta(w.k_delta, w.v_delta, w.pool, rows, w.positions, w.seq,
+                                  w.page_table, w.batch, style, L)
+        got = oracle.paged_delta_gather(w.k_delta, w.v_delta, w.pool, rope, si, w.positions,
+                                        w.seq, w.page_table, w.batch, style, L)
+        assert np.array_equal(got, want), style
+    # a table too short for one live row
+    w = W.paged(8, 1, 1, 64, 64, 4, 2, NEOX, 27, width=8, pad_frac=0.0, bad_frac=0.0,
+                pool_fill="sentinel")
+    p_max = int(w.positions.max())
+    rope = W.rope_table(1, p_max, 64, 10000.0)            # rows 0 .. p_max-1
+    got = oracle.paged_delta_gather(w.k_delta, w.v_delta, w.pool, rope, None, w.positions, w.seq,
+                                    w.page_table, 1, NEOX, L)
+    i = int(np.argmax(w.positions))
+    kid = int(w.page_table[0, 0, p_max // 64])
+    vid = int(w.page_table[0, 1, p_max // 64])
+    flat = got.reshape(2 * w.num_pages, 64, w.Hkv, w.D)
+    assert np.all(flat[kid, p_max % 64] == W.SENTINEL)
+    assert np.array_equal(flat[vid, p_max % 64], w.v_delta[i])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

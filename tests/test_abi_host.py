@@ -310,6 +310,37 @@ def test_paged_validation(kw, want):
     assert st == want, (kw, rkv.status_string(st), L.rkv_last_error())
 
 
+def gather_call(**kw):
+    base = dict(k=1 << 40, v=2 << 40, pool=3 << 40, rope=4 << 40, states=2, rows=512, si=8 << 40,
+                pos=5 << 40, seq=6 << 40, pt=7 << 40, N=16, batch=2, Hkv=2, D=128, R=128, P=8,
+                M=4, style=0)
+    base.update(kw)
+    b = base
+    return L.rkv_dflash_target_kv_cache_update_gather_rope(
+        b["k"], b["v"], b["pool"], b["rope"], b["states"], b["rows"], b["si"], b["pos"], b["seq"],
+        b["pt"], b["N"], b["batch"], b["Hkv"], b["D"], b["R"], b["P"], b["M"], b["style"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(states=-1), rkv.ERR_SHAPE), (dict(rows=-1), rkv.ERR_SHAPE), (dict(rope=0), rkv.ERR_NULL),
+    (dict(si=(8 << 40) + 4), rkv.ERR_ALIGNMENT), (dict(pool=(4 << 40) + 1024), rkv.ERR_ALIAS),
+    (dict(si=(3 << 40) + 64), rkv.ERR_ALIAS), (dict(R=24), rkv.ERR_UNSUPPORTED),
+    (dict(style=0x102), rkv.ERR_SHAPE), (dict(N=0), rkv.OK), (dict(P=0), rkv.OK),
+    # an empty rope table may be null: validation then stops at the unsupported D
+    (dict(rope=0, states=0, D=96, R=96), rkv.ERR_UNSUPPORTED),
+])
+def test_gather_validation(kw, want):
+    st = gather_call(**kw)
+    assert st == want, (kw, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+def test_gather_null_state_indices_accepted_by_validation():
+    # stateIndices may be null; stop before the launch with an empty pool
+    assert gather_call(si=0, P=0) == rkv.OK
+
+
 @no_gpu
 def test_paged_empty():
     assert paged_call(N=0) == rkv.OK

@@ -45,6 +45,8 @@ MUTATIONS = {
     "paged_offset_transposed": ("pool + (((size_t)kid * TPP + off) * hkv + h) * D",
                                 "pool + (((size_t)kid * TPP + h) * hkv + off % hkv) * D"),
     "capacity_check_inclusive": ("return cos_sin_len > kv_capacity ?", "return cos_sin_len >= kv_capacity ?"),
+    "gather_position_past_table": ("st >= rope_states || p >= rope_rows", "st >= rope_states || p > rope_rows"),
+    "gather_ignores_state_indices": ("int64_t st = state_indices ? state_indices[q]", "int64_t st = state_indices ? q"),
 }
 
 

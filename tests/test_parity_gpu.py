@@ -150,6 +150,39 @@ def test_paged_skip_reasons_and_inactive_batch():
     check(w)
 
 
+# ------------------------------------------------ paged, gather fused in --
+
+def test_config4_gather_fused():
+    check(W.config(41))
+
+
+@pytest.mark.parametrize("D,R,style,states,with_si", [
+    (128, 128, NEOX, 3, True), (128, 64, GPTJ, 2, True), (64, 64, GPTJ, 1, False),
+    (256, 112, NEOX, 4, False), (128, 0, NEOX, 2, True)])
+def test_paged_gather_shapes(D, R, style, states, with_si):
+    w = W.paged_gather(300, 7, 3, D, R, 64, 9, style, 6000 + D + R + states, rope_states=states,
+                       rope_rows=9 * 64 - 50, state_indices=with_si, width=43, pad_frac=0.2,
+                       bad_frac=0.2, name=f"paged_gather_D{D}_R{R}_s{style}_st{states}")
+    if with_si:
+        w.extra["state_indices"][1] = states        # a missing state
+        w.extra["state_indices"][2] = -1
+    check(w)
+
+
+def test_paged_gather_equals_gather_then_update():
+    """On the GPU, the fused call and the unfused call fed with the oracle's
+    gathered rows write the same pool, bit for bit."""
+    w = W.paged_gather(1024, 8, 4, 128, 128, 128, 16, NEOX, 6100, rope_states=2,
+                       name="paged_gather_vs_unfused")
+    rows = oracle.gather_delta_rope(w.extra["rope"], w.extra["state_indices"], w.positions, w.seq,
+                                    w.batch)
+    fused = run_gpu(w)["pool"]
+    w.extra["gather"] = False
+    w.cos_sin = rows
+    unfused = run_gpu(w)["pool"]
+    assert np.array_equal(fused, unfused)
+
+
 # ------------------------------------------------------- 64-bit addressing --
 
 def test_paged_pool_beyond_4g_elements():

@@ -255,6 +255,25 @@ def paged(N, batch, Hkv, D, R, num_pages, max_pages, style, seed, theta=10000.0,
 _TILE = 1 << 24
 
 
+def paged_gather(N, batch, Hkv, D, R, num_pages, max_pages, style, seed, rope_states=1,
+                 rope_rows=None, theta=10000.0, state_indices=True, width=None, pad_frac=0.10,
+                 bad_frac=0.05, pool_fill="normal", name="") -> Paged:
+    """Inputs of the paged update with the cos/sin gather fused in: the paged
+    workload plus a rope table [rope_states, rope_rows, R] (state k holds
+    positions offset by 7*k) and, optionally, per-sequence state indices
+    (a seeded draw in [0, rope_states))."""
+    w = paged(N, batch, Hkv, D, R, num_pages, max_pages, style, seed, theta=theta, width=width,
+              pad_frac=pad_frac, bad_frac=bad_frac, pool_fill=pool_fill, name=name)
+    r = rng(seed + 7)
+    rows = max_pages * TOKENS_PER_PAGE if rope_rows is None else rope_rows
+    w.extra["gather"] = True
+    w.extra["rope"] = rope_table(rope_states, rows, R, theta,
+                                 offsets=7 * np.arange(rope_states))
+    w.extra["state_indices"] = (r.integers(0, rope_states, size=batch).astype(np.int32)
+                                if state_indices else None)
+    return w
+
+
 def _fill(r, shape, how):
     if how == "sentinel":
         return sentinel_f16(shape)
@@ -289,6 +308,9 @@ def config(idx: int, style: int | None = None):
     if idx == 4:   # paged delta update
         return paged(4096, 32, 8, 128, 128, 8192, 128, NEOX, 1004,
                      name="paged_delta_n4096_p8192")
+    if idx == 41:  # paged delta update with the cos/sin gather fused in
+        return paged_gather(4096, 32, 8, 128, 128, 8192, 128, NEOX, 1004, rope_states=1,
+                            state_indices=False, name="paged_delta_gather_n4096_p8192")
     if idx == 5:   # large prefill
         r = rng(10050)
         offs = np.concatenate([[0], r.integers(1, 8193, size=3)])
