@@ -5,8 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``rkv_oracle.c``) with numpy marshalling: every wrapper copies its inputs and
 returns fresh output arrays, so a caller's arrays are never modified.
 
-fp16 arrays are ``uint16`` bit patterns; tables are ``float32``; index arrays
-are ``int32``.  The wrappers derive sizes from array shapes the same way the
+fp16 arrays are ``uint16`` bit patterns; fp8 (E4M3) caches are ``uint8``
+bit patterns; tables and scales are ``float32``; index arrays are ``int32``.  The wrappers derive sizes from array shapes the same way the
 pages' tensor signatures do (TensorRT-Edge-LLM, "Apply Rope Write KV" and
 "Dflash Runtime Kernels").
 """
@@ -56,6 +56,28 @@ def _declare(L):
     L.rkv_ref_double_to_half.argtypes = [ctypes.c_double]
     L.rkv_ref_rotate_row.restype = None
     L.rkv_ref_rotate_row.argtypes = [P, P, P, i32, i32, i32]
+    L.rkv_ref_rotate_row_wide.restype = None
+    L.rkv_ref_rotate_row_wide.argtypes = [P, P, P, i32, i32, i32]
+    L.rkv_ref_e4m3_to_double.restype = ctypes.c_double
+    L.rkv_ref_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    L.rkv_ref_double_to_e4m3.restype = ctypes.c_uint8
+    L.rkv_ref_double_to_e4m3.argtypes = [ctypes.c_double]
+    f32 = ctypes.c_float
+    L.rkv_ref_packed_qkv_fp8.restype = ctypes.c_int
+    L.rkv_ref_packed_qkv_fp8.argtypes = [P, i32, i32, i32, P, i32, i32, i32, i32, i32, P, i32,
+                                         f32, f32, i32]
+    L.rkv_ref_continuous_fp8.restype = ctypes.c_int
+    L.rkv_ref_continuous_fp8.argtypes = [P, i32, i32, i32, P, P, i32, i32, i32, i32, i32, P, i32,
+                                         P, f32, f32, i32]
+    L.rkv_ref_tree_fp8.restype = ctypes.c_int
+    L.rkv_ref_tree_fp8.argtypes = [P, i32, i32, i32, P, P, P, i32, i32, i32, i32, i32, P, i32, P,
+                                   f32, f32, i32]
+    L.rkv_ref_paged_delta_fp8.restype = ctypes.c_int
+    L.rkv_ref_paged_delta_fp8.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                          f32, f32, i32]
+    L.rkv_ref_paged_delta_gather_fp8.restype = ctypes.c_int
+    L.rkv_ref_paged_delta_gather_fp8.argtypes = [P, P, P, P, i32, i32, P, P, P, P, i32, i32, i32,
+                                                 i32, i32, i32, i32, f32, f32, i32]
     L.rkv_ref_packed_qkv.restype = ctypes.c_int
     L.rkv_ref_packed_qkv.argtypes = [P, i32, i32, i32, P, i32, i32, i32, i32, i32, P, i32, i32]
     L.rkv_ref_continuous.restype = ctypes.c_int
@@ -98,6 +120,27 @@ def rotate_row(x, cos_sin_row, rotary_dim: int, style: int, L=None) -> np.ndarra
     y = np.empty_like(x)
     (L or lib()).rkv_ref_rotate_row(_p(x), _p(y), _p(row), x.size, rotary_dim, style)
     return y
+
+
+def rotate_row_wide(x, cos_sin_row, rotary_dim: int, style: int, L=None) -> np.ndarray:
+    """The binary64 rotation of one head row, before rounding to fp16."""
+    x = _c(x, np.uint16)
+    row = _c(cos_sin_row, np.float32)
+    w = np.empty(x.size, dtype=np.float64)
+    (L or lib()).rkv_ref_rotate_row_wide(_p(x), _p(w), _p(row), x.size, rotary_dim, style)
+    return w
+
+
+def e4m3_to_double(b: int, L=None) -> float:
+    return (L or lib()).rkv_ref_e4m3_to_double(int(b))
+
+
+def double_to_e4m3(x: float, L=None) -> int:
+    return (L or lib()).rkv_ref_double_to_e4m3(float(x))
+
+
+def _scale(s) -> float:
+    return 1.0 if s is None else float(np.float32(s))
 
 
 def packed_qkv(cos_sin, qkv, cache, style: int, L=None):
@@ -208,6 +251,101 @@ def paged_delta_gather(k_delta, v_delta, pool, rope, state_indices, positions, s
     return pool
 
 
+def packed_qkv_fp8(cos_sin, qkv, cache8, k_scale, v_scale, style: int, L=None):
+    """Call 1 with an E4M3 cache.  Returns ``(qkv_out, cache8_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    qkv = _c(qkv, np.uint16).copy()
+    cache8 = _c(cache8, np.uint8).copy()
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache8.shape[2], cache8.shape[3]
+    rc = (L or lib()).rkv_ref_packed_qkv_fp8(_p(cos_sin), tb, tlen, R, _p(qkv), B, S,
+                                             H - 2 * Hkv, Hkv, D, _p(cache8), cap,
+                                             _scale(k_scale), _scale(v_scale), style)
+    if rc:
+        raise OracleError(rc, "packed_qkv_fp8")
+    return qkv, cache8
+
+
+def continuous_fp8(cos_sin, end_lens, qkv, cache8, q_out, k_scale, v_scale, style: int, L=None):
+    """Call 2 with an E4M3 cache.  Returns ``(cache8_out, q_out_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    end_lens = _c(end_lens, np.int32)
+    qkv = _c(qkv, np.uint16)
+    cache8 = _c(cache8, np.uint8).copy()
+    q_out = _c(q_out, np.uint16).copy()
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache8.shape[2], cache8.shape[3]
+    rc = (L or lib()).rkv_ref_continuous_fp8(_p(cos_sin), tb, tlen, R, _p(end_lens), _p(qkv), B,
+                                             S, H - 2 * Hkv, Hkv, D, _p(cache8), cap, _p(q_out),
+                                             _scale(k_scale), _scale(v_scale), style)
+    if rc:
+        raise OracleError(rc, "continuous_fp8")
+    return cache8, q_out
+
+
+def tree_fp8(cos_sin, end_lens, pos_ids, qkv, cache8, q_out, k_scale, v_scale, style: int,
+             L=None):
+    """Call 3 with an E4M3 cache.  Returns ``(cache8_out, q_out_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    end_lens = _c(end_lens, np.int32)
+    pos_ids = _c(pos_ids, np.int32)
+    qkv = _c(qkv, np.uint16)
+    cache8 = _c(cache8, np.uint8).copy()
+    q_out = _c(q_out, np.uint16).copy()
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache8.shape[2], cache8.shape[3]
+    rc = (L or lib()).rkv_ref_tree_fp8(_p(cos_sin), tb, tlen, R, _p(end_lens), _p(pos_ids),
+                                       _p(qkv), B, S, H - 2 * Hkv, Hkv, D, _p(cache8), cap,
+                                       _p(q_out), _scale(k_scale), _scale(v_scale), style)
+    if rc:
+        raise OracleError(rc, "tree_fp8")
+    return cache8, q_out
+
+
+def paged_delta_fp8(k_delta, v_delta, pool8, token_cos_sin, positions, seq, page_table,
+                    batch: int, k_scale, v_scale, style: int, L=None):
+    """Call 4 with an E4M3 pool.  Returns the updated pool."""
+    k_delta = _c(k_delta, np.uint16)
+    v_delta = _c(v_delta, np.uint16)
+    pool8 = _c(pool8, np.uint8).copy()
+    token_cos_sin = _c(token_cos_sin, np.float32)
+    positions = _c(positions, np.int32)
+    seq = _c(seq, np.int32)
+    page_table = _c(page_table, np.int32)
+    N, Hkv, D = k_delta.shape
+    rc = (L or lib()).rkv_ref_paged_delta_fp8(
+        _p(k_delta), _p(v_delta), _p(pool8), _p(token_cos_sin), _p(positions), _p(seq),
+        _p(page_table), N, batch, Hkv, D, token_cos_sin.shape[1], pool8.shape[1],
+        page_table.shape[2], _scale(k_scale), _scale(v_scale), style)
+    if rc:
+        raise OracleError(rc, "paged_delta_fp8")
+    return pool8
+
+
+def paged_delta_gather_fp8(k_delta, v_delta, pool8, rope, state_indices, positions, seq,
+                           page_table, batch: int, k_scale, v_scale, style: int, L=None):
+    """Call 4 with the gather fused in and an E4M3 pool.  Returns the updated pool."""
+    k_delta = _c(k_delta, np.uint16)
+    v_delta = _c(v_delta, np.uint16)
+    pool8 = _c(pool8, np.uint8).copy()
+    rope = _c(rope, np.float32)
+    si = None if state_indices is None else _c(state_indices, np.int32)
+    positions = _c(positions, np.int32)
+    seq = _c(seq, np.int32)
+    page_table = _c(page_table, np.int32)
+    N, Hkv, D = k_delta.shape
+    rc = (L or lib()).rkv_ref_paged_delta_gather_fp8(
+        _p(k_delta), _p(v_delta), _p(pool8), _p(rope), rope.shape[0], rope.shape[1], _p(si),
+        _p(positions), _p(seq), _p(page_table), N, batch, Hkv, D, rope.shape[2], pool8.shape[1],
+        page_table.shape[2], _scale(k_scale), _scale(v_scale), style)
+    if rc:
+        raise OracleError(rc, "paged_delta_gather_fp8")
+    return pool8
+
+
 def check_rope_capacity(cos_sin_len: int, kv_capacity: int, L=None) -> int:
     return (L or lib()).rkv_ref_check_rope_capacity(cos_sin_len, kv_capacity)
 
@@ -217,14 +355,39 @@ def run(w, L=None):
 
     Returns a dict of expected outputs keyed like the HIP binding's results:
     ``qkv`` (call 1), ``q_out`` (calls 2, 3), ``cache`` (calls 1-3), ``pool`` (call 4).
+    A workload whose ``extra["fp8"]`` holds ``k_scale`` / ``v_scale`` runs the
+    E4M3-cache variant of its call.
     """
+    fp8 = w.extra.get("fp8")
     if hasattr(w, "pool"):
+        if fp8:
+            ks, vs = fp8["k_scale"], fp8["v_scale"]
+            if w.extra.get("gather"):
+                return {"pool": paged_delta_gather_fp8(
+                    w.k_delta, w.v_delta, w.pool, w.extra["rope"], w.extra["state_indices"],
+                    w.positions, w.seq, w.page_table, w.batch, ks, vs, w.style, L=L)}
+            return {"pool": paged_delta_fp8(w.k_delta, w.v_delta, w.pool, w.cos_sin, w.positions,
+                                            w.seq, w.page_table, w.batch, ks, vs, w.style, L=L)}
         if w.extra.get("gather"):
             return {"pool": paged_delta_gather(w.k_delta, w.v_delta, w.pool, w.extra["rope"],
                                                w.extra["state_indices"], w.positions, w.seq,
                                                w.page_table, w.batch, w.style, L=L)}
         return {"pool": paged_delta(w.k_delta, w.v_delta, w.pool, w.cos_sin, w.positions, w.seq,
                                     w.page_table, w.batch, w.style, L=L)}
+    if fp8:
+        ks, vs = fp8["k_scale"], fp8["v_scale"]
+        if w.call == "packed":
+            q, c = packed_qkv_fp8(w.cos_sin, w.qkv, w.cache, ks, vs, w.style, L=L)
+            return {"qkv": q, "cache": c}
+        if w.call == "continuous":
+            c, q = continuous_fp8(w.cos_sin, w.end_lens, w.qkv, w.cache, w.q_out, ks, vs, w.style,
+                                  L=L)
+            return {"cache": c, "q_out": q}
+        if w.call == "tree":
+            c, q = tree_fp8(w.cos_sin, w.end_lens, w.pos_ids, w.qkv, w.cache, w.q_out, ks, vs,
+                            w.style, L=L)
+            return {"cache": c, "q_out": q}
+        raise ValueError(w.call)
     if w.call == "packed":
         q, c = packed_qkv(w.cos_sin, w.qkv, w.cache, w.style, L=L)
         return {"qkv": q, "cache": c}

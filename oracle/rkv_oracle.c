@@ -10,6 +10,8 @@
  * products of an 11-bit by a 24-bit significand are exact in binary64, so the
  * only roundings are the one binary64 subtraction/addition and the final
  * round-to-nearest-even to binary16.  Build with -ffp-contract=off.
+ * The fp8 variants take the same binary64 rotation, multiply it by the
+ * reciprocal scale in binary64 and round the product once to E4M3.
  *
  * Sources (cited by page title and section):
  *  [P1] TensorRT-Edge-LLM 0.4.0 C++ API, "Apply Rope Write KV":
@@ -45,6 +47,13 @@
  *  R23 fused gather: sequence q reads rope-table state stateIndices[q] (q
  *      itself without state indices; 0 for a single-state table); a row
  *      whose state or position has no table row writes no K (V as usual).
+ *  R24 fp8 cache ([P2] HAVE_K_SCALE / HAVE_V_SCALE): the cache value is the
+ *      rotated K (before any fp16 rounding; dims >= R unrotated) or the V
+ *      value, times the fp32 reciprocal of the per-tensor scale, rounded to
+ *      nearest-even E4M3; magnitudes past 448 saturate to 448, NaN stays NaN.
+ *      Q, and the in-place K of call 1, stay fp16 as in the fp16 variant.
+ *  R25 fp8 cache: a missing scale means 1; the reciprocal is 1/scale rounded
+ *      once to fp32; the product is formed in binary64 and rounded to E4M3.
  *  Parity unpinned against the original system for R6 and R7: no page fixes
  *  them; they are the plainest reading consistent with the rest.
  */
@@ -108,12 +117,12 @@ uint16_t rkv_ref_double_to_half(double x) {
  * (_get_neox_rotated_x: partner at +R/2; _get_gptj_rotated_x: adjacent
  * partner).  Frequency i drives pair i; cos_i = row[i], sin_i = row[R/2+i]
  * ([P2] _load_cos_sin with the half-width table; R1).  Written per pair:
- *   y_u = x_u*cos_i - x_v*sin_i,  y_v = x_v*cos_i + x_u*sin_i. */
-void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* row,
-                        int32_t head_dim, int32_t rotary_dim, int32_t style) {
-  uint16_t tmp[4096];
+ *   y_u = x_u*cos_i - x_v*sin_i,  y_v = x_v*cos_i + x_u*sin_i,
+ * each in binary64 (exact products, one rounding).  Dims >= R keep x (R3). */
+void rkv_ref_rotate_row_wide(const uint16_t* x, double* w, const float* row, int32_t head_dim,
+                             int32_t rotary_dim, int32_t style) {
   int half = rotary_dim / 2;
-  for (int d = 0; d < head_dim; ++d) tmp[d] = x[d];     /* R3: passthrough */
+  for (int d = 0; d < head_dim; ++d) w[d] = rkv_ref_half_to_double(x[d]);
   for (int i = 0; i < half; ++i) {
     int u, v;
     if (style == RKV_REF_NEOX) {
@@ -129,17 +138,86 @@ void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* row,
     double xv = rkv_ref_half_to_double(x[v]);
     double pu_c = xu * c, pv_s = xv * s;   /* exact products */
     double pv_c = xv * c, pu_s = xu * s;
-    tmp[u] = rkv_ref_double_to_half(pu_c - pv_s);
-    tmp[v] = rkv_ref_double_to_half(pv_c + pu_s);
+    w[u] = pu_c - pv_s;
+    w[v] = pv_c + pu_s;
   }
+}
+
+/* The fp16 result: each rotated element rounded once to binary16; dims >= R
+ * copied bit for bit (NaN payloads included).  y may equal x. */
+void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* row,
+                        int32_t head_dim, int32_t rotary_dim, int32_t style) {
+  double w[4096];
+  uint16_t tmp[4096];
+  rkv_ref_rotate_row_wide(x, w, row, head_dim, rotary_dim, style);
+  for (int d = 0; d < head_dim; ++d) tmp[d] = d < rotary_dim ? rkv_ref_double_to_half(w[d]) : x[d];
   for (int d = 0; d < head_dim; ++d) y[d] = tmp[d];
+}
+
+/* ----------------------------------------------------------------- fp8 -- */
+
+/* OCP 8-bit E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3
+ * mantissa bits; exponent field 0 encodes zero and subnormals (m * 2^-9);
+ * no infinities; S.1111.111 is NaN, so the largest finite value is 448. */
+double rkv_ref_e4m3_to_double(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int e = (b >> 3) & 0xf;
+  int m = b & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return sign ? -v : v;
+}
+
+/* binary64 -> E4M3, round to nearest even, saturating: magnitudes that round
+ * beyond 448 (and infinities) become 448 (R24); NaN stays NaN. */
+uint8_t rkv_ref_double_to_e4m3(double x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0;
+  if (isnan(x)) return (uint8_t)(sign | 0x7f);
+  double a = fabs(x);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7e);
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);
+  int ue = e2 - 1;             /* 2^ue <= a < 2^(ue+1) */
+  if (ue < -6) ue = -6;        /* subnormals share the quantum of the lowest binade */
+  double n = ldexp(a, 3 - ue); /* a / quantum, exact */
+  double fl = floor(n);
+  double rem = n - fl;
+  long long k = (long long)fl;
+  if (rem > 0.5 || (rem == 0.5 && (k & 1))) k += 1;
+  if (k >= 16) {
+    k >>= 1;
+    ue += 1;
+  }
+  if (k < 8) return (uint8_t)(sign | (uint8_t)k);                 /* subnormal */
+  if (ue + 7 > 15 || (ue + 7 == 15 && k - 8 == 7)) return (uint8_t)(sign | 0x7e);
+  return (uint8_t)(sign | (uint8_t)((ue + 7) << 3) | (uint8_t)(k - 8));
+}
+
+/* The scale step of the fp8 cache write ([P2] HAVE_K_SCALE / HAVE_V_SCALE):
+ * the reciprocal of the per-tensor scale, as an fp32 value. */
+static float reciprocal_of(float scale) { return (float)(1.0 / (double)scale); }
+
+/* One fp8 cache row: each value times the reciprocal scale, rounded once to
+ * E4M3. */
+static void store_row8(uint8_t* dst, const double* w, int32_t D, float rcp) {
+  for (int32_t d = 0; d < D; ++d) dst[d] = rkv_ref_double_to_e4m3(w[d] * (double)rcp);
+}
+
+static void widen_row(const uint16_t* x, double* w, int32_t D) {
+  for (int32_t d = 0; d < D; ++d) w[d] = rkv_ref_half_to_double(x[d]);
 }
 
 /* ------------------------------------------------------------ helpers -- */
 
 static int bad_common(const float* cos_sin, int32_t table_batch, int32_t table_len,
                       int32_t rotary_dim, const uint16_t* qkv, int32_t batch, int32_t seq_len,
-                      int32_t hq, int32_t hkv, int32_t head_dim, const uint16_t* cache,
+                      int32_t hq, int32_t hkv, int32_t head_dim, const void* cache,
                       int32_t capacity, int32_t style) {
   if (!cos_sin || !qkv || !cache) return 1;
   if (batch < 0 || seq_len < 0 || hq < 0 || hkv < 0 || capacity < 0 || table_len < 0) return 1;
@@ -168,21 +246,36 @@ static size_t cache_row(int32_t b, int32_t plane, int32_t h, int32_t slot, int32
 }
 
 /* One token of calls 2 and 3: rotate its Q rows into q_out, its K rows into
- * cache plane 0 at `slot`, copy its V rows into plane 1 at `slot`. */
+ * cache plane 0 at `slot`, copy its V rows into plane 1 at `slot`.  With an
+ * fp8 cache (cache8 != NULL) the cache rows are the rotated K / the V values
+ * times the reciprocal scales, rounded once to E4M3 (R24). */
 static void write_token(const float* row, const uint16_t* qkv, int32_t b, int32_t s,
                         int32_t slot, int32_t S, int32_t hq, int32_t hkv, int32_t D,
-                        int32_t R, uint16_t* cache, int32_t cap, uint16_t* q_out,
-                        int32_t style) {
+                        int32_t R, uint16_t* cache, uint8_t* cache8, float k_rcp, float v_rcp,
+                        int32_t cap, uint16_t* q_out, int32_t style) {
   int32_t H = hq + 2 * hkv;
+  double w[4096];
   for (int32_t h = 0; h < hq; ++h)
     rkv_ref_rotate_row(qkv + qkv_row(b, s, h, S, H, D),
                        q_out + (((size_t)b * S + s) * hq + h) * (size_t)D, row, D, R, style);
-  for (int32_t h = 0; h < hkv; ++h)
-    rkv_ref_rotate_row(qkv + qkv_row(b, s, hq + h, S, H, D),
-                       cache + cache_row(b, 0, h, slot, hkv, cap, D), row, D, R, style);
-  for (int32_t h = 0; h < hkv; ++h)
-    memcpy(cache + cache_row(b, 1, h, slot, hkv, cap, D),
-           qkv + qkv_row(b, s, hq + hkv + h, S, H, D), (size_t)D * sizeof(uint16_t));
+  for (int32_t h = 0; h < hkv; ++h) {
+    const uint16_t* k = qkv + qkv_row(b, s, hq + h, S, H, D);
+    if (cache8) {
+      rkv_ref_rotate_row_wide(k, w, row, D, R, style);
+      store_row8(cache8 + cache_row(b, 0, h, slot, hkv, cap, D), w, D, k_rcp);
+    } else {
+      rkv_ref_rotate_row(k, cache + cache_row(b, 0, h, slot, hkv, cap, D), row, D, R, style);
+    }
+  }
+  for (int32_t h = 0; h < hkv; ++h) {
+    const uint16_t* v = qkv + qkv_row(b, s, hq + hkv + h, S, H, D);
+    if (cache8) {
+      widen_row(v, w, D);
+      store_row8(cache8 + cache_row(b, 1, h, slot, hkv, cap, D), w, D, v_rcp);
+    } else {
+      memcpy(cache + cache_row(b, 1, h, slot, hkv, cap, D), v, (size_t)D * sizeof(uint16_t));
+    }
+  }
 }
 
 /* ------------------------------------------------------------- call 1 -- */
@@ -191,15 +284,17 @@ static void write_token(const float* row, const uint16_t* qkv, int32_t b, int32_
  * every sequence takes position s and cache slot s.  Q and K heads of the
  * packed tensor are rotated in place (R7); K also goes to cache plane 0 and
  * V, unrotated, to plane 1.  Slots >= S are not touched. */
-int rkv_ref_packed_qkv(const float* cos_sin, int32_t table_batch, int32_t table_len,
+static int packed_core(const float* cos_sin, int32_t table_batch, int32_t table_len,
                        int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
                        int32_t hq, int32_t hkv, int32_t head_dim, uint16_t* cache,
-                       int32_t capacity, int32_t style) {
+                       uint8_t* cache8, float k_rcp, float v_rcp, int32_t capacity,
+                       int32_t style) {
   if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
-                 head_dim, cache, capacity, style))
+                 head_dim, cache ? (const void*)cache : (const void*)cache8, capacity, style))
     return RKV_REF_ERR_ARG;
   if (seq_len > capacity || seq_len > table_len) return RKV_REF_ERR_CAPACITY;
   int32_t H = hq + 2 * hkv, D = head_dim, R = rotary_dim;
+  double w[4096];
   for (int32_t b = 0; b < batch; ++b) {
     for (int32_t s = 0; s < seq_len; ++s) {
       int32_t pos = s;
@@ -210,17 +305,47 @@ int rkv_ref_packed_qkv(const float* cos_sin, int32_t table_batch, int32_t table_
       }
       for (int32_t h = 0; h < hkv; ++h) {
         uint16_t* x = qkv + qkv_row(b, s, hq + h, seq_len, H, D);
+        if (cache8) {   /* the cache gets the unrounded rotation, scaled (R24) */
+          rkv_ref_rotate_row_wide(x, w, row, D, R, style);
+          store_row8(cache8 + cache_row(b, 0, h, pos, hkv, capacity, D), w, D, k_rcp);
+        }
         rkv_ref_rotate_row(x, x, row, D, R, style);
-        memcpy(cache + cache_row(b, 0, h, pos, hkv, capacity, D), x,
-               (size_t)D * sizeof(uint16_t));
+        if (!cache8)
+          memcpy(cache + cache_row(b, 0, h, pos, hkv, capacity, D), x,
+                 (size_t)D * sizeof(uint16_t));
       }
-      for (int32_t h = 0; h < hkv; ++h)
-        memcpy(cache + cache_row(b, 1, h, pos, hkv, capacity, D),
-               qkv + qkv_row(b, s, hq + hkv + h, seq_len, H, D),
-               (size_t)D * sizeof(uint16_t));
+      for (int32_t h = 0; h < hkv; ++h) {
+        const uint16_t* v = qkv + qkv_row(b, s, hq + hkv + h, seq_len, H, D);
+        if (cache8) {
+          widen_row(v, w, D);
+          store_row8(cache8 + cache_row(b, 1, h, pos, hkv, capacity, D), w, D, v_rcp);
+        } else {
+          memcpy(cache + cache_row(b, 1, h, pos, hkv, capacity, D), v,
+                 (size_t)D * sizeof(uint16_t));
+        }
+      }
     }
   }
   return RKV_REF_OK;
+}
+
+int rkv_ref_packed_qkv(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                       int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
+                       int32_t hq, int32_t hkv, int32_t head_dim, uint16_t* cache,
+                       int32_t capacity, int32_t style) {
+  if (!cache) return RKV_REF_ERR_ARG;
+  return packed_core(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
+                     head_dim, cache, NULL, 1.0f, 1.0f, capacity, style);
+}
+
+int rkv_ref_packed_qkv_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                           int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
+                           int32_t hq, int32_t hkv, int32_t head_dim, uint8_t* cache8,
+                           int32_t capacity, float k_scale, float v_scale, int32_t style) {
+  if (!cache8) return RKV_REF_ERR_ARG;
+  return packed_core(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
+                     head_dim, NULL, cache8, reciprocal_of(k_scale), reciprocal_of(v_scale),
+                     capacity, style);
 }
 
 /* ------------------------------------------------------------- call 2 -- */
@@ -229,13 +354,13 @@ int rkv_ref_packed_qkv(const float* cos_sin, int32_t table_batch, int32_t table_
  * length after the write (R5, and [P4]: the newest token sits at length-1),
  * so token s takes position and slot end-S+s.  Rotated Q goes to q_out, the
  * packed tensor is only read.  Out-of-range tokens write nothing (R10). */
-int rkv_ref_continuous(const float* cos_sin, int32_t table_batch, int32_t table_len,
-                       int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
-                       int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
-                       int32_t head_dim, uint16_t* cache, int32_t capacity, uint16_t* q_out,
-                       int32_t style) {
+static int continuous_core(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                           int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                           int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
+                           int32_t head_dim, uint16_t* cache, uint8_t* cache8, float k_rcp,
+                           float v_rcp, int32_t capacity, uint16_t* q_out, int32_t style) {
   if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
-                 head_dim, cache, capacity, style) ||
+                 head_dim, cache ? (const void*)cache : (const void*)cache8, capacity, style) ||
       !end_lens || !q_out)
     return RKV_REF_ERR_ARG;
   for (int32_t b = 0; b < batch; ++b) {
@@ -245,10 +370,32 @@ int rkv_ref_continuous(const float* cos_sin, int32_t table_batch, int32_t table_
       if (slot < 0 || slot >= capacity || pos >= table_len) continue;
       const float* row = table_row(cos_sin, table_batch, table_len, rotary_dim, b, (int32_t)pos);
       write_token(row, qkv, b, s, (int32_t)slot, seq_len, hq, hkv, head_dim, rotary_dim, cache,
-                  capacity, q_out, style);
+                  cache8, k_rcp, v_rcp, capacity, q_out, style);
     }
   }
   return RKV_REF_OK;
+}
+
+int rkv_ref_continuous(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                       int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                       int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
+                       int32_t head_dim, uint16_t* cache, int32_t capacity, uint16_t* q_out,
+                       int32_t style) {
+  if (!cache) return RKV_REF_ERR_ARG;
+  return continuous_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, qkv, batch,
+                         seq_len, hq, hkv, head_dim, cache, NULL, 1.0f, 1.0f, capacity, q_out,
+                         style);
+}
+
+int rkv_ref_continuous_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                           int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                           int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
+                           int32_t head_dim, uint8_t* cache8, int32_t capacity,
+                           uint16_t* q_out, float k_scale, float v_scale, int32_t style) {
+  if (!cache8) return RKV_REF_ERR_ARG;
+  return continuous_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, qkv, batch,
+                         seq_len, hq, hkv, head_dim, NULL, cache8, reciprocal_of(k_scale),
+                         reciprocal_of(v_scale), capacity, q_out, style);
 }
 
 /* ------------------------------------------------------------- call 3 -- */
@@ -256,13 +403,14 @@ int rkv_ref_continuous(const float* cos_sin, int32_t table_batch, int32_t table_
 /* [P1] launchApplyRopeWriteKVTreeDecoding: as call 2, but the rotary
  * position of token s is tokenPosIds[b, s]; the cache slot stays end-S+s,
  * since tree siblings share a position (R6). */
-int rkv_ref_tree(const float* cos_sin, int32_t table_batch, int32_t table_len,
-                 int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
-                 const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
-                 int32_t head_dim, uint16_t* cache, int32_t capacity, uint16_t* q_out,
-                 int32_t style) {
+static int tree_core(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                     int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                     const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t hq,
+                     int32_t hkv, int32_t head_dim, uint16_t* cache, uint8_t* cache8,
+                     float k_rcp, float v_rcp, int32_t capacity, uint16_t* q_out,
+                     int32_t style) {
   if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
-                 head_dim, cache, capacity, style) ||
+                 head_dim, cache ? (const void*)cache : (const void*)cache8, capacity, style) ||
       !end_lens || !pos_ids || !q_out)
     return RKV_REF_ERR_ARG;
   for (int32_t b = 0; b < batch; ++b) {
@@ -272,10 +420,31 @@ int rkv_ref_tree(const float* cos_sin, int32_t table_batch, int32_t table_len,
       if (slot < 0 || slot >= capacity || pos < 0 || pos >= table_len) continue;
       const float* row = table_row(cos_sin, table_batch, table_len, rotary_dim, b, (int32_t)pos);
       write_token(row, qkv, b, s, (int32_t)slot, seq_len, hq, hkv, head_dim, rotary_dim, cache,
-                  capacity, q_out, style);
+                  cache8, k_rcp, v_rcp, capacity, q_out, style);
     }
   }
   return RKV_REF_OK;
+}
+
+int rkv_ref_tree(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                 int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                 const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
+                 int32_t head_dim, uint16_t* cache, int32_t capacity, uint16_t* q_out,
+                 int32_t style) {
+  if (!cache) return RKV_REF_ERR_ARG;
+  return tree_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, pos_ids, qkv, batch,
+                   seq_len, hq, hkv, head_dim, cache, NULL, 1.0f, 1.0f, capacity, q_out, style);
+}
+
+int rkv_ref_tree_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                     int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                     const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t hq,
+                     int32_t hkv, int32_t head_dim, uint8_t* cache8, int32_t capacity,
+                     uint16_t* q_out, float k_scale, float v_scale, int32_t style) {
+  if (!cache8) return RKV_REF_ERR_ARG;
+  return tree_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, pos_ids, qkv, batch,
+                   seq_len, hq, hkv, head_dim, NULL, cache8, reciprocal_of(k_scale),
+                   reciprocal_of(v_scale), capacity, q_out, style);
 }
 
 /* ------------------------------------------------------------- call 4 -- */
@@ -298,13 +467,13 @@ static const float* rope_row_of(const float* rope, int32_t rope_states, int32_t 
                                 int32_t batch, int32_t rotary_dim);
 
 static int paged_update(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t* pool,
-                        const float* token_cos_sin, const float* rope, int32_t rope_states,
+                        uint8_t* pool8, float k_rcp, float v_rcp, const float* token_cos_sin, const float* rope, int32_t rope_states,
                         int32_t rope_rows, const int32_t* state_indices,
                         const int32_t* delta_positions, const int32_t* delta_to_seq,
                         const int32_t* page_table, int32_t num_delta, int32_t batch, int32_t hkv,
                         int32_t head_dim, int32_t rotary_dim, int32_t num_pages,
                         int32_t max_pages_per_seq, int32_t style) {
-  if (!k_delta || !v_delta || !pool || (!token_cos_sin && !rope) || !delta_positions ||
+  if (!k_delta || !v_delta || (!pool && !pool8) || (!token_cos_sin && !rope) || !delta_positions ||
       !delta_to_seq || !page_table)
     return RKV_REF_ERR_ARG;
   if (num_delta < 0 || batch < 0 || hkv < 0 || num_pages < 0 || max_pages_per_seq < 0 ||
@@ -316,6 +485,7 @@ static int paged_update(const uint16_t* k_delta, const uint16_t* v_delta, uint16
   if (style != RKV_REF_NEOX && style != RKV_REF_GPTJ) return RKV_REF_ERR_ARG;
   const int64_t TPP = RKV_REF_TOKENS_PER_PAGE;
   int32_t D = head_dim;
+  double w[4096];
   for (int32_t i = 0; i < num_delta; ++i) {
     int64_t p = delta_positions[i];
     int64_t q = delta_to_seq[i];
@@ -329,15 +499,28 @@ static int paged_update(const uint16_t* k_delta, const uint16_t* v_delta, uint16
                                      : rope_row_of(rope, rope_states, rope_rows, state_indices,
                                                    p, q, batch, rotary_dim);
     if (row && kid >= 0 && kid < num_pages) {
-      for (int32_t h = 0; h < hkv; ++h)
-        rkv_ref_rotate_row(k_delta + ((size_t)i * hkv + h) * D,
-                           pool + (((size_t)kid * TPP + off) * hkv + h) * D, row, D,
-                           rotary_dim, style);
+      for (int32_t h = 0; h < hkv; ++h) {
+        const uint16_t* k = k_delta + ((size_t)i * hkv + h) * D;
+        size_t dst = (((size_t)kid * TPP + off) * hkv + h) * D;
+        if (pool8) {
+          rkv_ref_rotate_row_wide(k, w, row, D, rotary_dim, style);
+          store_row8(pool8 + dst, w, D, k_rcp);
+        } else {
+          rkv_ref_rotate_row(k, pool + dst, row, D, rotary_dim, style);
+        }
+      }
     }
     if (vid >= num_pages && vid < 2 * (int64_t)num_pages) {
-      for (int32_t h = 0; h < hkv; ++h)
-        memcpy(pool + (((size_t)vid * TPP + off) * hkv + h) * D,
-               v_delta + ((size_t)i * hkv + h) * D, (size_t)D * sizeof(uint16_t));
+      for (int32_t h = 0; h < hkv; ++h) {
+        const uint16_t* v = v_delta + ((size_t)i * hkv + h) * D;
+        size_t dst = (((size_t)vid * TPP + off) * hkv + h) * D;
+        if (pool8) {
+          widen_row(v, w, D);
+          store_row8(pool8 + dst, w, D, v_rcp);
+        } else {
+          memcpy(pool + dst, v, (size_t)D * sizeof(uint16_t));
+        }
+      }
     }
   }
   return RKV_REF_OK;
@@ -349,8 +532,21 @@ int rkv_ref_paged_delta(const uint16_t* k_delta, const uint16_t* v_delta, uint16
                         int32_t num_delta, int32_t batch, int32_t hkv, int32_t head_dim,
                         int32_t rotary_dim, int32_t num_pages, int32_t max_pages_per_seq,
                         int32_t style) {
-  if (!token_cos_sin) return RKV_REF_ERR_ARG;
-  return paged_update(k_delta, v_delta, pool, token_cos_sin, NULL, 0, 0, NULL, delta_positions,
+  if (!token_cos_sin || !pool) return RKV_REF_ERR_ARG;
+  return paged_update(k_delta, v_delta, pool, NULL, 1.0f, 1.0f, token_cos_sin, NULL, 0, 0, NULL,
+                      delta_positions, delta_to_seq, page_table, num_delta, batch, hkv,
+                      head_dim, rotary_dim, num_pages, max_pages_per_seq, style);
+}
+
+int rkv_ref_paged_delta_fp8(const uint16_t* k_delta, const uint16_t* v_delta, uint8_t* pool8,
+                            const float* token_cos_sin, const int32_t* delta_positions,
+                            const int32_t* delta_to_seq, const int32_t* page_table,
+                            int32_t num_delta, int32_t batch, int32_t hkv, int32_t head_dim,
+                            int32_t rotary_dim, int32_t num_pages, int32_t max_pages_per_seq,
+                            float k_scale, float v_scale, int32_t style) {
+  if (!token_cos_sin || !pool8) return RKV_REF_ERR_ARG;
+  return paged_update(k_delta, v_delta, NULL, pool8, reciprocal_of(k_scale),
+                      reciprocal_of(v_scale), token_cos_sin, NULL, 0, 0, NULL, delta_positions,
                       delta_to_seq, page_table, num_delta, batch, hkv, head_dim, rotary_dim,
                       num_pages, max_pages_per_seq, style);
 }
@@ -398,10 +594,26 @@ int rkv_ref_paged_delta_gather(const uint16_t* k_delta, const uint16_t* v_delta,
                                int32_t num_delta, int32_t batch, int32_t hkv, int32_t head_dim,
                                int32_t rotary_dim, int32_t num_pages, int32_t max_pages_per_seq,
                                int32_t style) {
-  if (!rope) return RKV_REF_ERR_ARG;
-  return paged_update(k_delta, v_delta, pool, NULL, rope, rope_states, rope_rows, state_indices,
-                      delta_positions, delta_to_seq, page_table, num_delta, batch, hkv, head_dim,
-                      rotary_dim, num_pages, max_pages_per_seq, style);
+  if (!rope || !pool) return RKV_REF_ERR_ARG;
+  return paged_update(k_delta, v_delta, pool, NULL, 1.0f, 1.0f, NULL, rope, rope_states,
+                      rope_rows, state_indices, delta_positions, delta_to_seq, page_table,
+                      num_delta, batch, hkv, head_dim, rotary_dim, num_pages, max_pages_per_seq,
+                      style);
+}
+
+int rkv_ref_paged_delta_gather_fp8(const uint16_t* k_delta, const uint16_t* v_delta,
+                                   uint8_t* pool8, const float* rope, int32_t rope_states,
+                                   int32_t rope_rows, const int32_t* state_indices,
+                                   const int32_t* delta_positions, const int32_t* delta_to_seq,
+                                   const int32_t* page_table, int32_t num_delta, int32_t batch,
+                                   int32_t hkv, int32_t head_dim, int32_t rotary_dim,
+                                   int32_t num_pages, int32_t max_pages_per_seq, float k_scale,
+                                   float v_scale, int32_t style) {
+  if (!rope || !pool8) return RKV_REF_ERR_ARG;
+  return paged_update(k_delta, v_delta, NULL, pool8, reciprocal_of(k_scale),
+                      reciprocal_of(v_scale), NULL, rope, rope_states, rope_rows, state_indices,
+                      delta_positions, delta_to_seq, page_table, num_delta, batch, hkv,
+                      head_dim, rotary_dim, num_pages, max_pages_per_seq, style);
 }
 
 /* [P3] checkDFlashRopeCapacity: the table may be shorter than the padded

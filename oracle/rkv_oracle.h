@@ -33,6 +33,16 @@ double rkv_ref_half_to_double(uint16_t h);
 /* binary64 -> binary16, round to nearest, ties to even, with subnormals */
 uint16_t rkv_ref_double_to_half(double x);
 
+/* exact E4M3 -> binary64 (OCP 8-bit float, e4m3fn: no infinities, 0x7f/0xff NaN) */
+double rkv_ref_e4m3_to_double(uint8_t b);
+/* binary64 -> E4M3, round to nearest even, saturating to +-448, NaN kept */
+uint8_t rkv_ref_double_to_e4m3(double x);
+
+/* The rotation of one head row in binary64, before any rounding to fp16;
+ * w[d] = x[d] for d >= R. */
+void rkv_ref_rotate_row_wide(const uint16_t* x, double* w, const float* cos_sin_row,
+                             int32_t head_dim, int32_t rotary_dim, int32_t style);
+
 /* Rotate one head row x[0:D] with one table row [cos(R/2) | sin(R/2)];
  * y may equal x.  Dims d >= R are copied bit for bit. */
 void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* cos_sin_row,
@@ -83,6 +93,42 @@ int rkv_ref_paged_delta_gather(const uint16_t* k_delta, const uint16_t* v_delta,
                                int32_t num_delta, int32_t batch, int32_t num_kv_heads,
                                int32_t head_dim, int32_t rotary_dim, int32_t num_pages,
                                int32_t max_pages_per_seq, int32_t style);
+
+/* fp8 (E4M3) cache variants of the calls above: the same arguments with the
+ * cache (pool) as bytes plus the per-tensor scales; each cache value is the
+ * fp16 variant's unrounded K / V times 1/scale, rounded to E4M3. */
+int rkv_ref_packed_qkv_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                           int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           uint8_t* kv_cache, int32_t capacity, float k_scale, float v_scale,
+                           int32_t style);
+int rkv_ref_continuous_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                           int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                           int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, uint8_t* kv_cache,
+                           int32_t capacity, uint16_t* q_out, float k_scale, float v_scale,
+                           int32_t style);
+int rkv_ref_tree_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                     int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                     const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, uint8_t* kv_cache,
+                     int32_t capacity, uint16_t* q_out, float k_scale, float v_scale,
+                     int32_t style);
+int rkv_ref_paged_delta_fp8(const uint16_t* k_delta, const uint16_t* v_delta, uint8_t* pool,
+                            const float* token_cos_sin, const int32_t* delta_positions,
+                            const int32_t* delta_to_seq, const int32_t* page_table,
+                            int32_t num_delta, int32_t batch, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t rotary_dim, int32_t num_pages,
+                            int32_t max_pages_per_seq, float k_scale, float v_scale,
+                            int32_t style);
+int rkv_ref_paged_delta_gather_fp8(const uint16_t* k_delta, const uint16_t* v_delta,
+                                   uint8_t* pool, const float* rope, int32_t rope_states,
+                                   int32_t rope_rows, const int32_t* state_indices,
+                                   const int32_t* delta_positions, const int32_t* delta_to_seq,
+                                   const int32_t* page_table, int32_t num_delta, int32_t batch,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t rotary_dim,
+                                   int32_t num_pages, int32_t max_pages_per_seq, float k_scale,
+                                   float v_scale, int32_t style);
 
 /* Capacity check: RKV_REF_ERR_CAPACITY iff cos_sin_len > kv_capacity. */
 int rkv_ref_check_rope_capacity(int32_t cos_sin_len, int32_t kv_capacity);

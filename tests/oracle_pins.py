@@ -18,7 +18,14 @@ Each ``pin_*`` takes an oracle library handle ``L`` and raises
   (b, s, h) are located by scanning the whole cache;
 * bit-exact copies of all 65,536 fp16 patterns, untouched-slot sentinels,
   cross-call reductions, skip rules case by case, the capacity truth table
-  (``tests/golden/capacity_check.txt``).
+  (``tests/golden/capacity_check.txt``);
+* the fp8 (E4M3) cache variants: the codec against torch's float8_e4m3fn
+  conversions, against brute-force nearest-even search over the 256 codes and
+  against hand-worked values of the OCP format
+  (``tests/golden/e4m3_values.txt``); cache bytes against the exact rational
+  rotation (an explicit matrix in ``fractions.Fraction``) times the fp32
+  reciprocal scale, encoded by brute force; layout and skip rules against the
+  fp16 variant's.
 
 ``tests/test_oracle_pins.py`` runs every pin against the oracle;
 ``tests/test_oracle_mutations.py`` plants mistakes into a copy of the oracle
@@ -27,6 +34,7 @@ source and checks that some pin fails for each.
 from __future__ import annotations
 
 import os
+from fractions import Fraction
 
 import numpy as np
 
@@ -672,6 +680,292 @@ def pin_fused_gather_is_gather_then_update(L):
     flat = got.reshape(2 * w.num_pages, 64, w.Hkv, w.D)
     assert np.all(flat[kid, p_max % 64] == W.SENTINEL)
     assert np.array_equal(flat[vid, p_max % 64], w.v_delta[i])
+
+
+# ------------------------------------------------------------------- fp8 --
+
+def _e4m3_values():
+    """The 256 E4M3 codes decoded by torch (a library routine)."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _e4m3_positive():
+    """(magnitudes, codes) of the finite non-negative codes 0x00..0x7e, ascending."""
+    v = _e4m3_values()[:0x7F]
+    assert np.all(np.diff(v) > 0)
+    return v, np.arange(0x7F)
+
+
+def _nearest_e4m3(x) -> np.ndarray:
+    """Brute force: the code nearest to each double, ties to the even code,
+    magnitudes past 448 saturated, NaN kept (sign bit copied)."""
+    x = np.asarray(x, dtype=np.float64)
+    mags, codes = _e4m3_positive()
+    a = np.abs(x)
+    d = np.abs(a[..., None] - mags)                     # [..., 127]
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    even = cand & (codes % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    out = codes[pick].astype(np.uint8)
+    out = np.where(a >= 448.0, np.uint8(0x7E), out)
+    out = np.where(np.isnan(x), np.uint8(0x7F), out)
+    return np.where(np.signbit(x), out | np.uint8(0x80), out).astype(np.uint8)
+
+
+def _nearest_e4m3_exact(fr: Fraction) -> int:
+    """Brute force on an exact rational: nearest code, ties to even, saturating."""
+    mags, codes = _e4m3_positive()
+    a = abs(fr)
+    sign = 0x80 if fr < 0 else 0
+    if a >= 448:
+        return sign | 0x7E
+    i = int(np.searchsorted(mags, float(a)))
+    best, best_d = None, None
+    for j in (i - 2, i - 1, i, i + 1):
+        if 0 <= j < mags.size:
+            dj = abs(a - Fraction(float(mags[j])))
+            if best is None or dj < best_d or (dj == best_d and codes[j] % 2 == 0):
+                best, best_d = j, dj
+    return sign | int(codes[best])
+
+
+def _rcp(scale) -> float:
+    """fp32 reciprocal of an fp32 scale (numpy's IEEE division)."""
+    if scale is None:
+        return 1.0
+    return float(np.float32(1.0) / np.float32(scale))
+
+
+def pin_e4m3_decode_all_codes(L):
+    want = _e4m3_values()
+    got = np.array([oracle.e4m3_to_double(b, L) for b in range(256)])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_e4m3_encode_vs_torch(L):
+    """fp32 inputs below the saturation point round exactly as torch rounds
+    float32 -> float8_e4m3fn (nearest even); every midpoint between adjacent
+    codes and its two fp32 neighbours is included."""
+    import torch
+    mags, _ = _e4m3_positive()
+    mids = (mags[:-1] + mags[1:]) / 2
+    base = np.concatenate([mags, mids]).astype(np.float32)
+    xs = np.concatenate([base, np.nextafter(base, np.float32(np.inf)),
+                         np.nextafter(base, np.float32(0))])
+    r = np.random.default_rng(40)
+    xs = np.concatenate([xs, r.uniform(0, 447.9, 3000).astype(np.float32),
+                         np.exp2(r.uniform(-14, 8.8, 3000)).astype(np.float32)])
+    xs = xs[xs < 448]
+    xs = np.concatenate([xs, -xs])
+    want = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.double_to_e4m3(float(x), L) for x in xs], dtype=np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(xs[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def pin_e4m3_encode_brute_force(L):
+    """Doubles over the whole range, saturation, infinities, NaN and signed
+    zero, against a nearest-even search over all codes."""
+    r = np.random.default_rng(41)
+    xs = np.concatenate([np.exp2(r.uniform(-16, 12, 4000)), r.uniform(0, 500, 2000),
+                         [0.0, 447.9999, 448.0, 464.0, 480.0, 1e300, np.inf, np.nan,
+                          2.0 ** -10, 2.0 ** -10 * 1.0000001, 3 * 2.0 ** -10]])
+    xs = np.concatenate([xs, -xs])
+    got = np.array([oracle.double_to_e4m3(float(x), L) for x in xs], dtype=np.uint8)
+    want = _nearest_e4m3(xs)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(xs[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def pin_e4m3_hand_values(L):
+    """Values worked out from the OCP E4M3 definition (the golden file)."""
+    path = os.path.join(GOLDEN, "e4m3_values.txt")
+    n = 0
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        x, code = line.split()
+        x = float.fromhex(x) if "0x" in x.lower() and "p" in x.lower() else float(x)
+        assert oracle.double_to_e4m3(x, L) == int(code, 16), (x, code)
+        n += 1
+    assert n >= 20
+
+
+def pin_fp8_v_all_patterns(L):
+    """The V rows of every fp16 bit pattern reach the fp8 pool as the nearest
+    E4M3 code of v * (1/v_scale), for a missing scale (1) and for 2 and 0.0109."""
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    N, Hkv, D = 64, 16, 64
+    v_delta = allbits.reshape(N, Hkv, D)
+    k_delta = np.zeros_like(v_delta)
+    pos = np.arange(N, dtype=np.int32)
+    seq = np.zeros(N, dtype=np.int32)
+    pt = np.array([[[0], [1]]], dtype=np.int32)
+    cs = np.zeros((N, 0), dtype=np.float32)
+    for vs in (None, 2.0, 0.0109):
+        pool = np.full((2, 1, 64, Hkv, D), W.SENTINEL8, dtype=np.uint8)
+        out = oracle.paged_delta_fp8(k_delta, v_delta, pool, cs, pos, seq, pt, 1, None, vs,
+                                     NEOX, L)
+        with np.errstate(invalid="ignore"):
+            want = _nearest_e4m3(val(allbits) * _rcp(vs)).reshape(N, Hkv, D)
+        assert np.array_equal(out[1, 0], want), vs
+        assert np.all(out[0, 0] == 0)       # K of zeros is +0
+
+
+def pin_fp8_k_exact_rational(L):
+    """K cache bytes are the exact rotation (an explicit rotation matrix in
+    rational arithmetic) times the fp32 reciprocal scale, rounded once to the
+    nearest E4M3 code; the fp16 result never enters."""
+    r = np.random.default_rng(42)
+    B, S, Hq, Hkv, D, cap = 2, 16, 1, 4, 128, 16
+    for style, R, ks, n_tok in [(NEOX, 128, 0.0123, 32), (GPTJ, 96, None, 4),
+                                (NEOX, 64, 0.25, 4)]:
+        qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+        table = W.rope_table(2, cap, R, 10000.0, offsets=np.array([3, 1000]))
+        cache = np.full((B, 2, Hkv, cap, D), W.SENTINEL8, dtype=np.uint8)
+        _, c8 = oracle.packed_qkv_fp8(table, qkv, cache, ks, 1.0, style, L)
+        rcp = Fraction(_rcp(ks))
+        for t in range(n_tok):
+            b, s = divmod(t, S)
+            M = _rotation_matrix(table[b, s], D, R, style)
+            terms = [[(j, Fraction(float(M[i, j]))) for j in np.nonzero(M[i])[0]]
+                     for i in range(D)]
+            for h in range(Hkv):
+                x = [Fraction(float(v)) for v in val(qkv[b, s, Hq + h])]
+                want = [_nearest_e4m3_exact(sum(m * x[j] for j, m in terms[i]) * rcp)
+                        for i in range(D)]
+                assert c8[b, 0, h, s].tolist() == want, (style, R, b, s, h)
+
+
+def pin_fp8_layout_and_skips_match_fp16(L):
+    """Every call with an fp8 cache writes exactly the slots the fp16 variant
+    writes (sentinel-filled caches on both sides), leaves Q (and the in-place
+    K of call 1) as the fp16 variant leaves them, and its V bytes are the
+    nearest codes of the fp16 V values times 1/v_scale."""
+    ks, vs = 0.0123, 0.0109
+    rv = _rcp(vs)
+    for style in (NEOX, GPTJ):
+        # call 1
+        w = W.packed(2, 7, 3, 2, 64, 48, 9, style, 50 + style, table_batch=2, table_len=9)
+        q16, c16 = oracle.packed_qkv(w.cos_sin, w.qkv, w.cache, style, L)
+        c8 = np.full(w.cache.shape, W.SENTINEL8, dtype=np.uint8)
+        q8, c8 = oracle.packed_qkv_fp8(w.cos_sin, w.qkv, c8, ks, vs, style, L)
+        assert np.array_equal(q8, q16)
+        assert np.array_equal(c8 == W.SENTINEL8, c16 == W.SENTINEL)
+        assert np.array_equal(c8[:, 1, :, :w.S], _nearest_e4m3(val(c16[:, 1, :, :w.S]) * rv))
+        # calls 2 and 3 with out-of-range tokens
+        B, S, Hq, Hkv, D, cap = 3, 6, 2, 2, 64, 12
+        r = np.random.default_rng(60 + style)
+        qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+        table = W.rope_table(1, 10, D, 10000.0)
+        end = np.array([3, 12, 8], dtype=np.int32)
+        pos = np.array([[-1, 0, 1, 2, 9, 10]] * B, dtype=np.int32)
+        for call in ("continuous", "tree"):
+            cache16 = W.sentinel_f16((B, 2, Hkv, cap, D))
+            cache8 = np.full(cache16.shape, W.SENTINEL8, dtype=np.uint8)
+            qo = W.sentinel_f16((B, S, Hq, D))
+            if call == "continuous":
+                c16, q16 = oracle.continuous(table, end, qkv, cache16, qo, style, L)
+                c8, q8 = oracle.continuous_fp8(table, end, qkv, cache8, qo, ks, vs, style, L)
+            else:
+                c16, q16 = oracle.tree(table, end, pos, qkv, cache16, qo, style, L)
+                c8, q8 = oracle.tree_fp8(table, end, pos, qkv, cache8, qo, ks, vs, style, L)
+            assert np.array_equal(q8, q16), call
+            written = c16 != W.SENTINEL
+            assert np.array_equal(c8 != W.SENTINEL8, written), call
+            assert written.any() and not written.all()
+            v16 = c16[:, 1][written[:, 1]]
+            assert np.array_equal(c8[:, 1][written[:, 1]], _nearest_e4m3(val(v16) * rv)), call
+        # call 4, plain and with the gather fused in
+        w = W.paged(96, 4, 2, 64, 64, 12, 3, style, 70 + style, width=24, pool_fill="sentinel")
+        p16 = oracle.paged_delta(w.k_delta, w.v_delta, w.pool, w.cos_sin, w.positions, w.seq,
+                                 w.page_table, w.batch, style, L)
+        p8 = oracle.paged_delta_fp8(w.k_delta, w.v_delta,
+                                    np.full(w.pool.shape, W.SENTINEL8, np.uint8), w.cos_sin,
+                                    w.positions, w.seq, w.page_table, w.batch, ks, vs, style, L)
+        written = p16 != W.SENTINEL
+        assert np.array_equal(p8 != W.SENTINEL8, written)
+        assert np.array_equal(p8[1][written[1]], _nearest_e4m3(val(p16[1][written[1]]) * rv))
+        rope = W.rope_table(4, 200, 64, 10000.0, offsets=np.array([0, 3, 9, 27]))
+        si = np.array([3, 1, 0, 2], dtype=np.int32)
+        g16 = oracle.paged_delta_gather(w.k_delta, w.v_delta, w.pool, rope, si, w.positions,
+                                        w.seq, w.page_table, w.batch, style, L)
+        g8 = oracle.paged_delta_gather_fp8(w.k_delta, w.v_delta,
+                                           np.full(w.pool.shape, W.SENTINEL8, np.uint8), rope,
+                                           si, w.positions, w.seq, w.page_table, w.batch, ks, vs,
+                                           style, L)
+        gw = g16 != W.SENTINEL
+        assert np.array_equal(g8 != W.SENTINEL8, gw)
+        # K through the gather: the rotation with the gathered row
+        rows = oracle.gather_delta_rope(rope, si, w.positions, w.seq, w.batch, L)
+        k8 = oracle.paged_delta_fp8(w.k_delta, w.v_delta,
+                                    np.full(w.pool.shape, W.SENTINEL8, np.uint8), rows,
+                                    w.positions, w.seq, w.page_table, w.batch, ks, vs, style, L)
+        assert np.array_equal(g8[0], k8[0])
+
+
+def pin_fp8_k_near_fp16(L):
+    """Scale 1: each K byte decodes to within half an E4M3 quantum (plus the
+    fp16 rounding) of the fp16 variant's K."""
+    w = W.packed(1, 32, 2, 4, 128, 128, 32, NEOX, 80)
+    _, c16 = oracle.packed_qkv(w.cos_sin, w.qkv, w.cache, NEOX, L)
+    c8 = np.full(w.cache.shape, W.SENTINEL8, dtype=np.uint8)
+    _, c8 = oracle.packed_qkv_fp8(w.cos_sin, w.qkv, c8, None, None, NEOX, L)
+    k16 = val(c16[:, 0])
+    k8 = _e4m3_values()[c8[:, 0].astype(np.int64)]
+    a = np.abs(k16)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    quantum = 2.0 ** (e - 3)
+    assert np.all(np.abs(k8 - k16) <= quantum / 2 + 2.0 ** -11 * a + 2.0 ** -25)
+
+
+def pin_fp8_cross_call_reductions(L):
+    """The fp8 cache of call 2 from an empty cache equals call 1's (whose K
+    bytes are pinned exactly above), a linear-chain tree equals call 2, and the
+    paged update through an identity page table equals call 2's K and V."""
+    r = np.random.default_rng(90)
+    B, S, Hq, Hkv, D, cap = 2, 6, 2, 2, 64, 10
+    ks, vs = 0.0123, 0.0109
+    for style in (NEOX, GPTJ):
+        qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+        table = W.rope_table(1, cap, D, 10000.0)
+        cache = np.full((B, 2, Hkv, cap, D), W.SENTINEL8, dtype=np.uint8)
+        _, c1 = oracle.packed_qkv_fp8(table, qkv, cache, ks, vs, style, L)
+        end = np.full(B, S, dtype=np.int32)
+        c2, _ = oracle.continuous_fp8(table, end, qkv, cache, W.sentinel_f16((B, S, Hq, D)),
+                                      ks, vs, style, L)
+        assert np.array_equal(c1, c2), style
+        end = np.array([7, 10], dtype=np.int32)
+        c2, _ = oracle.continuous_fp8(table, end, qkv, cache, W.sentinel_f16((B, S, Hq, D)),
+                                      ks, vs, style, L)
+        pos = (end[:, None] - S + np.arange(S)[None, :]).astype(np.int32)
+        c3, _ = oracle.tree_fp8(table, end, pos, qkv, cache, W.sentinel_f16((B, S, Hq, D)),
+                                ks, vs, style, L)
+        assert np.array_equal(c2, c3), style
+        P = B
+        pt = np.empty((B, 2, 1), dtype=np.int32)
+        pt[:, 0, 0] = np.arange(B)
+        pt[:, 1, 0] = P + np.arange(B)
+        N = B * S
+        k_delta = qkv[:, :, Hq:Hq + Hkv].reshape(N, Hkv, D)
+        v_delta = qkv[:, :, Hq + Hkv:].reshape(N, Hkv, D)
+        posd = pos.reshape(-1).astype(np.int32)
+        seqd = np.repeat(np.arange(B), S).astype(np.int32)
+        pool = np.full((2, P, 64, Hkv, D), W.SENTINEL8, dtype=np.uint8)
+        pool = oracle.paged_delta_fp8(k_delta, v_delta, pool, table[0][posd], posd, seqd, pt, B,
+                                      ks, vs, style, L)
+        for b in range(B):
+            for plane in range(2):
+                got = pool[plane, b, :cap].transpose(1, 0, 2)
+                assert np.array_equal(got, c2[b, plane]), (style, b, plane)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

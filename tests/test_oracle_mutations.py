@@ -15,22 +15,23 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "rkv_oracle.c")
 
 MUTATIONS = {
-    "sub_becomes_add": ("double_to_half(pu_c - pv_s)", "double_to_half(pu_c + pv_s)"),
-    "add_becomes_sub": ("double_to_half(pv_c + pu_s)", "double_to_half(pv_c - pu_s)"),
-    "dropped_sin_term": ("double_to_half(pv_c + pu_s)", "double_to_half(pv_c)"),
+    "sub_becomes_add": ("w[u] = pu_c - pv_s;", "w[u] = pu_c + pv_s;"),
+    "add_becomes_sub": ("w[v] = pv_c + pu_s;", "w[v] = pv_c - pu_s;"),
+    "dropped_sin_term": ("w[v] = pv_c + pu_s;", "w[v] = pv_c;"),
     "sin_reads_cos_half": ("double s = (double)row[half + i];", "double s = (double)row[i];"),
     "neox_partner_off_by_one": ("v = i + half;", "v = i + half - (i > 0);"),
     "gptj_pair_swapped": ("u = 2 * i;\n      v = 2 * i + 1;", "u = 2 * i + 1;\n      v = 2 * i;"),
-    "ties_away_from_zero": ("(rem == 0.5 && (k & 1))", "(rem == 0.5)"),
+    "ties_away_from_zero": ("(rem == 0.5 && (k & 1))) k += 1;\n  if (k >= 2048)",
+                            "(rem == 0.5)) k += 1;\n  if (k >= 2048)"),
     "no_subnormal_clamp": ("if (ue < -14) ue = -14;", "if (ue < -15) ue = -15;"),
     "subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
-    "passthrough_zeroed": ("for (int d = 0; d < head_dim; ++d) tmp[d] = x[d];",
-                           "for (int d = 0; d < head_dim; ++d) tmp[d] = 0;"),
+    "passthrough_zeroed": ("? rkv_ref_double_to_half(w[d]) : x[d];",
+                           "? rkv_ref_double_to_half(w[d]) : 0;"),
     "table_batch_ignored": ("int32_t tb = (table_batch == 1) ? 0 : b;", "int32_t tb = 0;"),
     "k_into_v_plane": ("memcpy(cache + cache_row(b, 0, h, pos, hkv, capacity, D), x,",
                        "memcpy(cache + cache_row(b, 1, h, pos, hkv, capacity, D), x,"),
-    "k_not_rotated_in_place": ("        rkv_ref_rotate_row(x, x, row, D, R, style);\n        memcpy",
-                               "        memcpy"),
+    "k_not_rotated_in_place": ("        rkv_ref_rotate_row(x, x, row, D, R, style);\n        if (!cache8)",
+                               "        if (!cache8)"),
     "end_len_off_by_one": ("int64_t slot = (int64_t)end_lens[b] - seq_len + s;\n      int64_t pos = slot;",
                            "int64_t slot = (int64_t)end_lens[b] - seq_len + s + 1;\n      int64_t pos = slot;"),
     "tree_uses_slot_as_position": ("int64_t pos = pos_ids[(size_t)b * seq_len + s];",
@@ -42,11 +43,33 @@ MUTATIONS = {
                              "if (p > (int64_t)max_pages_per_seq * TPP) continue;"),
     "paged_v_plane_lower_bound": ("vid >= num_pages && vid < 2", "vid >= 0 && vid < 2"),
     "paged_inactive_sequence_kept": ("if (q >= batch) continue;", ""),
-    "paged_offset_transposed": ("pool + (((size_t)kid * TPP + off) * hkv + h) * D",
-                                "pool + (((size_t)kid * TPP + h) * hkv + off % hkv) * D"),
+    "paged_offset_transposed": ("size_t dst = (((size_t)kid * TPP + off) * hkv + h) * D;",
+                                "size_t dst = (((size_t)kid * TPP + h) * hkv + off % hkv) * D;"),
     "capacity_check_inclusive": ("return cos_sin_len > kv_capacity ?", "return cos_sin_len >= kv_capacity ?"),
     "gather_position_past_table": ("st >= rope_states || p >= rope_rows", "st >= rope_states || p > rope_rows"),
     "gather_ignores_state_indices": ("int64_t st = state_indices ? state_indices[q]", "int64_t st = state_indices ? q"),
+    # fp8 (E4M3) cache variants
+    "e4m3_overflow_to_nan": ("if (a >= 448.0) return (uint8_t)(sign | 0x7e);",
+                             "if (a >= 464.0) return (uint8_t)(sign | 0x7f);"),
+    "e4m3_ties_away_from_zero": ("(rem == 0.5 && (k & 1))) k += 1;\n  if (k >= 16)",
+                                 "(rem == 0.5)) k += 1;\n  if (k >= 16)"),
+    "e4m3_subnormal_clamp": ("if (ue < -6) ue = -6;", "if (ue < -7) ue = -7;"),
+    "e4m3_decode_subnormal": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "e4m3_decode_bias": ("v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 9);"),
+    "fp8_multiplies_by_scale": ("rkv_ref_double_to_e4m3(w[d] * (double)rcp)",
+                                "rkv_ref_double_to_e4m3(w[d] / (double)rcp)"),
+    "fp8_k_from_fp16_rounded": ("rkv_ref_double_to_e4m3(w[d] * (double)rcp)",
+                                "rkv_ref_double_to_e4m3(rkv_ref_half_to_double(rkv_ref_double_to_half(w[d])) * (double)rcp)"),
+    "fp8_k_uses_v_scale": ("store_row8(cache8 + cache_row(b, 0, h, slot, hkv, cap, D), w, D, k_rcp);",
+                           "store_row8(cache8 + cache_row(b, 0, h, slot, hkv, cap, D), w, D, v_rcp);"),
+    "fp8_k_unrotated": ("      rkv_ref_rotate_row_wide(k, w, row, D, rotary_dim, style);\n",
+                        "      widen_row(k, w, D);\n"),
+    "fp8_packed_v_into_k_plane": ("store_row8(cache8 + cache_row(b, 1, h, pos, hkv, capacity, D), w, D, v_rcp);",
+                                  "store_row8(cache8 + cache_row(b, 0, h, pos, hkv, capacity, D), w, D, v_rcp);"),
+    "fp8_paged_v_unscaled": ("          store_row8(pool8 + dst, w, D, v_rcp);",
+                             "          store_row8(pool8 + dst, w, D, 1.0f);"),
+    "fp8_reciprocal_truncated": ("return (float)(1.0 / (double)scale);",
+                                 "return (float)(1.0 / (double)scale) * (1.0f - 0x1p-23f);"),
 }
 
 

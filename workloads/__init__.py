@@ -30,6 +30,14 @@ TOKENS_PER_PAGE = 64
 # A quiet NaN with a payload: never produced by arithmetic, so a slot that
 # still holds it after a call was not written.
 SENTINEL = 0x7E5A
+# The E4M3 NaN code: finite inputs never produce it, so an fp8 cache byte
+# that still holds it was not written.
+SENTINEL8 = 0x7F
+# Per-tensor fp8 scales of the synthetic workloads: N(0,1) activations of
+# magnitude up to about 5 land near the top of the E4M3 range (448), and the
+# rare tails beyond 5.5 sigma saturate.
+K_SCALE = 0.0123
+V_SCALE = 0.0109
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -125,6 +133,7 @@ class Contig:
     end_lens: np.ndarray | None = None   # i32 [B]
     pos_ids: np.ndarray | None = None    # i32 [B, S]
     name: str = ""
+    extra: dict = field(default_factory=dict)
 
     @property
     def tokens(self) -> int:
@@ -253,6 +262,33 @@ def paged(N, batch, Hkv, D, R, num_pages, max_pages, style, seed, theta=10000.0,
 
 
 _TILE = 1 << 24
+
+
+def with_fp8_cache(w, seed: int, k_scale=K_SCALE, v_scale=V_SCALE, fill="bits"):
+    """The same workload with an E4M3 cache (pool): ``uint8`` bytes, filled
+    with seeded random bytes (``"bits"``) or the NaN sentinel, and fp32
+    per-tensor scales in ``extra["fp8"]`` (None means no scale)."""
+    r = rng(seed)
+    shape = w.pool.shape if hasattr(w, "pool") else w.cache.shape
+    if fill == "sentinel":
+        buf = np.full(shape, SENTINEL8, dtype=np.uint8)
+    elif fill == "bits":
+        n = int(np.prod(shape, dtype=np.int64))
+        if n <= _TILE:
+            buf = r.integers(0, 256, size=n, dtype=np.uint8).reshape(shape)
+        else:
+            block = r.integers(0, 256, size=_TILE, dtype=np.uint8)
+            buf = np.resize(block, n).reshape(shape)
+    else:
+        raise ValueError(fill)
+    if hasattr(w, "pool"):
+        w.pool = buf
+    else:
+        w.cache = buf
+    w.extra["fp8"] = {"k_scale": None if k_scale is None else np.float32(k_scale),
+                      "v_scale": None if v_scale is None else np.float32(v_scale)}
+    w.name = (w.name + "_fp8") if w.name else "fp8"
+    return w
 
 
 def paged_gather(N, batch, Hkv, D, R, num_pages, max_pages, style, seed, rope_states=1,
