@@ -7,9 +7,9 @@ seeded synthetic data already resident in HBM.  W warm-up steps, then K timed
 steps bracketed by device synchronisation; each launch is also bracketed by
 HIP events on its stream, which give the kernel's average duration for the
 roofline.  The same workload in the library's RKV_ROUND_EXACT mode and the
-other workloads (continuous write, tree write, paged delta update, and the
-paged update with the cos/sin gather fused in) are reported under
-"workloads".  The small workloads' inputs fit the 256 MB
+other workloads (continuous write, tree write, paged delta update, the
+paged update with the cos/sin gather fused in, and the prefill, continuous
+and paged calls into an E4M3 cache) are reported under "workloads".  The small workloads' inputs fit the 256 MB
 MALL, so a 1 GiB buffer is read before each of their timed launches to push
 them back to HBM (a read leaves clean lines, so the timed kernel inherits no
 write-back); their event-bracketed times include the events' own overhead
@@ -48,8 +48,12 @@ def log(*a):
 def bytes_contig(w) -> int:
     """Bytes the method must move for calls 1-3: per written token, its packed
     Q/K/V rows read, Q (and for call 1, K in place) written, K and V cache
-    rows written; each distinct cos/sin row read once; the index arrays."""
+    rows written (D bytes each for an E4M3 cache, 2D for fp16); each
+    distinct cos/sin row read once; the index arrays (and the two fp8
+    scales)."""
     D, R, Hq, Hkv = w.D, w.R, w.Hq, w.Hkv
+    fp8 = bool(w.extra.get("fp8"))
+    cb = 1 if fp8 else 2
     H = Hq + 2 * Hkv
     tb, tlen = w.cos_sin.shape[0], w.cos_sin.shape[1]
     if w.call == "packed":
@@ -68,15 +72,19 @@ def bytes_contig(w) -> int:
     for b in range(w.B):
         t = 0 if tb == 1 else b
         rows.update((t, int(p)) for p in np.asarray(pos[b])[valid[b]])
-    per_token = H * D * 2 + write_q + 2 * Hkv * D * 2
-    return n * per_token + len(rows) * R * 4 + index
+    per_token = H * D * 2 + write_q + 2 * Hkv * D * cb
+    return n * per_token + len(rows) * R * 4 + index + (8 if fp8 else 0)
 
 
 def bytes_paged(w) -> int:
     """Call 4: per non-skipped row its two page-table entries; per mapped K
     its delta row read, rotated row written and cos/sin row read; per mapped
-    V its delta row read and written; the two metadata arrays of all rows."""
+    V its delta row read and written (an E4M3 pool row is half the fp16 row);
+    the two metadata arrays of all rows (and the two fp8 scales)."""
     D, R, Hkv, P = w.D, w.R, w.Hkv, w.num_pages
+    fp8 = bool(w.extra.get("fp8"))
+    wrow = Hkv * D * (1 if fp8 else 2)
+    scales = 8 if fp8 else 0
     p, q = w.positions.astype(np.int64), w.seq.astype(np.int64)
     live = (p >= 0) & (q >= 0) & (q < w.batch) & (p < w.max_pages * 64)
     lp = np.where(live, p // 64, 0)
@@ -95,10 +103,11 @@ def bytes_paged(w) -> int:
         has_row = (st >= 0) & (st < rope.shape[0]) & (p < rope.shape[1])
         k_ok = k_ok & has_row
         rows_read = len({(int(a), int(b)) for a, b in zip(st[k_ok], p[k_ok])})
-        return int(k_ok.sum()) * 2 * row + rows_read * R * 4 + int(v_ok.sum()) * 2 * row \
-            + w.N * 8 + int(live.sum()) * 8 + (0 if si is None else si.size * 4)
-    return int(k_ok.sum()) * (2 * row + R * 4) + int(v_ok.sum()) * 2 * row \
-        + w.N * 8 + int(live.sum()) * 8
+        return int(k_ok.sum()) * (row + wrow) + rows_read * R * 4 \
+            + int(v_ok.sum()) * (row + wrow) + w.N * 8 + int(live.sum()) * 8 \
+            + (0 if si is None else si.size * 4) + scales
+    return int(k_ok.sum()) * (row + wrow + R * 4) + int(v_ok.sum()) * (row + wrow) \
+        + w.N * 8 + int(live.sum()) * 8 + scales
 
 
 def algorithmic_bytes(w) -> int:
@@ -163,8 +172,9 @@ def traffic_from_profile(kernel_name: str):
 def kernel_source_hash() -> str:
     d = os.path.join(ROOT, "rope_kv_cache_amd", "csrc")
     hsh = hashlib.sha256()
-    for f in ("rkv_kernels.hip", "rkv_rotate.hpp", "rkv_launch.hpp", "rkv_abi.hip"):
-        hsh.update(open(os.path.join(d, f), "rb").read())
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            hsh.update(open(os.path.join(d, f), "rb").read())
     return hsh.hexdigest()
 
 
@@ -260,6 +270,22 @@ def main():
     del t
     torch.cuda.empty_cache()
 
+    if not args.no_extra:
+        # the same prefill into an E4M3 cache with per-tensor scales
+        W.with_fp8_cache(w, 7005, fill="sentinel")
+        f8_bytes = algorithmic_bytes(w)
+        t = upload(w)
+        f8_ms, f8_wall = time_launches(w, t, max(10, args.steps // 2), 3)
+        f8_gbs = f8_bytes / (f8_ms * 1e-3) / 1e9
+        extra["prefill_fp8_cache"] = {
+            "workload": w.name, "cache": "E4M3, per-tensor k/v scales",
+            "kernel_us": f8_ms * 1e3, "GB/s": f8_gbs, "frac": f8_gbs / PEAK_HBM_GBS,
+            "tokens_per_s": w.tokens / (f8_ms * 1e-3), "algorithmic_bytes": f8_bytes}
+        log(f"[bench] fp8 cache: {f8_ms * 1e3:.1f} us, {f8_gbs:.0f} GB/s "
+            f"({f8_gbs / PEAK_HBM_GBS:.1%})")
+        del t
+        torch.cuda.empty_cache()
+
     if args.calib:
         src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -280,7 +306,11 @@ def main():
                  ("continuous_gptj", lambda: W.config(2, W.GPTJ)),
                  ("tree", lambda: W.config(3)),
                  ("paged_delta", lambda: W.config(4)),
-                 ("paged_delta_gather_fused", lambda: W.config(41))]
+                 ("paged_delta_gather_fused", lambda: W.config(41)),
+                 ("continuous_neox_fp8_cache",
+                  lambda: W.with_fp8_cache(W.config(2, W.NEOX), 7002, fill="sentinel")),
+                 ("paged_delta_fp8_cache",
+                  lambda: W.with_fp8_cache(W.config(4), 7004, fill="sentinel"))]
         for label, make in cases:
             log(f"[bench] generating {label}")
             x = make()

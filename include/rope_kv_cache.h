@@ -75,7 +75,12 @@ typedef enum {
   RKV_ROUND_EXACT = 0x100 /* correctly rounded results (see Rotation above) */
 } rkv_rope_style;
 
-typedef enum { RKV_F16 = 0, RKV_F32 = 1, RKV_I32 = 2 } rkv_dtype;
+typedef enum {
+  RKV_F16 = 0,
+  RKV_F32 = 1,
+  RKV_I32 = 2,
+  RKV_F8E4M3 = 3   /* OCP 8-bit float E4M3 ("e4m3fn"), one byte per element */
+} rkv_dtype;
 
 /* A dense row-major device tensor: element type, rank (<= 5) and extents.
  * The descriptor itself is host memory and is read only during the call. */
@@ -185,6 +190,66 @@ rkv_status rkv_dflash_target_kv_cache_update_gather_rope(
     int32_t numDeltaTokens, int32_t batchSize, int32_t numKVHeads, int32_t headDim,
     int32_t rotaryDim, int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle,
     hipStream_t stream);
+
+/* fp8 (E4M3) KV cache
+ * ---------------------
+ * The five calls below are the calls above with the cache (or pool) stored
+ * as E4M3 bytes and two per-tensor scales; everything else -- shapes,
+ * positions, slots, skip rules, qkv / qOut outputs, errors -- is unchanged.
+ * (sglang rope_cache.py, fused_qk_rope_reshape_and_cache with HAVE_K_SCALE /
+ * HAVE_V_SCALE: K and V are multiplied by the reciprocal of their scale
+ * before the cast to the cache type.)
+ *   kScale, vScale  [in] DEVICE pointers to one fp32 value each, or NULL for
+ *                   a scale of 1; read by the kernel when it runs, so they
+ *                   may be updated on the stream between calls.  4-byte
+ *                   aligned, not overlapping any output.
+ * Cache value.  A K element is the unrounded rotation (dims >= rotaryDim:
+ *   the fp16 input), a V element the fp16 input, times rcp = 1/scale
+ *   correctly rounded to fp32; that product is rounded to the nearest E4M3
+ *   value, ties to even, magnitudes beyond 448 (and infinities) saturate to
+ *   +-448, NaN stays NaN.  Q and call 1's in-place K are fp16 exactly as in
+ *   the fp16 calls.
+ * Arithmetic.  By default the rotation and the product are formed in
+ *   binary32 and converted by the hardware: the code is the correctly
+ *   rounded one or, rarely, its neighbour.  With RKV_ROUND_EXACT the
+ *   rotation and the product are formed in binary64 and the code is the
+ *   correctly rounded one, bit for bit.
+ * The cache descriptor (calls 1-3) has dtype RKV_F8E4M3 and the same shape
+ * as the fp16 cache; the paged pool (call 4) is [2, numPages, 64, Hkv, D]
+ * bytes.  Cache traffic halves: D bytes per head row instead of 2*D. */
+rkv_status rkv_apply_rope_write_kv_packed_qkv_fp8(const rkv_tensor* cosSinCache, rkv_tensor* qkv,
+                                                  rkv_tensor* kvCache, const float* kScale,
+                                                  const float* vScale, int32_t ropeStyle,
+                                                  hipStream_t stream);
+
+rkv_status rkv_apply_rope_write_kv_continuous_fp8(const rkv_tensor* cosSinCache,
+                                                  const rkv_tensor* kvCacheEndLens,
+                                                  const rkv_tensor* qkv, rkv_tensor* kvCache,
+                                                  rkv_tensor* qOut, const float* kScale,
+                                                  const float* vScale, int32_t ropeStyle,
+                                                  hipStream_t stream);
+
+rkv_status rkv_apply_rope_write_kv_tree_fp8(const rkv_tensor* cosSinCache,
+                                            const rkv_tensor* kvCacheEndLens,
+                                            const rkv_tensor* tokenPosIds, const rkv_tensor* qkv,
+                                            rkv_tensor* kvCache, rkv_tensor* qOut,
+                                            const float* kScale, const float* vScale,
+                                            int32_t ropeStyle, hipStream_t stream);
+
+rkv_status rkv_dflash_target_kv_cache_update_fp8(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint8_t* kvCache, const float* kScale,
+    const float* vScale, const float* tokenAlignedCosSin, const int32_t* deltaPositions,
+    const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
+    int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
+    int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
+
+rkv_status rkv_dflash_target_kv_cache_update_gather_rope_fp8(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint8_t* kvCache, const float* kScale,
+    const float* vScale, const float* ropeCosSin, int32_t ropeStates, int32_t ropeRows,
+    const int32_t* stateIndices, const int32_t* deltaPositions,
+    const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
+    int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
+    int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
 
 /* Host-only capacity check.
  * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",

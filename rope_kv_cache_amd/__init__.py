@@ -16,8 +16,17 @@ Functions (same names as the C entry points, without the ``rkv_`` prefix):
   dflash_target_kv_cache_update_gather_rope(k_delta, v_delta, kv_cache, rope_cos_sin, state_indices,
                                             delta_positions, delta_token_to_sequence, page_table,
                                             batch_size, rope_style)
+  apply_rope_write_kv_packed_qkv_fp8(cos_sin_cache, qkv, kv_cache, k_scale, v_scale, rope_style)
+  apply_rope_write_kv_continuous_fp8(..., kv_cache, q_out, k_scale, v_scale, rope_style)
+  apply_rope_write_kv_tree_fp8(..., kv_cache, q_out, k_scale, v_scale, rope_style)
+  dflash_target_kv_cache_update_fp8(k_delta, v_delta, kv_cache, k_scale, v_scale, ...)
+  dflash_target_kv_cache_update_gather_rope_fp8(k_delta, v_delta, kv_cache, k_scale, v_scale, ...)
   check_rope_capacity(cos_sin_seq_len, kv_capacity)
   tokens_per_page()
+
+The ``_fp8`` functions take an E4M3 cache (a ``torch.uint8`` or
+``torch.float8_e4m3fn`` tensor of the fp16 cache's shape) and per-tensor
+scales (one-element float32 device tensors, or None for a scale of 1).
 """
 from __future__ import annotations
 
@@ -36,8 +45,10 @@ ROUND_EXACT = 0x100   # OR into rope_style for correctly rounded (binary64) arit
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_ALIGNMENT, ERR_ALIAS, \
     ERR_HIP = range(9)
 
-_F16, _F32, _I32 = 0, 1, 2
-_DTYPES = {torch.float16: _F16, torch.float32: _F32, torch.int32: _I32}
+_F16, _F32, _I32, _F8 = 0, 1, 2, 3
+_DTYPES = {torch.float16: _F16, torch.float32: _F32, torch.int32: _I32, torch.uint8: _F8,
+           torch.float8_e4m3fn: _F8}
+_FP8_CACHE = (torch.uint8, torch.float8_e4m3fn)
 
 
 class RkvError(RuntimeError):
@@ -65,6 +76,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rkv_apply_rope_write_kv_tree": [T, T, T, T, T, T, i32, P],
         "rkv_dflash_target_kv_cache_update": [P, P, P, P, P, P, P] + [i32] * 8 + [P],
         "rkv_dflash_target_kv_cache_update_gather_rope": [P, P, P, P, i32, i32, P, P, P, P]
+        + [i32] * 8 + [P],
+        "rkv_apply_rope_write_kv_packed_qkv_fp8": [T, T, T, P, P, i32, P],
+        "rkv_apply_rope_write_kv_continuous_fp8": [T, T, T, T, T, P, P, i32, P],
+        "rkv_apply_rope_write_kv_tree_fp8": [T, T, T, T, T, T, P, P, i32, P],
+        "rkv_dflash_target_kv_cache_update_fp8": [P] * 9 + [i32] * 8 + [P],
+        "rkv_dflash_target_kv_cache_update_gather_rope_fp8": [P] * 6 + [i32, i32] + [P] * 4
         + [i32] * 8 + [P],
         "rkv_check_rope_capacity": [i32, i32],
         "rkv_tokens_per_page": [],
@@ -124,11 +141,35 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _scale_ptr(t):
+    """Device pointer of a one-element float32 scale tensor, or None."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() != 1 or not t.is_cuda:
+        raise ValueError("scales must be one-element float32 GPU tensors or None")
+    return t.data_ptr()
+
+
+def _cache_ok(kv_cache, fp8: bool) -> None:
+    if fp8 and kv_cache.dtype not in _FP8_CACHE:
+        raise ValueError("an fp8 cache must be torch.uint8 or torch.float8_e4m3fn")
+
+
 def apply_rope_write_kv_packed_qkv(cos_sin_cache, qkv, kv_cache, rope_style: int) -> None:
     dev = _device_of(cos_sin_cache, qkv, kv_cache)
     a, b, c = _desc(cos_sin_cache), _desc(qkv), _desc(kv_cache)
     _check(lib.rkv_apply_rope_write_kv_packed_qkv(ctypes.byref(a), ctypes.byref(b),
                                                   ctypes.byref(c), int(rope_style), _stream(dev)))
+
+
+def apply_rope_write_kv_packed_qkv_fp8(cos_sin_cache, qkv, kv_cache, k_scale, v_scale,
+                                       rope_style: int) -> None:
+    dev = _device_of(cos_sin_cache, qkv, kv_cache, k_scale, v_scale)
+    _cache_ok(kv_cache, True)
+    a, b, c = _desc(cos_sin_cache), _desc(qkv), _desc(kv_cache)
+    _check(lib.rkv_apply_rope_write_kv_packed_qkv_fp8(
+        ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), _scale_ptr(k_scale),
+        _scale_ptr(v_scale), int(rope_style), _stream(dev)))
 
 
 def apply_rope_write_kv_continuous(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out,
@@ -137,6 +178,16 @@ def apply_rope_write_kv_continuous(cos_sin_cache, kv_cache_end_lens, qkv, kv_cac
     d = [_desc(t) for t in (cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out)]
     _check(lib.rkv_apply_rope_write_kv_continuous(*[ctypes.byref(x) for x in d], int(rope_style),
                                                   _stream(dev)))
+
+
+def apply_rope_write_kv_continuous_fp8(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out,
+                                       k_scale, v_scale, rope_style: int) -> None:
+    dev = _device_of(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out, k_scale, v_scale)
+    _cache_ok(kv_cache, True)
+    d = [_desc(t) for t in (cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out)]
+    _check(lib.rkv_apply_rope_write_kv_continuous_fp8(
+        *[ctypes.byref(x) for x in d], _scale_ptr(k_scale), _scale_ptr(v_scale),
+        int(rope_style), _stream(dev)))
 
 
 def apply_rope_write_kv_tree(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache,
@@ -148,6 +199,52 @@ def apply_rope_write_kv_tree(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qk
                                             _stream(dev)))
 
 
+def apply_rope_write_kv_tree_fp8(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache,
+                                 q_out, k_scale, v_scale, rope_style: int) -> None:
+    dev = _device_of(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache, q_out,
+                     k_scale, v_scale)
+    _cache_ok(kv_cache, True)
+    d = [_desc(t) for t in (cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache,
+                            q_out)]
+    _check(lib.rkv_apply_rope_write_kv_tree_fp8(
+        *[ctypes.byref(x) for x in d], _scale_ptr(k_scale), _scale_ptr(v_scale),
+        int(rope_style), _stream(dev)))
+
+
+def _paged_checks(k_delta, v_delta, kv_cache, cos_sin, delta_positions, delta_token_to_sequence,
+                  page_table, batch_size, fp8: bool, gather: bool):
+    ts = (k_delta, v_delta, kv_cache, cos_sin, delta_positions, delta_token_to_sequence,
+          page_table)
+    cache_types = _FP8_CACHE if fp8 else (torch.float16,)
+    for t, dts in zip(ts, ((torch.float16,), (torch.float16,), cache_types, (torch.float32,),
+                           (torch.int32,), (torch.int32,), (torch.int32,))):
+        if t.dtype not in dts or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {' or '.join(map(str, dts))} tensor, "
+                             f"got {t.dtype}")
+    cs_rank = 3 if gather else 2
+    if k_delta.dim() != 3 or v_delta.shape != k_delta.shape or kv_cache.dim() != 5 \
+            or cos_sin.dim() != cs_rank or page_table.dim() != 3:
+        raise ValueError("shapes must be k/v_delta [N,Hkv,D], kv_cache [2,P,64,Hkv,D], "
+                         + ("rope_cos_sin [states,rows,R]" if gather else
+                            "token_aligned_cos_sin [N,R]") + ", page_table [B,2,M]")
+    N, Hkv, D = k_delta.shape
+    if tuple(kv_cache.shape[::2]) != (2, 64, D) or kv_cache.shape[3] != Hkv \
+            or (not gather and cos_sin.shape[0] != N) or delta_positions.numel() != N \
+            or delta_token_to_sequence.numel() != N or page_table.shape[1] != 2 \
+            or batch_size > page_table.shape[0]:
+        raise ValueError("inconsistent shapes")
+    return N, Hkv, D
+
+
+def _state_ptr(state_indices, batch_size):
+    if state_indices is None:
+        return None
+    if state_indices.dtype != torch.int32 or not state_indices.is_contiguous() \
+            or state_indices.numel() < batch_size:
+        raise ValueError("state_indices must be a contiguous int32 tensor of batch_size entries")
+    return state_indices.data_ptr()
+
+
 def dflash_target_kv_cache_update(k_delta, v_delta, kv_cache, token_aligned_cos_sin,
                                   delta_positions, delta_token_to_sequence, page_table,
                                   batch_size: int, rope_style: int) -> None:
@@ -157,23 +254,27 @@ def dflash_target_kv_cache_update(k_delta, v_delta, kv_cache, token_aligned_cos_
     ts = (k_delta, v_delta, kv_cache, token_aligned_cos_sin, delta_positions,
           delta_token_to_sequence, page_table)
     dev = _device_of(*ts)
-    for t, dt in zip(ts, (torch.float16, torch.float16, torch.float16, torch.float32, torch.int32,
-                          torch.int32, torch.int32)):
-        if t.dtype != dt or not t.is_contiguous():
-            raise ValueError(f"expected contiguous {dt}, got {t.dtype}")
-    if k_delta.dim() != 3 or v_delta.shape != k_delta.shape or kv_cache.dim() != 5 \
-            or token_aligned_cos_sin.dim() != 2 or page_table.dim() != 3:
-        raise ValueError("shapes must be k/v_delta [N,Hkv,D], kv_cache [2,P,64,Hkv,D], "
-                         "token_aligned_cos_sin [N,R], page_table [B,2,M]")
-    N, Hkv, D = k_delta.shape
-    if tuple(kv_cache.shape[::2]) != (2, 64, D) or kv_cache.shape[3] != Hkv \
-            or token_aligned_cos_sin.shape[0] != N or delta_positions.numel() != N \
-            or delta_token_to_sequence.numel() != N or page_table.shape[1] != 2 \
-            or batch_size > page_table.shape[0]:
-        raise ValueError("inconsistent shapes")
+    N, Hkv, D = _paged_checks(*ts, batch_size, fp8=False, gather=False)
     _check(lib.rkv_dflash_target_kv_cache_update(
         *[t.data_ptr() for t in ts], N, int(batch_size), Hkv, D, token_aligned_cos_sin.shape[1],
         kv_cache.shape[1], page_table.shape[2], int(rope_style), _stream(dev)))
+
+
+def dflash_target_kv_cache_update_fp8(k_delta, v_delta, kv_cache, k_scale, v_scale,
+                                      token_aligned_cos_sin, delta_positions,
+                                      delta_token_to_sequence, page_table, batch_size: int,
+                                      rope_style: int) -> None:
+    """Call 4 into an E4M3 pool [2, numPages, 64, Hkv, D] with per-tensor scales."""
+    ts = (k_delta, v_delta, kv_cache, token_aligned_cos_sin, delta_positions,
+          delta_token_to_sequence, page_table)
+    dev = _device_of(*ts, k_scale, v_scale)
+    N, Hkv, D = _paged_checks(*ts, batch_size, fp8=True, gather=False)
+    _check(lib.rkv_dflash_target_kv_cache_update_fp8(
+        k_delta.data_ptr(), v_delta.data_ptr(), kv_cache.data_ptr(), _scale_ptr(k_scale),
+        _scale_ptr(v_scale), token_aligned_cos_sin.data_ptr(), delta_positions.data_ptr(),
+        delta_token_to_sequence.data_ptr(), page_table.data_ptr(), N, int(batch_size), Hkv, D,
+        token_aligned_cos_sin.shape[1], kv_cache.shape[1], page_table.shape[2], int(rope_style),
+        _stream(dev)))
 
 
 def dflash_target_kv_cache_update_gather_rope(k_delta, v_delta, kv_cache, rope_cos_sin,
@@ -186,30 +287,31 @@ def dflash_target_kv_cache_update_gather_rope(k_delta, v_delta, kv_cache, rope_c
     ts = (k_delta, v_delta, kv_cache, rope_cos_sin, delta_positions, delta_token_to_sequence,
           page_table)
     dev = _device_of(*ts, state_indices)
-    for t, dt in zip(ts, (torch.float16, torch.float16, torch.float16, torch.float32, torch.int32,
-                          torch.int32, torch.int32)):
-        if t.dtype != dt or not t.is_contiguous():
-            raise ValueError(f"expected contiguous {dt}, got {t.dtype}")
-    if state_indices is not None and (state_indices.dtype != torch.int32
-                                      or not state_indices.is_contiguous()
-                                      or state_indices.numel() < batch_size):
-        raise ValueError("state_indices must be a contiguous int32 tensor of batch_size entries")
-    if k_delta.dim() != 3 or v_delta.shape != k_delta.shape or kv_cache.dim() != 5 \
-            or rope_cos_sin.dim() != 3 or page_table.dim() != 3:
-        raise ValueError("shapes must be k/v_delta [N,Hkv,D], kv_cache [2,P,64,Hkv,D], "
-                         "rope_cos_sin [states,rows,R], page_table [B,2,M]")
-    N, Hkv, D = k_delta.shape
-    if tuple(kv_cache.shape[::2]) != (2, 64, D) or kv_cache.shape[3] != Hkv \
-            or delta_positions.numel() != N or delta_token_to_sequence.numel() != N \
-            or page_table.shape[1] != 2 or batch_size > page_table.shape[0]:
-        raise ValueError("inconsistent shapes")
+    N, Hkv, D = _paged_checks(*ts, batch_size, fp8=False, gather=True)
     states, rows, R = rope_cos_sin.shape
     _check(lib.rkv_dflash_target_kv_cache_update_gather_rope(
         k_delta.data_ptr(), v_delta.data_ptr(), kv_cache.data_ptr(), rope_cos_sin.data_ptr(),
-        states, rows, state_indices.data_ptr() if state_indices is not None else None,
-        delta_positions.data_ptr(), delta_token_to_sequence.data_ptr(), page_table.data_ptr(),
-        N, int(batch_size), Hkv, D, R, kv_cache.shape[1], page_table.shape[2], int(rope_style),
-        _stream(dev)))
+        states, rows, _state_ptr(state_indices, batch_size), delta_positions.data_ptr(),
+        delta_token_to_sequence.data_ptr(), page_table.data_ptr(), N, int(batch_size), Hkv, D, R,
+        kv_cache.shape[1], page_table.shape[2], int(rope_style), _stream(dev)))
+
+
+def dflash_target_kv_cache_update_gather_rope_fp8(k_delta, v_delta, kv_cache, k_scale, v_scale,
+                                                  rope_cos_sin, state_indices, delta_positions,
+                                                  delta_token_to_sequence, page_table,
+                                                  batch_size: int, rope_style: int) -> None:
+    """The fused-gather call 4 into an E4M3 pool with per-tensor scales."""
+    ts = (k_delta, v_delta, kv_cache, rope_cos_sin, delta_positions, delta_token_to_sequence,
+          page_table)
+    dev = _device_of(*ts, state_indices, k_scale, v_scale)
+    N, Hkv, D = _paged_checks(*ts, batch_size, fp8=True, gather=True)
+    states, rows, R = rope_cos_sin.shape
+    _check(lib.rkv_dflash_target_kv_cache_update_gather_rope_fp8(
+        k_delta.data_ptr(), v_delta.data_ptr(), kv_cache.data_ptr(), _scale_ptr(k_scale),
+        _scale_ptr(v_scale), rope_cos_sin.data_ptr(), states, rows,
+        _state_ptr(state_indices, batch_size), delta_positions.data_ptr(),
+        delta_token_to_sequence.data_ptr(), page_table.data_ptr(), N, int(batch_size), Hkv, D, R,
+        kv_cache.shape[1], page_table.shape[2], int(rope_style), _stream(dev)))
 
 
 def check_rope_capacity(cos_sin_seq_len: int, kv_capacity: int) -> None:

@@ -9,20 +9,34 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "librkv.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("rkv_abi.hip", "rkv_kernels.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("rkv_abi.hip", "rkv_kernels.hip",
+                                            "rkv_kernels_fp8.hip")]
+OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-command-line-argument"]
 
 
 def build(out: str = LIB_PATH, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, "-o", out + ".tmp", *SOURCES]
-    subprocess.run(cmd, check=True)
+    """Compile every source to an object (in parallel), then link."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    tag = os.path.basename(out).replace(".so", "")
+
+    def compile_one(src):
+        obj = os.path.join(OBJ_DIR, f"{tag}_{os.path.basename(src)}.o")
+        subprocess.run([HIPCC, *FLAGS, *extra, "-c", "-o", obj, src], check=True)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, "-o", out + ".tmp",
+                    *objs], check=True)
     os.replace(out + ".tmp", out)
     return out
 

@@ -31,7 +31,9 @@ void clear_error() { g_err[0] = '\0'; }
 constexpr long long kResidentWaves = 8192;
 constexpr long long kStreamingGroups = 65536;
 
-int elem_size(int32_t dtype) { return dtype == RKV_F16 ? 2 : 4; }
+int elem_size(int32_t dtype) {
+  return dtype == RKV_F8E4M3 ? 1 : dtype == RKV_F16 ? 2 : 4;
+}
 
 struct Span {
   const char* name;
@@ -127,17 +129,29 @@ rkv_status launched(hipError_t e) {
   return RKV_OK;
 }
 
-// Shared validation of calls 1-3.  `call` selects which descriptors exist.
+// The per-tensor fp8 scales: each null (scale 1) or one fp32 value.
+rkv_status check_scales(const float* k_scale, const float* v_scale, Span* spans) {
+  if (((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+    return fail(RKV_ERR_ALIGNMENT, "kScale / vScale must be 4-byte aligned");
+  spans[0] = Span{"kScale", (uintptr_t)k_scale, (uintptr_t)k_scale + (k_scale ? 4u : 0u)};
+  spans[1] = Span{"vScale", (uintptr_t)v_scale, (uintptr_t)v_scale + (v_scale ? 4u : 0u)};
+  return RKV_OK;
+}
+
+// Shared validation of calls 1-3.  `call` selects which descriptors exist;
+// `fp8` selects the E4M3 cache (with its scales) over the fp16 one.
 rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_lens,
                   const rkv_tensor* pos_ids, const rkv_tensor* qkv, rkv_tensor* cache,
-                  rkv_tensor* q_out, int32_t style, hipStream_t stream) {
+                  rkv_tensor* q_out, bool fp8, const float* k_scale, const float* v_scale,
+                  int32_t style, hipStream_t stream) {
   clear_error();
   rkv_status st;
-  Span s_cs, s_qkv, s_cache, s_qo = {}, s_end = {}, s_pos = {};
+  Span s_cs, s_qkv, s_cache, s_qo = {}, s_end = {}, s_pos = {}, s_sc[2] = {};
   if ((st = check_tensor(cos_sin, "cosSinCache", RKV_F32, 3, &s_cs))) return st;
   if ((st = check_tensor(qkv, "qkv", RKV_F16, 4, &s_qkv))) return st;
-  if ((st = check_tensor(cache, "kvCache", RKV_F16, 5, &s_cache))) return st;
+  if ((st = check_tensor(cache, "kvCache", fp8 ? RKV_F8E4M3 : RKV_F16, 5, &s_cache))) return st;
   if ((st = check_style(style))) return st;
+  if (fp8 && (st = check_scales(k_scale, v_scale, s_sc))) return st;
 
   const long long B = qkv->shape[0], S = qkv->shape[1], H = qkv->shape[2], D = qkv->shape[3];
   const long long Hkv = cache->shape[2], cap = cache->shape[3];
@@ -171,7 +185,7 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
     return fail(RKV_ERR_CAPACITY, "S=%lld exceeds capacity %lld or cos/sin length %lld", S, cap,
                 TL);
   {
-    Span outs[3], ins[4];
+    Span outs[3], ins[6];
     int no = 0, ni = 0;
     outs[no++] = s_cache;
     if (call == rkv::kCallPacked) {
@@ -183,6 +197,10 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
       if (call == rkv::kCallTree) ins[ni++] = s_pos;
     }
     ins[ni++] = s_cs;
+    if (fp8) {
+      ins[ni++] = s_sc[0];
+      ins[ni++] = s_sc[1];
+    }
     if ((st = check_no_alias(outs, no, ins, ni))) return st;
   }
   const long long tokens = B * S;
@@ -192,7 +210,10 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   rkv::ContigParams p{};
   p.cos_sin = (const float*)cos_sin->data;
   p.qkv = (uint16_t*)qkv->data;
-  p.cache = (uint16_t*)cache->data;
+  p.cache = fp8 ? nullptr : (uint16_t*)cache->data;
+  p.cache8 = fp8 ? (uint8_t*)cache->data : nullptr;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.q_out = q_out ? (uint16_t*)q_out->data : nullptr;
   p.end_lens = end_lens ? (const int32_t*)end_lens->data : nullptr;
   p.pos_ids = pos_ids ? (const int32_t*)pos_ids->data : nullptr;
@@ -212,13 +233,17 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.total_waves = (int32_t)(tokens * p.waves_per_token);
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_token);
   p.div_seq = rkv::make_fastdiv((uint32_t)S);
-  return launched(
-      rkv::launch_contig(p, call, (int)D, layout_of(style), exact_of(style), stream));
+  return launched(fp8 ? rkv::launch_contig_fp8(p, call, (int)D, layout_of(style),
+                                               exact_of(style), stream)
+                      : rkv::launch_contig(p, call, (int)D, layout_of(style), exact_of(style),
+                                           stream));
 }
 
 // Shared validation and launch of call 4, with the cos/sin rows given per
-// delta row (tokenAlignedCosSin) or gathered from a rope table.
-rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCache,
+// delta row (tokenAlignedCosSin) or gathered from a rope table, into an
+// fp16 pool or (fp8) an E4M3 pool with its scales.
+rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, bool fp8,
+                 const float* k_scale, const float* v_scale,
                  const float* tokenAlignedCosSin, const float* rope, int32_t ropeStates,
                  int32_t ropeRows, const int32_t* stateIndices, const int32_t* deltaPositions,
                  const int32_t* deltaTokenToSequence, const int32_t* pageTable,
@@ -232,6 +257,8 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCac
     return fail(RKV_ERR_SHAPE, "negative size argument");
   if ((st = check_style(ropeStyle))) return st;
   if ((st = check_dims(headDim, rotaryDim))) return st;
+  Span s_sc[2] = {};
+  if (fp8 && (st = check_scales(k_scale, v_scale, s_sc))) return st;
   const long long N = numDeltaTokens, Hkv = numKVHeads, D = headDim, R = rotaryDim;
   long long delta_elems, pool_elems, pt_elems, cs_elems;
   if (!mul_ok(N * Hkv, D, &delta_elems) ||
@@ -259,19 +286,23 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCac
   auto span = [](const char* n, const void* p, long long bytes) {
     return Span{n, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
   };
-  Span out = span("kvCache", kvCache, pool_elems * 2);
+  Span out = span("kvCache", kvCache, pool_elems * (fp8 ? 1 : 2));
   Span ins[] = {span("kDelta", kDelta, delta_elems * 2), span("vDelta", vDelta, delta_elems * 2),
                 span(cs_name, cs, cs_elems * 4), span("deltaPositions", deltaPositions, N * 4),
                 span("deltaTokenToSequence", deltaTokenToSequence, N * 4),
                 span("pageTable", pageTable, pt_elems * 4),
-                span("stateIndices", stateIndices, stateIndices ? batchSize * 4LL : 0)};
-  if ((st = check_no_alias(&out, 1, ins, 7))) return st;
+                span("stateIndices", stateIndices, stateIndices ? batchSize * 4LL : 0),
+                s_sc[0], s_sc[1]};
+  if ((st = check_no_alias(&out, 1, ins, 9))) return st;
   if (pool_elems == 0 || pt_elems == 0) return RKV_OK;   // nothing can be written
 
   rkv::PagedParams p{};
   p.k_delta = kDelta;
   p.v_delta = vDelta;
-  p.pool = kvCache;
+  p.pool = fp8 ? nullptr : (uint16_t*)kvCache;
+  p.pool8 = fp8 ? (uint8_t*)kvCache : nullptr;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.cos_sin = tokenAlignedCosSin;
   p.rope = rope;
   p.state_idx = stateIndices;
@@ -293,8 +324,10 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, uint16_t* kvCac
   p.waves_per_row = sp.waves_per_item;
   p.total_waves = (int32_t)(N * p.waves_per_row);
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
-  return launched(rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle),
-                                    gather, stream));
+  return launched(fp8 ? rkv::launch_paged_fp8(p, headDim, layout_of(ropeStyle),
+                                              exact_of(ropeStyle), gather, stream)
+                      : rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle),
+                                          gather, stream));
 }
 
 }  // namespace
@@ -304,8 +337,8 @@ extern "C" {
 rkv_status rkv_apply_rope_write_kv_packed_qkv(const rkv_tensor* cosSinCache, rkv_tensor* qkv,
                                               rkv_tensor* kvCache, int32_t ropeStyle,
                                               hipStream_t stream) {
-  return contig(rkv::kCallPacked, cosSinCache, nullptr, nullptr, qkv, kvCache, nullptr, ropeStyle,
-                stream);
+  return contig(rkv::kCallPacked, cosSinCache, nullptr, nullptr, qkv, kvCache, nullptr, false,
+                nullptr, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_apply_rope_write_kv_continuous(const rkv_tensor* cosSinCache,
@@ -314,7 +347,7 @@ rkv_status rkv_apply_rope_write_kv_continuous(const rkv_tensor* cosSinCache,
                                               rkv_tensor* qOut, int32_t ropeStyle,
                                               hipStream_t stream) {
   return contig(rkv::kCallContinuous, cosSinCache, kvCacheEndLens, nullptr, qkv, kvCache, qOut,
-                ropeStyle, stream);
+                false, nullptr, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_apply_rope_write_kv_tree(const rkv_tensor* cosSinCache,
@@ -323,7 +356,7 @@ rkv_status rkv_apply_rope_write_kv_tree(const rkv_tensor* cosSinCache,
                                         rkv_tensor* kvCache, rkv_tensor* qOut,
                                         int32_t ropeStyle, hipStream_t stream) {
   return contig(rkv::kCallTree, cosSinCache, kvCacheEndLens, tokenPosIds, qkv, kvCache, qOut,
-                ropeStyle, stream);
+                false, nullptr, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_dflash_target_kv_cache_update(
@@ -332,8 +365,8 @@ rkv_status rkv_dflash_target_kv_cache_update(
     const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
     int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
     int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream) {
-  return paged(kDelta, vDelta, kvCache, tokenAlignedCosSin, nullptr, 0, 0, nullptr,
-               deltaPositions, deltaTokenToSequence, pageTable, numDeltaTokens, batchSize,
+  return paged(kDelta, vDelta, kvCache, false, nullptr, nullptr, tokenAlignedCosSin, nullptr, 0,
+               0, nullptr, deltaPositions, deltaTokenToSequence, pageTable, numDeltaTokens, batchSize,
                numKVHeads, headDim, rotaryDim, numPages, maxPagesPerSeq, ropeStyle, false, stream);
 }
 
@@ -344,9 +377,62 @@ rkv_status rkv_dflash_target_kv_cache_update_gather_rope(
     int32_t numDeltaTokens, int32_t batchSize, int32_t numKVHeads, int32_t headDim,
     int32_t rotaryDim, int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle,
     hipStream_t stream) {
-  return paged(kDelta, vDelta, kvCache, nullptr, ropeCosSin, ropeStates, ropeRows, stateIndices,
-               deltaPositions, deltaTokenToSequence, pageTable, numDeltaTokens, batchSize,
+  return paged(kDelta, vDelta, kvCache, false, nullptr, nullptr, nullptr, ropeCosSin, ropeStates,
+               ropeRows, stateIndices, deltaPositions, deltaTokenToSequence, pageTable, numDeltaTokens, batchSize,
                numKVHeads, headDim, rotaryDim, numPages, maxPagesPerSeq, ropeStyle, true, stream);
+}
+
+rkv_status rkv_apply_rope_write_kv_packed_qkv_fp8(const rkv_tensor* cosSinCache, rkv_tensor* qkv,
+                                                  rkv_tensor* kvCache, const float* kScale,
+                                                  const float* vScale, int32_t ropeStyle,
+                                                  hipStream_t stream) {
+  return contig(rkv::kCallPacked, cosSinCache, nullptr, nullptr, qkv, kvCache, nullptr, true,
+                kScale, vScale, ropeStyle, stream);
+}
+
+rkv_status rkv_apply_rope_write_kv_continuous_fp8(const rkv_tensor* cosSinCache,
+                                                  const rkv_tensor* kvCacheEndLens,
+                                                  const rkv_tensor* qkv, rkv_tensor* kvCache,
+                                                  rkv_tensor* qOut, const float* kScale,
+                                                  const float* vScale, int32_t ropeStyle,
+                                                  hipStream_t stream) {
+  return contig(rkv::kCallContinuous, cosSinCache, kvCacheEndLens, nullptr, qkv, kvCache, qOut,
+                true, kScale, vScale, ropeStyle, stream);
+}
+
+rkv_status rkv_apply_rope_write_kv_tree_fp8(const rkv_tensor* cosSinCache,
+                                            const rkv_tensor* kvCacheEndLens,
+                                            const rkv_tensor* tokenPosIds, const rkv_tensor* qkv,
+                                            rkv_tensor* kvCache, rkv_tensor* qOut,
+                                            const float* kScale, const float* vScale,
+                                            int32_t ropeStyle, hipStream_t stream) {
+  return contig(rkv::kCallTree, cosSinCache, kvCacheEndLens, tokenPosIds, qkv, kvCache, qOut,
+                true, kScale, vScale, ropeStyle, stream);
+}
+
+rkv_status rkv_dflash_target_kv_cache_update_fp8(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint8_t* kvCache, const float* kScale,
+    const float* vScale, const float* tokenAlignedCosSin, const int32_t* deltaPositions,
+    const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
+    int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
+    int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream) {
+  return paged(kDelta, vDelta, kvCache, true, kScale, vScale, tokenAlignedCosSin, nullptr, 0, 0,
+               nullptr, deltaPositions, deltaTokenToSequence, pageTable, numDeltaTokens,
+               batchSize, numKVHeads, headDim, rotaryDim, numPages, maxPagesPerSeq, ropeStyle,
+               false, stream);
+}
+
+rkv_status rkv_dflash_target_kv_cache_update_gather_rope_fp8(
+    const uint16_t* kDelta, const uint16_t* vDelta, uint8_t* kvCache, const float* kScale,
+    const float* vScale, const float* ropeCosSin, int32_t ropeStates, int32_t ropeRows,
+    const int32_t* stateIndices, const int32_t* deltaPositions,
+    const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
+    int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
+    int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream) {
+  return paged(kDelta, vDelta, kvCache, true, kScale, vScale, nullptr, ropeCosSin, ropeStates,
+               ropeRows, stateIndices, deltaPositions, deltaTokenToSequence, pageTable,
+               numDeltaTokens, batchSize, numKVHeads, headDim, rotaryDim, numPages,
+               maxPagesPerSeq, ropeStyle, true, stream);
 }
 
 rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {

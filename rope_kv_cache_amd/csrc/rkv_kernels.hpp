@@ -1,0 +1,367 @@
+// HIP kernels for gfx950: fused RoPE + KV-cache write.
+//
+// Work decomposition.  The unit is a (token, head) row of D fp16 values.  A
+// wave instruction moves 1 KB: lane l holds 16-byte chunk l % (D/8) of row
+// l / (D/8) of a "row group" of 512/D consecutive head rows of one token
+// (one delta row for the paged call).  A wave owns G consecutive row groups
+// of one token: it issues their G loads first, then resolves the token's
+// cache slot and rotary position, fetches the cos/sin values its lanes
+// need, rotates Q and K rows (NeoX partners come from a neighbouring lane
+// by ds_bpermute; GPT-J pairs stay in the lane) and stores.  Waves are laid
+// out token-major, so the chip sweeps the packed tensor in address order
+// with one load per lane in flight per wave.  Measured on MI355X, this
+// fine-grained, address-ordered sweep moves the call's mixed read/write
+// traffic faster than per-lane batches of several loads.  There is no
+// contraction anywhere: the path is bandwidth-bound, so there is no MFMA.
+//
+// fp8 cache (kFp8).  Same decomposition; a lane keeps its chunk's rotation
+// unrounded, writes Q (and call 1's in-place K) as fp16 and the cache row
+// chunk as 8 E4M3 bytes of value * (1/scale), the per-tensor scales read
+// from device memory (sglang rope_cache.py, HAVE_K_SCALE / HAVE_V_SCALE).
+//
+// This header holds the kernel templates; rkv_kernels.hip instantiates the
+// fp16-cache kernels and rkv_kernels_fp8.hip the fp8-cache ones.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "rkv_launch.hpp"
+#include "rkv_rotate.hpp"
+
+namespace rkv {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void st16(uint16_t* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Streaming (non-temporal) 16-byte accesses for data touched exactly once.
+// On the large packed prefill they lift the kernel from ~250 us to ~228 us
+// (measured on MI355X); the reused cos/sin rows keep ordinary loads.
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
+__device__ __forceinline__ void st16_stream(uint16_t* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte stores of E4M3 cache chunks.
+__device__ __forceinline__ void st8(uint8_t* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+__device__ __forceinline__ void st8_stream(uint8_t* p, uint2 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2*>(p));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Renumber them so that XCD x works through one contiguous range of
+// work items: neighbouring tokens then share an L2.
+__device__ __forceinline__ int block_id_xcd_major() {
+  const int n = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int x = bid & 7, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + (bid >> 3);
+}
+
+__device__ __forceinline__ int wave_id_uniform() {
+  return __builtin_amdgcn_readfirstlane(block_id_xcd_major() * kWavesPerBlock +
+                                        (int)(threadIdx.x >> 6));
+}
+
+// ------------------------------------------------------------ calls 1-3 --
+//
+// Call 1 (packed prefill): position = slot = s; Q and K rotated in place in
+//   qkv, K also to cache plane 0, V copied to plane 1.
+// Call 2 (continuous): position = slot = endLens[b] - S + s; Q to qOut.
+// Call 3 (tree): slot = endLens[b] - S + s, position = tokenPosIds[b, s].
+// Calls 2 and 3 skip a token whose slot or position is out of range.
+// (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV".)
+template <int D, int kCall, int kStyle, bool kExact, int G, bool kFp8>
+__global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerGroup = kWave / kLanesPerRow;
+
+  const int wave = wave_id_uniform();
+  if (wave >= p.total_waves) return;
+  const int token = (int)fast_div((uint32_t)wave, p.div_waves);
+  const int part = wave - token * p.waves_per_token;
+  const int b = (int)fast_div((uint32_t)token, p.div_seq);
+  const int s = token - b * p.S;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane % kLanesPerRow;
+  const int row_in_group = lane / kLanesPerRow;
+  const ChunkRole role = chunk_role<kStyle>(c, p.R);
+
+  const int H = p.Hq + 2 * p.Hkv;
+  uint16_t* const tok_base = p.qkv + (size_t)token * H * D;
+
+  // Row loads first: they do not depend on the slot or the position.
+  uint4 x[G];
+  int row[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    row[g] = (part * G + g) * kRowsPerGroup + row_in_group;
+    x[g] = row[g] < H ? ld16_stream(tok_base + (size_t)row[g] * D + 8 * c) : make_uint4(0, 0, 0, 0);
+  }
+  float k_rcp = 1.f, v_rcp = 1.f;
+  if constexpr (kFp8) {
+    k_rcp = scale_reciprocal(p.k_scale);
+    v_rcp = scale_reciprocal(p.v_scale);
+  }
+
+  int slot = s, pos = s;
+  if constexpr (kCall != kCallPacked) {
+    const long long slot64 = (long long)p.end_lens[b] - p.S + s;
+    const long long pos64 = (kCall == kCallTree) ? (long long)p.pos_ids[token] : slot64;
+    if (slot64 < 0 || slot64 >= p.cap || pos64 < 0 || pos64 >= p.table_len) return;
+    slot = (int)slot64;
+    pos = (int)pos64;
+  }
+
+  float cs[8], sn[8];
+  if (role.rotary) {
+    const int tb = (p.table_batch == 1) ? 0 : b;
+    load_cos_sin<kStyle>(p.cos_sin + ((size_t)tb * p.table_len + pos) * p.R, role.freq0, p.R,
+                         cs, sn);
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int r = row[g];
+    const bool is_q = r < p.Hq;
+    const bool is_k = !is_q && r < p.Hq + p.Hkv;
+    const int h = is_k ? r - p.Hq : r - p.Hq - p.Hkv;
+    const size_t cache_row =
+        (((size_t)b * 2 + (is_k ? 0 : 1)) * p.Hkv + h) * (size_t)p.cap + slot;
+    uint16_t* const q_dst = (kCall == kCallPacked) ? tok_base + (size_t)r * D
+                                                   : p.q_out + ((size_t)token * p.Hq + r) * D;
+    if constexpr (kFp8) {
+      WideT<kExact> w[8];
+      const bool rot = rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn, w);
+      if (r >= H) continue;
+      if (is_q) {
+        st16_stream(q_dst + 8 * c, narrow_chunk<kExact>(w, x[g], rot));
+      } else {
+        st8_stream(p.cache8 + cache_row * D + 8 * c, to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp));
+        if (kCall == kCallPacked && is_k)
+          st16_stream(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], rot));
+      }
+    } else {
+      const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn);
+      if (r >= H) continue;
+      if (is_q) {
+        st16_stream(q_dst + 8 * c, y);
+      } else {
+        st16_stream(p.cache + cache_row * D + 8 * c, y);
+        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- call 4 --
+//
+// Paged delta update (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
+// launchDFlashTargetKVCacheUpdate).  Delta row i has 2*Hkv head rows: K
+// heads first, then V heads; a wave owns G row groups of one delta row.
+// The pool is addressed as [2*numPages][64][Hkv][D] by canonical page id,
+// in 64-bit.  The delta rows and the row's cos/sin values do not depend on
+// the index metadata, so they are requested first; the position/sequence
+// loads and then the page-table loads overlap with them, and only the
+// stores wait for the page ids.
+//
+// kGather fuses the page's cos/sin gather (launchDFlashGatherDeltaRope)
+// into the update: the row's cos/sin values come from the rope table row of
+// (state of its sequence, its position), read once the position and
+// sequence are known (in parallel with the page-table lookup); a row with
+// no such table row writes no K.
+template <int D, int kStyle, bool kExact, int G, bool kGather, bool kFp8>
+__global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerGroup = kWave / kLanesPerRow;
+  constexpr int kTpp = kTokensPerPage;
+
+  const int wave = wave_id_uniform();
+  if (wave >= p.total_waves) return;
+  const int i = (int)fast_div((uint32_t)wave, p.div_waves);
+  const int part = wave - i * p.waves_per_row;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane % kLanesPerRow;
+  const int row_in_group = lane / kLanesPerRow;
+  const ChunkRole role = chunk_role<kStyle>(c, p.R);
+  const int rows = 2 * p.Hkv;
+  const size_t delta_row = (size_t)i * p.Hkv;
+
+  uint4 x[G];
+  int row[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int r = (part * G + g) * kRowsPerGroup + row_in_group;
+    row[g] = r;
+    x[g] = make_uint4(0, 0, 0, 0);
+    if (r < p.Hkv)
+      x[g] = ld16(p.k_delta + (delta_row + r) * D + 8 * c);
+    else if (r < rows)
+      x[g] = ld16(p.v_delta + (delta_row + (r - p.Hkv)) * D + 8 * c);
+  }
+  float k_rcp = 1.f, v_rcp = 1.f;
+  if constexpr (kFp8) {
+    k_rcp = scale_reciprocal(p.k_scale);
+    v_rcp = scale_reciprocal(p.v_scale);
+  }
+  float cs[8], sn[8];
+  const bool has_k = part * G * kRowsPerGroup < p.Hkv;   // wave-uniform
+  if constexpr (!kGather) {
+    if (has_k && role.rotary)
+      load_cos_sin<kStyle>(p.cos_sin + (size_t)i * p.R, role.freq0, p.R, cs, sn);
+  }
+
+  const int pos = p.positions[i];
+  const int seq = p.seq[i];
+  if (pos < 0 || seq < 0 || seq >= p.batch || (long long)pos >= (long long)p.max_pages * kTpp)
+    return;
+  const int lp = pos / kTpp;
+  const int off = pos - lp * kTpp;
+  const int* pt = p.page_table + (size_t)seq * 2 * p.max_pages;
+  const int kid = pt[lp];
+  const int vid = pt[p.max_pages + lp];
+  bool k_ok = kid >= 0 && kid < p.num_pages;
+  const bool v_ok = vid >= p.num_pages && (long long)vid < 2LL * p.num_pages;
+  if constexpr (kGather) {
+    if (has_k) {
+      const int st = p.state_idx ? p.state_idx[seq] : (p.rope_states == 1 ? 0 : seq);
+      const bool rope_ok = st >= 0 && st < p.rope_states && pos < p.rope_rows;
+      k_ok = k_ok && rope_ok;
+      if (rope_ok && role.rotary)
+        load_cos_sin<kStyle>(p.rope + ((size_t)st * p.rope_rows + pos) * p.R, role.freq0, p.R, cs,
+                             sn);
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int r = row[g];
+    const bool is_k = r < p.Hkv;
+    const int h = is_k ? r : r - p.Hkv;
+    const size_t page = (size_t)(is_k ? kid : vid);
+    const size_t pool_row = (page * kTpp + off) * p.Hkv + h;
+    if constexpr (kFp8) {
+      WideT<kExact> w[8];
+      rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn, w);
+      if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
+      st8(p.pool8 + pool_row * D + 8 * c, to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp));
+    } else {
+      const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn);
+      if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
+      st16(p.pool + pool_row * D + 8 * c, y);
+    }
+  }
+}
+
+// ------------------------------------------------------------- launches --
+
+namespace detail {
+
+template <int V>
+using Int = std::integral_constant<int, V>;
+
+// Turn runtime launch choices into template arguments.
+template <typename F>
+hipError_t with_d(int D, F&& f) {
+  switch (D) {
+    case 64: return f(Int<64>{});
+    case 128: return f(Int<128>{});
+    case 256: return f(Int<256>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename F>
+hipError_t with_style_exact(int style, bool exact, F&& f) {
+  if (style == kNeox) return exact ? f(Int<kNeox>{}, Int<1>{}) : f(Int<kNeox>{}, Int<0>{});
+  return exact ? f(Int<kGptj>{}, Int<1>{}) : f(Int<kGptj>{}, Int<0>{});
+}
+
+template <typename F>
+hipError_t with_groups(int g, F&& f) {
+  switch (g) {
+    case 1: return f(Int<1>{});
+    case 2: return f(Int<2>{});
+    case 4: return f(Int<4>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+inline unsigned blocks_for(int32_t waves) {
+  return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+template <int kCall, bool kFp8>
+hipError_t launch_contig_call(const ContigParams& p, int D, int style, bool exact,
+                              hipStream_t stream) {
+  return with_d(D, [&](auto d) {
+    return with_style_exact(style, exact, [&](auto st, auto ex) {
+      return with_groups(p.groups_per_wave, [&](auto g) {
+        hipLaunchKernelGGL(
+            (contig_kernel<decltype(d)::value, kCall, decltype(st)::value, decltype(ex)::value != 0,
+                           decltype(g)::value, kFp8>),
+            dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p);
+        return hipGetLastError();
+      });
+    });
+  });
+}
+
+template <bool kFp8>
+hipError_t launch_contig_t(const ContigParams& p, int call, int D, int style, bool exact,
+                           hipStream_t stream) {
+  switch (call) {
+    case kCallPacked: return launch_contig_call<kCallPacked, kFp8>(p, D, style, exact, stream);
+    case kCallContinuous:
+      return launch_contig_call<kCallContinuous, kFp8>(p, D, style, exact, stream);
+    case kCallTree: return launch_contig_call<kCallTree, kFp8>(p, D, style, exact, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool kGather, bool kFp8>
+hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
+                          hipStream_t stream) {
+  return with_d(D, [&](auto d) {
+    return with_style_exact(style, exact, [&](auto st, auto ex) {
+      return with_groups(p.groups_per_wave, [&](auto g) {
+        hipLaunchKernelGGL((paged_kernel<decltype(d)::value, decltype(st)::value,
+                                         decltype(ex)::value != 0, decltype(g)::value, kGather,
+                                         kFp8>),
+                           dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p);
+        return hipGetLastError();
+      });
+    });
+  });
+}
+
+template <bool kFp8>
+hipError_t launch_paged_t(const PagedParams& p, int D, int style, bool exact, bool gather,
+                          hipStream_t stream) {
+  return gather ? launch_paged_g<true, kFp8>(p, D, style, exact, stream)
+                : launch_paged_g<false, kFp8>(p, D, style, exact, stream);
+}
+
+}  // namespace detail
+
+}  // namespace rkv

@@ -33,7 +33,10 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
 struct ContigParams {
   const float* cos_sin;     // [table_batch, table_len, R]
   uint16_t* qkv;            // [B, S, Hq + 2*Hkv, D]; written only by call 1
-  uint16_t* cache;          // [B, 2, Hkv, cap, D]
+  uint16_t* cache;          // [B, 2, Hkv, cap, D] fp16 cache, or
+  uint8_t* cache8;          // [B, 2, Hkv, cap, D] E4M3 cache (fp8 kernels)
+  const float* k_scale;     // fp8: per-tensor scales (one fp32 each) or null for 1
+  const float* v_scale;
   uint16_t* q_out;          // [B, S, Hq, D]; calls 2 and 3
   const int32_t* end_lens;  // [B]; calls 2 and 3
   const int32_t* pos_ids;   // [B, S]; call 3
@@ -49,7 +52,10 @@ struct ContigParams {
 struct PagedParams {
   const uint16_t* k_delta;  // [N, Hkv, D]
   const uint16_t* v_delta;  // [N, Hkv, D]
-  uint16_t* pool;           // [2 * num_pages, 64, Hkv, D]
+  uint16_t* pool;           // [2 * num_pages, 64, Hkv, D] fp16 pool, or
+  uint8_t* pool8;           // [2 * num_pages, 64, Hkv, D] E4M3 pool (fp8 kernels)
+  const float* k_scale;     // fp8: per-tensor scales (one fp32 each) or null for 1
+  const float* v_scale;
   const float* cos_sin;     // [N, R]
   const int32_t* positions; // [N]
   const int32_t* seq;       // [N]
@@ -68,5 +74,9 @@ hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool
                          hipStream_t stream);
 hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool gather,
                         hipStream_t stream);
+hipError_t launch_contig_fp8(const ContigParams& p, int call, int D, int style, bool exact,
+                             hipStream_t stream);
+hipError_t launch_paged_fp8(const PagedParams& p, int D, int style, bool exact, bool gather,
+                            hipStream_t stream);
 
 }  // namespace rkv

@@ -29,10 +29,19 @@
 // because binary32 carries more than two extra bits (Boldo & Melquiond,
 // "Emulation of FMA and correctly rounded sums: proved algorithms using
 // rounding to odd", IEEE Trans. Computers 2008).
+//
+// fp8 cache.  The E4M3 cache value is the unrounded rotation (binary32 in
+// the default mode, binary64 exact) times the reciprocal scale, clamped to
+// +-448 and converted by the hardware (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950,
+// round to nearest even).  In the exact mode the binary64 product is first
+// narrowed to binary32 with round-to-odd, which again makes the final
+// rounding a correct one.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace rkv {
 
@@ -46,41 +55,68 @@ __device__ __forceinline__ uint32_t f2h_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// binary64 -> binary16, round to nearest even, via round-to-odd binary32.
-__device__ __forceinline__ uint32_t narrow_exact(double y) {
+// binary64 -> binary32 rounded to odd: truncate toward zero, then set the
+// last bit when the result is inexact (NaN stays NaN).
+__device__ __forceinline__ float narrow_odd(double y) {
   float f = (float)y;                      // round to nearest even
   double back = (double)f;                 // exact
   uint32_t bits = __builtin_bit_cast(uint32_t, f);
-  if (back != y) {                         // inexact (NaN stays NaN)
+  if (back != y) {
     if (__builtin_fabs(back) > __builtin_fabs(y)) bits -= 1u;   // toward zero
     bits |= 1u;                            // odd
   }
-  return f2h_bits(__builtin_bit_cast(float, bits));
+  return __builtin_bit_cast(float, bits);
 }
 
-// x*c + sign*(p*s), with sign = -1 (first pair member) or +1 (second).
+// binary64 -> binary16, round to nearest even, via round-to-odd binary32.
+__device__ __forceinline__ uint32_t narrow_exact(double y) { return f2h_bits(narrow_odd(y)); }
+
+// The unrounded rotated value: binary64 in the exact mode, else binary32.
+template <bool kExact>
+using WideT = typename std::conditional<kExact, double, float>::type;
+
+template <bool kExact>
+__device__ __forceinline__ WideT<kExact> widen(uint32_t bits16) {
+  return (WideT<kExact>)h2f(bits16);       // exact either way
+}
+
+template <bool kExact>
+__device__ __forceinline__ uint32_t narrow16(WideT<kExact> y) {
+  if constexpr (kExact) return narrow_exact(y);
+  else return f2h_bits(y);
+}
+
+// x*c + sign*(p*s), with sign = -1 (first pair member) or +1 (second),
+// before the rounding to fp16.
 //
-// kExact: binary64 products and sum (exact up to the one binary64 rounding),
-// narrowed with round-to-odd -- bit-identical to a correctly rounded result.
+// kExact: binary64 products and sum (exact up to the one binary64 rounding).
 // Otherwise binary32, compensated: ps = RN(p*s) and its exact rounding error
 // e = fma(p, s, -ps) are formed first, then y = RN(RN(x*c - ps) - e) (the
 // first by one fma).  The two remaining roundings put y within about 2^-23
 // relative of the exact value, with no loss under cancellation, so the fp16
 // result is the correctly rounded one or its neighbour.
 template <bool kExact>
-__device__ __forceinline__ uint32_t rot1(uint32_t x_bits, uint32_t p_bits, float c, float s,
-                                         bool first) {
+__device__ __forceinline__ WideT<kExact> rot1_wide(uint32_t x_bits, uint32_t p_bits, float c,
+                                                   float s, bool first) {
   if constexpr (kExact) {
     double x = (double)h2f(x_bits), pv = (double)h2f(p_bits);
     double ps = pv * (double)s;               // exact
-    return narrow_exact(__builtin_fma(x, (double)c, first ? -ps : ps));
+    return __builtin_fma(x, (double)c, first ? -ps : ps);
   } else {
     const float x = h2f(x_bits), pv = h2f(p_bits);
     const float sv = first ? -s : s;
     const float ps = pv * sv;
     const float e = __builtin_fmaf(pv, sv, -ps);   // exact: pv*sv - ps
-    return f2h_bits(__builtin_fmaf(x, c, ps) + e);
+    return __builtin_fmaf(x, c, ps) + e;
   }
+}
+
+// The rotated element rounded to fp16: correctly rounded with kExact, else
+// the correctly rounded value or its neighbour.
+template <bool kExact>
+__device__ __forceinline__ uint32_t rot1(uint32_t x_bits, uint32_t p_bits, float c, float s,
+                                         bool first) {
+  return narrow16<kExact>(rot1_wide<kExact>(x_bits, p_bits, c, s, first));
 }
 
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
@@ -187,6 +223,85 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 x, int lane, const ChunkRole
     if (rotate_row && role.rotary) return rotate_gptj<kExact>(x, c, s);
     return x;
   }
+}
+
+// The same rotation as rotate_chunk, kept unrounded: w[k] is element k of
+// the chunk before the rounding to fp16 (its fp16 value widened when the
+// chunk is not rotated).  Returns whether the chunk was rotated.  Must be
+// called by every lane of the wave with the same control flow.
+template <int kStyle, bool kExact>
+__device__ __forceinline__ bool rotate_chunk_wide(uint4 x, int lane, const ChunkRole& role,
+                                                  bool rotate_row, const float (&c)[8],
+                                                  const float (&s)[8], WideT<kExact> (&w)[8]) {
+  const uint32_t xa[4] = {x.x, x.y, x.z, x.w};
+  const bool rot = rotate_row && role.rotary;
+  if constexpr (kStyle == kNeox) {
+    const uint4 p = lane_fetch(x, lane + role.partner);
+    const uint32_t pa[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (rot) {
+        w[2 * k] = rot1_wide<kExact>(lo16(xa[k]), lo16(pa[k]), c[2 * k], s[2 * k], role.first);
+        w[2 * k + 1] =
+            rot1_wide<kExact>(hi16(xa[k]), hi16(pa[k]), c[2 * k + 1], s[2 * k + 1], role.first);
+      } else {
+        w[2 * k] = widen<kExact>(lo16(xa[k]));
+        w[2 * k + 1] = widen<kExact>(hi16(xa[k]));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (rot) {
+        w[2 * k] = rot1_wide<kExact>(lo16(xa[k]), hi16(xa[k]), c[k], s[k], true);
+        w[2 * k + 1] = rot1_wide<kExact>(hi16(xa[k]), lo16(xa[k]), c[k], s[k], false);
+      } else {
+        w[2 * k] = widen<kExact>(lo16(xa[k]));
+        w[2 * k + 1] = widen<kExact>(hi16(xa[k]));
+      }
+    }
+  }
+  return rot;
+}
+
+// fp16 chunk from unrounded values; an unrotated chunk keeps its bits.
+template <bool kExact>
+__device__ __forceinline__ uint4 narrow_chunk(const WideT<kExact> (&w)[8], uint4 x, bool rot) {
+  if (!rot) return x;
+  return make_uint4(pack2(narrow16<kExact>(w[0]), narrow16<kExact>(w[1])),
+                    pack2(narrow16<kExact>(w[2]), narrow16<kExact>(w[3])),
+                    pack2(narrow16<kExact>(w[4]), narrow16<kExact>(w[5])),
+                    pack2(narrow16<kExact>(w[6]), narrow16<kExact>(w[7])));
+}
+
+// Finite magnitudes beyond the largest E4M3 value saturate to it; NaN
+// fails both comparisons and passes through.
+__device__ __forceinline__ float saturate_e4m3(float v) {
+  return v > 448.f ? 448.f : (v < -448.f ? -448.f : v);
+}
+
+// Eight E4M3 bytes (element k in byte k) of w[k] * rcp.
+template <bool kExact>
+__device__ __forceinline__ uint2 to_e4m3(const WideT<kExact> (&w)[8], float rcp) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if constexpr (kExact) v[k] = saturate_e4m3(narrow_odd(w[k] * (double)rcp));
+    else v[k] = saturate_e4m3(w[k] * rcp);
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// The fp32 reciprocal of a per-tensor scale read from device memory
+// (1 when there is none), correctly rounded: the binary64 quotient rounded
+// to binary32 (binary64 has more than 2*24+2 bits, so the double rounding
+// is innocuous).
+__device__ __forceinline__ float scale_reciprocal(const float* scale) {
+  return scale ? (float)(1.0 / (double)*scale) : 1.0f;
 }
 
 }  // namespace rkv

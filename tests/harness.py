@@ -13,7 +13,13 @@ Comparison rules:
 * ``compare`` also counts rotated elements whose bits differ and their
   largest distance in fp16 ulps, so that a test can require bit equality
   (the library's RKV_ROUND_EXACT mode) or at most one ulp (its default
-  binary32 arithmetic).
+  binary32 arithmetic);
+* an fp8 (E4M3) cache or pool starts filled with the E4M3 NaN code, which
+  finite inputs never produce, so the oracle's output marks the bytes it
+  wrote: everywhere else the device must leave that code; written bytes must
+  be within one code step of the oracle's (both NaN counts as equal), and
+  the count and largest step are reported so that a test can require bit
+  equality.
 """
 from __future__ import annotations
 
@@ -27,6 +33,8 @@ TOL_ABS = 1e-3
 
 
 def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    if a.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).to(device)
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
@@ -34,6 +42,18 @@ def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 def host16(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().view(np.uint16)
+
+
+def host8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint8)
+
+
+def _scale_tensor(v, device):
+    return None if v is None else torch.tensor([float(v)], dtype=torch.float32, device=device)
+
+
+def is_fp8(w) -> bool:
+    return bool(w.extra.get("fp8"))
 
 
 def upload(w, device="cuda") -> dict:
@@ -46,9 +66,11 @@ def upload(w, device="cuda") -> dict:
             t["rope"] = dev(w.extra["rope"], device)
             si = w.extra["state_indices"]
             t["state_indices"] = None if si is None else dev(si, device)
+        _upload_scales(w, t, device)
         return t
     t = {"cos_sin": dev(w.cos_sin, device), "qkv": dev(w.qkv, device),
          "cache": dev(w.cache, device)}
+    _upload_scales(w, t, device)
     if w.call != "packed":
         t["q_out"] = dev(w.q_out, device)
         t["end_lens"] = dev(w.end_lens, device)
@@ -57,11 +79,20 @@ def upload(w, device="cuda") -> dict:
     return t
 
 
+def _upload_scales(w, t, device):
+    if is_fp8(w):
+        t["k_scale"] = _scale_tensor(w.extra["fp8"]["k_scale"], device)
+        t["v_scale"] = _scale_tensor(w.extra["fp8"]["v_scale"], device)
+
+
 def launch(w, t: dict, exact: bool = False) -> None:
     """One call of the library on the uploaded workload; ``exact`` ORs
     ROUND_EXACT into the rope style (binary64, correctly rounded)."""
     import rope_kv_cache_amd as rkv
     style = w.style | (rkv.ROUND_EXACT if exact else 0)
+    if is_fp8(w):
+        _launch_fp8(rkv, w, t, style)
+        return
     if isinstance(w, W.Paged) and w.extra.get("gather"):
         rkv.dflash_target_kv_cache_update_gather_rope(t["k_delta"], t["v_delta"], t["pool"],
                                                       t["rope"], t["state_indices"],
@@ -81,11 +112,32 @@ def launch(w, t: dict, exact: bool = False) -> None:
                                      t["cache"], t["q_out"], style)
 
 
+def _launch_fp8(rkv, w, t, style):
+    ks, vs = t["k_scale"], t["v_scale"]
+    if isinstance(w, W.Paged) and w.extra.get("gather"):
+        rkv.dflash_target_kv_cache_update_gather_rope_fp8(
+            t["k_delta"], t["v_delta"], t["pool"], ks, vs, t["rope"], t["state_indices"],
+            t["positions"], t["seq"], t["page_table"], w.batch, style)
+    elif isinstance(w, W.Paged):
+        rkv.dflash_target_kv_cache_update_fp8(t["k_delta"], t["v_delta"], t["pool"], ks, vs,
+                                              t["cos_sin"], t["positions"], t["seq"],
+                                              t["page_table"], w.batch, style)
+    elif w.call == "packed":
+        rkv.apply_rope_write_kv_packed_qkv_fp8(t["cos_sin"], t["qkv"], t["cache"], ks, vs, style)
+    elif w.call == "continuous":
+        rkv.apply_rope_write_kv_continuous_fp8(t["cos_sin"], t["end_lens"], t["qkv"], t["cache"],
+                                               t["q_out"], ks, vs, style)
+    else:
+        rkv.apply_rope_write_kv_tree_fp8(t["cos_sin"], t["end_lens"], t["pos_ids"], t["qkv"],
+                                         t["cache"], t["q_out"], ks, vs, style)
+
+
 def download(w, t: dict) -> dict:
     torch.cuda.synchronize()
+    cache_host = host8 if is_fp8(w) else host16
     if isinstance(w, W.Paged):
-        return {"pool": host16(t["pool"])}
-    out = {"cache": host16(t["cache"])}
+        return {"pool": cache_host(t["pool"])}
+    out = {"cache": cache_host(t["cache"])}
     if w.call == "packed":
         out["qkv"] = host16(t["qkv"])
     else:
@@ -143,12 +195,54 @@ def _ulps(g: np.ndarray, r: np.ndarray) -> np.ndarray:
     return np.abs(ordered(g) - ordered(r))
 
 
+def _e4m3_steps(g: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """Distance in E4M3 code steps (+0 and -0 are 0 steps apart)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x80, -(x & 0x7F), x)
+    return np.abs(ordered(g) - ordered(r))
+
+
+def _is_nan8(x: np.ndarray) -> np.ndarray:
+    return (x & 0x7F) == 0x7F
+
+
+def _compare_fp8(w, key, g, ref, report):
+    diff = g != ref
+    if not diff.any():
+        report[key] = 0
+        return
+    unwritten = ref == W.SENTINEL8
+    bad = diff & unwritten
+    if bad.any():
+        idx = tuple(int(i) for i in np.argwhere(bad)[0])
+        raise AssertionError(f"{w.name}: {key}{list(idx)} written by the device only: "
+                             f"{g[idx]:#04x} ({int(bad.sum())} such bytes)")
+    where = np.nonzero(diff)
+    gd, rd = g[where], ref[where]
+    both_nan = _is_nan8(gd) & _is_nan8(rd)
+    steps = np.where(both_nan, 0, _e4m3_steps(gd, rd))
+    steps = np.where(_is_nan8(gd) ^ _is_nan8(rd), 999, steps)
+    if steps.max() > 1:
+        k = int(np.argmax(steps))
+        idx = tuple(int(a[k]) for a in where)
+        raise AssertionError(f"{w.name}: {key}{list(idx)} more than one E4M3 step from the "
+                             f"oracle: gpu {gd[k]:#04x} oracle {rd[k]:#04x} "
+                             f"({int((steps > 1).sum())} such bytes)")
+    report[key] = int((steps > 0).sum())
+    report[key + "_max_code_step"] = int(steps.max())
+    report[key + "_nan_sign_differs"] = int(both_nan.sum())
+
+
 def compare(w, got: dict, want: dict) -> dict:
     """Assert the parity rules; return {key: n_rotated_bit_differences}."""
     report = {}
     for key, ref in want.items():
         g = got[key]
         assert g.shape == ref.shape, (key, g.shape, ref.shape)
+        if ref.dtype == np.uint8:
+            _compare_fp8(w, key, g, ref, report)
+            continue
         diff = g != ref
         if not diff.any():
             report[key] = 0

@@ -357,3 +357,132 @@ def test_binding_rejects_host_tensors():
     cache = torch.zeros(1, 2, 2, 16, 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         rkv.apply_rope_write_kv_packed_qkv(cs, qkv, cache, rkv.ROPE_NEOX)
+
+
+# ------------------------------------------------------------ fp8 calls ---
+
+F8 = 3
+
+
+def call_packed_fp8(cs, qkv, cache, ks=None, vs=None, style=0):
+    b = ctypes.byref
+    return L.rkv_apply_rope_write_kv_packed_qkv_fp8(b(cs), b(qkv), b(cache), ks, vs, style, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("case,want", [
+    ("fp16_cache", rkv.ERR_DTYPE), ("f32_cache", rkv.ERR_DTYPE),
+    ("misaligned_k_scale", rkv.ERR_ALIGNMENT), ("misaligned_v_scale", rkv.ERR_ALIGNMENT),
+    ("cache_covers_k_scale", rkv.ERR_ALIAS), ("qkv_covers_v_scale", rkv.ERR_ALIAS),
+    ("null_scales_then_D_96", rkv.ERR_UNSUPPORTED), ("empty", rkv.OK),
+    ("misaligned_cache", rkv.ERR_ALIGNMENT),
+])
+def test_packed_fp8_validation(case, want):
+    cs, qkv, cache = packed_args()
+    cache.dtype = F8
+    ks, vs = 9 << 40, 10 << 40
+    if case == "fp16_cache":
+        cache.dtype = F16
+    elif case == "f32_cache":
+        cache.dtype = F32
+    elif case == "misaligned_k_scale":
+        ks += 2
+    elif case == "misaligned_v_scale":
+        vs += 1
+    elif case == "cache_covers_k_scale":
+        ks = cache.data + 1024
+    elif case == "qkv_covers_v_scale":
+        vs = qkv.data + 64      # qkv is an output of call 1
+    elif case == "null_scales_then_D_96":
+        cs, qkv, cache = packed_args(D=96, R=96)
+        cache.dtype = F8
+        ks = vs = None
+    elif case == "empty":
+        cs, qkv, cache = packed_args(B=0)
+        cache.dtype = F8
+    elif case == "misaligned_cache":
+        cache.data = cache.data + 8
+    st = call_packed_fp8(cs, qkv, cache, ks, vs)
+    assert st == want, (case, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+def test_fp16_calls_reject_an_fp8_cache():
+    cs, qkv, cache = packed_args()
+    cache.dtype = F8
+    assert call_packed(cs, qkv, cache) == rkv.ERR_DTYPE
+    a = cont_args()
+    a[3].dtype = F8
+    assert call_cont(a) == rkv.ERR_DTYPE
+
+
+@no_gpu
+def test_continuous_and_tree_fp8_validation():
+    a = cont_args()
+    a[3].dtype = F8
+    b = ctypes.byref
+    st = L.rkv_apply_rope_write_kv_continuous_fp8(*[b(x) for x in a], a[3].data + 16, None, 0,
+                                                  None)
+    assert st == rkv.ERR_ALIAS, L.rkv_last_error()
+    t = tree_args()
+    t[4].dtype = F16
+    st = L.rkv_apply_rope_write_kv_tree_fp8(*[b(x) for x in t], None, None, 0, None)
+    assert st == rkv.ERR_DTYPE
+    t[4].dtype = F8
+    t[2].shape[1] = 3
+    st = L.rkv_apply_rope_write_kv_tree_fp8(*[b(x) for x in t], None, None, 0, None)
+    assert st == rkv.ERR_SHAPE
+    c = cont_args(B=0)
+    c[3].dtype = F8
+    assert L.rkv_apply_rope_write_kv_continuous_fp8(*[b(x) for x in c], None, None, 0,
+                                                    None) == rkv.OK
+
+
+def paged_fp8_call(**kw):
+    base = dict(k=1 << 40, v=2 << 40, pool=3 << 40, ks=11 << 40, vs=12 << 40, cs=4 << 40,
+                pos=5 << 40, seq=6 << 40, pt=7 << 40, N=16, batch=2, Hkv=2, D=128, R=128, P=8,
+                M=4, style=0)
+    base.update(kw)
+    b = base
+    return L.rkv_dflash_target_kv_cache_update_fp8(
+        b["k"], b["v"], b["pool"], b["ks"], b["vs"], b["cs"], b["pos"], b["seq"], b["pt"],
+        b["N"], b["batch"], b["Hkv"], b["D"], b["R"], b["P"], b["M"], b["style"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(ks=(11 << 40) + 2), rkv.ERR_ALIGNMENT), (dict(ks=(3 << 40) + 4), rkv.ERR_ALIAS),
+    (dict(vs=(3 << 40) + 262140), rkv.ERR_ALIAS),       # last byte of the 262,144-byte pool
+    (dict(pool=0), rkv.ERR_NULL), (dict(R=24), rkv.ERR_UNSUPPORTED), (dict(N=0), rkv.OK),
+    (dict(P=0), rkv.OK), (dict(ks=0, vs=0, P=0), rkv.OK),
+])
+def test_paged_fp8_validation(kw, want):
+    st = paged_fp8_call(**kw)
+    assert st == want, (kw, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+def test_gather_fp8_validation():
+    def call(**kw):
+        base = dict(k=1 << 40, v=2 << 40, pool=3 << 40, ks=11 << 40, vs=12 << 40, rope=4 << 40,
+                    states=2, rows=512, si=8 << 40, pos=5 << 40, seq=6 << 40, pt=7 << 40, N=16,
+                    batch=2, Hkv=2, D=128, R=128, P=8, M=4, style=0)
+        base.update(kw)
+        b = base
+        return L.rkv_dflash_target_kv_cache_update_gather_rope_fp8(
+            b["k"], b["v"], b["pool"], b["ks"], b["vs"], b["rope"], b["states"], b["rows"],
+            b["si"], b["pos"], b["seq"], b["pt"], b["N"], b["batch"], b["Hkv"], b["D"], b["R"],
+            b["P"], b["M"], b["style"], None)
+    assert call(vs=(12 << 40) + 1) == rkv.ERR_ALIGNMENT
+    assert call(vs=(3 << 40) + 8) == rkv.ERR_ALIAS
+    assert call(rope=0) == rkv.ERR_NULL
+    assert call(P=0) == rkv.OK
+
+
+def test_fp8_binding_rejects_fp16_cache():
+    import torch
+    cs = torch.zeros(1, 16, 128)
+    qkv = torch.zeros(1, 8, 8, 128, dtype=torch.float16)
+    cache = torch.zeros(1, 2, 2, 16, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        rkv.apply_rope_write_kv_packed_qkv_fp8(cs, qkv, cache, None, None, rkv.ROPE_NEOX)

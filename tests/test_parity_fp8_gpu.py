@@ -1,0 +1,171 @@
+"""GPU parity of the fp8 (E4M3) cache calls against the CPU oracle.
+
+Each workload is the fp16 workload with its cache (pool) replaced by E4M3
+bytes filled with the E4M3 NaN code and per-tensor scales; the harness's
+fp8 rule applies: bytes the oracle leaves untouched stay untouched, written
+bytes are within one code step of the oracle in the default mode and equal
+to it, bit for bit, with RKV_ROUND_EXACT.  Q (and call 1's in-place K) are
+fp16 outputs under the fp16 rules.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from harness import compare, dev, download, expected, host8, launch, run_gpu, upload
+
+pytestmark = pytest.mark.gpu
+
+NEOX, GPTJ = W.NEOX, W.GPTJ
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def fp8(w, seed, k_scale=W.K_SCALE, v_scale=W.V_SCALE):
+    return W.with_fp8_cache(w, seed, k_scale, v_scale, fill="sentinel")
+
+
+def check(w, modes=("fast", "exact")):
+    _say(f"[parity-fp8] {w.name} tokens={w.tokens}")
+    want = expected(w)
+    for mode in modes:
+        got = run_gpu(w, exact=(mode == "exact"))
+        rep = compare(w, got, want)
+        _say(f"[parity-fp8] {w.name} {mode}: {rep}")
+        if mode == "exact":
+            diffs = {k: v for k, v in rep.items() if not k.endswith(("_max_ulp", "_max_code_step"))
+                     and v}
+            assert not diffs, f"exact mode not bit-identical: {rep}"
+        else:
+            assert all(v <= 1 for k, v in rep.items() if k.endswith(("_max_ulp",
+                                                                      "_max_code_step"))), rep
+
+
+@pytest.mark.parametrize("idx,style", [(1, None), (2, NEOX), (2, GPTJ), (3, None), (4, None),
+                                       (41, None), (5, None)],
+                         ids=["prefill_tiny", "continuous_neox", "continuous_gptj", "tree",
+                              "paged_delta", "paged_delta_gather", "prefill_large"])
+def test_config_fp8(idx, style):
+    w = W.config(idx, style) if idx == 2 else W.config(idx)
+    check(fp8(w, 7000 + idx))
+
+
+SMALL = []
+for D in (64, 128, 256):
+    for R in sorted({0, 16, D // 2, D}):
+        for style in (NEOX, GPTJ):
+            SMALL.append((D, R, style))
+
+
+@pytest.mark.parametrize("D,R,style", SMALL, ids=lambda v: str(v))
+@pytest.mark.parametrize("call", ["packed", "continuous", "tree"])
+def test_small_shapes_fp8(call, D, R, style):
+    seed = 7100 + D + R * 3 + style * 7 + {"packed": 0, "continuous": 1, "tree": 2}[call] * 1000
+    B, S, Hq, Hkv, cap = 3, 37, 5, 3, 96
+    if call == "packed":
+        w = W.packed(B, S, Hq, Hkv, D, R, cap, style, seed, table_batch=B, table_len=50,
+                     offsets=np.array([0, 7, 40]), name=f"packed_D{D}_R{R}_s{style}")
+    elif call == "continuous":
+        w = W.continuous(B, S, Hq, Hkv, D, R, cap, style, seed, 20, 110, table_len=90,
+                         name=f"continuous_D{D}_R{R}_s{style}")
+    else:
+        w = W.tree(B, S, Hq, Hkv, D, R, cap, style, seed, 20, 110,
+                   name=f"tree_D{D}_R{R}_s{style}")
+    check(fp8(w, seed))
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(None, None), (1.0, 0.5), (1e-3, 3e-3),
+                                             (64.0, 0.0123), (0.0123, None)],
+                         ids=["no_scale", "unit_half", "saturating", "subnormal", "k_only"])
+def test_scales(k_scale, v_scale):
+    """Scales that leave values unscaled, saturate most of them (|x|/1e-3
+    beyond 448) or push them into the E4M3 subnormals."""
+    w = W.continuous(4, 33, 6, 2, 128, 128, 64, GPTJ, 7300, 33, 64, name="continuous_scales")
+    check(fp8(w, 7301, k_scale, v_scale))
+    w = W.paged(200, 5, 3, 64, 48, 20, 4, NEOX, 7302, width=40, name="paged_scales")
+    check(fp8(w, 7303, k_scale, v_scale))
+
+
+def test_every_fp16_value_through_v():
+    """All 65,536 fp16 bit patterns (NaN and infinities included) as V rows
+    of the paged call, for three V scales."""
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    N, Hkv, D = 64, 16, 64
+    for vs in (None, 2.0, 0.0109):
+        w = W.Paged(NEOX, N, 1, Hkv, D, 0, 1, 1, np.zeros((N, Hkv, D), np.uint16),
+                    allbits.reshape(N, Hkv, D).copy(), W.sentinel_f16((2, 1, 64, Hkv, D)),
+                    np.zeros((N, 0), np.float32), np.arange(N, dtype=np.int32),
+                    np.zeros(N, np.int32), np.array([[[0], [1]]], np.int32),
+                    name=f"v_all_patterns_scale_{vs}")
+        w = fp8(w, 1, None, vs)
+        want = expected(w)["pool"]
+        for exact in (False, True):
+            got = run_gpu(w, exact=exact)["pool"]
+            nan_w = (want & 0x7F) == 0x7F
+            nan_g = (got & 0x7F) == 0x7F
+            assert np.array_equal(nan_w, nan_g), vs
+            _say(f"[parity-fp8] {w.name} exact={exact}: NaN codes whose sign bit differs: "
+                 f"{int(((want ^ got) & 0x80)[nan_w].astype(bool).sum())}")
+            same = ~nan_w
+            assert np.array_equal(got[same], want[same]), \
+                (vs, exact, int((got[same] != want[same]).sum()))
+
+
+def test_paged_skips_and_gather_fp8():
+    w = W.paged(512, 8, 2, 128, 128, 96, 8, NEOX, 7400, width=64, name="paged_skips_fp8")
+    r = np.random.default_rng(7401)
+    k = r.choice(w.N, 60, replace=False)
+    w.positions[k[:10]] = -1
+    w.seq[k[10:20]] = -3
+    w.seq[k[20:30]] = 6
+    w.positions[k[30:40]] = w.max_pages * 64
+    w.positions[k[40:50]] = 2 ** 31 - 1
+    w.batch = 6
+    check(fp8(w, 7402))
+    w = W.paged_gather(300, 7, 3, 128, 64, 64, 9, GPTJ, 7403, rope_states=3,
+                       rope_rows=9 * 64 - 50, width=43, pad_frac=0.2, bad_frac=0.2,
+                       name="paged_gather_fp8")
+    w.extra["state_indices"][1] = 3
+    w.extra["state_indices"][2] = -1
+    check(fp8(w, 7404))
+
+
+def test_empty_inputs_fp8():
+    for B, S in [(0, 4), (3, 0)]:
+        check(fp8(W.packed(B, S, 2, 1, 64, 64, 8, NEOX, 1, name=f"empty_{B}_{S}"), 1))
+    check(fp8(W.paged(0, 2, 2, 64, 64, 4, 2, NEOX, 5, name="empty_paged"), 1))
+
+
+def test_scale_is_read_when_the_kernel_runs():
+    """The scales are device values: updating them on the stream between two
+    launches changes the second launch's bytes."""
+    w = fp8(W.continuous(2, 16, 4, 2, 128, 128, 32, NEOX, 7500, 16, 32, name="scale_update"),
+            7501, 0.02, 0.02)
+    t = upload(w)
+    launch(w, t)
+    first = download(w, t)
+    t["k_scale"].fill_(0.04)
+    t["v_scale"].fill_(0.01)
+    t["cache"].fill_(W.SENTINEL8)
+    launch(w, t, exact=True)
+    second = download(w, t)
+    w.extra["fp8"] = {"k_scale": np.float32(0.04), "v_scale": np.float32(0.01)}
+    want = expected(w)
+    assert np.array_equal(second["cache"], want["cache"])
+    assert not np.array_equal(first["cache"], second["cache"])
+
+
+def test_fp8_cache_tensor_may_be_float8_typed():
+    """A torch.float8_e4m3fn cache is accepted and written like a uint8 one."""
+    import rope_kv_cache_amd as rkv
+    w = fp8(W.packed(2, 9, 3, 2, 64, 64, 12, GPTJ, 7600, name="packed_f8_dtype"), 7601)
+    want = expected(w)
+    t = upload(w)
+    cache = t["cache"].view(torch.float8_e4m3fn)
+    rkv.apply_rope_write_kv_packed_qkv_fp8(t["cos_sin"], t["qkv"], cache, t["k_scale"],
+                                           t["v_scale"], GPTJ | rkv.ROUND_EXACT)
+    torch.cuda.synchronize()
+    assert np.array_equal(host8(t["cache"]), want["cache"])
