@@ -117,11 +117,6 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
     row[g] = (part * G + g) * kRowsPerGroup + row_in_group;
     x[g] = row[g] < H ? ld16_stream(tok_base + (size_t)row[g] * D + 8 * c) : make_uint4(0, 0, 0, 0);
   }
-  float k_rcp = 1.f, v_rcp = 1.f;
-  if constexpr (kFp8) {
-    k_rcp = scale_reciprocal(p.k_scale);
-    v_rcp = scale_reciprocal(p.v_scale);
-  }
 
   int slot = s, pos = s;
   if constexpr (kCall != kCallPacked) {
@@ -138,6 +133,9 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
     load_cos_sin<kStyle>(p.cos_sin + ((size_t)tb * p.table_len + pos) * p.R, role.freq0, p.R,
                          cs, sn);
   }
+  // fp8: the scales, read while the row and cos/sin loads are in flight
+  float k_rcp = 1.f, v_rcp = 1.f;
+  if constexpr (kFp8) load_reciprocal_scales(p.k_scale, p.v_scale, k_rcp, v_rcp);
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -219,11 +217,6 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
     else if (r < rows)
       x[g] = ld16(p.v_delta + (delta_row + (r - p.Hkv)) * D + 8 * c);
   }
-  float k_rcp = 1.f, v_rcp = 1.f;
-  if constexpr (kFp8) {
-    k_rcp = scale_reciprocal(p.k_scale);
-    v_rcp = scale_reciprocal(p.v_scale);
-  }
   float cs[8], sn[8];
   const bool has_k = part * G * kRowsPerGroup < p.Hkv;   // wave-uniform
   if constexpr (!kGather) {
@@ -252,6 +245,9 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
                              sn);
     }
   }
+  // fp8: the scales, read while the row, cos/sin and page-table loads are in flight
+  float k_rcp = 1.f, v_rcp = 1.f;
+  if constexpr (kFp8) load_reciprocal_scales(p.k_scale, p.v_scale, k_rcp, v_rcp);
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {

@@ -296,12 +296,35 @@ __device__ __forceinline__ uint2 to_e4m3(const WideT<kExact> (&w)[8], float rcp)
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
-// The fp32 reciprocal of a per-tensor scale read from device memory
-// (1 when there is none), correctly rounded: the binary64 quotient rounded
-// to binary32 (binary64 has more than 2*24+2 bits, so the double rounding
-// is innocuous).
-__device__ __forceinline__ float scale_reciprocal(const float* scale) {
-  return scale ? (float)(1.0 / (double)*scale) : 1.0f;
+// A per-tensor scale that is not given is 1: the kernels then read this
+// constant instead, so the scale load needs no branch and both scale loads
+// are in flight together.
+static __device__ float kUnitScale = 1.0f;   // global memory, never written
+
+__device__ __forceinline__ float load_scale(const float* scale) {
+  return *(scale ? scale : &kUnitScale);
+}
+
+// The fp32 reciprocal of a scale, correctly rounded: the binary64 quotient
+// rounded to binary32 (binary64 has more than 2*24+2 bits, so the double
+// rounding is innocuous).
+__device__ __forceinline__ float reciprocal(float scale) {
+  return (float)(1.0 / (double)scale);
+}
+
+// Both reciprocal scales, computed where this is called.  The first empty
+// volatile asm takes both raw scales, so the two scalar loads are issued
+// together and share one wait; the second keeps the compiler from sinking
+// the loads and that wait into the branch that first uses the reciprocals.
+// Callers place this after their vector loads are issued, so the wait
+// overlaps those loads' latency.
+__device__ __forceinline__ void load_reciprocal_scales(const float* k_scale, const float* v_scale,
+                                                       float& k_rcp, float& v_rcp) {
+  const float ks = load_scale(k_scale), vs = load_scale(v_scale);
+  asm volatile("" ::"s"(ks), "s"(vs));
+  k_rcp = reciprocal(ks);
+  v_rcp = reciprocal(vs);
+  asm volatile("" : "+v"(k_rcp), "+v"(v_rcp));
 }
 
 }  // namespace rkv
