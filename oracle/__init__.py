@@ -92,6 +92,20 @@ def _declare(L):
     L.rkv_ref_paged_delta_gather.restype = ctypes.c_int
     L.rkv_ref_paged_delta_gather.argtypes = [P, P, P, P, i32, i32, P, P, P, P, i32, i32, i32,
                                              i32, i32, i32, i32, i32]
+    L.rkv_ref_mean_square.restype = ctypes.c_double
+    L.rkv_ref_mean_square.argtypes = [P, i32]
+    L.rkv_ref_rms_normalize.restype = None
+    L.rkv_ref_rms_normalize.argtypes = [P, P, P, i32, ctypes.c_double]
+    f64 = ctypes.c_double
+    L.rkv_ref_packed_qkv_qknorm.restype = ctypes.c_int
+    L.rkv_ref_packed_qkv_qknorm.argtypes = [P, i32, i32, i32, P, i32, i32, i32, i32, i32, P, P,
+                                            i32, P, P, f64, f32, f32, i32]
+    L.rkv_ref_continuous_qknorm.restype = ctypes.c_int
+    L.rkv_ref_continuous_qknorm.argtypes = [P, i32, i32, i32, P, P, i32, i32, i32, i32, i32, P, P,
+                                            i32, P, P, P, f64, f32, f32, i32]
+    L.rkv_ref_tree_qknorm.restype = ctypes.c_int
+    L.rkv_ref_tree_qknorm.argtypes = [P, i32, i32, i32, P, P, P, i32, i32, i32, i32, i32, P, P,
+                                      i32, P, P, P, f64, f32, f32, i32]
     L.rkv_ref_check_rope_capacity.restype = ctypes.c_int
     L.rkv_ref_check_rope_capacity.argtypes = [i32, i32]
     return L
@@ -137,6 +151,21 @@ def e4m3_to_double(b: int, L=None) -> float:
 
 def double_to_e4m3(x: float, L=None) -> int:
     return (L or lib()).rkv_ref_double_to_e4m3(float(x))
+
+
+def mean_square(x, L=None) -> float:
+    """Exact mean of squares of an fp16 row (uint16 [D]), rounded once."""
+    x = _c(x, np.uint16)
+    return (L or lib()).rkv_ref_mean_square(_p(x), x.size)
+
+
+def rms_normalize(x, weight, eps: float, L=None) -> np.ndarray:
+    """The RMS-normalised row in binary64 (before rotation and rounding)."""
+    x = _c(x, np.uint16)
+    wt = _c(weight, np.float32)
+    n = np.empty(x.size, dtype=np.float64)
+    (L or lib()).rkv_ref_rms_normalize(_p(x), _p(n), _p(wt), x.size, float(eps))
+    return n
 
 
 def _scale(s) -> float:
@@ -346,6 +375,81 @@ def paged_delta_gather_fp8(k_delta, v_delta, pool8, rope, state_indices, positio
     return pool8
 
 
+def _norm_args(q_weight, k_weight):
+    qw = None if q_weight is None else _c(q_weight, np.float32)
+    kw = None if k_weight is None else _c(k_weight, np.float32)
+    return qw, kw
+
+
+def _cache_pair(cache):
+    """(fp16 cache, E4M3 cache) from one array: uint16 -> fp16, uint8 -> E4M3."""
+    if cache.dtype == np.uint8:
+        return None, _c(cache, np.uint8).copy()
+    return _c(cache, np.uint16).copy(), None
+
+
+def packed_qkv_qknorm(cos_sin, qkv, cache, q_weight, k_weight, eps, style: int, k_scale=None,
+                      v_scale=None, L=None):
+    """Call 1 with Q/K RMS norm; ``cache`` uint16 (fp16) or uint8 (E4M3).
+    Returns ``(qkv_out, cache_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    qkv = _c(qkv, np.uint16).copy()
+    c16, c8 = _cache_pair(cache)
+    qw, kw = _norm_args(q_weight, k_weight)
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache.shape[2], cache.shape[3]
+    rc = (L or lib()).rkv_ref_packed_qkv_qknorm(
+        _p(cos_sin), tb, tlen, R, _p(qkv), B, S, H - 2 * Hkv, Hkv, D, _p(c16), _p(c8), cap,
+        _p(qw), _p(kw), float(eps), _scale(k_scale), _scale(v_scale), style)
+    if rc:
+        raise OracleError(rc, "packed_qkv_qknorm")
+    return qkv, (c16 if c8 is None else c8)
+
+
+def continuous_qknorm(cos_sin, end_lens, qkv, cache, q_out, q_weight, k_weight, eps, style: int,
+                      k_scale=None, v_scale=None, L=None):
+    """Call 2 with Q/K RMS norm.  Returns ``(cache_out, q_out_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    end_lens = _c(end_lens, np.int32)
+    qkv = _c(qkv, np.uint16)
+    c16, c8 = _cache_pair(cache)
+    q_out = _c(q_out, np.uint16).copy()
+    qw, kw = _norm_args(q_weight, k_weight)
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache.shape[2], cache.shape[3]
+    rc = (L or lib()).rkv_ref_continuous_qknorm(
+        _p(cos_sin), tb, tlen, R, _p(end_lens), _p(qkv), B, S, H - 2 * Hkv, Hkv, D, _p(c16),
+        _p(c8), cap, _p(q_out), _p(qw), _p(kw), float(eps), _scale(k_scale), _scale(v_scale),
+        style)
+    if rc:
+        raise OracleError(rc, "continuous_qknorm")
+    return (c16 if c8 is None else c8), q_out
+
+
+def tree_qknorm(cos_sin, end_lens, pos_ids, qkv, cache, q_out, q_weight, k_weight, eps,
+                style: int, k_scale=None, v_scale=None, L=None):
+    """Call 3 with Q/K RMS norm.  Returns ``(cache_out, q_out_out)``."""
+    cos_sin = _c(cos_sin, np.float32)
+    end_lens = _c(end_lens, np.int32)
+    pos_ids = _c(pos_ids, np.int32)
+    qkv = _c(qkv, np.uint16)
+    c16, c8 = _cache_pair(cache)
+    q_out = _c(q_out, np.uint16).copy()
+    qw, kw = _norm_args(q_weight, k_weight)
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache.shape[2], cache.shape[3]
+    rc = (L or lib()).rkv_ref_tree_qknorm(
+        _p(cos_sin), tb, tlen, R, _p(end_lens), _p(pos_ids), _p(qkv), B, S, H - 2 * Hkv, Hkv, D,
+        _p(c16), _p(c8), cap, _p(q_out), _p(qw), _p(kw), float(eps), _scale(k_scale),
+        _scale(v_scale), style)
+    if rc:
+        raise OracleError(rc, "tree_qknorm")
+    return (c16 if c8 is None else c8), q_out
+
+
 def check_rope_capacity(cos_sin_len: int, kv_capacity: int, L=None) -> int:
     return (L or lib()).rkv_ref_check_rope_capacity(cos_sin_len, kv_capacity)
 
@@ -356,7 +460,8 @@ def run(w, L=None):
     Returns a dict of expected outputs keyed like the HIP binding's results:
     ``qkv`` (call 1), ``q_out`` (calls 2, 3), ``cache`` (calls 1-3), ``pool`` (call 4).
     A workload whose ``extra["fp8"]`` holds ``k_scale`` / ``v_scale`` runs the
-    E4M3-cache variant of its call.
+    E4M3-cache variant of its call; one whose ``extra["qknorm"]`` holds
+    ``q_weight`` / ``k_weight`` / ``eps`` runs the Q/K-norm variant (calls 1-3).
     """
     fp8 = w.extra.get("fp8")
     if hasattr(w, "pool"):
@@ -374,6 +479,22 @@ def run(w, L=None):
                                                w.page_table, w.batch, w.style, L=L)}
         return {"pool": paged_delta(w.k_delta, w.v_delta, w.pool, w.cos_sin, w.positions, w.seq,
                                     w.page_table, w.batch, w.style, L=L)}
+    norm = w.extra.get("qknorm")
+    if norm:
+        ks, vs = (fp8["k_scale"], fp8["v_scale"]) if fp8 else (None, None)
+        qw, kw, eps = norm["q_weight"], norm["k_weight"], norm["eps"]
+        if w.call == "packed":
+            q, c = packed_qkv_qknorm(w.cos_sin, w.qkv, w.cache, qw, kw, eps, w.style, ks, vs, L=L)
+            return {"qkv": q, "cache": c}
+        if w.call == "continuous":
+            c, q = continuous_qknorm(w.cos_sin, w.end_lens, w.qkv, w.cache, w.q_out, qw, kw, eps,
+                                     w.style, ks, vs, L=L)
+            return {"cache": c, "q_out": q}
+        if w.call == "tree":
+            c, q = tree_qknorm(w.cos_sin, w.end_lens, w.pos_ids, w.qkv, w.cache, w.q_out, qw, kw,
+                               eps, w.style, ks, vs, L=L)
+            return {"cache": c, "q_out": q}
+        raise ValueError(w.call)
     if fp8:
         ks, vs = fp8["k_scale"], fp8["v_scale"]
         if w.call == "packed":

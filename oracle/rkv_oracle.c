@@ -26,6 +26,9 @@
  *       checkDFlashRopeCapacity.
  *  [P4] libmir-cuda execution.rs, Dynamic::new: the newest token of a cache
  *       of length L sits at position L - 1.
+ *  [P5] libmir-cuda execution.rs, DecodeAttentionBf16: the qkv_postprocess
+ *       step (query / key norm weights, rms_norm_epsilon) ahead of the KV
+ *       store.
  *
  * Readings where the pages are silent (same numbering as the design notes):
  *  R1  a table row holds cos in [0, R/2) and sin in [R/2, R).
@@ -54,8 +57,13 @@
  *      Q, and the in-place K of call 1, stay fp16 as in the fp16 variant.
  *  R25 fp8 cache: a missing scale means 1; the reciprocal is 1/scale rounded
  *      once to fp32; the product is formed in binary64 and rounded to E4M3.
- *  Parity unpinned against the original system for R6 and R7: no page fixes
- *  them; they are the plainest reading consistent with the rest.
+ *  R26 Q/K RMS norm ([P5] qkv_postprocess with query / key norm weights and
+ *      rms_norm_epsilon): each Q (K) head row x becomes
+ *      n_d = x_d * w_d / sqrt(mean_d(x_d^2) + eps) before the rotation, with
+ *      one fp32 weight vector [D] for all Q heads and one for all K heads;
+ *      dims >= R carry n_d; V is not normalised; one rounding at the end.
+ *  Parity unpinned against the original system for R6, R7 and R26: no page
+ *  fixes them; they are the plainest reading consistent with the rest.
  */
 #include "rkv_oracle.h"
 
@@ -118,11 +126,12 @@ uint16_t rkv_ref_double_to_half(double x) {
  * partner).  Frequency i drives pair i; cos_i = row[i], sin_i = row[R/2+i]
  * ([P2] _load_cos_sin with the half-width table; R1).  Written per pair:
  *   y_u = x_u*cos_i - x_v*sin_i,  y_v = x_v*cos_i + x_u*sin_i,
- * each in binary64 (exact products, one rounding).  Dims >= R keep x (R3). */
-void rkv_ref_rotate_row_wide(const uint16_t* x, double* w, const float* row, int32_t head_dim,
-                             int32_t rotary_dim, int32_t style) {
+ * in binary64: each product and the sum rounded once (for fp16 inputs the
+ * products are exact, so only the sum rounds).  Dims >= R keep x (R3). */
+static void rotate_values(const double* in, double* w, const float* row, int32_t head_dim,
+                          int32_t rotary_dim, int32_t style) {
   int half = rotary_dim / 2;
-  for (int d = 0; d < head_dim; ++d) w[d] = rkv_ref_half_to_double(x[d]);
+  for (int d = 0; d < head_dim; ++d) w[d] = in[d];
   for (int i = 0; i < half; ++i) {
     int u, v;
     if (style == RKV_REF_NEOX) {
@@ -134,24 +143,86 @@ void rkv_ref_rotate_row_wide(const uint16_t* x, double* w, const float* row, int
     }
     double c = (double)row[i];
     double s = (double)row[half + i];
-    double xu = rkv_ref_half_to_double(x[u]);
-    double xv = rkv_ref_half_to_double(x[v]);
-    double pu_c = xu * c, pv_s = xv * s;   /* exact products */
+    double xu = in[u];
+    double xv = in[v];
+    double pu_c = xu * c, pv_s = xv * s;
     double pv_c = xv * c, pu_s = xu * s;
     w[u] = pu_c - pv_s;
     w[v] = pv_c + pu_s;
   }
 }
 
-/* The fp16 result: each rotated element rounded once to binary16; dims >= R
- * copied bit for bit (NaN payloads included).  y may equal x. */
-void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* row,
-                        int32_t head_dim, int32_t rotary_dim, int32_t style) {
+static void widen_row(const uint16_t* x, double* w, int32_t D) {
+  for (int32_t d = 0; d < D; ++d) w[d] = rkv_ref_half_to_double(x[d]);
+}
+
+/* --------------------------------------------------------------- norm -- */
+
+/* The mean of the squares of a head row of fp16 values, computed exactly and
+ * rounded once to binary64.  Every fp16 value is an integer multiple of
+ * 2^-24 below 2^16, so its square is an integer multiple of 2^-48 below 2^32:
+ * the squares are summed exactly as 128-bit integer counts of 2^-48.  A row
+ * holding NaN gives NaN, one holding an infinity (and no NaN) infinity. */
+double rkv_ref_mean_square(const uint16_t* x, int32_t head_dim) {
+  unsigned __int128 acc = 0;
+  int has_nan = 0, has_inf = 0;
+  for (int32_t d = 0; d < head_dim; ++d) {
+    double a = fabs(rkv_ref_half_to_double(x[d]));
+    if (isnan(a)) has_nan = 1;
+    else if (isinf(a)) has_inf = 1;
+    else {
+      unsigned long long k = (unsigned long long)(a * 16777216.0);   /* a * 2^24, exact */
+      acc += (unsigned __int128)k * k;
+    }
+  }
+  if (has_nan) return NAN;
+  if (has_inf) return INFINITY;
+  return ldexp((double)acc, -48) / (double)head_dim;   /* one rounding; the rest is exact */
+}
+
+/* RMS normalisation of one head row (libmir-cuda execution.rs,
+ * DecodeAttentionBf16: the qkv_postprocess step takes query and key norm
+ * weights and the model's rms_norm_epsilon before it produces the rotated
+ * Q and K; R26): n_d = x_d * r * w_d with r = 1 / sqrt(mean(x^2) + eps), in
+ * binary64 (sqrt, the division and the two products rounded once each). */
+void rkv_ref_rms_normalize(const uint16_t* x, double* n, const float* weight, int32_t head_dim,
+                           double eps) {
+  double r = 1.0 / sqrt(rkv_ref_mean_square(x, head_dim) + eps);
+  for (int32_t d = 0; d < head_dim; ++d)
+    n[d] = (rkv_ref_half_to_double(x[d]) * r) * (double)weight[d];
+}
+
+/* The unrounded output of one Q or K head row: RMS-normalised first when a
+ * weight is given (R26), then rotated. */
+static void head_row_wide(const uint16_t* x, double* w, const float* row, int32_t D, int32_t R,
+                          int32_t style, const float* norm_w, double eps) {
+  double in[4096];
+  if (norm_w)
+    rkv_ref_rms_normalize(x, in, norm_w, D, eps);
+  else
+    widen_row(x, in, D);
+  rotate_values(in, w, row, D, R, style);
+}
+
+/* The same rounded once to binary16.  A row that is not normalised keeps
+ * the input bits of dims >= R (NaN payloads included).  y may equal x. */
+static void head_row16(const uint16_t* x, uint16_t* y, const float* row, int32_t D, int32_t R,
+                       int32_t style, const float* norm_w, double eps) {
   double w[4096];
   uint16_t tmp[4096];
-  rkv_ref_rotate_row_wide(x, w, row, head_dim, rotary_dim, style);
-  for (int d = 0; d < head_dim; ++d) tmp[d] = d < rotary_dim ? rkv_ref_double_to_half(w[d]) : x[d];
-  for (int d = 0; d < head_dim; ++d) y[d] = tmp[d];
+  head_row_wide(x, w, row, D, R, style, norm_w, eps);
+  for (int d = 0; d < D; ++d) tmp[d] = (d < R || norm_w) ? rkv_ref_double_to_half(w[d]) : x[d];
+  for (int d = 0; d < D; ++d) y[d] = tmp[d];
+}
+
+void rkv_ref_rotate_row_wide(const uint16_t* x, double* w, const float* row, int32_t head_dim,
+                             int32_t rotary_dim, int32_t style) {
+  head_row_wide(x, w, row, head_dim, rotary_dim, style, NULL, 0.0);
+}
+
+void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* row, int32_t head_dim,
+                        int32_t rotary_dim, int32_t style) {
+  head_row16(x, y, row, head_dim, rotary_dim, style, NULL, 0.0);
 }
 
 /* ----------------------------------------------------------------- fp8 -- */
@@ -209,10 +280,6 @@ static void store_row8(uint8_t* dst, const double* w, int32_t D, float rcp) {
   for (int32_t d = 0; d < D; ++d) dst[d] = rkv_ref_double_to_e4m3(w[d] * (double)rcp);
 }
 
-static void widen_row(const uint16_t* x, double* w, int32_t D) {
-  for (int32_t d = 0; d < D; ++d) w[d] = rkv_ref_half_to_double(x[d]);
-}
-
 /* ------------------------------------------------------------ helpers -- */
 
 static int bad_common(const float* cos_sin, int32_t table_batch, int32_t table_len,
@@ -248,23 +315,25 @@ static size_t cache_row(int32_t b, int32_t plane, int32_t h, int32_t slot, int32
 /* One token of calls 2 and 3: rotate its Q rows into q_out, its K rows into
  * cache plane 0 at `slot`, copy its V rows into plane 1 at `slot`.  With an
  * fp8 cache (cache8 != NULL) the cache rows are the rotated K / the V values
- * times the reciprocal scales, rounded once to E4M3 (R24). */
+ * times the reciprocal scales, rounded once to E4M3 (R24).  Q and K rows are
+ * RMS-normalised before the rotation when their weight is given (R26). */
 static void write_token(const float* row, const uint16_t* qkv, int32_t b, int32_t s,
                         int32_t slot, int32_t S, int32_t hq, int32_t hkv, int32_t D,
                         int32_t R, uint16_t* cache, uint8_t* cache8, float k_rcp, float v_rcp,
-                        int32_t cap, uint16_t* q_out, int32_t style) {
+                        int32_t cap, uint16_t* q_out, const float* q_w, const float* k_w,
+                        double eps, int32_t style) {
   int32_t H = hq + 2 * hkv;
   double w[4096];
   for (int32_t h = 0; h < hq; ++h)
-    rkv_ref_rotate_row(qkv + qkv_row(b, s, h, S, H, D),
-                       q_out + (((size_t)b * S + s) * hq + h) * (size_t)D, row, D, R, style);
+    head_row16(qkv + qkv_row(b, s, h, S, H, D), q_out + (((size_t)b * S + s) * hq + h) * (size_t)D,
+               row, D, R, style, q_w, eps);
   for (int32_t h = 0; h < hkv; ++h) {
     const uint16_t* k = qkv + qkv_row(b, s, hq + h, S, H, D);
     if (cache8) {
-      rkv_ref_rotate_row_wide(k, w, row, D, R, style);
+      head_row_wide(k, w, row, D, R, style, k_w, eps);
       store_row8(cache8 + cache_row(b, 0, h, slot, hkv, cap, D), w, D, k_rcp);
     } else {
-      rkv_ref_rotate_row(k, cache + cache_row(b, 0, h, slot, hkv, cap, D), row, D, R, style);
+      head_row16(k, cache + cache_row(b, 0, h, slot, hkv, cap, D), row, D, R, style, k_w, eps);
     }
   }
   for (int32_t h = 0; h < hkv; ++h) {
@@ -288,7 +357,7 @@ static int packed_core(const float* cos_sin, int32_t table_batch, int32_t table_
                        int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
                        int32_t hq, int32_t hkv, int32_t head_dim, uint16_t* cache,
                        uint8_t* cache8, float k_rcp, float v_rcp, int32_t capacity,
-                       int32_t style) {
+                       const float* q_w, const float* k_w, double eps, int32_t style) {
   if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
                  head_dim, cache ? (const void*)cache : (const void*)cache8, capacity, style))
     return RKV_REF_ERR_ARG;
@@ -301,15 +370,15 @@ static int packed_core(const float* cos_sin, int32_t table_batch, int32_t table_
       const float* row = table_row(cos_sin, table_batch, table_len, R, b, pos);
       for (int32_t h = 0; h < hq; ++h) {
         uint16_t* x = qkv + qkv_row(b, s, h, seq_len, H, D);
-        rkv_ref_rotate_row(x, x, row, D, R, style);
+        head_row16(x, x, row, D, R, style, q_w, eps);
       }
       for (int32_t h = 0; h < hkv; ++h) {
         uint16_t* x = qkv + qkv_row(b, s, hq + h, seq_len, H, D);
         if (cache8) {   /* the cache gets the unrounded rotation, scaled (R24) */
-          rkv_ref_rotate_row_wide(x, w, row, D, R, style);
+          head_row_wide(x, w, row, D, R, style, k_w, eps);
           store_row8(cache8 + cache_row(b, 0, h, pos, hkv, capacity, D), w, D, k_rcp);
         }
-        rkv_ref_rotate_row(x, x, row, D, R, style);
+        head_row16(x, x, row, D, R, style, k_w, eps);
         if (!cache8)
           memcpy(cache + cache_row(b, 0, h, pos, hkv, capacity, D), x,
                  (size_t)D * sizeof(uint16_t));
@@ -335,7 +404,7 @@ int rkv_ref_packed_qkv(const float* cos_sin, int32_t table_batch, int32_t table_
                        int32_t capacity, int32_t style) {
   if (!cache) return RKV_REF_ERR_ARG;
   return packed_core(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
-                     head_dim, cache, NULL, 1.0f, 1.0f, capacity, style);
+                     head_dim, cache, NULL, 1.0f, 1.0f, capacity, NULL, NULL, 0.0, style);
 }
 
 int rkv_ref_packed_qkv_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
@@ -345,7 +414,7 @@ int rkv_ref_packed_qkv_fp8(const float* cos_sin, int32_t table_batch, int32_t ta
   if (!cache8) return RKV_REF_ERR_ARG;
   return packed_core(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
                      head_dim, NULL, cache8, reciprocal_of(k_scale), reciprocal_of(v_scale),
-                     capacity, style);
+                     capacity, NULL, NULL, 0.0, style);
 }
 
 /* ------------------------------------------------------------- call 2 -- */
@@ -358,7 +427,8 @@ static int continuous_core(const float* cos_sin, int32_t table_batch, int32_t ta
                            int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
                            int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
                            int32_t head_dim, uint16_t* cache, uint8_t* cache8, float k_rcp,
-                           float v_rcp, int32_t capacity, uint16_t* q_out, int32_t style) {
+                           float v_rcp, int32_t capacity, uint16_t* q_out, const float* q_w,
+                           const float* k_w, double eps, int32_t style) {
   if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
                  head_dim, cache ? (const void*)cache : (const void*)cache8, capacity, style) ||
       !end_lens || !q_out)
@@ -370,7 +440,7 @@ static int continuous_core(const float* cos_sin, int32_t table_batch, int32_t ta
       if (slot < 0 || slot >= capacity || pos >= table_len) continue;
       const float* row = table_row(cos_sin, table_batch, table_len, rotary_dim, b, (int32_t)pos);
       write_token(row, qkv, b, s, (int32_t)slot, seq_len, hq, hkv, head_dim, rotary_dim, cache,
-                  cache8, k_rcp, v_rcp, capacity, q_out, style);
+                  cache8, k_rcp, v_rcp, capacity, q_out, q_w, k_w, eps, style);
     }
   }
   return RKV_REF_OK;
@@ -384,7 +454,7 @@ int rkv_ref_continuous(const float* cos_sin, int32_t table_batch, int32_t table_
   if (!cache) return RKV_REF_ERR_ARG;
   return continuous_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, qkv, batch,
                          seq_len, hq, hkv, head_dim, cache, NULL, 1.0f, 1.0f, capacity, q_out,
-                         style);
+                         NULL, NULL, 0.0, style);
 }
 
 int rkv_ref_continuous_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
@@ -395,7 +465,7 @@ int rkv_ref_continuous_fp8(const float* cos_sin, int32_t table_batch, int32_t ta
   if (!cache8) return RKV_REF_ERR_ARG;
   return continuous_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, qkv, batch,
                          seq_len, hq, hkv, head_dim, NULL, cache8, reciprocal_of(k_scale),
-                         reciprocal_of(v_scale), capacity, q_out, style);
+                         reciprocal_of(v_scale), capacity, q_out, NULL, NULL, 0.0, style);
 }
 
 /* ------------------------------------------------------------- call 3 -- */
@@ -408,7 +478,7 @@ static int tree_core(const float* cos_sin, int32_t table_batch, int32_t table_le
                      const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t hq,
                      int32_t hkv, int32_t head_dim, uint16_t* cache, uint8_t* cache8,
                      float k_rcp, float v_rcp, int32_t capacity, uint16_t* q_out,
-                     int32_t style) {
+                     const float* q_w, const float* k_w, double eps, int32_t style) {
   if (bad_common(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
                  head_dim, cache ? (const void*)cache : (const void*)cache8, capacity, style) ||
       !end_lens || !pos_ids || !q_out)
@@ -420,7 +490,7 @@ static int tree_core(const float* cos_sin, int32_t table_batch, int32_t table_le
       if (slot < 0 || slot >= capacity || pos < 0 || pos >= table_len) continue;
       const float* row = table_row(cos_sin, table_batch, table_len, rotary_dim, b, (int32_t)pos);
       write_token(row, qkv, b, s, (int32_t)slot, seq_len, hq, hkv, head_dim, rotary_dim, cache,
-                  cache8, k_rcp, v_rcp, capacity, q_out, style);
+                  cache8, k_rcp, v_rcp, capacity, q_out, q_w, k_w, eps, style);
     }
   }
   return RKV_REF_OK;
@@ -433,7 +503,8 @@ int rkv_ref_tree(const float* cos_sin, int32_t table_batch, int32_t table_len,
                  int32_t style) {
   if (!cache) return RKV_REF_ERR_ARG;
   return tree_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, pos_ids, qkv, batch,
-                   seq_len, hq, hkv, head_dim, cache, NULL, 1.0f, 1.0f, capacity, q_out, style);
+                   seq_len, hq, hkv, head_dim, cache, NULL, 1.0f, 1.0f, capacity, q_out, NULL,
+                   NULL, 0.0, style);
 }
 
 int rkv_ref_tree_fp8(const float* cos_sin, int32_t table_batch, int32_t table_len,
@@ -444,7 +515,56 @@ int rkv_ref_tree_fp8(const float* cos_sin, int32_t table_batch, int32_t table_le
   if (!cache8) return RKV_REF_ERR_ARG;
   return tree_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, pos_ids, qkv, batch,
                    seq_len, hq, hkv, head_dim, NULL, cache8, reciprocal_of(k_scale),
-                   reciprocal_of(v_scale), capacity, q_out, style);
+                   reciprocal_of(v_scale), capacity, q_out, NULL, NULL, 0.0, style);
+}
+
+/* ------------------------------------------ calls 1-3 with Q/K RMS norm -- */
+
+/* Calls 1-3 with Q and K heads RMS-normalised before the rotation (R26):
+ * q_w / k_w are the per-dimension weights [D] of the Q and K heads, either
+ * may be NULL (those heads are not normalised); eps must be finite and
+ * >= 0.  Exactly one of cache (fp16) and cache8 (E4M3, with the scales) is
+ * given. */
+static int norm_args_bad(const uint16_t* cache, const uint8_t* cache8, double eps) {
+  return (!cache == !cache8) || !isfinite(eps) || eps < 0.0;
+}
+
+int rkv_ref_packed_qkv_qknorm(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                              int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
+                              int32_t hq, int32_t hkv, int32_t head_dim, uint16_t* cache,
+                              uint8_t* cache8, int32_t capacity, const float* q_weight,
+                              const float* k_weight, double eps, float k_scale, float v_scale,
+                              int32_t style) {
+  if (norm_args_bad(cache, cache8, eps)) return RKV_REF_ERR_ARG;
+  return packed_core(cos_sin, table_batch, table_len, rotary_dim, qkv, batch, seq_len, hq, hkv,
+                     head_dim, cache, cache8, reciprocal_of(k_scale), reciprocal_of(v_scale),
+                     capacity, q_weight, k_weight, eps, style);
+}
+
+int rkv_ref_continuous_qknorm(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                              int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                              int32_t batch, int32_t seq_len, int32_t hq, int32_t hkv,
+                              int32_t head_dim, uint16_t* cache, uint8_t* cache8,
+                              int32_t capacity, uint16_t* q_out, const float* q_weight,
+                              const float* k_weight, double eps, float k_scale, float v_scale,
+                              int32_t style) {
+  if (norm_args_bad(cache, cache8, eps)) return RKV_REF_ERR_ARG;
+  return continuous_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, qkv, batch,
+                         seq_len, hq, hkv, head_dim, cache, cache8, reciprocal_of(k_scale),
+                         reciprocal_of(v_scale), capacity, q_out, q_weight, k_weight, eps, style);
+}
+
+int rkv_ref_tree_qknorm(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                        int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                        const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t hq,
+                        int32_t hkv, int32_t head_dim, uint16_t* cache, uint8_t* cache8,
+                        int32_t capacity, uint16_t* q_out, const float* q_weight,
+                        const float* k_weight, double eps, float k_scale, float v_scale,
+                        int32_t style) {
+  if (norm_args_bad(cache, cache8, eps)) return RKV_REF_ERR_ARG;
+  return tree_core(cos_sin, table_batch, table_len, rotary_dim, end_lens, pos_ids, qkv, batch,
+                   seq_len, hq, hkv, head_dim, cache, cache8, reciprocal_of(k_scale),
+                   reciprocal_of(v_scale), capacity, q_out, q_weight, k_weight, eps, style);
 }
 
 /* ------------------------------------------------------------- call 4 -- */

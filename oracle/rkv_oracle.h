@@ -43,6 +43,12 @@ uint8_t rkv_ref_double_to_e4m3(double x);
 void rkv_ref_rotate_row_wide(const uint16_t* x, double* w, const float* cos_sin_row,
                              int32_t head_dim, int32_t rotary_dim, int32_t style);
 
+/* Mean of the squares of an fp16 head row, computed exactly, rounded once. */
+double rkv_ref_mean_square(const uint16_t* x, int32_t head_dim);
+/* RMS normalisation: n_d = x_d * r * w_d, r = 1 / sqrt(mean_square + eps). */
+void rkv_ref_rms_normalize(const uint16_t* x, double* n, const float* weight, int32_t head_dim,
+                           double eps);
+
 /* Rotate one head row x[0:D] with one table row [cos(R/2) | sin(R/2)];
  * y may equal x.  Dims d >= R are copied bit for bit. */
 void rkv_ref_rotate_row(const uint16_t* x, uint16_t* y, const float* cos_sin_row,
@@ -129,6 +135,30 @@ int rkv_ref_paged_delta_gather_fp8(const uint16_t* k_delta, const uint16_t* v_de
                                    int32_t num_kv_heads, int32_t head_dim, int32_t rotary_dim,
                                    int32_t num_pages, int32_t max_pages_per_seq, float k_scale,
                                    float v_scale, int32_t style);
+
+/* Calls 1-3 with Q and K heads RMS-normalised before the rotation: q_weight /
+ * k_weight [D] (either may be NULL), eps finite and >= 0; exactly one of
+ * cache (fp16) and cache8 (E4M3 with k_scale / v_scale) is non-NULL. */
+int rkv_ref_packed_qkv_qknorm(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                              int32_t rotary_dim, uint16_t* qkv, int32_t batch, int32_t seq_len,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              uint16_t* cache, uint8_t* cache8, int32_t capacity,
+                              const float* q_weight, const float* k_weight, double eps,
+                              float k_scale, float v_scale, int32_t style);
+int rkv_ref_continuous_qknorm(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                              int32_t rotary_dim, const int32_t* end_lens, const uint16_t* qkv,
+                              int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, uint16_t* cache,
+                              uint8_t* cache8, int32_t capacity, uint16_t* q_out,
+                              const float* q_weight, const float* k_weight, double eps,
+                              float k_scale, float v_scale, int32_t style);
+int rkv_ref_tree_qknorm(const float* cos_sin, int32_t table_batch, int32_t table_len,
+                        int32_t rotary_dim, const int32_t* end_lens, const int32_t* pos_ids,
+                        const uint16_t* qkv, int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, uint16_t* cache, uint8_t* cache8,
+                        int32_t capacity, uint16_t* q_out, const float* q_weight,
+                        const float* k_weight, double eps, float k_scale, float v_scale,
+                        int32_t style);
 
 /* Capacity check: RKV_REF_ERR_CAPACITY iff cos_sin_len > kv_capacity. */
 int rkv_ref_check_rope_capacity(int32_t cos_sin_len, int32_t kv_capacity);

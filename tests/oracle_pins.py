@@ -968,4 +968,203 @@ def pin_fp8_cross_call_reductions(L):
                 assert np.array_equal(got, c2[b, plane]), (style, b, plane)
 
 
+# ------------------------------------------------------------ Q/K norm --
+
+def _exact_mean_square(bits) -> float:
+    """Python integers: each fp16 value times 2^24 is an integer; the mean
+    of squares as an exact fraction, converted once (float(Fraction) rounds
+    correctly)."""
+    v = val(bits)
+    if np.isnan(v).any():
+        return float("nan")
+    if np.isinf(v).any():
+        return float("inf")
+    total = sum(int(round(abs(float(a)) * 2 ** 24)) ** 2 for a in v)
+    return float(Fraction(total, 2 ** 48 * len(v)))
+
+
+def pin_mean_square_exact(L):
+    r = np.random.default_rng(100)
+    rows = [W.normal_f16(r, (128,)), W.normal_f16(r, (64,)), W.normal_f16(r, (256,)),
+            f16(r.uniform(-6e4, 6e4, 128)), f16(np.exp2(r.uniform(-24, 15, 128)))]
+    # one large square and many small ones: a running binary64 sum would drop
+    # the small ones, the exact mean keeps them
+    big = np.full(256, 2.0 ** -12)
+    big[0] = 2.0 ** 15
+    rows.append(f16(big))
+    rows.append(np.arange(1, 129, dtype=np.uint16))            # subnormals only
+    rows.append(np.zeros(64, dtype=np.uint16))
+    tiny = np.zeros(64, dtype=np.uint16)
+    tiny[9] = 0x8001                                           # one -2^-24: the sum is 2^-48
+    rows.append(tiny)
+    for x in rows:
+        assert oracle.mean_square(x, L) == _exact_mean_square(x), x[:4]
+    x = W.normal_f16(r, (64,))
+    x[5] = 0x7C00
+    assert np.isinf(oracle.mean_square(x, L))
+    x[6] = 0x7E00
+    assert np.isnan(oracle.mean_square(x, L))
+
+
+def pin_rms_norm_closed_forms(L):
+    r = np.random.default_rng(101)
+    wt = (0.5 + r.random(128)).astype(np.float32)
+    # a row of +-2^k: mean square 2^2k, so with eps = 0 the row becomes +-w exactly
+    for k in (-20, -3, 0, 7, 15):
+        signs = r.choice([-1.0, 1.0], 128)
+        n = oracle.rms_normalize(f16(signs * 2.0 ** k), wt, 0.0, L)
+        assert np.array_equal(n, signs * wt.astype(np.float64)), k
+    # scale invariance by powers of two (exact) with eps = 0
+    x = W.normal_f16(r, (128,))
+    for j in (-4, 3):
+        xs = f16(val(x) * 2.0 ** j)
+        assert np.array_equal(oracle.rms_normalize(xs, wt, 0.0, L),
+                              oracle.rms_normalize(x, wt, 0.0, L)), j
+    # with unit weights the normalised row has mean square 1
+    n = oracle.rms_normalize(x, np.ones(128, np.float32), 0.0, L)
+    assert abs(np.mean(n ** 2) - 1.0) < 1e-14
+    # a dominant epsilon: n = x * w / sqrt(ms + eps)
+    eps = 1e6
+    n = oracle.rms_normalize(x, wt, eps, L)
+    ms = np.mean(val(x) ** 2)
+    assert np.allclose(n, val(x) * wt / np.sqrt(ms + eps), rtol=1e-14, atol=0)
+    # a zero row with eps = 0 is 0/0
+    assert np.isnan(oracle.rms_normalize(np.zeros(64, np.uint16), wt[:64], 0.0, L)).all()
+
+
+def _numpy_qknorm_packed(cos_sin, qkv, Hq, Hkv, qw, kw, eps, style):
+    """Independent float64 model of call 1 with Q/K norm: r = sqrt(D)/||x||
+    (np.linalg.norm, pairwise summation), then the rotation as a complex
+    multiplication, rounded to fp16 by numpy."""
+    B, S, H, D = qkv.shape
+    R = cos_sin.shape[2]
+    half = R // 2
+    out = qkv.copy()
+    for b in range(B):
+        t = 0 if cos_sin.shape[0] == 1 else b
+        for s in range(S):
+            c = cos_sin[t, s, :half].astype(np.float64)
+            sn = cos_sin[t, s, half:].astype(np.float64)
+            for h in range(Hq + Hkv):
+                wt = qw if h < Hq else kw
+                x = val(qkv[b, s, h])
+                if wt is not None:
+                    nrm = np.linalg.norm(x) / np.sqrt(D)
+                    x = x * wt.astype(np.float64) / np.sqrt(nrm ** 2 + eps)
+                y = x.copy()
+                if style == NEOX:
+                    z = (x[:half] + 1j * x[half:R]) * (c + 1j * sn)
+                    y[:half], y[half:R] = z.real, z.imag
+                else:
+                    z = (x[0:R:2] + 1j * x[1:R:2]) * (c + 1j * sn)
+                    y[0:R:2], y[1:R:2] = z.real, z.imag
+                out[b, s, h] = f16(y) if (wt is not None or R == D) else \
+                    np.concatenate([f16(y[:R]), qkv[b, s, h, R:]])
+    return out
+
+
+def pin_qknorm_against_numpy(L):
+    """Whole call 1 with Q/K norm against the independent numpy model: at
+    most one fp16 ulp apart (the two binary64 evaluations differ in the last
+    bits) and equal almost everywhere."""
+    for style, D, R, eps in [(NEOX, 128, 128, 1e-6), (GPTJ, 64, 32, 1e-5), (NEOX, 128, 64, 0.0)]:
+        w = W.with_qk_norm(W.packed(2, 6, 3, 2, D, R, 8, style, 110 + D + R), 111 + R, eps=eps,
+                           scale=7.0)
+        n = w.extra["qknorm"]
+        got, _ = oracle.packed_qkv_qknorm(w.cos_sin, w.qkv, w.cache, n["q_weight"],
+                                          n["k_weight"], n["eps"], style, L=L)
+        want = _numpy_qknorm_packed(w.cos_sin, w.qkv, w.Hq, w.Hkv, n["q_weight"], n["k_weight"],
+                                    n["eps"], style)
+        g = got.view(np.float16).astype(np.float64)
+        e = want.view(np.float16).astype(np.float64)
+        diff = got != want
+        assert diff.mean() < 1e-3, (style, D, R, diff.mean())
+        ulp = np.spacing(np.abs(want.view(np.float16))).astype(np.float64)
+        assert np.all(np.abs(g - e) <= ulp), (style, D, R)
+
+
+def pin_qknorm_weight_roles(L):
+    """Q heads use the Q weight, K heads the K weight, V is untouched; a
+    side without a weight is the plain call's output for that side."""
+    r = np.random.default_rng(120)
+    B, S, Hq, Hkv, D, cap = 1, 4, 2, 2, 64, 4
+    qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+    qkv[:, :, Hq:Hq + Hkv] = qkv[:, :, :Hkv]                  # K heads copy Q heads 0..Hkv-1
+    table = np.zeros((1, cap, 0), dtype=np.float32)            # R = 0: no rotation
+    ones = np.ones(D, np.float32)
+    cache = W.sentinel_f16((B, 2, Hkv, cap, D))
+    q2, c2 = oracle.packed_qkv_qknorm(table, qkv, cache, ones, 2 * ones, 1e-6, NEOX, L=L)
+    assert np.array_equal(val(q2[:, :, Hq:Hq + Hkv]), 2 * val(q2[:, :, :Hkv]))
+    assert np.array_equal(q2[:, :, Hq + Hkv:], qkv[:, :, Hq + Hkv:])
+    assert np.array_equal(c2[0, 1].transpose(1, 0, 2), qkv[0, :, Hq + Hkv:])
+    assert np.array_equal(c2[0, 0].transpose(1, 0, 2), q2[0, :, Hq:Hq + Hkv])
+    # no Q weight: Q rows as the plain call leaves them (here unrotated, R = 0)
+    q3, _ = oracle.packed_qkv_qknorm(table, qkv, cache, None, ones, 1e-6, NEOX, L=L)
+    assert np.array_equal(q3[:, :, :Hq], qkv[:, :, :Hq])
+    assert np.array_equal(q3[:, :, Hq:Hq + Hkv], q2[:, :, :Hkv])
+
+
+def pin_qknorm_without_weights_is_the_plain_call(L):
+    for w in (W.packed(2, 5, 3, 2, 64, 48, 8, GPTJ, 130),
+              W.continuous(2, 5, 3, 2, 64, 64, 12, NEOX, 131, 3, 12),
+              W.tree(2, 5, 3, 2, 128, 64, 16, NEOX, 132, 5, 16)):
+        plain = oracle.run(w, L=L)
+        w.extra["qknorm"] = {"q_weight": None, "k_weight": None, "eps": 1e-6}
+        normed = oracle.run(w, L=L)
+        for k in plain:
+            assert np.array_equal(plain[k], normed[k]), (w.call, k)
+        W.with_fp8_cache(w, 133, fill="sentinel")
+        normed = oracle.run(w, L=L)
+        del w.extra["qknorm"]
+        plain = oracle.run(w, L=L)
+        for k in plain:
+            assert np.array_equal(plain[k], normed[k]), (w.call, k, "fp8")
+
+
+def pin_qknorm_fp8_and_calls_agree(L):
+    """With norm, the E4M3 cache is written where the fp16 cache is, its V
+    bytes are the nearest codes of V/v_scale, its K bytes decode to within
+    half a quantum (plus the fp16 rounding) of the fp16 K times 1/k_scale;
+    call 2 from an empty cache equals call 1, a linear tree equals call 2."""
+    for style in (NEOX, GPTJ):
+        w = W.with_qk_norm(W.packed(2, 6, 3, 2, 128, 96, 10, style, 140 + style), 141, scale=3.0)
+        n = w.extra["qknorm"]
+        q16, c16 = oracle.run(w, L=L)["qkv"], oracle.run(w, L=L)["cache"]
+        c8 = np.full(w.cache.shape, W.SENTINEL8, np.uint8)
+        q8, c8 = oracle.packed_qkv_qknorm(w.cos_sin, w.qkv, c8, n["q_weight"], n["k_weight"],
+                                          n["eps"], style, 1.0, 0.5, L=L)
+        assert np.array_equal(q8, q16)
+        written = c16 != W.SENTINEL
+        assert np.array_equal(c8 != W.SENTINEL8, written)
+        assert np.array_equal(c8[:, 1][written[:, 1]], _nearest_e4m3(val(c16[:, 1][written[:, 1]]) * 2))
+        k16 = val(c16[:, 0][written[:, 0]])
+        k8 = _e4m3_values()[c8[:, 0][written[:, 0]].astype(np.int64)]
+        a = np.abs(k16)
+        quantum = 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3)
+        assert np.all(np.abs(k8 - k16) <= quantum / 2 + 2.0 ** -11 * a + 2.0 ** -25)
+        # call 2 with end = S from an empty cache is call 1
+        end = np.full(w.B, w.S, np.int32)
+        c2, qo = oracle.continuous_qknorm(w.cos_sin, end, w.qkv, w.cache,
+                                          W.sentinel_f16((w.B, w.S, w.Hq, w.D)), n["q_weight"],
+                                          n["k_weight"], n["eps"], style, L=L)
+        assert np.array_equal(c2, c16) and np.array_equal(qo, q16[:, :, :w.Hq])
+        pos = np.tile(np.arange(w.S, dtype=np.int32), (w.B, 1))
+        c3, qo3 = oracle.tree_qknorm(w.cos_sin, end, pos, w.qkv, w.cache,
+                                     W.sentinel_f16((w.B, w.S, w.Hq, w.D)), n["q_weight"],
+                                     n["k_weight"], n["eps"], style, L=L)
+        assert np.array_equal(c3, c2) and np.array_equal(qo3, qo)
+
+
+def pin_qknorm_argument_errors(L):
+    w = W.packed(1, 2, 1, 1, 64, 64, 4, NEOX, 150)
+    ones = np.ones(64, np.float32)
+    for eps in (-1e-6, float("inf"), float("nan")):
+        try:
+            oracle.packed_qkv_qknorm(w.cos_sin, w.qkv, w.cache, ones, ones, eps, NEOX, L=L)
+        except oracle.OracleError as e:
+            assert e.code == oracle.ERR_ARG
+        else:
+            raise AssertionError(f"eps {eps} accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

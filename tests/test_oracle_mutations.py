@@ -27,10 +27,11 @@ MUTATIONS = {
     "subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     "passthrough_zeroed": ("? rkv_ref_double_to_half(w[d]) : x[d];",
                            "? rkv_ref_double_to_half(w[d]) : 0;"),
+    "passthrough_rounded_from_unnormalised": ("(d < R || norm_w) ?", "(d < R) ?"),
     "table_batch_ignored": ("int32_t tb = (table_batch == 1) ? 0 : b;", "int32_t tb = 0;"),
     "k_into_v_plane": ("memcpy(cache + cache_row(b, 0, h, pos, hkv, capacity, D), x,",
                        "memcpy(cache + cache_row(b, 1, h, pos, hkv, capacity, D), x,"),
-    "k_not_rotated_in_place": ("        rkv_ref_rotate_row(x, x, row, D, R, style);\n        if (!cache8)",
+    "k_not_rotated_in_place": ("        head_row16(x, x, row, D, R, style, k_w, eps);\n        if (!cache8)",
                                "        if (!cache8)"),
     "end_len_off_by_one": ("int64_t slot = (int64_t)end_lens[b] - seq_len + s;\n      int64_t pos = slot;",
                            "int64_t slot = (int64_t)end_lens[b] - seq_len + s + 1;\n      int64_t pos = slot;"),
@@ -68,6 +69,22 @@ MUTATIONS = {
                                   "store_row8(cache8 + cache_row(b, 0, h, pos, hkv, capacity, D), w, D, v_rcp);"),
     "fp8_paged_v_unscaled": ("          store_row8(pool8 + dst, w, D, v_rcp);",
                              "          store_row8(pool8 + dst, w, D, 1.0f);"),
+    # Q/K RMS norm
+    "norm_mean_over_d_minus_1": ("ldexp((double)acc, -48) / (double)head_dim;",
+                                 "ldexp((double)acc, -48) / (double)(head_dim - 1);"),
+    "norm_sum_drops_last_bit": ("ldexp((double)acc, -48) / (double)head_dim;",
+                                "ldexp((double)(acc >> 1 << 1), -48) / (double)head_dim;"),
+    "norm_eps_dropped": ("1.0 / sqrt(rkv_ref_mean_square(x, head_dim) + eps);",
+                         "1.0 / sqrt(rkv_ref_mean_square(x, head_dim));"),
+    "norm_eps_outside_sqrt": ("1.0 / sqrt(rkv_ref_mean_square(x, head_dim) + eps);",
+                              "1.0 / (sqrt(rkv_ref_mean_square(x, head_dim)) + eps);"),
+    "norm_weight_dropped": ("(rkv_ref_half_to_double(x[d]) * r) * (double)weight[d];",
+                            "(rkv_ref_half_to_double(x[d]) * r);"),
+    "norm_k_uses_q_weight": ("head_row16(x, x, row, D, R, style, k_w, eps);",
+                             "head_row16(x, x, row, D, R, style, q_w, eps);"),
+    "norm_q_uses_k_weight_calls_2_3": ("               row, D, R, style, q_w, eps);",
+                                       "               row, D, R, style, k_w, eps);"),
+    "norm_nan_row_ignored": ("if (has_nan) return NAN;", ""),
     "fp8_reciprocal_truncated": ("return (float)(1.0 / (double)scale);",
                                  "return (float)(1.0 / (double)scale) * (1.0f - 0x1p-23f);"),
 }

@@ -310,6 +310,22 @@ def paged_gather(N, batch, Hkv, D, R, num_pages, max_pages, style, seed, rope_st
     return w
 
 
+def with_qk_norm(w, seed: int, eps: float = 1e-6, q_weight=True, k_weight=True, scale=1.0):
+    """The same workload (calls 1-3) with Q/K RMS norm before the rotation:
+    fp32 per-dimension weights [D] drawn seeded around 1 (0.5 + U[0, 1)), or
+    None for a side that is not normalised; ``scale`` multiplies the packed
+    activations (held in fp16) so that the norm has something to undo."""
+    r = rng(seed)
+    qw = (0.5 + r.random(w.D)).astype(np.float32) if q_weight else None
+    kw = (0.5 + r.random(w.D)).astype(np.float32) if k_weight else None
+    if scale != 1.0:
+        x = w.qkv.view(np.float16).astype(np.float32) * np.float32(scale)
+        w.qkv = x.astype(np.float16).view(np.uint16)
+    w.extra["qknorm"] = {"q_weight": qw, "k_weight": kw, "eps": float(np.float32(eps))}
+    w.name = (w.name + "_qknorm") if w.name else "qknorm"
+    return w
+
+
 def _fill(r, shape, how):
     if how == "sentinel":
         return sentinel_f16(shape)
