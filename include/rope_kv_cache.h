@@ -251,6 +251,52 @@ rkv_status rkv_dflash_target_kv_cache_update_gather_rope_fp8(
     int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
     int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
 
+/* Q/K RMS norm fused before the rotation
+ * ---------------------------------------
+ * Calls 1-3 with each Q and K head row normalised before it is rotated: the
+ * postprocess step of the libmir-cuda decode path (execution.rs,
+ * DecodeAttentionBf16: qkv_postprocess with query / key norm weights and the
+ * model's rms_norm_epsilon, ahead of the KV store).  That page gives the
+ * parameters only; the reading taken here:
+ *   n_d = x_d * w_d / sqrt(mean_d(x_d^2) + epsilon)
+ * over the whole head row (all headDim dims), with one weight vector for all
+ * Q heads and one for all K heads; the rotation then acts on n, dims >=
+ * rotaryDim carry n_d, and the result is rounded once (to fp16, or scaled to
+ * E4M3).  V is not normalised.
+ *   qNormWeight, kNormWeight  [in] DEVICE fp32 [headDim] each, 16-byte
+ *                             aligned, or NULL: those heads are not
+ *                             normalised (both NULL is the plain call).
+ *   epsilon                   [in] finite, >= 0 (else RKV_ERR_SHAPE).
+ *   kvCache                   f16 (RKV_F16) or E4M3 (RKV_F8E4M3) descriptor:
+ *                             its dtype selects the cache format;
+ *   kScale, vScale            the E4M3 cache's scales as in the _fp8 calls;
+ *                             must be NULL with an fp16 cache (else
+ *                             RKV_ERR_DTYPE).
+ * Everything else is as in calls 1-3.  Arithmetic: by default binary32 (the
+ * sum of squares reduced across the row's lanes, v_rsq_f32, the compensated
+ * rotation), within the tolerance the tests state; with RKV_ROUND_EXACT the
+ * mean square is exact and rounded once, sqrt, the division, each product
+ * and each sum are binary64 operations in a fixed order, and the result is
+ * bit-identical to the reference evaluation. */
+rkv_status rkv_apply_rope_write_kv_packed_qkv_qknorm(const rkv_tensor* cosSinCache,
+                                                     rkv_tensor* qkv, rkv_tensor* kvCache,
+                                                     const float* qNormWeight,
+                                                     const float* kNormWeight, float epsilon,
+                                                     const float* kScale, const float* vScale,
+                                                     int32_t ropeStyle, hipStream_t stream);
+
+rkv_status rkv_apply_rope_write_kv_continuous_qknorm(
+    const rkv_tensor* cosSinCache, const rkv_tensor* kvCacheEndLens, const rkv_tensor* qkv,
+    rkv_tensor* kvCache, rkv_tensor* qOut, const float* qNormWeight, const float* kNormWeight,
+    float epsilon, const float* kScale, const float* vScale, int32_t ropeStyle,
+    hipStream_t stream);
+
+rkv_status rkv_apply_rope_write_kv_tree_qknorm(
+    const rkv_tensor* cosSinCache, const rkv_tensor* kvCacheEndLens,
+    const rkv_tensor* tokenPosIds, const rkv_tensor* qkv, rkv_tensor* kvCache, rkv_tensor* qOut,
+    const float* qNormWeight, const float* kNormWeight, float epsilon, const float* kScale,
+    const float* vScale, int32_t ropeStyle, hipStream_t stream);
+
 /* Host-only capacity check.
  * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
  *  checkDFlashRopeCapacity.)

@@ -24,6 +24,13 @@ Functions (same names as the C entry points, without the ``rkv_`` prefix):
   check_rope_capacity(cos_sin_seq_len, kv_capacity)
   tokens_per_page()
 
+  apply_rope_write_kv_packed_qkv_qknorm(cos_sin_cache, qkv, kv_cache, q_norm_weight, k_norm_weight,
+                                        epsilon, rope_style, k_scale=None, v_scale=None)
+  apply_rope_write_kv_continuous_qknorm(..., kv_cache, q_out, q_norm_weight, k_norm_weight, epsilon, ...)
+  apply_rope_write_kv_tree_qknorm(..., kv_cache, q_out, q_norm_weight, k_norm_weight, epsilon, ...)
+
+The ``_qknorm`` functions RMS-normalise Q and K heads before the rotation
+(weights: float32 [D] GPU tensors or None); their cache may be fp16 or E4M3.
 The ``_fp8`` functions take an E4M3 cache (a ``torch.uint8`` or
 ``torch.float8_e4m3fn`` tensor of the fp16 cache's shape) and per-tensor
 scales (one-element float32 device tensors, or None for a scale of 1).
@@ -83,6 +90,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rkv_dflash_target_kv_cache_update_fp8": [P] * 9 + [i32] * 8 + [P],
         "rkv_dflash_target_kv_cache_update_gather_rope_fp8": [P] * 6 + [i32, i32] + [P] * 4
         + [i32] * 8 + [P],
+        "rkv_apply_rope_write_kv_packed_qkv_qknorm": [T, T, T, P, P, ctypes.c_float, P, P, i32,
+                                                      P],
+        "rkv_apply_rope_write_kv_continuous_qknorm": [T, T, T, T, T, P, P, ctypes.c_float, P, P,
+                                                      i32, P],
+        "rkv_apply_rope_write_kv_tree_qknorm": [T, T, T, T, T, T, P, P, ctypes.c_float, P, P, i32,
+                                                P],
         "rkv_check_rope_capacity": [i32, i32],
         "rkv_tokens_per_page": [],
         "rkv_last_error": [],
@@ -209,6 +222,65 @@ def apply_rope_write_kv_tree_fp8(cos_sin_cache, kv_cache_end_lens, token_pos_ids
     _check(lib.rkv_apply_rope_write_kv_tree_fp8(
         *[ctypes.byref(x) for x in d], _scale_ptr(k_scale), _scale_ptr(v_scale),
         int(rope_style), _stream(dev)))
+
+
+def _weight_ptr(t, D):
+    """Device pointer of a float32 [D] norm weight, or None."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() != D or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"norm weights must be contiguous float32 GPU tensors of {D} elements")
+    return t.data_ptr()
+
+
+def _norm_scales(kv_cache, k_scale, v_scale):
+    if kv_cache.dtype == torch.float16:
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("k_scale / v_scale apply to an E4M3 cache only")
+        return None, None
+    _cache_ok(kv_cache, True)
+    return _scale_ptr(k_scale), _scale_ptr(v_scale)
+
+
+def apply_rope_write_kv_packed_qkv_qknorm(cos_sin_cache, qkv, kv_cache, q_norm_weight,
+                                          k_norm_weight, epsilon: float, rope_style: int,
+                                          k_scale=None, v_scale=None) -> None:
+    dev = _device_of(cos_sin_cache, qkv, kv_cache, q_norm_weight, k_norm_weight, k_scale,
+                     v_scale)
+    ks, vs = _norm_scales(kv_cache, k_scale, v_scale)
+    D = qkv.shape[-1]
+    a, b, c = _desc(cos_sin_cache), _desc(qkv), _desc(kv_cache)
+    _check(lib.rkv_apply_rope_write_kv_packed_qkv_qknorm(
+        ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), _weight_ptr(q_norm_weight, D),
+        _weight_ptr(k_norm_weight, D), float(epsilon), ks, vs, int(rope_style), _stream(dev)))
+
+
+def apply_rope_write_kv_continuous_qknorm(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out,
+                                          q_norm_weight, k_norm_weight, epsilon: float,
+                                          rope_style: int, k_scale=None, v_scale=None) -> None:
+    dev = _device_of(cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out, q_norm_weight,
+                     k_norm_weight, k_scale, v_scale)
+    ks, vs = _norm_scales(kv_cache, k_scale, v_scale)
+    D = qkv.shape[-1]
+    d = [_desc(t) for t in (cos_sin_cache, kv_cache_end_lens, qkv, kv_cache, q_out)]
+    _check(lib.rkv_apply_rope_write_kv_continuous_qknorm(
+        *[ctypes.byref(x) for x in d], _weight_ptr(q_norm_weight, D),
+        _weight_ptr(k_norm_weight, D), float(epsilon), ks, vs, int(rope_style), _stream(dev)))
+
+
+def apply_rope_write_kv_tree_qknorm(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv,
+                                    kv_cache, q_out, q_norm_weight, k_norm_weight,
+                                    epsilon: float, rope_style: int, k_scale=None,
+                                    v_scale=None) -> None:
+    dev = _device_of(cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache, q_out,
+                     q_norm_weight, k_norm_weight, k_scale, v_scale)
+    ks, vs = _norm_scales(kv_cache, k_scale, v_scale)
+    D = qkv.shape[-1]
+    d = [_desc(t) for t in (cos_sin_cache, kv_cache_end_lens, token_pos_ids, qkv, kv_cache,
+                            q_out)]
+    _check(lib.rkv_apply_rope_write_kv_tree_qknorm(
+        *[ctypes.byref(x) for x in d], _weight_ptr(q_norm_weight, D),
+        _weight_ptr(k_norm_weight, D), float(epsilon), ks, vs, int(rope_style), _stream(dev)))
 
 
 def _paged_checks(k_delta, v_delta, kv_cache, cos_sin, delta_positions, delta_token_to_sequence,

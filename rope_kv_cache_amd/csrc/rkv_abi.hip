@@ -138,20 +138,40 @@ rkv_status check_scales(const float* k_scale, const float* v_scale, Span* spans)
   return RKV_OK;
 }
 
+// Q/K norm arguments of calls 1-3 (a null `norm` means no normalisation).
+struct NormArgs {
+  const float* q_w = nullptr;
+  const float* k_w = nullptr;
+  float eps = 0.f;
+};
+
 // Shared validation of calls 1-3.  `call` selects which descriptors exist;
-// `fp8` selects the E4M3 cache (with its scales) over the fp16 one.
+// `fp8` selects the E4M3 cache (with its scales) over the fp16 one; `norm`
+// (non-null) selects the Q/K-norm kernels.
 rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_lens,
                   const rkv_tensor* pos_ids, const rkv_tensor* qkv, rkv_tensor* cache,
                   rkv_tensor* q_out, bool fp8, const float* k_scale, const float* v_scale,
-                  int32_t style, hipStream_t stream) {
+                  const NormArgs* norm, int32_t style, hipStream_t stream) {
   clear_error();
   rkv_status st;
-  Span s_cs, s_qkv, s_cache, s_qo = {}, s_end = {}, s_pos = {}, s_sc[2] = {};
+  Span s_cs, s_qkv, s_cache, s_qo = {}, s_end = {}, s_pos = {}, s_sc[2] = {}, s_nw[2] = {};
   if ((st = check_tensor(cos_sin, "cosSinCache", RKV_F32, 3, &s_cs))) return st;
   if ((st = check_tensor(qkv, "qkv", RKV_F16, 4, &s_qkv))) return st;
   if ((st = check_tensor(cache, "kvCache", fp8 ? RKV_F8E4M3 : RKV_F16, 5, &s_cache))) return st;
   if ((st = check_style(style))) return st;
   if (fp8 && (st = check_scales(k_scale, v_scale, s_sc))) return st;
+  if (norm) {
+    if (!(norm->eps >= 0.f) || norm->eps > 3.4e38f)
+      return fail(RKV_ERR_SHAPE, "epsilon %g must be finite and >= 0", (double)norm->eps);
+    const long long wbytes = qkv->shape[3] * 4;
+    const float* ws[2] = {norm->q_w, norm->k_w};
+    const char* names[2] = {"qNormWeight", "kNormWeight"};
+    for (int k = 0; k < 2; ++k) {
+      if ((uintptr_t)ws[k] & 15u)
+        return fail(RKV_ERR_ALIGNMENT, "%s is not 16-byte aligned", names[k]);
+      s_nw[k] = Span{names[k], (uintptr_t)ws[k], (uintptr_t)ws[k] + (ws[k] ? wbytes : 0)};
+    }
+  }
 
   const long long B = qkv->shape[0], S = qkv->shape[1], H = qkv->shape[2], D = qkv->shape[3];
   const long long Hkv = cache->shape[2], cap = cache->shape[3];
@@ -185,7 +205,7 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
     return fail(RKV_ERR_CAPACITY, "S=%lld exceeds capacity %lld or cos/sin length %lld", S, cap,
                 TL);
   {
-    Span outs[3], ins[6];
+    Span outs[3], ins[8];
     int no = 0, ni = 0;
     outs[no++] = s_cache;
     if (call == rkv::kCallPacked) {
@@ -201,6 +221,10 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
       ins[ni++] = s_sc[0];
       ins[ni++] = s_sc[1];
     }
+    if (norm) {
+      ins[ni++] = s_nw[0];
+      ins[ni++] = s_nw[1];
+    }
     if ((st = check_no_alias(outs, no, ins, ni))) return st;
   }
   const long long tokens = B * S;
@@ -214,6 +238,11 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.cache8 = fp8 ? (uint8_t*)cache->data : nullptr;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  if (norm) {
+    p.q_norm_w = norm->q_w;
+    p.k_norm_w = norm->k_w;
+    p.eps = norm->eps;
+  }
   p.q_out = q_out ? (uint16_t*)q_out->data : nullptr;
   p.end_lens = end_lens ? (const int32_t*)end_lens->data : nullptr;
   p.pos_ids = pos_ids ? (const int32_t*)pos_ids->data : nullptr;
@@ -233,10 +262,13 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.total_waves = (int32_t)(tokens * p.waves_per_token);
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_token);
   p.div_seq = rkv::make_fastdiv((uint32_t)S);
-  return launched(fp8 ? rkv::launch_contig_fp8(p, call, (int)D, layout_of(style),
-                                               exact_of(style), stream)
-                      : rkv::launch_contig(p, call, (int)D, layout_of(style), exact_of(style),
-                                           stream));
+  const int lay = layout_of(style);
+  const bool ex = exact_of(style);
+  if (norm)
+    return launched(fp8 ? rkv::launch_contig_norm_fp8(p, call, (int)D, lay, ex, stream)
+                        : rkv::launch_contig_norm(p, call, (int)D, lay, ex, stream));
+  return launched(fp8 ? rkv::launch_contig_fp8(p, call, (int)D, lay, ex, stream)
+                      : rkv::launch_contig(p, call, (int)D, lay, ex, stream));
 }
 
 // Shared validation and launch of call 4, with the cos/sin rows given per
@@ -338,7 +370,7 @@ rkv_status rkv_apply_rope_write_kv_packed_qkv(const rkv_tensor* cosSinCache, rkv
                                               rkv_tensor* kvCache, int32_t ropeStyle,
                                               hipStream_t stream) {
   return contig(rkv::kCallPacked, cosSinCache, nullptr, nullptr, qkv, kvCache, nullptr, false,
-                nullptr, nullptr, ropeStyle, stream);
+                nullptr, nullptr, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_apply_rope_write_kv_continuous(const rkv_tensor* cosSinCache,
@@ -347,7 +379,7 @@ rkv_status rkv_apply_rope_write_kv_continuous(const rkv_tensor* cosSinCache,
                                               rkv_tensor* qOut, int32_t ropeStyle,
                                               hipStream_t stream) {
   return contig(rkv::kCallContinuous, cosSinCache, kvCacheEndLens, nullptr, qkv, kvCache, qOut,
-                false, nullptr, nullptr, ropeStyle, stream);
+                false, nullptr, nullptr, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_apply_rope_write_kv_tree(const rkv_tensor* cosSinCache,
@@ -356,7 +388,7 @@ rkv_status rkv_apply_rope_write_kv_tree(const rkv_tensor* cosSinCache,
                                         rkv_tensor* kvCache, rkv_tensor* qOut,
                                         int32_t ropeStyle, hipStream_t stream) {
   return contig(rkv::kCallTree, cosSinCache, kvCacheEndLens, tokenPosIds, qkv, kvCache, qOut,
-                false, nullptr, nullptr, ropeStyle, stream);
+                false, nullptr, nullptr, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_dflash_target_kv_cache_update(
@@ -387,7 +419,7 @@ rkv_status rkv_apply_rope_write_kv_packed_qkv_fp8(const rkv_tensor* cosSinCache,
                                                   const float* vScale, int32_t ropeStyle,
                                                   hipStream_t stream) {
   return contig(rkv::kCallPacked, cosSinCache, nullptr, nullptr, qkv, kvCache, nullptr, true,
-                kScale, vScale, ropeStyle, stream);
+                kScale, vScale, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_apply_rope_write_kv_continuous_fp8(const rkv_tensor* cosSinCache,
@@ -397,7 +429,7 @@ rkv_status rkv_apply_rope_write_kv_continuous_fp8(const rkv_tensor* cosSinCache,
                                                   const float* vScale, int32_t ropeStyle,
                                                   hipStream_t stream) {
   return contig(rkv::kCallContinuous, cosSinCache, kvCacheEndLens, nullptr, qkv, kvCache, qOut,
-                true, kScale, vScale, ropeStyle, stream);
+                true, kScale, vScale, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_apply_rope_write_kv_tree_fp8(const rkv_tensor* cosSinCache,
@@ -407,7 +439,7 @@ rkv_status rkv_apply_rope_write_kv_tree_fp8(const rkv_tensor* cosSinCache,
                                             const float* kScale, const float* vScale,
                                             int32_t ropeStyle, hipStream_t stream) {
   return contig(rkv::kCallTree, cosSinCache, kvCacheEndLens, tokenPosIds, qkv, kvCache, qOut,
-                true, kScale, vScale, ropeStyle, stream);
+                true, kScale, vScale, nullptr, ropeStyle, stream);
 }
 
 rkv_status rkv_dflash_target_kv_cache_update_fp8(
@@ -433,6 +465,62 @@ rkv_status rkv_dflash_target_kv_cache_update_gather_rope_fp8(
                ropeRows, stateIndices, deltaPositions, deltaTokenToSequence, pageTable,
                numDeltaTokens, batchSize, numKVHeads, headDim, rotaryDim, numPages,
                maxPagesPerSeq, ropeStyle, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The fp8 flag of a Q/K-norm call follows the cache descriptor's dtype;
+// scales come with an E4M3 cache only.
+rkv_status norm_call(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_lens,
+                     const rkv_tensor* pos_ids, const rkv_tensor* qkv, rkv_tensor* cache,
+                     rkv_tensor* q_out, const float* qNormWeight, const float* kNormWeight,
+                     float epsilon, const float* kScale, const float* vScale, int32_t style,
+                     hipStream_t stream) {
+  clear_error();
+  if (!cache) return fail(RKV_ERR_NULL, "kvCache: null descriptor");
+  const bool fp8 = cache->dtype == RKV_F8E4M3;
+  if (!fp8 && (kScale || vScale))
+    return fail(RKV_ERR_DTYPE, "kScale / vScale apply to an E4M3 cache only");
+  NormArgs n;
+  n.q_w = qNormWeight;
+  n.k_w = kNormWeight;
+  n.eps = epsilon;
+  return contig(call, cos_sin, end_lens, pos_ids, qkv, cache, q_out, fp8, kScale, vScale, &n,
+                style, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+rkv_status rkv_apply_rope_write_kv_packed_qkv_qknorm(const rkv_tensor* cosSinCache,
+                                                     rkv_tensor* qkv, rkv_tensor* kvCache,
+                                                     const float* qNormWeight,
+                                                     const float* kNormWeight, float epsilon,
+                                                     const float* kScale, const float* vScale,
+                                                     int32_t ropeStyle, hipStream_t stream) {
+  return norm_call(rkv::kCallPacked, cosSinCache, nullptr, nullptr, qkv, kvCache, nullptr,
+                   qNormWeight, kNormWeight, epsilon, kScale, vScale, ropeStyle, stream);
+}
+
+rkv_status rkv_apply_rope_write_kv_continuous_qknorm(
+    const rkv_tensor* cosSinCache, const rkv_tensor* kvCacheEndLens, const rkv_tensor* qkv,
+    rkv_tensor* kvCache, rkv_tensor* qOut, const float* qNormWeight, const float* kNormWeight,
+    float epsilon, const float* kScale, const float* vScale, int32_t ropeStyle,
+    hipStream_t stream) {
+  return norm_call(rkv::kCallContinuous, cosSinCache, kvCacheEndLens, nullptr, qkv, kvCache, qOut,
+                   qNormWeight, kNormWeight, epsilon, kScale, vScale, ropeStyle, stream);
+}
+
+rkv_status rkv_apply_rope_write_kv_tree_qknorm(
+    const rkv_tensor* cosSinCache, const rkv_tensor* kvCacheEndLens,
+    const rkv_tensor* tokenPosIds, const rkv_tensor* qkv, rkv_tensor* kvCache, rkv_tensor* qOut,
+    const float* qNormWeight, const float* kNormWeight, float epsilon, const float* kScale,
+    const float* vScale, int32_t ropeStyle, hipStream_t stream) {
+  return norm_call(rkv::kCallTree, cosSinCache, kvCacheEndLens, tokenPosIds, qkv, kvCache, qOut,
+                   qNormWeight, kNormWeight, epsilon, kScale, vScale, ropeStyle, stream);
 }
 
 rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {

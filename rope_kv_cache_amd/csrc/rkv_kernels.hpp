@@ -19,8 +19,15 @@
 // chunk as 8 E4M3 bytes of value * (1/scale), the per-tensor scales read
 // from device memory (sglang rope_cache.py, HAVE_K_SCALE / HAVE_V_SCALE).
 //
+// Q/K RMS norm (kNorm, calls 1-3).  Same decomposition; each Q or K row
+// with a weight vector is normalised before its rotation: the lanes of a row
+// reduce its sum of squares, each lane scales its own 8 values (and, for a
+// NeoX rotary lane, its partner's 8 values, fetched as fp16 bits) by
+// 1/rms and the per-dimension weights.
+//
 // This header holds the kernel templates; rkv_kernels.hip instantiates the
-// fp16-cache kernels and rkv_kernels_fp8.hip the fp8-cache ones.
+// fp16-cache kernels, rkv_kernels_fp8.hip the fp8-cache ones and
+// rkv_kernels_norm*.hip the Q/K-norm ones.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -89,7 +96,7 @@ __device__ __forceinline__ int wave_id_uniform() {
 // Call 3 (tree): slot = endLens[b] - S + s, position = tokenPosIds[b, s].
 // Calls 2 and 3 skip a token whose slot or position is out of range.
 // (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV".)
-template <int D, int kCall, int kStyle, bool kExact, int G, bool kFp8>
+template <int D, int kCall, int kStyle, bool kExact, int G, bool kFp8, bool kNorm>
 __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
@@ -133,6 +140,19 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
     load_cos_sin<kStyle>(p.cos_sin + ((size_t)tb * p.table_len + pos) * p.R, role.freq0, p.R,
                          cs, sn);
   }
+  // norm: each row's weights (its own dims, and a NeoX partner's), requested
+  // with the cos/sin loads
+  float nws[G][8] = {}, nwp[G][8] = {};
+  bool normed[G] = {};
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int r = row[g];
+      const float* wsrc = r < p.Hq ? p.q_norm_w : (r < p.Hq + p.Hkv ? p.k_norm_w : nullptr);
+      normed[g] = wsrc != nullptr && r < H;
+      if (normed[g]) load_norm_weights<kStyle>(wsrc, c, role, nws[g], nwp[g]);
+    }
+  }
   // fp8: the scales, read while the row and cos/sin loads are in flight
   float k_rcp = 1.f, v_rcp = 1.f;
   if constexpr (kFp8) load_reciprocal_scales(p.k_scale, p.v_scale, k_rcp, v_rcp);
@@ -147,16 +167,28 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
         (((size_t)b * 2 + (is_k ? 0 : 1)) * p.Hkv + h) * (size_t)p.cap + slot;
     uint16_t* const q_dst = (kCall == kCallPacked) ? tok_base + (size_t)r * D
                                                    : p.q_out + ((size_t)token * p.Hq + r) * D;
-    if constexpr (kFp8) {
+    if constexpr (kFp8 || kNorm) {
+      // the unrounded row values, then fp16 and / or E4M3 from them
       WideT<kExact> w[8];
-      const bool rot = rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn, w);
+      bool comp;
+      if constexpr (kNorm) {
+        const WideT<kExact> rr = row_rms_reciprocal<D, kExact>(x[g], p.eps);
+        comp = rotate_chunk_norm<kStyle, kExact>(x[g], lane, role, is_q || is_k, normed[g], rr,
+                                                 nws[g], nwp[g], cs, sn, w);
+      } else {
+        comp = rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn, w);
+      }
       if (r >= H) continue;
       if (is_q) {
-        st16_stream(q_dst + 8 * c, narrow_chunk<kExact>(w, x[g], rot));
-      } else {
+        st16_stream(q_dst + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
+      } else if constexpr (kFp8) {
         st8_stream(p.cache8 + cache_row * D + 8 * c, to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp));
         if (kCall == kCallPacked && is_k)
-          st16_stream(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], rot));
+          st16_stream(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
+      } else {
+        const uint4 y = narrow_chunk<kExact>(w, x[g], comp);
+        st16_stream(p.cache + cache_row * D + 8 * c, y);
+        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
       }
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn);
@@ -307,7 +339,7 @@ inline unsigned blocks_for(int32_t waves) {
   return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
-template <int kCall, bool kFp8>
+template <int kCall, bool kFp8, bool kNorm>
 hipError_t launch_contig_call(const ContigParams& p, int D, int style, bool exact,
                               hipStream_t stream) {
   return with_d(D, [&](auto d) {
@@ -315,7 +347,7 @@ hipError_t launch_contig_call(const ContigParams& p, int D, int style, bool exac
       return with_groups(p.groups_per_wave, [&](auto g) {
         hipLaunchKernelGGL(
             (contig_kernel<decltype(d)::value, kCall, decltype(st)::value, decltype(ex)::value != 0,
-                           decltype(g)::value, kFp8>),
+                           decltype(g)::value, kFp8, kNorm>),
             dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p);
         return hipGetLastError();
       });
@@ -323,14 +355,15 @@ hipError_t launch_contig_call(const ContigParams& p, int D, int style, bool exac
   });
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kNorm>
 hipError_t launch_contig_t(const ContigParams& p, int call, int D, int style, bool exact,
                            hipStream_t stream) {
   switch (call) {
-    case kCallPacked: return launch_contig_call<kCallPacked, kFp8>(p, D, style, exact, stream);
+    case kCallPacked:
+      return launch_contig_call<kCallPacked, kFp8, kNorm>(p, D, style, exact, stream);
     case kCallContinuous:
-      return launch_contig_call<kCallContinuous, kFp8>(p, D, style, exact, stream);
-    case kCallTree: return launch_contig_call<kCallTree, kFp8>(p, D, style, exact, stream);
+      return launch_contig_call<kCallContinuous, kFp8, kNorm>(p, D, style, exact, stream);
+    case kCallTree: return launch_contig_call<kCallTree, kFp8, kNorm>(p, D, style, exact, stream);
     default: return hipErrorInvalidValue;
   }
 }

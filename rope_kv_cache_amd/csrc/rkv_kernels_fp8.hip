@@ -5,7 +5,7 @@ namespace rkv {
 
 hipError_t launch_contig_fp8(const ContigParams& p, int call, int D, int style, bool exact,
                              hipStream_t stream) {
-  return detail::launch_contig_t<true>(p, call, D, style, exact, stream);
+  return detail::launch_contig_t<true, false>(p, call, D, style, exact, stream);
 }
 
 hipError_t launch_paged_fp8(const PagedParams& p, int D, int style, bool exact, bool gather,

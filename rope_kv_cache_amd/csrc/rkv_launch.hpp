@@ -37,6 +37,9 @@ struct ContigParams {
   uint8_t* cache8;          // [B, 2, Hkv, cap, D] E4M3 cache (fp8 kernels)
   const float* k_scale;     // fp8: per-tensor scales (one fp32 each) or null for 1
   const float* v_scale;
+  const float* q_norm_w;    // Q/K norm: per-dimension weights [D] of Q and K heads,
+  const float* k_norm_w;    //   or null (those heads are not normalised)
+  float eps;                // Q/K norm: added to the mean square
   uint16_t* q_out;          // [B, S, Hq, D]; calls 2 and 3
   const int32_t* end_lens;  // [B]; calls 2 and 3
   const int32_t* pos_ids;   // [B, S]; call 3
@@ -76,6 +79,10 @@ hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool
                         hipStream_t stream);
 hipError_t launch_contig_fp8(const ContigParams& p, int call, int D, int style, bool exact,
                              hipStream_t stream);
+hipError_t launch_contig_norm(const ContigParams& p, int call, int D, int style, bool exact,
+                              hipStream_t stream);
+hipError_t launch_contig_norm_fp8(const ContigParams& p, int call, int D, int style, bool exact,
+                                  hipStream_t stream);
 hipError_t launch_paged_fp8(const PagedParams& p, int D, int style, bool exact, bool gather,
                             hipStream_t stream);
 

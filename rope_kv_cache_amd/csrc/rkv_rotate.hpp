@@ -30,6 +30,18 @@
 // "Emulation of FMA and correctly rounded sums: proved algorithms using
 // rounding to odd", IEEE Trans. Computers 2008).
 //
+// Q/K RMS norm.  A normalised row is n_d = x_d * r * w_d with
+// r = 1/sqrt(mean(x^2) + eps); the rotation then acts on n.  The row's sum
+// of squares is reduced over its D/8 lanes by an xor butterfly of
+// ds_swizzle.  Exact mode: every fp16 square is a multiple of 2^-48 below
+// 2^32; split into a multiple of 2^-13 and a remainder, both partial sums
+// are exact in binary64 in any order, so their sum is the correctly rounded
+// sum of squares (what the definition rounds once); sqrt and the division
+// are correctly rounded binary64 operations.  The rotation of normalised
+// values, no longer exact products, rounds each product and the sum
+// separately (no contraction).  Default mode: binary32 sum, v_rsq_f32, and
+// the compensated rotation on the binary32 normalised values.
+//
 // fp8 cache.  The E4M3 cache value is the unrounded rotation (binary32 in
 // the default mode, binary64 exact) times the reciprocal scale, clamped to
 // +-448 and converted by the hardware (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950,
@@ -325,6 +337,154 @@ __device__ __forceinline__ void load_reciprocal_scales(const float* k_scale, con
   k_rcp = reciprocal(ks);
   v_rcp = reciprocal(vs);
   asm volatile("" : "+v"(k_rcp), "+v"(v_rcp));
+}
+
+// ---------------------------------------------------------------- norm --
+
+template <int kXor>
+__device__ __forceinline__ float swizzle_xor(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F | (kXor << 10)));
+}
+
+template <int kXor>
+__device__ __forceinline__ double swizzle_xor(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x1F | (kXor << 10));
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x1F | (kXor << 10));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the kLanes consecutive, aligned lanes of one row (a power of two
+// <= 32); every lane of the row gets the same total.  Called by every lane.
+template <int kLanes, typename T>
+__device__ __forceinline__ T row_sum(T v) {
+  if constexpr (kLanes > 1) v += swizzle_xor<1>(v);
+  if constexpr (kLanes > 2) v += swizzle_xor<2>(v);
+  if constexpr (kLanes > 4) v += swizzle_xor<4>(v);
+  if constexpr (kLanes > 8) v += swizzle_xor<8>(v);
+  if constexpr (kLanes > 16) v += swizzle_xor<16>(v);
+  return v;
+}
+
+// 1 / sqrt(mean of squares + eps) of the row whose chunk this lane holds.
+// Called by every lane (the reduction exchanges data across lanes).
+template <int D, bool kExact>
+__device__ __forceinline__ WideT<kExact> row_rms_reciprocal(uint4 x, float eps) {
+  const uint32_t xa[4] = {x.x, x.y, x.z, x.w};
+  if constexpr (kExact) {
+    double hi = 0.0, lo = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const double v = (double)h2f(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1]));
+      const double q = v * v;                                      // exact
+      const double h = __builtin_trunc(q * 8192.0) * (1.0 / 8192.0);   // exact
+      hi += h;
+      lo += (h == q) ? 0.0 : q - h;                                // exact; keeps inf / NaN
+    }
+    hi = row_sum<D / 8>(hi);
+    lo = row_sum<D / 8>(lo);
+    const double ms = (hi + lo) * (1.0 / D);                       // one rounding
+    return 1.0 / __builtin_sqrt(ms + (double)eps);
+  } else {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float v = h2f(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1]));
+      ss = __builtin_fmaf(v, v, ss);
+    }
+    ss = row_sum<D / 8>(ss);
+    return __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  }
+}
+
+// x*c + sign*(p*s) for values that are not fp16 (normalised rows).  Exact
+// mode: each product and the sum rounded once in binary64, no contraction.
+// Default mode: the same compensated binary32 evaluation as rot1_wide.
+template <bool kExact>
+__device__ __forceinline__ WideT<kExact> rot1_general(WideT<kExact> x, WideT<kExact> p, float c,
+                                                      float s, bool first) {
+  if constexpr (kExact) {
+#pragma clang fp contract(off)
+    const double a = x * (double)c;
+    const double b = p * (double)s;
+    return first ? a - b : a + b;
+  } else {
+    const float sv = first ? -s : s;
+    const float ps = p * sv;
+    const float e = __builtin_fmaf(p, sv, -ps);
+    return __builtin_fmaf(x, c, ps) + e;
+  }
+}
+
+// The weights a lane needs: its own 8 dims and, for a NeoX rotary lane, its
+// partner chunk's 8 dims.
+template <int kStyle>
+__device__ __forceinline__ void load_norm_weights(const float* w, int c, const ChunkRole& role,
+                                                  float (&ws)[8], float (&wp)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(w + 8 * c);
+  const float4 b = *reinterpret_cast<const float4*>(w + 8 * c + 4);
+  ws[0] = a.x; ws[1] = a.y; ws[2] = a.z; ws[3] = a.w;
+  ws[4] = b.x; ws[5] = b.y; ws[6] = b.z; ws[7] = b.w;
+  if constexpr (kStyle == kNeox) {
+    if (role.rotary) {
+      const int pc = c + role.partner;
+      const float4 e = *reinterpret_cast<const float4*>(w + 8 * pc);
+      const float4 f = *reinterpret_cast<const float4*>(w + 8 * pc + 4);
+      wp[0] = e.x; wp[1] = e.y; wp[2] = e.z; wp[3] = e.w;
+      wp[4] = f.x; wp[5] = f.y; wp[6] = f.z; wp[7] = f.w;
+    }
+  }
+}
+
+// The chunk's unrounded output when its row may be normalised: n = x*r*w
+// (normed rows; else n = x), rotated when rotate_row and the chunk is
+// rotary.  Returns whether the output must be rounded from w (rotated or
+// normalised) rather than copied from x.  Called by every lane.
+template <int kStyle, bool kExact>
+__device__ __forceinline__ bool rotate_chunk_norm(uint4 x, int lane, const ChunkRole& role,
+                                                  bool rotate_row, bool normed, WideT<kExact> r,
+                                                  const float (&ws)[8], const float (&wp)[8],
+                                                  const float (&c)[8], const float (&s)[8],
+                                                  WideT<kExact> (&w)[8]) {
+  using T = WideT<kExact>;
+  const uint32_t xa[4] = {x.x, x.y, x.z, x.w};
+  const bool rot = rotate_row && role.rotary;
+  T n[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const T v = widen<kExact>(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1]));
+    const T t = v * r;
+    n[k] = normed ? t * (T)ws[k] : v;
+  }
+  if constexpr (kStyle == kNeox) {
+    const uint4 pch = lane_fetch(x, lane + role.partner);
+    const uint32_t pa[4] = {pch.x, pch.y, pch.z, pch.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (rot) {
+        const T v = widen<kExact>(k & 1 ? hi16(pa[k >> 1]) : lo16(pa[k >> 1]));
+        const T t = v * r;
+        const T np = normed ? t * (T)wp[k] : v;
+        w[k] = rot1_general<kExact>(n[k], np, c[k], s[k], role.first);
+      } else {
+        w[k] = n[k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (rot) {
+        w[2 * k] = rot1_general<kExact>(n[2 * k], n[2 * k + 1], c[k], s[k], true);
+        w[2 * k + 1] = rot1_general<kExact>(n[2 * k + 1], n[2 * k], c[k], s[k], false);
+      } else {
+        w[2 * k] = n[2 * k];
+        w[2 * k + 1] = n[2 * k + 1];
+      }
+    }
+  }
+  return rot || normed;
 }
 
 }  // namespace rkv

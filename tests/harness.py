@@ -83,6 +83,10 @@ def _upload_scales(w, t, device):
     if is_fp8(w):
         t["k_scale"] = _scale_tensor(w.extra["fp8"]["k_scale"], device)
         t["v_scale"] = _scale_tensor(w.extra["fp8"]["v_scale"], device)
+    norm = w.extra.get("qknorm")
+    if norm:
+        for key in ("q_weight", "k_weight"):
+            t[key] = None if norm[key] is None else dev(norm[key], device)
 
 
 def launch(w, t: dict, exact: bool = False) -> None:
@@ -90,6 +94,9 @@ def launch(w, t: dict, exact: bool = False) -> None:
     ROUND_EXACT into the rope style (binary64, correctly rounded)."""
     import rope_kv_cache_amd as rkv
     style = w.style | (rkv.ROUND_EXACT if exact else 0)
+    if w.extra.get("qknorm"):
+        _launch_qknorm(rkv, w, t, style)
+        return
     if is_fp8(w):
         _launch_fp8(rkv, w, t, style)
         return
@@ -132,6 +139,22 @@ def _launch_fp8(rkv, w, t, style):
                                          t["cache"], t["q_out"], ks, vs, style)
 
 
+def _launch_qknorm(rkv, w, t, style):
+    eps = w.extra["qknorm"]["eps"]
+    ks, vs = (t["k_scale"], t["v_scale"]) if is_fp8(w) else (None, None)
+    qw, kw = t["q_weight"], t["k_weight"]
+    if w.call == "packed":
+        rkv.apply_rope_write_kv_packed_qkv_qknorm(t["cos_sin"], t["qkv"], t["cache"], qw, kw, eps,
+                                                  style, ks, vs)
+    elif w.call == "continuous":
+        rkv.apply_rope_write_kv_continuous_qknorm(t["cos_sin"], t["end_lens"], t["qkv"],
+                                                  t["cache"], t["q_out"], qw, kw, eps, style, ks,
+                                                  vs)
+    else:
+        rkv.apply_rope_write_kv_tree_qknorm(t["cos_sin"], t["end_lens"], t["pos_ids"], t["qkv"],
+                                            t["cache"], t["q_out"], qw, kw, eps, style, ks, vs)
+
+
 def download(w, t: dict) -> dict:
     torch.cuda.synchronize()
     cache_host = host8 if is_fp8(w) else host16
@@ -162,8 +185,11 @@ def expected(w, L=None) -> dict:
 
 def rotated_mask_parts(w, key):
     """Index expressions (tuples of slices) covering the elements of output
-    ``key`` that may hold a rotated value."""
+    ``key`` that may hold a rotated value (with Q/K norm, every dim of a
+    normalised head is computed)."""
     R = w.R
+    if w.extra.get("qknorm"):
+        R = w.D
     if key == "pool":
         return [(0, Ellipsis, slice(0, R))]
     if key == "cache":
@@ -186,6 +212,20 @@ def _within_tol(g: np.ndarray, r: np.ndarray) -> np.ndarray:
     both_nan = np.isnan(gv) & np.isnan(rv)
     same_inf = np.isinf(gv) & np.isinf(rv) & (gv == rv)
     return ok | both_nan | same_inf
+
+
+def _is_nan16(x: np.ndarray) -> np.ndarray:
+    return ((x & 0x7C00) == 0x7C00) & ((x & 0x3FF) != 0)
+
+
+INFO_SUFFIXES = ("_max_ulp", "_max_ulp_ge_2m6", "_max_code_step", "_nan_bits_differ",
+                 "_nan_sign_differs")
+
+
+def exact_diffs(rep: dict) -> dict:
+    """Counts of elements that differ from the oracle (informational keys
+    such as ulp maxima and NaN sign differences left out)."""
+    return {k: v for k, v in rep.items() if not k.endswith(INFO_SUFFIXES) and v}
 
 
 def _ulps(g: np.ndarray, r: np.ndarray) -> np.ndarray:
@@ -256,6 +296,15 @@ def compare(w, got: dict, want: dict) -> dict:
             raise AssertionError(
                 f"{w.name}: {key}{list(idx)} differs outside rotated Q/K: gpu {g[idx]:#06x} "
                 f"oracle {ref[idx]:#06x} ({int(bad.sum())} such elements)")
+        # computed NaN results match as NaN: IEEE 754 leaves the sign (and
+        # payload) of a NaN produced by an invalid operation unspecified
+        nan_pair = diff & _is_nan16(g) & _is_nan16(ref) & rot
+        if nan_pair.any():
+            report[key + "_nan_bits_differ"] = int(nan_pair.sum())
+            diff = diff & ~nan_pair
+            if not diff.any():
+                report[key] = 0
+                continue
         where = np.nonzero(diff)
         gd, rd = g[where], ref[where]
         tol_ok = _within_tol(gd, rd)
@@ -266,5 +315,8 @@ def compare(w, got: dict, want: dict) -> dict:
                 f"{w.name}: {key}{list(idx)} outside tolerance: gpu {gd[k]:#06x} "
                 f"oracle {rd[k]:#06x}")
         report[key] = int(diff.sum())
-        report[key + "_max_ulp"] = int(_ulps(gd, rd).max())
+        ulps = _ulps(gd, rd)
+        report[key + "_max_ulp"] = int(ulps.max())
+        big = np.abs(rd.view(np.float16).astype(np.float64)) >= 2.0 ** -6
+        report[key + "_max_ulp_ge_2m6"] = int(ulps[big].max()) if big.any() else 0
     return report

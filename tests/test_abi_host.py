@@ -486,3 +486,87 @@ def test_fp8_binding_rejects_fp16_cache():
     cache = torch.zeros(1, 2, 2, 16, 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         rkv.apply_rope_write_kv_packed_qkv_fp8(cs, qkv, cache, None, None, rkv.ROPE_NEOX)
+
+
+# ------------------------------------------------------ Q/K-norm calls ---
+
+def call_packed_norm(cs, qkv, cache, qw=None, kw=None, eps=1e-6, ks=None, vs=None, style=0):
+    b = ctypes.byref
+    return L.rkv_apply_rope_write_kv_packed_qkv_qknorm(b(cs), b(qkv), b(cache), qw, kw,
+                                                       ctypes.c_float(eps), ks, vs, style, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("case,want", [
+    ("eps_negative", rkv.ERR_SHAPE), ("eps_nan", rkv.ERR_SHAPE), ("eps_inf", rkv.ERR_SHAPE),
+    ("q_weight_misaligned", rkv.ERR_ALIGNMENT), ("k_weight_misaligned", rkv.ERR_ALIGNMENT),
+    ("cache_covers_k_weight", rkv.ERR_ALIAS), ("qkv_covers_q_weight", rkv.ERR_ALIAS),
+    ("scales_with_fp16_cache", rkv.ERR_DTYPE), ("f32_cache", rkv.ERR_DTYPE),
+    ("fp8_cache_then_D_96", rkv.ERR_UNSUPPORTED), ("no_weights_then_D_96", rkv.ERR_UNSUPPORTED),
+    ("empty", rkv.OK), ("empty_fp8", rkv.OK),
+])
+def test_packed_qknorm_validation(case, want):
+    cs, qkv, cache = packed_args()
+    qw, kw, eps, ks, vs = 13 << 40, 14 << 40, 1e-6, None, None
+    if case == "eps_negative":
+        eps = -1e-6
+    elif case == "eps_nan":
+        eps = float("nan")
+    elif case == "eps_inf":
+        eps = float("inf")
+    elif case == "q_weight_misaligned":
+        qw += 4
+    elif case == "k_weight_misaligned":
+        kw += 8
+    elif case == "cache_covers_k_weight":
+        kw = cache.data + 4096
+    elif case == "qkv_covers_q_weight":
+        qw = qkv.data + 256
+    elif case == "scales_with_fp16_cache":
+        ks = 9 << 40
+    elif case == "f32_cache":
+        cache.dtype = F32
+    elif case == "fp8_cache_then_D_96":
+        cs, qkv, cache = packed_args(D=96, R=96)
+        cache.dtype = F8
+        ks, vs = 9 << 40, 10 << 40
+    elif case == "no_weights_then_D_96":
+        cs, qkv, cache = packed_args(D=96, R=96)
+        qw = kw = None
+    elif case == "empty":
+        cs, qkv, cache = packed_args(B=0)
+    elif case == "empty_fp8":
+        cs, qkv, cache = packed_args(S=0)
+        cache.dtype = F8
+    st = call_packed_norm(cs, qkv, cache, qw, kw, eps, ks, vs)
+    assert st == want, (case, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+def test_continuous_and_tree_qknorm_validation():
+    b = ctypes.byref
+    a = cont_args()
+    st = L.rkv_apply_rope_write_kv_continuous_qknorm(*[b(x) for x in a], 13 << 40, a[4].data,
+                                                     ctypes.c_float(1e-6), None, None, 0, None)
+    assert st == rkv.ERR_ALIAS, L.rkv_last_error()          # k weight inside qOut
+    t = tree_args()
+    st = L.rkv_apply_rope_write_kv_tree_qknorm(*[b(x) for x in t], None, None,
+                                               ctypes.c_float(-1.0), None, None, 0, None)
+    assert st == rkv.ERR_SHAPE
+    c = cont_args(B=0)
+    assert L.rkv_apply_rope_write_kv_continuous_qknorm(*[b(x) for x in c], None, None,
+                                                       ctypes.c_float(0.0), None, None, 0,
+                                                       None) == rkv.OK
+    assert L.rkv_apply_rope_write_kv_packed_qkv_qknorm(None, None, None, None, None,
+                                                       ctypes.c_float(0.0), None, None, 0,
+                                                       None) == rkv.ERR_NULL
+
+
+def test_qknorm_binding_rejects_bad_weights():
+    import torch
+    cs = torch.zeros(1, 16, 128)
+    qkv = torch.zeros(1, 8, 8, 128, dtype=torch.float16)
+    cache = torch.zeros(1, 2, 2, 16, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        rkv.apply_rope_write_kv_packed_qkv_qknorm(cs, qkv, cache, None, None, 1e-6,
+                                                  rkv.ROPE_NEOX, k_scale=torch.ones(1))

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 import workloads as W
-from harness import compare, dev, download, expected, host16, launch, run_gpu, upload
+from harness import (compare, dev, download, exact_diffs, expected, host16, launch, run_gpu,
+                     upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +37,7 @@ def check(w, modes=("fast", "exact")):
         rep = compare(w, got, want)
         _say(f"[parity] {w.name} {mode}: rotated elements differing from the oracle: {rep}")
         if mode == "exact":
-            diffs = {k: v for k, v in rep.items() if not k.endswith("_max_ulp") and v}
+            diffs = exact_diffs(rep)
             assert not diffs, f"exact mode not bit-identical: {rep}"
         else:
             ulps = {k: v for k, v in rep.items() if k.endswith("_max_ulp")}
