@@ -8,8 +8,9 @@ steps bracketed by device synchronisation; each launch is also bracketed by
 HIP events on its stream, which give the kernel's average duration for the
 roofline.  The same workload in the library's RKV_ROUND_EXACT mode and the
 other workloads (continuous write, tree write, paged delta update, the
-paged update with the cos/sin gather fused in, and the prefill, continuous
-and paged calls into an E4M3 cache) are reported under "workloads".  The small workloads' inputs fit the 256 MB
+paged update with the cos/sin gather fused in, the prefill, continuous
+and paged calls into an E4M3 cache, and the prefill and continuous calls
+with Q/K RMS norm) are reported under "workloads".  The small workloads' inputs fit the 256 MB
 MALL, so a 1 GiB buffer is read before each of their timed launches to push
 them back to HBM (a read leaves clean lines, so the timed kernel inherits no
 write-back); their event-bracketed times include the events' own overhead
@@ -50,7 +51,7 @@ def bytes_contig(w) -> int:
     Q/K/V rows read, Q (and for call 1, K in place) written, K and V cache
     rows written (D bytes each for an E4M3 cache, 2D for fp16); each
     distinct cos/sin row read once; the index arrays (and the two fp8
-    scales)."""
+    scales, and the Q/K norm weights)."""
     D, R, Hq, Hkv = w.D, w.R, w.Hq, w.Hkv
     fp8 = bool(w.extra.get("fp8"))
     cb = 1 if fp8 else 2
@@ -73,7 +74,9 @@ def bytes_contig(w) -> int:
         t = 0 if tb == 1 else b
         rows.update((t, int(p)) for p in np.asarray(pos[b])[valid[b]])
     per_token = H * D * 2 + write_q + 2 * Hkv * D * cb
-    return n * per_token + len(rows) * R * 4 + index + (8 if fp8 else 0)
+    norm = w.extra.get("qknorm") or {}
+    weights = sum(D * 4 for k in ("q_weight", "k_weight") if norm.get(k) is not None)
+    return n * per_token + len(rows) * R * 4 + index + (8 if fp8 else 0) + weights
 
 
 def bytes_paged(w) -> int:
@@ -285,6 +288,21 @@ def main():
             f"({f8_gbs / PEAK_HBM_GBS:.1%})")
         del t
         torch.cuda.empty_cache()
+        # the same prefill with Q/K RMS norm before the rotation, fp16 cache
+        w = W.config(HEADLINE)
+        W.with_qk_norm(w, 7105)
+        nb = algorithmic_bytes(w)
+        t = upload(w)
+        n_ms, _ = time_launches(w, t, max(10, args.steps // 2), 3)
+        n_gbs = nb / (n_ms * 1e-3) / 1e9
+        extra["prefill_qknorm"] = {
+            "workload": w.name, "norm": "RMS norm of Q and K heads before the rotation",
+            "kernel_us": n_ms * 1e3, "GB/s": n_gbs, "frac": n_gbs / PEAK_HBM_GBS,
+            "tokens_per_s": w.tokens / (n_ms * 1e-3), "algorithmic_bytes": nb}
+        log(f"[bench] Q/K norm: {n_ms * 1e3:.1f} us, {n_gbs:.0f} GB/s "
+            f"({n_gbs / PEAK_HBM_GBS:.1%})")
+        del t
+        torch.cuda.empty_cache()
 
     if args.calib:
         src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
@@ -310,7 +328,8 @@ def main():
                  ("continuous_neox_fp8_cache",
                   lambda: W.with_fp8_cache(W.config(2, W.NEOX), 7002, fill="sentinel")),
                  ("paged_delta_fp8_cache",
-                  lambda: W.with_fp8_cache(W.config(4), 7004, fill="sentinel"))]
+                  lambda: W.with_fp8_cache(W.config(4), 7004, fill="sentinel")),
+                 ("continuous_neox_qknorm", lambda: W.with_qk_norm(W.config(2, W.NEOX), 7102))]
         for label, make in cases:
             log(f"[bench] generating {label}")
             x = make()

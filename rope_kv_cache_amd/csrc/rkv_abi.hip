@@ -25,9 +25,14 @@ rkv_status fail(rkv_status st, const char* fmt, ...) {
 void clear_error() { g_err[0] = '\0'; }
 
 // Launch shape.  A wave handles G row groups (512/D rows each) of one work
-// item.  Large launches are bandwidth-bound and run fastest with one row
-// group per wave; small ones are latency-bound, so they take G = 2 or 4
-// when that keeps every wave resident at once (256 CUs x 4 SIMDs x 8 waves).
+// item.  Large launches are bandwidth-bound: the plain binary32 kernel runs
+// fastest with one row group per wave, while the kernels with more
+// arithmetic per byte (exact mode, E4M3 cache, Q/K norm) run faster with at
+// least two, whose loads are in flight together while the wave computes
+// (measured on the large prefill: 236 -> 221 us with an E4M3 cache, 266 ->
+// 241 us with Q/K norm, 272 -> 247 us exact).  Small launches are
+// latency-bound, so they take G = 2 or 4 when that keeps every wave
+// resident at once (256 CUs x 4 SIMDs x 8 waves).
 constexpr long long kResidentWaves = 8192;
 constexpr long long kStreamingGroups = 65536;
 
@@ -112,10 +117,12 @@ struct Split {
   int32_t waves_per_item;
 };
 
-// Returns G = 0 when the wave count would not fit in int32.
-Split pick_split(long long items, long long groups_per_item) {
+// Returns G = 0 when the wave count would not fit in int32.  `heavy`: the
+// kernel does more arithmetic per byte; it starts from G = 2 when a work
+// item has two row groups or more.
+Split pick_split(long long items, long long groups_per_item, bool heavy) {
   auto waves = [&](int g) { return items * ((groups_per_item + g - 1) / g); };
-  int g = 1;
+  int g = (heavy && groups_per_item >= 2) ? 2 : 1;
   if (items * groups_per_item <= kStreamingGroups) {
     while (g < 4 && waves(g) > kResidentWaves) g *= 2;
   }
@@ -255,7 +262,8 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.table_len = (int32_t)TL;
   p.R = (int32_t)R;
   const long long rows_per_group = 512 / D;
-  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group);
+  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group,
+                              exact_of(style) || fp8 || norm != nullptr);
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_token = sp.waves_per_item;
@@ -350,7 +358,8 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.num_pages = numPages;
   p.max_pages = maxPagesPerSeq;
   const long long rows_per_group = 512 / D;
-  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group);
+  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group,
+                              exact_of(ropeStyle) || fp8);
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_row = sp.waves_per_item;

@@ -32,15 +32,15 @@
 //
 // Q/K RMS norm.  A normalised row is n_d = x_d * r * w_d with
 // r = 1/sqrt(mean(x^2) + eps); the rotation then acts on n.  The row's sum
-// of squares is reduced over its D/8 lanes by an xor butterfly of
-// ds_swizzle.  Exact mode: every fp16 square is a multiple of 2^-48 below
+// of squares is reduced over its D/8 lanes by a butterfly of lane moves.  Exact mode: every fp16 square is a multiple of 2^-48 below
 // 2^32; split into a multiple of 2^-13 and a remainder, both partial sums
 // are exact in binary64 in any order, so their sum is the correctly rounded
 // sum of squares (what the definition rounds once); sqrt and the division
 // are correctly rounded binary64 operations.  The rotation of normalised
 // values, no longer exact products, rounds each product and the sum
 // separately (no contraction).  Default mode: binary32 sum, v_rsq_f32, and
-// the compensated rotation on the binary32 normalised values.
+// the compensated rotation on the binary32 normalised values.  The row
+// reduction uses DPP lane moves inside 16-lane rows.
 //
 // fp8 cache.  The E4M3 cache value is the unrounded rotation (binary32 in
 // the default mode, binary64 exact) times the reciprocal scale, clamped to
@@ -356,16 +356,60 @@ __device__ __forceinline__ double swizzle_xor(double v) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Sum over the kLanes consecutive, aligned lanes of one row (a power of two
-// <= 32); every lane of the row gets the same total.  Called by every lane.
 template <int kLanes, typename T>
-__device__ __forceinline__ T row_sum(T v) {
+__device__ __forceinline__ T row_sum_swizzle(T v) {
   if constexpr (kLanes > 1) v += swizzle_xor<1>(v);
   if constexpr (kLanes > 2) v += swizzle_xor<2>(v);
   if constexpr (kLanes > 4) v += swizzle_xor<4>(v);
   if constexpr (kLanes > 8) v += swizzle_xor<8>(v);
   if constexpr (kLanes > 16) v += swizzle_xor<16>(v);
   return v;
+}
+
+// DPP lane moves inside a row of 16 lanes (GFX9 encodings): quad_perm
+// [1,0,3,2] and [2,3,0,1], row_half_mirror (lane i <- 7-i within each 8),
+// row_mirror (lane i <- 15-i).
+constexpr int kDppQuadSwap1 = 0xB1;
+constexpr int kDppQuadSwap2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ double dpp_move(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kCtrl, 0xF, 0xF,
+                                                            false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), kCtrl,
+                                                            0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The same sum with DPP moves inside 16-lane rows (no LDS round trip):
+// each step adds the value of a lane in the other half of the current
+// group, so after log2(kLanes) steps every lane holds the group's total,
+// the same value in every lane (addition is commutative).  Groups of 32
+// take a last ds_swizzle step across the two 16-lane rows.
+template <int kLanes, typename T>
+__device__ __forceinline__ T row_sum_dpp(T v) {
+  if constexpr (kLanes > 1) v += dpp_move<kDppQuadSwap1>(v);
+  if constexpr (kLanes > 2) v += dpp_move<kDppQuadSwap2>(v);
+  if constexpr (kLanes > 4) v += dpp_move<kDppHalfMirror>(v);
+  if constexpr (kLanes > 8) v += dpp_move<kDppMirror>(v);
+  if constexpr (kLanes > 16) v += swizzle_xor<16>(v);
+  return v;
+}
+
+// Sum over the kLanes consecutive, aligned lanes of one row (a power of two
+// <= 32); every lane of the row gets the same total.  Called by every lane.
+template <int kLanes, typename T>
+__device__ __forceinline__ T row_sum(T v) {
+  return row_sum_dpp<kLanes>(v);
 }
 
 // 1 / sqrt(mean of squares + eps) of the row whose chunk this lane holds.
