@@ -106,6 +106,10 @@ def _declare(L):
     L.rkv_ref_tree_qknorm.restype = ctypes.c_int
     L.rkv_ref_tree_qknorm.argtypes = [P, i32, i32, i32, P, P, P, i32, i32, i32, i32, i32, P, P,
                                       i32, P, P, P, f64, f32, f32, i32]
+    L.rkv_ref_prepare_delta_metadata.restype = ctypes.c_int
+    L.rkv_ref_prepare_delta_metadata.argtypes = [P, P, i32, P, P, i32]
+    L.rkv_ref_linear_tree_metadata.restype = ctypes.c_int
+    L.rkv_ref_linear_tree_metadata.argtypes = [P, P, i32, i32]
     L.rkv_ref_check_rope_capacity.restype = ctypes.c_int
     L.rkv_ref_check_rope_capacity.argtypes = [i32, i32]
     return L
@@ -448,6 +452,30 @@ def tree_qknorm(cos_sin, end_lens, pos_ids, qkv, cache, q_out, q_weight, k_weigh
     if rc:
         raise OracleError(rc, "tree_qknorm")
     return (c16 if c8 is None else c8), q_out
+
+
+def prepare_delta_metadata(old_lengths, delta_lengths, delta_width: int, L=None):
+    """Returns ``(delta_positions, delta_token_to_sequence)``, int32 [B * width]."""
+    old = _c(old_lengths, np.int32)
+    dl = _c(delta_lengths, np.int32)
+    B = old.size
+    pos = np.empty(B * delta_width, dtype=np.int32)
+    seq = np.empty(B * delta_width, dtype=np.int32)
+    rc = (L or lib()).rkv_ref_prepare_delta_metadata(_p(old), _p(dl), delta_width, _p(pos),
+                                                     _p(seq), B)
+    if rc:
+        raise OracleError(rc, "prepare_delta_metadata")
+    return pos, seq
+
+
+def linear_tree_metadata(batch: int, verify_size: int, L=None):
+    """Returns ``(parent_ids, depths)``, int32 [B, verify_size]."""
+    par = np.empty((batch, verify_size), dtype=np.int32)
+    dep = np.empty((batch, verify_size), dtype=np.int32)
+    rc = (L or lib()).rkv_ref_linear_tree_metadata(_p(par), _p(dep), batch, verify_size)
+    if rc:
+        raise OracleError(rc, "linear_tree_metadata")
+    return par, dep
 
 
 def check_rope_capacity(cos_sin_len: int, kv_capacity: int, L=None) -> int:

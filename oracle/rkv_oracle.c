@@ -62,7 +62,10 @@
  *      n_d = x_d * w_d / sqrt(mean_d(x_d^2) + eps) before the rotation, with
  *      one fp32 weight vector [D] for all Q heads and one for all K heads;
  *      dims >= R carry n_d; V is not normalised; one rounding at the end.
- *  Parity unpinned against the original system for R6, R7 and R26: no page
+ *  R28 delta metadata (signature only on [P3]): rows are b*deltaWidth + j;
+ *      valid for j < min(deltaLengths[b], deltaWidth) at position
+ *      oldDraftCacheLengths[b] + j, owner b; padding rows are -1 / -1.
+ *  Parity unpinned against the original system for R6, R7, R26 and R28: no page
  *  fixes them; they are the plainest reading consistent with the rest.
  */
 #include "rkv_oracle.h"
@@ -734,6 +737,51 @@ int rkv_ref_paged_delta_gather_fp8(const uint16_t* k_delta, const uint16_t* v_de
                       reciprocal_of(v_scale), NULL, rope, rope_states, rope_rows, state_indices,
                       delta_positions, delta_to_seq, page_table, num_delta, batch, hkv,
                       head_dim, rotary_dim, num_pages, max_pages_per_seq, style);
+}
+
+/* --------------------------------------------------- metadata builders -- */
+
+/* [P3] launchDFlashPrepareDeltaMetadata (signature only; R28): the delta
+ * rows are token-major, deltaWidth rows per sequence.  Row b*width + j is
+ * token j of sequence b's delta when j < min(deltaLengths[b], width): its
+ * position continues the old draft cache, oldDraftCacheLengths[b] + j (the
+ * page's proposal-input kernel puts the delta right after the old length),
+ * its owner is b.  Every other row is padding: -1 in both arrays.  A
+ * position beyond the int32 range is written as padding too. */
+int rkv_ref_prepare_delta_metadata(const int32_t* old_lengths, const int32_t* delta_lengths,
+                                   int32_t delta_width, int32_t* delta_positions,
+                                   int32_t* delta_to_seq, int32_t batch) {
+  if (!old_lengths || !delta_lengths || !delta_positions || !delta_to_seq) return RKV_REF_ERR_ARG;
+  if (batch < 0 || delta_width < 0) return RKV_REF_ERR_ARG;
+  for (int32_t b = 0; b < batch; ++b) {
+    int64_t len = delta_lengths[b];
+    for (int32_t j = 0; j < delta_width; ++j) {
+      size_t i = (size_t)b * delta_width + j;
+      int64_t pos = (int64_t)old_lengths[b] + j;
+      if (j < len && pos <= INT32_MAX) {
+        delta_positions[i] = (int32_t)pos;
+        delta_to_seq[i] = b;
+      } else {
+        delta_positions[i] = -1;
+        delta_to_seq[i] = -1;
+      }
+    }
+  }
+  return RKV_REF_OK;
+}
+
+/* [P3] launchDFlashBuildLinearTreeMetadata: a linear verification path of
+ * verifySize nodes per sequence; node 0 is the root (parent -1, depth 0),
+ * node i > 0 has parent i - 1 and depth i. */
+int rkv_ref_linear_tree_metadata(int32_t* parent_ids, int32_t* depths, int32_t batch,
+                                 int32_t verify_size) {
+  if (!parent_ids || !depths || batch < 0 || verify_size < 0) return RKV_REF_ERR_ARG;
+  for (int32_t b = 0; b < batch; ++b)
+    for (int32_t i = 0; i < verify_size; ++i) {
+      parent_ids[(size_t)b * verify_size + i] = i - 1;
+      depths[(size_t)b * verify_size + i] = i;
+    }
+  return RKV_REF_OK;
 }
 
 /* [P3] checkDFlashRopeCapacity: the table may be shorter than the padded

@@ -160,6 +160,16 @@ int rkv_ref_tree_qknorm(const float* cos_sin, int32_t table_batch, int32_t table
                         const float* k_weight, double eps, float k_scale, float v_scale,
                         int32_t style);
 
+/* Delta metadata: row b*delta_width + j -> (old_lengths[b] + j, b) for
+ * j < min(delta_lengths[b], delta_width), else (-1, -1). */
+int rkv_ref_prepare_delta_metadata(const int32_t* old_lengths, const int32_t* delta_lengths,
+                                   int32_t delta_width, int32_t* delta_positions,
+                                   int32_t* delta_to_seq, int32_t batch);
+
+/* Linear tree: parent i-1 (-1 for the root), depth i, for every sequence. */
+int rkv_ref_linear_tree_metadata(int32_t* parent_ids, int32_t* depths, int32_t batch,
+                                 int32_t verify_size);
+
 /* Capacity check: RKV_REF_ERR_CAPACITY iff cos_sin_len > kv_capacity. */
 int rkv_ref_check_rope_capacity(int32_t cos_sin_len, int32_t kv_capacity);
 

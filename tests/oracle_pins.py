@@ -1167,4 +1167,84 @@ def pin_qknorm_argument_errors(L):
             raise AssertionError(f"eps {eps} accepted")
 
 
+# ------------------------------------------------------------ metadata --
+
+def pin_delta_metadata_golden(L):
+    n = 0
+    for line in open(os.path.join(GOLDEN, "delta_metadata.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        width, old, dl, pos, seq = [f.split() for f in line.split("|")]
+        got_p, got_s = oracle.prepare_delta_metadata(np.array(old, np.int32),
+                                                     np.array(dl, np.int32), int(width[0]), L)
+        assert got_p.tolist() == [int(v) for v in pos], (line, got_p)
+        assert got_s.tolist() == [int(v) for v in seq], (line, got_s)
+        n += 1
+    assert n == 3
+
+
+def pin_delta_metadata_invariants(L):
+    """Each sequence owns a prefix of its block of width rows, of length
+    clamp(deltaLength, 0, width), at consecutive positions from its old
+    length; every other row is padding in both arrays."""
+    r = np.random.default_rng(160)
+    B, width = 37, 24
+    old = r.integers(0, 100000, B).astype(np.int32)
+    dl = r.integers(-3, width + 5, B).astype(np.int32)
+    pos, seq = oracle.prepare_delta_metadata(old, dl, width, L)
+    pos, seq = pos.reshape(B, width), seq.reshape(B, width)
+    for b in range(B):
+        k = min(max(int(dl[b]), 0), width)
+        assert np.array_equal(pos[b, :k], old[b] + np.arange(k)), b
+        assert np.all(seq[b, :k] == b) and np.all(pos[b, k:] == -1) and np.all(seq[b, k:] == -1)
+
+
+def pin_linear_tree_metadata(L):
+    """Node 0 is the root; each later node's parent is the previous node;
+    each depth is the number of parent steps to the root (walked here)."""
+    par, dep = oracle.linear_tree_metadata(3, 9, L)
+    for b in range(3):
+        assert par[b, 0] == -1
+        for i in range(1, 9):
+            assert par[b, i] == i - 1
+        for i in range(9):
+            steps, node = 0, i
+            while par[b, node] != -1:
+                node, steps = par[b, node], steps + 1
+            assert dep[b, i] == steps
+    p0, d0 = oracle.linear_tree_metadata(0, 5, L)
+    assert p0.size == 0 and d0.size == 0
+
+
+def pin_metadata_feeds_the_writes(L):
+    """The builders' outputs drive calls 3 and 4 exactly like the direct
+    positions: call 3 with tokenPosIds = end - S + linear depth equals call
+    2; call 4 fed by the delta metadata through an identity page table
+    writes what call 2 writes for the same tokens."""
+    r = np.random.default_rng(170)
+    B, S, Hq, Hkv, D = 3, 6, 2, 2, 64
+    qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+    table = W.rope_table(1, 64, D, 10000.0)
+    end = np.array([6, 40, 17], np.int32)
+    cache = W.sentinel_f16((B, 2, Hkv, 64, D))
+    c2, q2 = oracle.continuous(table, end, qkv, cache, W.sentinel_f16((B, S, Hq, D)), NEOX, L)
+    _, dep = oracle.linear_tree_metadata(B, S, L)
+    c3, q3 = oracle.tree(table, end, (end[:, None] - S + dep).astype(np.int32), qkv, cache,
+                         W.sentinel_f16((B, S, Hq, D)), NEOX, L)
+    assert np.array_equal(c2, c3) and np.array_equal(q2, q3)
+    old = (end - S).astype(np.int32)
+    pos, seq = oracle.prepare_delta_metadata(old, np.full(B, S, np.int32), S, L)
+    pt = np.empty((B, 2, 1), np.int32)
+    pt[:, 0, 0] = np.arange(B)
+    pt[:, 1, 0] = B + np.arange(B)
+    rows = table[0][np.maximum(pos, 0)]
+    pool = oracle.paged_delta(qkv[:, :, Hq:Hq + Hkv].reshape(B * S, Hkv, D),
+                              qkv[:, :, Hq + Hkv:].reshape(B * S, Hkv, D),
+                              W.sentinel_f16((2, B, 64, Hkv, D)), rows, pos, seq, pt, B, NEOX, L)
+    for b in range(B):
+        for plane in range(2):
+            assert np.array_equal(pool[plane, b].transpose(1, 0, 2), c2[b, plane]), (b, plane)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -85,6 +85,16 @@ MUTATIONS = {
     "norm_q_uses_k_weight_calls_2_3": ("               row, D, R, style, q_w, eps);",
                                        "               row, D, R, style, k_w, eps);"),
     "norm_nan_row_ignored": ("if (has_nan) return NAN;", ""),
+    # metadata builders
+    "delta_len_inclusive": ("if (j < len && pos <= INT32_MAX)", "if (j <= len && pos <= INT32_MAX)"),
+    "delta_overflow_unchecked": ("if (j < len && pos <= INT32_MAX)", "if (j < len)"),
+    "delta_position_off_by_one": ("int64_t pos = (int64_t)old_lengths[b] + j;",
+                                  "int64_t pos = (int64_t)old_lengths[b] + j + 1;"),
+    "delta_padding_owner_kept": ("        delta_to_seq[i] = -1;", "        delta_to_seq[i] = b;"),
+    "tree_root_parent_zero": ("parent_ids[(size_t)b * verify_size + i] = i - 1;",
+                              "parent_ids[(size_t)b * verify_size + i] = i > 0 ? i - 1 : 0;"),
+    "tree_depth_off_by_one": ("depths[(size_t)b * verify_size + i] = i;",
+                              "depths[(size_t)b * verify_size + i] = i + 1;"),
     "fp8_reciprocal_truncated": ("return (float)(1.0 / (double)scale);",
                                  "return (float)(1.0 / (double)scale) * (1.0f - 0x1p-23f);"),
 }
