@@ -522,10 +522,14 @@ def pin_skip_rules_paged(L):
     pool0 = W.sentinel_f16((2, P, 64, Hkv, D))
 
     def run(pos, seq, kid, vid):
-        pt = np.zeros((batch, 2, M), dtype=np.int32)
+        # the table has a row for one sequence beyond the active batch (the
+        # page's pageTable is [B, ...] while batchSize is the active count),
+        # holding valid ids, so that a row of an inactive sequence that were
+        # kept would write somewhere
+        pt = np.zeros((batch + 1, 2, M), dtype=np.int32)
         pt[:, 0, :] = 1
         pt[:, 1, :] = P + 1
-        if 0 <= seq < batch and 0 <= pos < M * 64:
+        if 0 <= seq <= batch and 0 <= pos < M * 64:
             pt[seq, 0, pos // 64] = kid
             pt[seq, 1, pos // 64] = vid
         out = oracle.paged_delta(k, v, pool0, cs, np.array([pos], np.int32),
