@@ -9,8 +9,9 @@ HIP events on its stream, which give the kernel's average duration for the
 roofline.  The same workload in the library's RKV_ROUND_EXACT mode and the
 other workloads (continuous write, tree write, paged delta update, the
 paged update with the cos/sin gather fused in, the prefill, continuous
-and paged calls into an E4M3 cache, and the prefill and continuous calls
-with Q/K RMS norm) are reported under "workloads".  The small workloads' inputs fit the 256 MB
+and paged calls into an E4M3 cache, the prefill and continuous calls
+with Q/K RMS norm, and the two device index builders) are reported under
+"workloads".  The small workloads' inputs fit the 256 MB
 MALL, so a 1 GiB buffer is read before each of their timed launches to push
 them back to HBM (a read leaves clean lines, so the timed kernel inherits no
 write-back); their event-bracketed times include the events' own overhead
@@ -156,6 +157,48 @@ def time_launches(w, t, steps, warmup, flush=None, exact=False):
         torch.cuda.synchronize()
     kernel_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
     return kernel_ms, wall
+
+
+def time_calls(fn, steps, warmup=3):
+    """Average duration of fn()'s launch, events on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        starts[k].record(stream)
+        fn()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+
+def metadata_builders(steps):
+    """The two device index builders on the paged workload's shape (32
+    sequences x 128 delta rows) and on a 16 x 64 linear verification tree."""
+    import torch
+    import rope_kv_cache_amd as rkv
+    r = np.random.default_rng(7200)
+    B, width = 32, 128
+    old = torch.from_numpy(r.integers(0, 8064, B).astype(np.int32)).cuda()
+    dl = torch.from_numpy(r.integers(100, 129, B).astype(np.int32)).cuda()
+    pos = torch.empty(B * width, dtype=torch.int32, device="cuda")
+    seq = torch.empty_like(pos)
+    d_ms = time_calls(lambda: rkv.dflash_prepare_delta_metadata(old, dl, width, pos, seq), steps)
+    par = torch.empty((16, 64), dtype=torch.int32, device="cuda")
+    dep = torch.empty_like(par)
+    t_ms = time_calls(lambda: rkv.dflash_build_linear_tree_metadata(par, dep), steps)
+    return {
+        "delta_metadata_b32_w128": {"kernel_us_events": d_ms * 1e3,
+                                    "algorithmic_bytes": 2 * B * 4 + 2 * B * width * 4,
+                                    "note": "launch-bound: 32 KB of output"},
+        "linear_tree_b16_v64": {"kernel_us_events": t_ms * 1e3,
+                                "algorithmic_bytes": 2 * 16 * 64 * 4,
+                                "note": "launch-bound: 8 KB of output"},
+    }
 
 
 def traffic_from_profile(kernel_name: str):
@@ -346,6 +389,10 @@ def main():
             del tx, x
             torch.cuda.empty_cache()
         del flush_buf
+        meta = metadata_builders(max(10, args.steps // 2))
+        for k, v in meta.items():
+            log(f"[bench] {k}: {v['kernel_us_events']:.2f} us")
+        extra.update(meta)
         result["workloads"] = extra
 
     if not args.no_cpu:

@@ -297,6 +297,40 @@ rkv_status rkv_apply_rope_write_kv_tree_qknorm(
     const float* qNormWeight, const float* kNormWeight, float epsilon, const float* kScale,
     const float* vScale, int32_t ropeStyle, hipStream_t stream);
 
+/* Device metadata builders
+ * ------------------------
+ * Delta metadata for call 4 (TensorRT-Edge-LLM C++ API, "Dflash Runtime
+ * Kernels", launchDFlashPrepareDeltaMetadata; the page gives the signature
+ * only, the reading here follows its proposal-input kernel, which places a
+ * sequence's delta right after its old draft cache length).
+ *   oldDraftCacheLengths  [in]  i32 [batchSize] draft cache length before the delta
+ *   deltaLengths          [in]  i32 [batchSize] delta tokens of each sequence
+ *   deltaWidth            rows reserved per sequence (token-major layout)
+ *   deltaPositions        [out] i32 [batchSize * deltaWidth]
+ *   deltaTokenToSequence  [out] i32 [batchSize * deltaWidth]
+ * Row b*deltaWidth + j is token j of sequence b's delta when
+ * j < min(deltaLengths[b], deltaWidth): position oldDraftCacheLengths[b] + j,
+ * owner b.  Every other row (and a position beyond the int32 range) is
+ * padding: -1 in both arrays, which call 4 skips.  Device pointers,
+ * 4-byte aligned; outputs may not overlap inputs or each other.  Nothing is
+ * enqueued when batchSize*deltaWidth is 0. */
+rkv_status rkv_dflash_prepare_delta_metadata(const int32_t* oldDraftCacheLengths,
+                                             const int32_t* deltaLengths, int32_t deltaWidth,
+                                             int32_t* deltaPositions,
+                                             int32_t* deltaTokenToSequence, int32_t batchSize,
+                                             hipStream_t stream);
+
+/* Tree metadata of a linear verification path (same page,
+ * launchDFlashBuildLinearTreeMetadata): for every sequence, node 0 is the
+ * root (parent -1, depth 0) and node i > 0 has parent i - 1 and depth i.
+ *   treeParentIds, treeDepths  [out] i32 [batchSize, verifySize], device,
+ *                              4-byte aligned, not overlapping.
+ * With these depths, call 3 at tokenPosIds = endLens[b] - S + depth writes
+ * exactly what call 2 writes. */
+rkv_status rkv_dflash_build_linear_tree_metadata(int32_t* treeParentIds, int32_t* treeDepths,
+                                                 int32_t batchSize, int32_t verifySize,
+                                                 hipStream_t stream);
+
 /* Host-only capacity check.
  * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
  *  checkDFlashRopeCapacity.)

@@ -21,6 +21,9 @@ Functions (same names as the C entry points, without the ``rkv_`` prefix):
   apply_rope_write_kv_tree_fp8(..., kv_cache, q_out, k_scale, v_scale, rope_style)
   dflash_target_kv_cache_update_fp8(k_delta, v_delta, kv_cache, k_scale, v_scale, ...)
   dflash_target_kv_cache_update_gather_rope_fp8(k_delta, v_delta, kv_cache, k_scale, v_scale, ...)
+  dflash_prepare_delta_metadata(old_draft_cache_lengths, delta_lengths, delta_width,
+                                delta_positions, delta_token_to_sequence)
+  dflash_build_linear_tree_metadata(tree_parent_ids, tree_depths)
   check_rope_capacity(cos_sin_seq_len, kv_capacity)
   tokens_per_page()
 
@@ -96,6 +99,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                       i32, P],
         "rkv_apply_rope_write_kv_tree_qknorm": [T, T, T, T, T, T, P, P, ctypes.c_float, P, P, i32,
                                                 P],
+        "rkv_dflash_prepare_delta_metadata": [P, P, i32, P, P, i32, P],
+        "rkv_dflash_build_linear_tree_metadata": [P, P, i32, i32, P],
         "rkv_check_rope_capacity": [i32, i32],
         "rkv_tokens_per_page": [],
         "rkv_last_error": [],
@@ -384,6 +389,39 @@ def dflash_target_kv_cache_update_gather_rope_fp8(k_delta, v_delta, kv_cache, k_
         _state_ptr(state_indices, batch_size), delta_positions.data_ptr(),
         delta_token_to_sequence.data_ptr(), page_table.data_ptr(), N, int(batch_size), Hkv, D, R,
         kv_cache.shape[1], page_table.shape[2], int(rope_style), _stream(dev)))
+
+
+def _int32_vec(t, n, name):
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous int32 tensor of {n} elements")
+
+
+def dflash_prepare_delta_metadata(old_draft_cache_lengths, delta_lengths, delta_width: int,
+                                  delta_positions, delta_token_to_sequence) -> None:
+    """Fill delta_positions / delta_token_to_sequence (int32 [B * delta_width])
+    from the per-sequence old lengths and delta lengths (int32 [B])."""
+    dev = _device_of(old_draft_cache_lengths, delta_lengths, delta_positions,
+                     delta_token_to_sequence)
+    B = old_draft_cache_lengths.numel()
+    _int32_vec(old_draft_cache_lengths, B, "old_draft_cache_lengths")
+    _int32_vec(delta_lengths, B, "delta_lengths")
+    _int32_vec(delta_positions, B * delta_width, "delta_positions")
+    _int32_vec(delta_token_to_sequence, B * delta_width, "delta_token_to_sequence")
+    _check(lib.rkv_dflash_prepare_delta_metadata(
+        old_draft_cache_lengths.data_ptr(), delta_lengths.data_ptr(), int(delta_width),
+        delta_positions.data_ptr(), delta_token_to_sequence.data_ptr(), B, _stream(dev)))
+
+
+def dflash_build_linear_tree_metadata(tree_parent_ids, tree_depths) -> None:
+    """Fill int32 [B, verify_size] parent ids and depths of a linear path."""
+    dev = _device_of(tree_parent_ids, tree_depths)
+    if tree_parent_ids.dim() != 2 or tree_depths.shape != tree_parent_ids.shape:
+        raise ValueError("tree_parent_ids and tree_depths must be [B, verify_size]")
+    B, V = tree_parent_ids.shape
+    _int32_vec(tree_parent_ids, B * V, "tree_parent_ids")
+    _int32_vec(tree_depths, B * V, "tree_depths")
+    _check(lib.rkv_dflash_build_linear_tree_metadata(tree_parent_ids.data_ptr(),
+                                                     tree_depths.data_ptr(), B, V, _stream(dev)))
 
 
 def check_rope_capacity(cos_sin_seq_len: int, kv_capacity: int) -> None:

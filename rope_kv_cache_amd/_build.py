@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "librkv.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("rkv_abi.hip", "rkv_kernels.hip",
                                             "rkv_kernels_fp8.hip", "rkv_kernels_norm.hip",
-                                            "rkv_kernels_norm_fp8.hip")]
+                                            "rkv_kernels_norm_fp8.hip", "rkv_meta.hip")]
 OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

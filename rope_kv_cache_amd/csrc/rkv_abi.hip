@@ -532,6 +532,56 @@ rkv_status rkv_apply_rope_write_kv_tree_qknorm(
                    qNormWeight, kNormWeight, epsilon, kScale, vScale, ropeStyle, stream);
 }
 
+rkv_status rkv_dflash_prepare_delta_metadata(const int32_t* oldDraftCacheLengths,
+                                             const int32_t* deltaLengths, int32_t deltaWidth,
+                                             int32_t* deltaPositions,
+                                             int32_t* deltaTokenToSequence, int32_t batchSize,
+                                             hipStream_t stream) {
+  clear_error();
+  if (batchSize < 0 || deltaWidth < 0) return fail(RKV_ERR_SHAPE, "negative size argument");
+  const long long rows = (long long)batchSize * deltaWidth;
+  if (rows > INT32_MAX) return fail(RKV_ERR_UNSUPPORTED, "batchSize*deltaWidth exceeds 2^31-1");
+  if (rows == 0) return RKV_OK;
+  if (!oldDraftCacheLengths || !deltaLengths || !deltaPositions || !deltaTokenToSequence)
+    return fail(RKV_ERR_NULL, "null metadata pointer");
+  const void* ptrs[] = {oldDraftCacheLengths, deltaLengths, deltaPositions, deltaTokenToSequence};
+  for (const void* q : ptrs)
+    if ((uintptr_t)q & 3u) return fail(RKV_ERR_ALIGNMENT, "metadata arrays must be 4-byte aligned");
+  auto span = [](const char* n, const void* q, long long bytes) {
+    return Span{n, (uintptr_t)q, (uintptr_t)q + (uintptr_t)bytes};
+  };
+  Span outs[] = {span("deltaPositions", deltaPositions, rows * 4),
+                 span("deltaTokenToSequence", deltaTokenToSequence, rows * 4)};
+  Span ins[] = {span("oldDraftCacheLengths", oldDraftCacheLengths, batchSize * 4LL),
+                span("deltaLengths", deltaLengths, batchSize * 4LL)};
+  rkv_status st;
+  if ((st = check_no_alias(outs, 2, ins, 2))) return st;
+  return launched(rkv::launch_delta_metadata(oldDraftCacheLengths, deltaLengths, deltaWidth,
+                                             deltaPositions, deltaTokenToSequence, (int32_t)rows,
+                                             stream));
+}
+
+rkv_status rkv_dflash_build_linear_tree_metadata(int32_t* treeParentIds, int32_t* treeDepths,
+                                                 int32_t batchSize, int32_t verifySize,
+                                                 hipStream_t stream) {
+  clear_error();
+  if (batchSize < 0 || verifySize < 0) return fail(RKV_ERR_SHAPE, "negative size argument");
+  const long long nodes = (long long)batchSize * verifySize;
+  if (nodes > INT32_MAX) return fail(RKV_ERR_UNSUPPORTED, "batchSize*verifySize exceeds 2^31-1");
+  if (nodes == 0) return RKV_OK;
+  if (!treeParentIds || !treeDepths) return fail(RKV_ERR_NULL, "null tree metadata pointer");
+  if (((uintptr_t)treeParentIds & 3u) || ((uintptr_t)treeDepths & 3u))
+    return fail(RKV_ERR_ALIGNMENT, "tree metadata arrays must be 4-byte aligned");
+  Span outs[] = {Span{"treeParentIds", (uintptr_t)treeParentIds,
+                      (uintptr_t)treeParentIds + (uintptr_t)(nodes * 4)},
+                 Span{"treeDepths", (uintptr_t)treeDepths,
+                      (uintptr_t)treeDepths + (uintptr_t)(nodes * 4)}};
+  rkv_status st;
+  if ((st = check_no_alias(outs, 2, nullptr, 0))) return st;
+  return launched(rkv::launch_linear_tree(treeParentIds, treeDepths, verifySize, (int32_t)nodes,
+                                          stream));
+}
+
 rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {
   clear_error();
   if (cosSinSeqLen > kvCapacity)

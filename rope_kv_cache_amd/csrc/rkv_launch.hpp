@@ -86,4 +86,12 @@ hipError_t launch_contig_norm_fp8(const ContigParams& p, int call, int D, int st
 hipError_t launch_paged_fp8(const PagedParams& p, int D, int style, bool exact, bool gather,
                             hipStream_t stream);
 
+// Index builders (rkv_meta.hip): rows = batch * width > 0, nodes = batch *
+// verify > 0, all pointers valid device arrays of that many int32.
+hipError_t launch_delta_metadata(const int32_t* old_lengths, const int32_t* delta_lengths,
+                                 int32_t width, int32_t* positions, int32_t* owners,
+                                 int32_t rows, hipStream_t stream);
+hipError_t launch_linear_tree(int32_t* parents, int32_t* depths, int32_t verify, int32_t nodes,
+                              hipStream_t stream);
+
 }  // namespace rkv

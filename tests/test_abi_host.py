@@ -570,3 +570,35 @@ def test_qknorm_binding_rejects_bad_weights():
     with pytest.raises(ValueError):
         rkv.apply_rope_write_kv_packed_qkv_qknorm(cs, qkv, cache, None, None, 1e-6,
                                                   rkv.ROPE_NEOX, k_scale=torch.ones(1))
+
+
+# ------------------------------------------------------ metadata builders ---
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), rkv.ERR_SHAPE), (dict(width=-1), rkv.ERR_SHAPE),
+    (dict(B=1 << 20, width=1 << 12), rkv.ERR_UNSUPPORTED), (dict(old=0), rkv.ERR_NULL),
+    (dict(pos=0), rkv.ERR_NULL), (dict(seq=(4 << 40) + 2), rkv.ERR_ALIGNMENT),
+    (dict(pos=(1 << 40) + 8), rkv.ERR_ALIAS),          # positions start inside old lengths
+    (dict(seq=(3 << 40) + 4 * 16 * 8 - 4), rkv.ERR_ALIAS),   # owners overlap positions' end
+    (dict(B=0), rkv.OK), (dict(width=0), rkv.OK), (dict(B=0, old=0, pos=0), rkv.OK),
+])
+def test_delta_metadata_validation(kw, want):
+    a = dict(old=1 << 40, dl=2 << 40, width=16, pos=3 << 40, seq=4 << 40, B=8)
+    a.update(kw)
+    st = L.rkv_dflash_prepare_delta_metadata(a["old"], a["dl"], a["width"], a["pos"], a["seq"],
+                                             a["B"], None)
+    assert st == want, (kw, rkv.status_string(st), L.rkv_last_error())
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), rkv.ERR_SHAPE), (dict(V=-2), rkv.ERR_SHAPE), (dict(par=0), rkv.ERR_NULL),
+    (dict(dep=(2 << 40) + 1), rkv.ERR_ALIGNMENT), (dict(dep=(1 << 40) + 64), rkv.ERR_ALIAS),
+    (dict(B=1 << 16, V=1 << 16), rkv.ERR_UNSUPPORTED), (dict(V=0), rkv.OK), (dict(B=0), rkv.OK),
+])
+def test_linear_tree_validation(kw, want):
+    a = dict(par=1 << 40, dep=2 << 40, B=4, V=64)
+    a.update(kw)
+    st = L.rkv_dflash_build_linear_tree_metadata(a["par"], a["dep"], a["B"], a["V"], None)
+    assert st == want, (kw, rkv.status_string(st), L.rkv_last_error())
