@@ -4,9 +4,9 @@ A step is one call of the library on the headline workload: empty-cache
 prefill of packed QKV in place, B=4, S=8192, Hq=64, Hkv=8, D=R=128, GPT-J,
 per-sequence cos/sin tables (1.43 GB of algorithmic traffic).  Inputs are
 seeded synthetic data already resident in HBM.  W warm-up steps, then K timed
-steps bracketed by device synchronisation; each launch is also bracketed by
-HIP events on its stream, which give the kernel's average duration for the
-roofline.  The same workload in the library's RKV_ROUND_EXACT mode and the
+steps back to back, bracketed by device synchronisation and by one pair of
+HIP events on the launch stream, whose span / K is the kernel's average
+duration for the roofline.  The same workload in the library's RKV_ROUND_EXACT mode and the
 other workloads (continuous write, tree write, paged delta update, the
 paged update with the cos/sin gather fused in, the prefill, continuous
 and paged calls into an E4M3 cache, the prefill and continuous calls
@@ -122,8 +122,15 @@ def algorithmic_bytes(w) -> int:
 # ----------------------------------------------------------------- timing --
 
 def time_launches(w, t, steps, warmup, flush=None, exact=False):
-    """Average kernel duration (events around each launch, on the launch
-    stream) and wall time per step between device synchronisations."""
+    """Kernel duration and wall time of `steps` launches.
+
+    Without `flush`: the launches run back to back on the current stream,
+    bracketed by one pair of HIP events and by device synchronisations, so
+    that nothing but the launches is timed; the kernel duration is the
+    events' span divided by the launch count (the gaps between back-to-back
+    launches, about a microsecond, are included).  With `flush` (small
+    workloads): a flush runs before each launch, so each launch has its own
+    pair of events (their overhead included)."""
     import torch
     from harness import launch as launch_exact
 
@@ -136,25 +143,26 @@ def time_launches(w, t, steps, warmup, flush=None, exact=False):
             flush()
         launch(w, t)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     wall = 0.0
     if flush is None:
-        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for k in range(steps):
-            starts[k].record(stream)
+        start.record(stream)
+        for _ in range(steps):
             launch(w, t)
-            ends[k].record(stream)
+        end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    else:
-        for k in range(steps):
-            flush()
-            starts[k].record(stream)
-            launch(w, t)
-            ends[k].record(stream)
-        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps, wall
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        flush()
+        starts[k].record(stream)
+        launch(w, t)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
     kernel_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
     return kernel_ms, wall
 
