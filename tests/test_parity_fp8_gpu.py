@@ -169,3 +169,56 @@ def test_fp8_cache_tensor_may_be_float8_typed():
                                            t["v_scale"], GPTJ | rkv.ROUND_EXACT)
     torch.cuda.synchronize()
     assert np.array_equal(host8(t["cache"]), want["cache"])
+
+
+@pytest.mark.parametrize("D,R,style,Hkv", [(64, 64, NEOX, 4), (64, 32, GPTJ, 3),
+                                           (128, 0, NEOX, 2), (256, 256, GPTJ, 2),
+                                           (256, 112, NEOX, 5)])
+def test_paged_shapes_fp8(D, R, style, Hkv):
+    w = W.paged(300, 7, Hkv, D, R, 64, 9, style, 7700 + D + R + Hkv, width=43, pad_frac=0.2,
+                bad_frac=0.2, name=f"paged_fp8_D{D}_R{R}_s{style}_H{Hkv}")
+    check(fp8(w, 7701 + D))
+
+
+def test_fp8_pool_beyond_4g_elements():
+    """An E4M3 pool of 5.2e9 bytes: the highest pages of both planes sit past
+    2^31 and 2^32 elements.  The oracle runs on the used pages renamed into a
+    compact pool; untouched pages are checked on the device."""
+    import rope_kv_cache_amd as rkv
+    Hkv, D, R, P, M, N = 8, 128, 128, 40000, 4, 48
+    r = np.random.default_rng(7800)
+    batch = N // 16
+    pos = np.tile(np.arange(16, dtype=np.int32) * 17 % (M * 64), batch)
+    seq = np.repeat(np.arange(batch, dtype=np.int32), 16)
+    k_ids = P - 1 - np.arange(batch * M)
+    v_ids = 2 * P - 1 - np.arange(batch * M)
+    pt = np.stack([k_ids.reshape(batch, M), v_ids.reshape(batch, M)], axis=1).astype(np.int32)
+    k_delta = W.normal_f16(r, (N, Hkv, D))
+    v_delta = W.normal_f16(r, (N, Hkv, D))
+    cs = W.rope_rows(pos, R, 10000.0)
+    used_k, used_v = np.sort(k_ids), np.sort(v_ids)
+    nc = used_k.size
+    cpt = np.empty_like(pt)
+    cpt[:, 0] = np.searchsorted(used_k, pt[:, 0])
+    cpt[:, 1] = nc + np.searchsorted(used_v, pt[:, 1])
+    small = np.full((2, nc, 64, Hkv, D), W.SENTINEL8, np.uint8)
+    want = oracle.paged_delta_fp8(k_delta, v_delta, small, cs, pos, seq, cpt, batch, W.K_SCALE,
+                                  W.V_SCALE, NEOX)
+    _say("[parity-fp8] E4M3 pool 5.2 GB")
+    pool = torch.full((2, P, 64, Hkv, D), W.SENTINEL8, dtype=torch.uint8, device="cuda")
+    ks = torch.tensor([W.K_SCALE], dtype=torch.float32, device="cuda")
+    vs = torch.tensor([W.V_SCALE], dtype=torch.float32, device="cuda")
+    rkv.dflash_target_kv_cache_update_fp8(dev(k_delta), dev(v_delta), pool, ks, vs, dev(cs),
+                                          dev(pos), dev(seq), dev(pt), batch,
+                                          NEOX | rkv.ROUND_EXACT)
+    torch.cuda.synchronize()
+    flat = pool.view(2 * P, 64 * Hkv * D)
+    touched = (flat != W.SENTINEL8).any(dim=1).nonzero().flatten().cpu().numpy()
+    assert set(touched.tolist()) <= set(used_k.tolist()) | set(used_v.tolist())
+    wflat = want.reshape(2 * nc, 64, Hkv, D)
+    for plane, used in ((0, used_k), (1, used_v)):
+        for rank, pid in enumerate(used):
+            g = host8(pool.view(2 * P, 64, Hkv, D)[pid])
+            assert np.array_equal(g, wflat[plane * nc + rank]), (plane, pid)
+    del pool
+    torch.cuda.empty_cache()
