@@ -301,7 +301,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "call": "packed QKV prefill, in place", "B": w.B,
                    "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "R": w.R, "style": "gptj",
