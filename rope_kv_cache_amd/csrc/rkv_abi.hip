@@ -30,9 +30,11 @@ void clear_error() { g_err[0] = '\0'; }
 // arithmetic per byte (exact mode, E4M3 cache, Q/K norm) run faster with at
 // least two, whose loads are in flight together while the wave computes
 // (measured on the large prefill: 236 -> 221 us with an E4M3 cache, 266 ->
-// 241 us with Q/K norm, 272 -> 247 us exact).  Small launches are
-// latency-bound, so they take G = 2 or 4 when that keeps every wave
-// resident at once (256 CUs x 4 SIMDs x 8 waves).
+// 241 us with Q/K norm, 272 -> 247 us exact; four were no better).  Small
+// launches are latency-bound, so they take G = 2 or 4 when that keeps every
+// wave resident at once (256 CUs x 4 SIMDs x 8 waves); there the Q/K-norm
+// kernel, with the longest chain between load and store, starts from four
+// (12.8 -> 11.9 us on the continuous workload; four slowed the E4M3 ones).
 constexpr long long kResidentWaves = 8192;
 constexpr long long kStreamingGroups = 65536;
 
@@ -117,13 +119,16 @@ struct Split {
   int32_t waves_per_item;
 };
 
-// Returns G = 0 when the wave count would not fit in int32.  `heavy`: the
-// kernel does more arithmetic per byte; it starts from G = 2 when a work
-// item has two row groups or more.
-Split pick_split(long long items, long long groups_per_item, bool heavy) {
+// Returns G = 0 when the wave count would not fit in int32.  g_large /
+// g_small: the row groups per wave a kernel starts from in large and small
+// launches (capped by the row groups a work item has).
+Split pick_split(long long items, long long groups_per_item, int g_large, int g_small) {
   auto waves = [&](int g) { return items * ((groups_per_item + g - 1) / g); };
-  int g = (heavy && groups_per_item >= 2) ? 2 : 1;
-  if (items * groups_per_item <= kStreamingGroups) {
+  const bool small = items * groups_per_item <= kStreamingGroups;
+  const int start = small ? g_small : g_large;
+  int g = 1;
+  while (g < start && 2 * g <= groups_per_item) g *= 2;
+  if (small) {
     while (g < 4 && waves(g) > kResidentWaves) g *= 2;
   }
   while (g < 4 && waves(g) > INT32_MAX) g *= 2;
@@ -262,8 +267,9 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.table_len = (int32_t)TL;
   p.R = (int32_t)R;
   const long long rows_per_group = 512 / D;
-  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group,
-                              exact_of(style) || fp8 || norm != nullptr);
+  const bool heavy = exact_of(style) || fp8 || norm != nullptr;
+  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, heavy ? 2 : 1,
+                              norm ? 4 : (heavy ? 2 : 1));
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_token = sp.waves_per_item;
@@ -358,8 +364,9 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.num_pages = numPages;
   p.max_pages = maxPagesPerSeq;
   const long long rows_per_group = 512 / D;
-  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group,
-                              exact_of(ropeStyle) || fp8);
+  const int g_start = (exact_of(ropeStyle) || fp8) ? 2 : 1;
+  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group, g_start,
+                              g_start);
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_row = sp.waves_per_item;
