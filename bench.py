@@ -20,6 +20,7 @@ of a few microseconds, so rocprofv3's kernel trace is the reference there.
 Prints one JSON line on stdout; progress goes to stderr.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+                      [--calib] [--floors]
 """
 from __future__ import annotations
 
@@ -209,6 +210,47 @@ def metadata_builders(steps):
     }
 
 
+def floors(steps):
+    """Lower bounds for the small workloads on this chip, timed like them (a
+    1 GiB read before each launch pushes the inputs out of the MALL): a
+    plain device copy moving the paged workload's bytes (15.2 MB read, 15.2
+    MB written) and a near-empty kernel (one fp32 zeroed)."""
+    import torch
+    import workloads as W
+    flush_buf = torch.ones(1 << 29, dtype=torch.float16, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        torch.sum(flush_buf, dim=0, dtype=torch.float32, out=flush_sink)
+
+    half = algorithmic_bytes(W.config(4)) // 2
+    src = torch.ones(half // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    tiny = torch.ones(1, dtype=torch.float32, device="cuda")
+    out = {}
+    for label, fn, nbytes in (("copy_paged_bytes", lambda: dst.copy_(src), 2 * src.numel() * 2),
+                              ("near_empty_kernel", lambda: tiny.zero_(), 4)):
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for k in range(steps):
+            flush()
+            st[k].record(stream)
+            fn()
+            en[k].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in zip(st, en)]))
+        out[label] = {"kernel_us_events": ms * 1e3, "bytes": nbytes,
+                      "GB/s": nbytes / (ms * 1e-3) / 1e9}
+        log(f"[bench] floor {label}: {ms * 1e3:.2f} us by events")
+    return {"floors": out, "note": "event-bracketed single launches after a 1 GiB read; "
+                                   "rocprofv3 kernel durations are the reference"}
+
+
 def traffic_from_profile(kernel_name: str):
     """HBM bytes per launch measured with rocprofv3 counters, if the recorded
     kernel source still matches the current one."""
@@ -261,6 +303,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--floors", action="store_true",
+                    help="only time the floors of the small workloads: a torch copy moving the "
+                         "paged workload's bytes and a near-empty kernel, each after the same "
+                         "MALL flush")
     ap.add_argument("--calib", action="store_true",
                     help="also run a 1 GiB elementwise copy (1 GiB read + 1 GiB written per "
                          "launch) to scale HBM byte counters")
@@ -279,6 +325,9 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     log(f"[bench] device: {torch.cuda.get_device_name(0)}")
+    if args.floors:
+        print(json.dumps(floors(max(10, args.steps // 2))), flush=True)
+        return
 
     log("[bench] generating the headline workload")
     w = W.config(HEADLINE)
