@@ -1,0 +1,73 @@
+"""bench.py on the host: its algorithmic byte counts (the numerator of every
+roofline figure) against closed forms written out by hand, and its refusal
+of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as W  # noqa: E402
+
+
+def _headline():
+    """The large prefill's shapes only (the byte count needs no data)."""
+    return W.Contig("packed", W.GPTJ, 4, 8192, 64, 8, 128, 128, 16384,
+                    np.empty((4, 8192, 128), np.float32), None, None,
+                    name="prefill_b4_s8192_h64_d128")
+
+
+def test_headline_bytes():
+    """Large prefill: per token, 80 head rows of 256 B read, 72 rotated rows
+    written in place, 16 cache rows written; each of the 4 x 8192 table rows
+    (512 B) read once."""
+    w = _headline()
+    per_token = 80 * 256 + 72 * 256 + 16 * 256
+    assert bench.algorithmic_bytes(w) == 32768 * per_token + 32768 * 512 == 1426063360
+
+
+def test_variant_bytes():
+    w = _headline()
+    w.cache = np.empty(0, np.uint16)
+    w.extra["fp8"] = {"k_scale": np.float32(1), "v_scale": np.float32(1)}
+    # cache rows of 128 B instead of 256 B, plus the two 4-byte scales
+    assert bench.algorithmic_bytes(w) == 32768 * (80 * 256 + 72 * 256 + 16 * 128) \
+        + 32768 * 512 + 8
+    w = _headline()
+    w.extra["qknorm"] = {"q_weight": np.ones(128, np.float32), "k_weight": np.ones(128, np.float32),
+                         "eps": 1e-6}
+    # plus the two fp32 weight vectors of 128 entries
+    assert bench.algorithmic_bytes(w) == 1426063360 + 2 * 128 * 4
+
+
+def test_paged_bytes_by_row():
+    """Paged workload: the per-row rule applied row by row in a plain loop.
+    (The workload's metadata with a sentinel-filled pool: the pool is drawn
+    last, so the index arrays are those of the benchmarked workload.)"""
+    w = W.paged(4096, 32, 8, 128, 128, 8192, 128, W.NEOX, 1004, pool_fill="sentinel")
+    row = w.Hkv * w.D * 2
+    total = 0
+    for i in range(w.N):
+        p, q = int(w.positions[i]), int(w.seq[i])
+        total += 8                                    # its position and sequence
+        if p < 0 or q < 0 or q >= w.batch or p >= w.max_pages * 64:
+            continue
+        total += 8                                    # its two page-table entries
+        kid = int(w.page_table[q, 0, p // 64])
+        vid = int(w.page_table[q, 1, p // 64])
+        if 0 <= kid < w.num_pages:
+            total += 2 * row + w.R * 4                # K read + written, cos/sin row
+        if w.num_pages <= vid < 2 * w.num_pages:
+            total += 2 * row                          # V read + written
+    assert bench.algorithmic_bytes(w) == total == 30381456
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
