@@ -327,6 +327,8 @@ def with_qk_norm(w, seed: int, eps: float = 1e-6, q_weight=True, k_weight=True, 
 
 
 def _fill(r, shape, how):
+    if how == "none":   # no cache / pool: for callers that need only the index arrays
+        return np.empty((0,), dtype=np.uint16)
     if how == "sentinel":
         return sentinel_f16(shape)
     if how == "normal":
