@@ -342,6 +342,16 @@ rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity);
 /* Tokens per page of the paged pool: 64. */
 int32_t rkv_tokens_per_page(void);
 
+/* Row groups per wave (1, 2 or 4) of the kernel that this thread's most
+ * recent rope / KV-cache call (calls 1-4 and their fp8 and Q/K-norm forms)
+ * launched; 0 when that call launched nothing (an error, or an input with
+ * no rows).  The metadata builders and the capacity check reset it to 0;
+ * the other query functions leave it.  A row group is the 1 KB of
+ * 512/headDim consecutive head rows that one wave instruction moves.  The
+ * choice depends on the sizes and the kernel flavour only, never on data;
+ * it is reported for tests and tuning and has no effect on results. */
+int32_t rkv_last_launch_groups_per_wave(void);
+
 /* Message for the last error raised on this thread ("" if none).  The
  * pointer stays valid until the next call on the same thread. */
 const char* rkv_last_error(void);

@@ -26,6 +26,7 @@ Functions (same names as the C entry points, without the ``rkv_`` prefix):
   dflash_build_linear_tree_metadata(tree_parent_ids, tree_depths)
   check_rope_capacity(cos_sin_seq_len, kv_capacity)
   tokens_per_page()
+  last_launch_groups_per_wave()
 
   apply_rope_write_kv_packed_qkv_qknorm(cos_sin_cache, qkv, kv_cache, q_norm_weight, k_norm_weight,
                                         epsilon, rope_style, k_scale=None, v_scale=None)
@@ -103,6 +104,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rkv_dflash_build_linear_tree_metadata": [P, P, i32, i32, P],
         "rkv_check_rope_capacity": [i32, i32],
         "rkv_tokens_per_page": [],
+        "rkv_last_launch_groups_per_wave": [],
         "rkv_last_error": [],
         "rkv_status_string": [i32],
     }
@@ -430,3 +432,9 @@ def check_rope_capacity(cos_sin_seq_len: int, kv_capacity: int) -> None:
 
 def tokens_per_page() -> int:
     return lib.rkv_tokens_per_page()
+
+
+def last_launch_groups_per_wave() -> int:
+    """Row groups per wave (1, 2 or 4) of the kernel this thread's last
+    rope / KV-cache call launched; 0 if it launched none."""
+    return lib.rkv_last_launch_groups_per_wave()

@@ -13,6 +13,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local int32_t g_last_groups = 0;   // row groups per wave of this thread's last launch
 
 rkv_status fail(rkv_status st, const char* fmt, ...) {
   va_list ap;
@@ -22,7 +23,10 @@ rkv_status fail(rkv_status st, const char* fmt, ...) {
   return st;
 }
 
-void clear_error() { g_err[0] = '\0'; }
+void clear_error() {
+  g_err[0] = '\0';
+  g_last_groups = 0;
+}
 
 // Launch shape.  A wave handles G row groups (512/D rows each) of one work
 // item.  Large launches are bandwidth-bound: the plain binary32 kernel runs
@@ -137,7 +141,10 @@ Split pick_split(long long items, long long groups_per_item, int g_large, int g_
 }
 
 rkv_status launched(hipError_t e) {
-  if (e != hipSuccess) return fail(RKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) {
+    g_last_groups = 0;
+    return fail(RKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
   return RKV_OK;
 }
 
@@ -278,6 +285,7 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.div_seq = rkv::make_fastdiv((uint32_t)S);
   const int lay = layout_of(style);
   const bool ex = exact_of(style);
+  g_last_groups = p.groups_per_wave;
   if (norm)
     return launched(fp8 ? rkv::launch_contig_norm_fp8(p, call, (int)D, lay, ex, stream)
                         : rkv::launch_contig_norm(p, call, (int)D, lay, ex, stream));
@@ -372,6 +380,7 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.waves_per_row = sp.waves_per_item;
   p.total_waves = (int32_t)(N * p.waves_per_row);
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
+  g_last_groups = p.groups_per_wave;
   return launched(fp8 ? rkv::launch_paged_fp8(p, headDim, layout_of(ropeStyle),
                                               exact_of(ropeStyle), gather, stream)
                       : rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle),
@@ -598,6 +607,8 @@ rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {
 }
 
 int32_t rkv_tokens_per_page(void) { return rkv::kTokensPerPage; }
+
+int32_t rkv_last_launch_groups_per_wave(void) { return g_last_groups; }
 
 const char* rkv_last_error(void) { return g_err; }
 

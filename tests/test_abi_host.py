@@ -45,7 +45,7 @@ def test_header_declares_the_calls():
     for want in ["rkv_apply_rope_write_kv_packed_qkv", "rkv_apply_rope_write_kv_continuous",
                  "rkv_apply_rope_write_kv_tree", "rkv_dflash_target_kv_cache_update",
                  "rkv_check_rope_capacity", "rkv_tokens_per_page", "rkv_last_error",
-                 "rkv_status_string"]:
+                 "rkv_status_string", "rkv_last_launch_groups_per_wave"]:
         assert want in names
 
 
@@ -200,6 +200,7 @@ def test_packed_validation(case, want):
     st = call_packed(cs, qkv, cache, style)
     assert st == want, (case, rkv.status_string(st), L.rkv_last_error())
     assert L.rkv_last_error() != b""
+    assert rkv.last_launch_groups_per_wave() == 0
 
 
 @no_gpu
@@ -207,6 +208,7 @@ def test_packed_empty_is_ok_without_launch():
     for B, S in [(0, 8), (2, 0)]:
         cs, qkv, cache = packed_args(B=B, S=S)
         assert call_packed(cs, qkv, cache) == rkv.OK
+        assert rkv.last_launch_groups_per_wave() == 0
     # zero heads: nothing to do
     cs, qkv, cache = packed_args(Hq=0, Hkv=0)
     assert call_packed(cs, qkv, cache) == rkv.OK

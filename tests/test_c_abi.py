@@ -34,6 +34,7 @@ int main(void) {
                                                 RKV_ROPE_GPTJ | RKV_ROUND_EXACT, NULL)
       != RKV_ERR_DTYPE)
     return 10;
+  if (rkv_last_launch_groups_per_wave() != 0) return 11;   /* nothing was launched */
   printf("c abi ok\n");
   return 0;
 }

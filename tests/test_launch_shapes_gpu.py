@@ -1,0 +1,115 @@
+"""Every launch shape of every kernel flavour against the CPU oracle.
+
+The library picks how many 1 KB row groups a wave handles (1, 2 or 4) from
+the launch's size and the kernel flavour; each choice is a separate kernel
+instantiation.  For each call and flavour these tests run a ladder of sizes
+(a few tokens; about 12 k and 24 k row groups, where a small launch doubles
+the groups per wave to keep every wave resident; about 80 k row groups,
+where large launches start from their streaming choice; and a large launch
+whose tokens have a single row group), read the choice back through
+``rkv_last_launch_groups_per_wave`` and hold every launch to the parity bar
+of the other GPU tests: bit-identical with RKV_ROUND_EXACT, within one fp16
+ulp (one E4M3 code step) in the default mode.  The ladder must reach all
+three choices in each mode, so a change of the launch rule that strands an
+instantiation fails here instead of going untested.
+"""
+import pytest
+
+import rope_kv_cache_amd as rkv
+import workloads as W
+from harness import compare, download, exact_diffs, expected, launch, upload
+
+pytestmark = pytest.mark.gpu
+
+NEOX, GPTJ = W.NEOX, W.GPTJ
+MODES = ("fast", "exact")
+
+# name, B, S, Hq, Hkv, D, R, style
+CONTIG_LADDER = [
+    ("tiny", 2, 16, 9, 2, 128, 128, NEOX),
+    ("groups12k", 3, 1000, 9, 2, 128, 64, GPTJ),
+    ("groups24k", 4, 1500, 9, 2, 128, 128, GPTJ),
+    ("groups80k", 4, 5000, 9, 2, 128, 64, NEOX),
+    ("one_group_70k", 4, 17500, 4, 2, 64, 64, GPTJ),
+]
+
+# name, N, batch, Hkv, D, R, maxPagesPerSeq, style (numPages = batch * maxPages)
+PAGED_LADDER = [
+    ("tiny", 64, 2, 5, 128, 128, 2, NEOX),
+    ("groups9k", 3000, 6, 5, 128, 64, 16, GPTJ),
+    ("groups18k", 6000, 12, 5, 128, 128, 16, NEOX),
+    ("groups75k", 25000, 50, 5, 128, 128, 16, GPTJ),
+    ("one_group_70k", 70000, 70, 2, 128, 128, 16, NEOX),
+]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _contig(call, name, B, S, Hq, Hkv, D, R, style, seed):
+    cap = S + 64
+    label = f"{call}_{name}"
+    if call == "packed":
+        return W.packed(B, S, Hq, Hkv, D, R, cap, style, seed, name=label)
+    if call == "continuous":
+        return W.continuous(B, S, Hq, Hkv, D, R, cap, style, seed, S, cap, name=label)
+    return W.tree(B, S, Hq, Hkv, D, R, cap, style, seed, S, cap, name=label)
+
+
+def _flavoured(w, flavour, seed):
+    if flavour in ("norm", "norm_fp8"):
+        W.with_qk_norm(w, seed + 1, scale=2.0)
+    if flavour in ("fp8", "norm_fp8"):
+        W.with_fp8_cache(w, seed + 2, fill="sentinel")
+    return w
+
+
+def _run_ladder(workloads, flavour):
+    """Parity of every workload in both modes; returns {mode: set of G}."""
+    seen = {m: set() for m in MODES}
+    for w in workloads:
+        want = expected(w)
+        for mode in MODES:
+            t = upload(w)
+            launch(w, t, exact=(mode == "exact"))
+            g = rkv.last_launch_groups_per_wave()
+            got = download(w, t)
+            del t
+            rep = compare(w, got, want)
+            _say(f"[shapes] {w.name} {flavour} {mode}: G={g} {rep}")
+            assert g in (1, 2, 4), g
+            seen[mode].add(g)
+            if mode == "exact":
+                assert not exact_diffs(rep), f"exact mode not bit-identical: {rep}"
+            else:
+                keys = ("_max_ulp_ge_2m6", "_max_code_step") if "norm" in flavour else \
+                    ("_max_ulp", "_max_code_step")
+                assert all(v <= 1 for k, v in rep.items() if k.endswith(keys)), rep
+    return seen
+
+
+@pytest.mark.parametrize("flavour", ["fp16", "fp8", "norm", "norm_fp8"])
+@pytest.mark.parametrize("call", ["packed", "continuous", "tree"])
+def test_contig_launch_shapes(call, flavour):
+    ws = (_flavoured(_contig(call, *row, 9000 + 10 * k), flavour, 9000 + 10 * k)
+          for k, row in enumerate(CONTIG_LADDER))
+    seen = _run_ladder(ws, flavour)
+    for mode in MODES:
+        assert seen[mode] == {1, 2, 4}, (mode, seen)
+
+
+@pytest.mark.parametrize("flavour", ["fp16", "fp8"])
+@pytest.mark.parametrize("gather", [False, True], ids=["table_rows", "gather_fused"])
+def test_paged_launch_shapes(gather, flavour):
+    def make(k, name, N, batch, Hkv, D, R, max_pages, style):
+        seed = 9500 + 10 * k
+        label = f"paged_{'gather_' if gather else ''}{name}"
+        args = (N, batch, Hkv, D, R, batch * max_pages, max_pages, style, seed)
+        w = W.paged_gather(*args, rope_states=2, name=label) if gather else \
+            W.paged(*args, name=label)
+        return _flavoured(w, flavour, seed)
+
+    seen = _run_ladder((make(k, *row) for k, row in enumerate(PAGED_LADDER)), flavour)
+    for mode in MODES:
+        assert seen[mode] == {1, 2, 4}, (mode, seen)
