@@ -3,7 +3,9 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It wraps ``liboracle_rkv.so`` (plain C,
 ``rkv_oracle.c``) with numpy marshalling: every wrapper copies its inputs and
-returns fresh output arrays, so a caller's arrays are never modified.
+returns fresh output arrays, so a caller's arrays are never modified -- except
+``packed_qkv_in_place``, which hands the caller's arrays to the C call as they
+are (for timing the oracle's own work, without the copies).
 
 fp16 arrays are ``uint16`` bit patterns; fp8 (E4M3) caches are ``uint8``
 bit patterns; tables and scales are ``float32``; index arrays are ``int32``.  The wrappers derive sizes from array shapes the same way the
@@ -189,6 +191,23 @@ def packed_qkv(cos_sin, qkv, cache, style: int, L=None):
     if rc:
         raise OracleError(rc, "packed_qkv")
     return qkv, cache
+
+
+def packed_qkv_in_place(cos_sin, qkv, cache, style: int, L=None) -> None:
+    """Call 1 on the caller's own arrays: ``qkv`` and ``cache`` are
+    overwritten.  The arrays must already be C-contiguous with the oracle's
+    dtypes (nothing is copied or converted)."""
+    for name, a, dt in (("cos_sin", cos_sin, np.float32), ("qkv", qkv, np.uint16),
+                        ("cache", cache, np.uint16)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise ValueError(f"{name} must be a C-contiguous {np.dtype(dt).name} array")
+    tb, tlen, R = cos_sin.shape
+    B, S, H, D = qkv.shape
+    Hkv, cap = cache.shape[2], cache.shape[3]
+    rc = (L or lib()).rkv_ref_packed_qkv(_p(cos_sin), tb, tlen, R, _p(qkv), B, S, H - 2 * Hkv,
+                                         Hkv, D, _p(cache), cap, style)
+    if rc:
+        raise OracleError(rc, "packed_qkv_in_place")
 
 
 def continuous(cos_sin, end_lens, qkv, cache, q_out, style: int, L=None):
