@@ -177,12 +177,14 @@ def packed(B, S, Hq, Hkv, D, R, cap, style, seed, table_batch=1, table_len=None,
 
 
 def continuous(B, S, Hq, Hkv, D, R, cap, style, seed, end_lo, end_hi, theta=10000.0,
-               table_len=None, cache_fill="normal", name="") -> Contig:
+               table_len=None, cache_fill="normal", table_batch=1, name="") -> Contig:
+    """Call-2 inputs.  ``table_batch`` B gives each sequence its own table
+    (sequence b's positions offset by 5*b), 1 a shared one."""
     r = rng(seed)
     tlen = cap if table_len is None else table_len
     qkv = normal_f16(r, (B, S, Hq + 2 * Hkv, D))
     end = r.integers(end_lo, end_hi + 1, size=B).astype(np.int32)
-    cos_sin = rope_table(1, tlen, R, theta)
+    cos_sin = rope_table(table_batch, tlen, R, theta, offsets=5 * np.arange(table_batch))
     cache = _fill(r, (B, 2, Hkv, cap, D), cache_fill)
     q_out = sentinel_f16((B, S, Hq, D))
     return Contig("continuous", style, B, S, Hq, Hkv, D, R, cap, cos_sin, qkv, cache,
@@ -190,14 +192,16 @@ def continuous(B, S, Hq, Hkv, D, R, cap, style, seed, end_lo, end_hi, theta=1000
 
 
 def tree(B, S, Hq, Hkv, D, R, cap, style, seed, end_lo, end_hi, theta=10000.0,
-         max_depth=8, cache_fill="normal", name="") -> Contig:
+         max_depth=8, cache_fill="normal", table_batch=1, name="") -> Contig:
+    """Call-3 inputs: one seeded random tree per sequence, positions
+    end - S + depth; ``table_batch`` as for ``continuous``."""
     r = rng(seed)
     qkv = normal_f16(r, (B, S, Hq + 2 * Hkv, D))
     end = r.integers(end_lo, end_hi + 1, size=B).astype(np.int32)
     pos = np.empty((B, S), dtype=np.int32)
     for b in range(B):
         pos[b] = end[b] - S + random_tree_depths(r, S, max_depth)
-    cos_sin = rope_table(1, cap, R, theta)
+    cos_sin = rope_table(table_batch, cap, R, theta, offsets=5 * np.arange(table_batch))
     cache = _fill(r, (B, 2, Hkv, cap, D), cache_fill)
     q_out = sentinel_f16((B, S, Hq, D))
     return Contig("tree", style, B, S, Hq, Hkv, D, R, cap, cos_sin, qkv, cache,
