@@ -445,7 +445,13 @@ __device__ __forceinline__ WideT<kExact> row_rms_reciprocal(uint4 x, float eps) 
 
 // x*c + sign*(p*s) for values that are not fp16 (normalised rows).  Exact
 // mode: each product and the sum rounded once in binary64, no contraction.
-// Default mode: the same compensated binary32 evaluation as rot1_wide.
+// Default mode: one fused multiply-add over the rounded product p*s.  The
+// normalised inputs already carry two binary32 roundings each, so the
+// compensation term of rot1_wide (exact for fp16 inputs) would not tighten
+// the result; without it the large prefill with Q/K norm runs about 3%
+// faster (measured on MI355X: 248 -> 240 us median).  Where |result| >=
+// 2^-6 the error stays far below half an fp16 ulp, so the fp16 result is
+// the correctly rounded one or its neighbour.
 template <bool kExact>
 __device__ __forceinline__ WideT<kExact> rot1_general(WideT<kExact> x, WideT<kExact> p, float c,
                                                       float s, bool first) {
@@ -455,10 +461,7 @@ __device__ __forceinline__ WideT<kExact> rot1_general(WideT<kExact> x, WideT<kEx
     const double b = p * (double)s;
     return first ? a - b : a + b;
   } else {
-    const float sv = first ? -s : s;
-    const float ps = p * sv;
-    const float e = __builtin_fmaf(p, sv, -ps);
-    return __builtin_fmaf(x, c, ps) + e;
+    return __builtin_fmaf(x, c, p * (first ? -s : s));
   }
 }
 
