@@ -21,9 +21,9 @@
 //
 // Q/K RMS norm (kNorm, calls 1-3).  Same decomposition; each Q or K row
 // with a weight vector is normalised before its rotation: the lanes of a row
-// reduce its sum of squares, each lane scales its own 8 values (and, for a
-// NeoX rotary lane, its partner's 8 values, fetched as fp16 bits) by
-// 1/rms and the per-dimension weights.
+// reduce its sum of squares and each lane scales its own 8 values by 1/rms
+// and the per-dimension weights (loaded once per wave); a NeoX rotary lane
+// takes its partner's normalised values from the partner lane.
 //
 // This header holds the kernel templates; rkv_kernels.hip instantiates the
 // fp16-cache kernels, rkv_kernels_fp8.hip the fp8-cache ones and
@@ -140,17 +140,22 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
     load_cos_sin<kStyle>(p.cos_sin + ((size_t)tb * p.table_len + pos) * p.R, role.freq0, p.R,
                          cs, sn);
   }
-  // norm: each row's weights (its own dims, and a NeoX partner's), requested
-  // with the cos/sin loads
-  float nws[G][8] = {}, nwp[G][8] = {};
+  // norm: the weights of the lane's chunk for the Q rows and for the K rows
+  // among this wave's rows (the chunk index is the same in every row group),
+  // requested once per wave with the cos/sin loads
+  float qws[8] = {}, qwp[8] = {}, kws[8] = {}, kwp[8] = {};
   bool normed[G] = {};
   if constexpr (kNorm) {
+    const int r_lo = part * G * kRowsPerGroup, r_end = r_lo + G * kRowsPerGroup;
+    if (p.q_norm_w && r_lo < p.Hq)
+      load_norm_weights<kStyle, kExact>(p.q_norm_w, c, role, qws, qwp);
+    if (p.k_norm_w && r_lo < p.Hq + p.Hkv && r_end > p.Hq)
+      load_norm_weights<kStyle, kExact>(p.k_norm_w, c, role, kws, kwp);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int r = row[g];
       const float* wsrc = r < p.Hq ? p.q_norm_w : (r < p.Hq + p.Hkv ? p.k_norm_w : nullptr);
       normed[g] = wsrc != nullptr && r < H;
-      if (normed[g]) load_norm_weights<kStyle>(wsrc, c, role, nws[g], nwp[g]);
     }
   }
   // fp8: the scales, read while the row and cos/sin loads are in flight
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
       if constexpr (kNorm) {
         const WideT<kExact> rr = row_rms_reciprocal<D, kExact>(x[g], p.eps);
         comp = rotate_chunk_norm<kStyle, kExact>(x[g], lane, role, is_q || is_k, normed[g], rr,
-                                                 nws[g], nwp[g], cs, sn, w);
+                                                 is_q ? qws : kws, is_q ? qwp : kwp, cs, sn, w);
       } else {
         comp = rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn, w);
       }

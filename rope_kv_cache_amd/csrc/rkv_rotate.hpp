@@ -465,16 +465,17 @@ __device__ __forceinline__ WideT<kExact> rot1_general(WideT<kExact> x, WideT<kEx
   }
 }
 
-// The weights a lane needs: its own 8 dims and, for a NeoX rotary lane, its
-// partner chunk's 8 dims.
-template <int kStyle>
+// The weights a lane needs: its own 8 dims and, for a NeoX rotary lane in
+// exact mode, its partner chunk's 8 dims (the default mode fetches the
+// partner's normalised values from the partner lane instead).
+template <int kStyle, bool kExact>
 __device__ __forceinline__ void load_norm_weights(const float* w, int c, const ChunkRole& role,
                                                   float (&ws)[8], float (&wp)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(w + 8 * c);
   const float4 b = *reinterpret_cast<const float4*>(w + 8 * c + 4);
   ws[0] = a.x; ws[1] = a.y; ws[2] = a.z; ws[3] = a.w;
   ws[4] = b.x; ws[5] = b.y; ws[6] = b.z; ws[7] = b.w;
-  if constexpr (kStyle == kNeox) {
+  if constexpr (kStyle == kNeox && kExact) {
     if (role.rotary) {
       const int pc = c + role.partner;
       const float4 e = *reinterpret_cast<const float4*>(w + 8 * pc);
@@ -489,6 +490,13 @@ __device__ __forceinline__ void load_norm_weights(const float* w, int c, const C
 // (normed rows; else n = x), rotated when rotate_row and the chunk is
 // rotary.  Returns whether the output must be rounded from w (rotated or
 // normalised) rather than copied from x.  Called by every lane.
+//
+// NeoX partners: in the default mode the partner lane's own n values are
+// fetched (8 binary32 values by ds_bpermute).  Every lane of a row holds
+// the same 1/rms and the partner lane applies the same formula with its own
+// weights, so these are bit for bit the values this lane would compute, and
+// no partner weights are needed.  Exact mode fetches the partner's fp16 bits
+// and normalises them here with the partner's weights (wp).
 template <int kStyle, bool kExact>
 __device__ __forceinline__ bool rotate_chunk_norm(uint4 x, int lane, const ChunkRole& role,
                                                   bool rotate_row, bool normed, WideT<kExact> r,
@@ -506,19 +514,34 @@ __device__ __forceinline__ bool rotate_chunk_norm(uint4 x, int lane, const Chunk
     n[k] = normed ? t * (T)ws[k] : v;
   }
   if constexpr (kStyle == kNeox) {
-    const uint4 pch = lane_fetch(x, lane + role.partner);
-    const uint32_t pa[4] = {pch.x, pch.y, pch.z, pch.w};
+    T np[8];
+    if constexpr (kExact) {
+      const uint4 pch = lane_fetch(x, lane + role.partner);
+      const uint32_t pa[4] = {pch.x, pch.y, pch.z, pch.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (rot) {
+      for (int k = 0; k < 8; ++k) {
         const T v = widen<kExact>(k & 1 ? hi16(pa[k >> 1]) : lo16(pa[k >> 1]));
         const T t = v * r;
-        const T np = normed ? t * (T)wp[k] : v;
-        w[k] = rot1_general<kExact>(n[k], np, c[k], s[k], role.first);
-      } else {
-        w[k] = n[k];
+        np[k] = normed ? t * (T)wp[k] : v;
       }
+    } else {
+      const uint4 lo = lane_fetch(make_uint4(__builtin_bit_cast(uint32_t, n[0]),
+                                             __builtin_bit_cast(uint32_t, n[1]),
+                                             __builtin_bit_cast(uint32_t, n[2]),
+                                             __builtin_bit_cast(uint32_t, n[3])),
+                                  lane + role.partner);
+      const uint4 hi = lane_fetch(make_uint4(__builtin_bit_cast(uint32_t, n[4]),
+                                             __builtin_bit_cast(uint32_t, n[5]),
+                                             __builtin_bit_cast(uint32_t, n[6]),
+                                             __builtin_bit_cast(uint32_t, n[7])),
+                                  lane + role.partner);
+      const uint32_t pa[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) np[k] = __builtin_bit_cast(float, pa[k]);
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = rot ? rot1_general<kExact>(n[k], np[k], c[k], s[k], role.first) : n[k];
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
