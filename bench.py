@@ -441,6 +441,17 @@ def main():
             "kernel_us": ex_ms * 1e3, "GB/s": ex_gbs, "frac": ex_gbs / PEAK_HBM_GBS,
             "tokens_per_s": w.tokens / (ex_ms * 1e-3)}
         log(f"[bench] exact mode: {ex_ms * 1e3:.1f} us, {ex_gbs:.0f} GB/s")
+        # the same data in the NeoX layout (same bytes; each lane fetches 8 cos/sin pairs)
+        style0, w.style = w.style, W.NEOX
+        nx_ms, _ = time_launches(w, t, max(10, args.steps // 2), 3)
+        w.style = style0
+        nx_gbs = nbytes / (nx_ms * 1e-3) / 1e9
+        extra["prefill_neox"] = {
+            "workload": w.name, "layout": "NeoX (rotate-half pairs)",
+            "kernel_us": nx_ms * 1e3, "GB/s": nx_gbs, "frac": nx_gbs / PEAK_HBM_GBS,
+            "tokens_per_s": w.tokens / (nx_ms * 1e-3)}
+        log(f"[bench] NeoX layout: {nx_ms * 1e3:.1f} us, {nx_gbs:.0f} GB/s "
+            f"({nx_gbs / PEAK_HBM_GBS:.1%})")
     del t
     torch.cuda.empty_cache()
 
@@ -472,6 +483,16 @@ def main():
             "tokens_per_s": w.tokens / (n_ms * 1e-3), "algorithmic_bytes": nb}
         log(f"[bench] Q/K norm: {n_ms * 1e3:.1f} us, {n_gbs:.0f} GB/s "
             f"({n_gbs / PEAK_HBM_GBS:.1%})")
+        w.style = W.NEOX
+        nn_ms, _ = time_launches(w, t, max(10, args.steps // 2), 3)
+        nn_gbs = nb / (nn_ms * 1e-3) / 1e9
+        extra["prefill_qknorm_neox"] = {
+            "workload": w.name, "norm": "RMS norm of Q and K heads before the rotation",
+            "layout": "NeoX (rotate-half pairs)",
+            "kernel_us": nn_ms * 1e3, "GB/s": nn_gbs, "frac": nn_gbs / PEAK_HBM_GBS,
+            "tokens_per_s": w.tokens / (nn_ms * 1e-3), "algorithmic_bytes": nb}
+        log(f"[bench] Q/K norm, NeoX layout: {nn_ms * 1e3:.1f} us, {nn_gbs:.0f} GB/s "
+            f"({nn_gbs / PEAK_HBM_GBS:.1%})")
         del t
         torch.cuda.empty_cache()
 

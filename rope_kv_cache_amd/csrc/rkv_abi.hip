@@ -34,7 +34,12 @@ void clear_error() {
 // arithmetic per byte (exact mode, E4M3 cache, Q/K norm) run faster with at
 // least two, whose loads are in flight together while the wave computes
 // (measured on the large prefill: 236 -> 221 us with an E4M3 cache, 266 ->
-// 241 us with Q/K norm, 272 -> 247 us exact; four were no better).  Small
+// 241 us with Q/K norm, 272 -> 247 us exact; four were no better).  A wave
+// fetches its cos/sin values once for all its row groups, and a NeoX lane
+// needs twice as many as a GPT-J lane (8 frequencies instead of 4), so the
+// NeoX kernels take one step more: two row groups for the plain kernel
+// (large NeoX prefill 245-251 -> 236 us), four with Q/K norm (254 -> 244
+// us); the paged update takes two for NeoX as for its heavier kernels.  Small
 // launches are latency-bound, so they take G = 2 or 4 when that keeps every
 // wave resident at once (256 CUs x 4 SIMDs x 8 waves); there the Q/K-norm
 // kernel, with the longest chain between load and store, starts from four
@@ -275,7 +280,9 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.R = (int32_t)R;
   const long long rows_per_group = 512 / D;
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
-  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, heavy ? 2 : 1,
+  const bool neox = layout_of(style) == RKV_ROPE_NEOX;
+  const int g_large = norm ? (neox ? 4 : 2) : ((heavy || neox) ? 2 : 1);
+  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, g_large,
                               norm ? 4 : (heavy ? 2 : 1));
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
@@ -372,7 +379,8 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.num_pages = numPages;
   p.max_pages = maxPagesPerSeq;
   const long long rows_per_group = 512 / D;
-  const int g_start = (exact_of(ropeStyle) || fp8) ? 2 : 1;
+  const int g_start =
+      (exact_of(ropeStyle) || fp8 || layout_of(ropeStyle) == RKV_ROPE_NEOX) ? 2 : 1;
   const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group, g_start,
                               g_start);
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");

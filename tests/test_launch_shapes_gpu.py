@@ -5,8 +5,9 @@ the launch's size and the kernel flavour; each choice is a separate kernel
 instantiation.  For each call and flavour these tests run a ladder of sizes
 (a few tokens; about 12 k and 24 k row groups, where a small launch doubles
 the groups per wave to keep every wave resident; about 80 k row groups,
-where large launches start from their streaming choice; and a large launch
-whose tokens have a single row group), read the choice back through
+where large launches start from their streaming choice, which differs
+between the GPT-J and NeoX layouts; and a large launch whose tokens have a
+single row group), read the choice back through
 ``rkv_last_launch_groups_per_wave`` and hold every launch to the parity bar
 of the other GPU tests: bit-identical with RKV_ROUND_EXACT, within one fp16
 ulp (one E4M3 code step) in the default mode.  The ladder must reach all
@@ -29,7 +30,8 @@ CONTIG_LADDER = [
     ("tiny", 2, 16, 9, 2, 128, 128, NEOX),
     ("groups12k", 3, 1000, 9, 2, 128, 64, GPTJ),
     ("groups24k", 4, 1500, 9, 2, 128, 128, GPTJ),
-    ("groups80k", 4, 5000, 9, 2, 128, 64, NEOX),
+    ("groups80k", 4, 5000, 9, 2, 128, 64, GPTJ),
+    ("groups80k_neox", 4, 5000, 9, 2, 128, 128, NEOX),
     ("one_group_70k", 4, 17500, 4, 2, 64, 64, GPTJ),
 ]
 
