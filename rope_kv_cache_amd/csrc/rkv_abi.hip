@@ -39,7 +39,9 @@ void clear_error() {
 // needs twice as many as a GPT-J lane (8 frequencies instead of 4), so the
 // NeoX kernels take one step more: two row groups for the plain kernel
 // (large NeoX prefill 245-251 -> 236 us), four with Q/K norm (254 -> 244
-// us); the paged update takes two for NeoX as for its heavier kernels.  Small
+// us); the paged update takes two for NeoX as for its heavier kernels.  Q/K
+// norm into an E4M3 cache takes four in both layouts (GPT-J 242 -> 231 us,
+// NeoX 266 -> 248 us).  Small
 // launches are latency-bound, so they take G = 2 or 4 when that keeps every
 // wave resident at once (256 CUs x 4 SIMDs x 8 waves); there the Q/K-norm
 // kernel, with the longest chain between load and store, starts from four
@@ -281,7 +283,7 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   const long long rows_per_group = 512 / D;
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
   const bool neox = layout_of(style) == RKV_ROPE_NEOX;
-  const int g_large = norm ? (neox ? 4 : 2) : ((heavy || neox) ? 2 : 1);
+  const int g_large = norm ? ((neox || fp8) ? 4 : 2) : ((heavy || neox) ? 2 : 1);
   const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, g_large,
                               norm ? 4 : (heavy ? 2 : 1));
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");

@@ -6,8 +6,8 @@ instantiation.  For each call and flavour these tests run a ladder of sizes
 (a few tokens; about 12 k and 24 k row groups, where a small launch doubles
 the groups per wave to keep every wave resident; about 80 k row groups,
 where large launches start from their streaming choice, which differs
-between the GPT-J and NeoX layouts; and a large launch whose tokens have a
-single row group), read the choice back through
+between the GPT-J and NeoX layouts; and large launches whose tokens have
+one or three row groups, which cap the choice), read the choice back through
 ``rkv_last_launch_groups_per_wave`` and hold every launch to the parity bar
 of the other GPU tests: bit-identical with RKV_ROUND_EXACT, within one fp16
 ulp (one E4M3 code step) in the default mode.  The ladder must reach all
@@ -33,6 +33,7 @@ CONTIG_LADDER = [
     ("groups80k", 4, 5000, 9, 2, 128, 64, GPTJ),
     ("groups80k_neox", 4, 5000, 9, 2, 128, 128, NEOX),
     ("one_group_70k", 4, 17500, 4, 2, 64, 64, GPTJ),
+    ("three_groups_24k", 4, 6000, 8, 2, 128, 128, NEOX),
 ]
 
 # name, N, batch, Hkv, D, R, maxPagesPerSeq, style (numPages = batch * maxPages)
