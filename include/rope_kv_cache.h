@@ -28,7 +28,11 @@
  *   rules are given per call).
  * Supported shapes.  headDim in {64, 128, 256}; rotaryDim a multiple of 16
  *   with 0 <= rotaryDim <= headDim.  Other values return
- *   RKV_ERR_UNSUPPORTED.
+ *   RKV_ERR_UNSUPPORTED, as do token or delta-row counts beyond 2^31 - 1 and
+ *   launches that would need more waves than one dispatch holds (2^32 - 1
+ *   work-items, 2^26 waves).  A wave handles up to four 1 KB row groups of
+ *   one token or delta row (512/headDim head rows each), so the limit is
+ *   about 2^28 row groups, and lower when tokens have few heads.
  * Rotation.  For frequency i < rotaryDim/2 with c = row[i] and
  *   s = row[rotaryDim/2 + i] of the token's cos/sin row, the pair (u, v)
  *   becomes (x_u*c - x_v*s, x_v*c + x_u*s), rounded to fp16 to nearest-even.

@@ -130,9 +130,10 @@ struct Split {
   int32_t waves_per_item;
 };
 
-// Returns G = 0 when the wave count would not fit in int32.  g_large /
-// g_small: the row groups per wave a kernel starts from in large and small
-// launches (capped by the row groups a work item has).
+// Returns G = 0 when even four row groups per wave leave more waves than one
+// dispatch can hold (2^32 - 1 work-items).  g_large / g_small: the row
+// groups per wave a kernel starts from in large and small launches (capped
+// by the row groups a work item has).
 Split pick_split(long long items, long long groups_per_item, int g_large, int g_small) {
   auto waves = [&](int g) { return items * ((groups_per_item + g - 1) / g); };
   const bool small = items * groups_per_item <= kStreamingGroups;
@@ -142,8 +143,8 @@ Split pick_split(long long items, long long groups_per_item, int g_large, int g_
   if (small) {
     while (g < 4 && waves(g) > kResidentWaves) g *= 2;
   }
-  while (g < 4 && waves(g) > INT32_MAX) g *= 2;
-  if (waves(g) > INT32_MAX) return Split{0, 0};
+  while (g < 4 && waves(g) > rkv::kMaxWavesPerLaunch) g *= 2;
+  if (waves(g) > rkv::kMaxWavesPerLaunch) return Split{0, 0};
   return Split{g, (int32_t)((groups_per_item + g - 1) / g)};
 }
 

@@ -40,8 +40,8 @@
 
 namespace rkv {
 
-constexpr int kWave = 64;
-constexpr int kBlock = 256;
+constexpr int kWave = kWaveLanes;
+constexpr int kBlock = kBlockThreads;
 constexpr int kWavesPerBlock = kBlock / kWave;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

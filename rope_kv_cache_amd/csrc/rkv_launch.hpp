@@ -11,6 +11,14 @@ enum Call : int { kCallPacked = 0, kCallContinuous = 1, kCallTree = 2 };
 
 constexpr int kTokensPerPage = 64;
 
+// Workgroup shape of the rope kernels: 256 threads, 4 waves of 64 lanes.
+constexpr int kBlockThreads = 256;
+constexpr int kWaveLanes = 64;
+// A dispatch covers at most 2^32 - 1 work-items, which bounds the waves of
+// one launch.
+constexpr long long kMaxWavesPerLaunch =
+    (0xFFFFFFFFLL / kBlockThreads) * (kBlockThreads / kWaveLanes);
+
 // Division by a launch constant d >= 1 for numerators n < 2^31, by
 // multiply-high and shift (Granlund & Montgomery, "Division by invariant
 // integers using multiplication", PLDI 1994, round-up method):

@@ -214,6 +214,19 @@ def test_packed_empty_is_ok_without_launch():
     assert call_packed(cs, qkv, cache) == rkv.OK
 
 
+@no_gpu
+def test_more_waves_than_one_dispatch_is_unsupported():
+    """2^24 tokens of 80 heads need 2^24 * 5 waves even at four row groups per
+    wave: more than one dispatch's 2^32 - 1 work-items hold."""
+    S = 1 << 24
+    cs = fake(F32, 1, S, 128, addr=1 << 42)
+    qkv = fake(F16, 1, S, 80, 128, addr=2 << 42)
+    cache = fake(F16, 1, 2, 8, S, 128, addr=3 << 42)
+    st = call_packed(cs, qkv, cache, style=1)
+    assert st == rkv.ERR_UNSUPPORTED, (rkv.status_string(st), L.rkv_last_error())
+    assert b"too many rows" in L.rkv_last_error()
+
+
 # -------------------------------------------------------- calls 2 and 3 ---
 
 @no_gpu
