@@ -256,6 +256,8 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   }
   const long long tokens = B * S;
   if (tokens > INT32_MAX) return fail(RKV_ERR_UNSUPPORTED, "B*S=%lld exceeds 2^31-1", tokens);
+  if (H > INT32_MAX - 64)   // a token's head rows are indexed in int32
+    return fail(RKV_ERR_UNSUPPORTED, "%lld heads per token is too many", H);
   if (tokens == 0 || H == 0) return RKV_OK;
 
   rkv::ContigParams p{};
@@ -331,6 +333,8 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
       !mul_ok(gather ? (long long)ropeStates * ropeRows : N, R, &cs_elems) ||
       pool_elems > (INT64_MAX / 2))
     return fail(RKV_ERR_SHAPE, "sizes overflow");
+  if (2 * Hkv > INT32_MAX - 64)   // a delta row's 2*Hkv head rows are indexed in int32
+    return fail(RKV_ERR_UNSUPPORTED, "numKVHeads %lld too large", Hkv);
   if (N == 0 || Hkv == 0) return RKV_OK;
   const float* cs = gather ? rope : tokenAlignedCosSin;
   const char* cs_name = gather ? "ropeCosSin" : "tokenAlignedCosSin";

@@ -319,6 +319,7 @@ def paged_call(**kw):
     (dict(cs=(4 << 40) + 8), rkv.ERR_ALIGNMENT),
     (dict(pool=(1 << 40) + 4096), rkv.ERR_ALIAS), (dict(pt=(3 << 40) + 64), rkv.ERR_ALIAS),
     (dict(P=1 << 30, Hkv=1 << 20), rkv.ERR_SHAPE),
+    (dict(N=1, P=0, Hkv=(1 << 30) + 1, D=64, R=64), rkv.ERR_UNSUPPORTED),
 ])
 def test_paged_validation(kw, want):
     st = paged_call(**kw)
