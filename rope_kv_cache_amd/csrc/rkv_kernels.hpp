@@ -9,9 +9,10 @@
 // need, rotates Q and K rows (NeoX partners come from a neighbouring lane
 // by ds_bpermute; GPT-J pairs stay in the lane) and stores.  Waves are laid
 // out token-major, so the chip sweeps the packed tensor in address order
-// with one load per lane in flight per wave.  Measured on MI355X, this
+// with G (1, 2 or 4, chosen by the host per kernel flavour and launch size)
+// loads per lane in flight per wave.  Measured on MI355X, this
 // fine-grained, address-ordered sweep moves the call's mixed read/write
-// traffic faster than per-lane batches of several loads.  There is no
+// traffic faster than per-lane batches of many loads.  There is no
 // contraction anywhere: the path is bandwidth-bound, so there is no MFMA.
 //
 // fp8 cache (kFp8).  Same decomposition; a lane keeps its chunk's rotation
