@@ -292,12 +292,19 @@ def traffic_from_profile(kernel_name: str):
     return float(m.group(1))
 
 
-def kernel_source_hash() -> str:
-    d = os.path.join(ROOT, "rope_kv_cache_amd", "csrc")
+def kernel_source_hash(d=None) -> str:
+    """SHA-256 of the library's HIP sources (in `d`, by default the
+    package's csrc) with comments and blank space removed: a traffic profile
+    stays valid across comment edits and is void once any code changes."""
+    d = d or os.path.join(ROOT, "rope_kv_cache_amd", "csrc")
     hsh = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".hpp")):
-            hsh.update(open(os.path.join(d, f), "rb").read())
+            text = open(os.path.join(d, f)).read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            hsh.update(f.encode())
+            hsh.update(" ".join(text.split()).encode())
     return hsh.hexdigest()
 
 

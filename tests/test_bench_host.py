@@ -71,3 +71,13 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_kernel_source_hash_ignores_comments_only(tmp_path):
+    src = "// header\n__global__ void k(int* p) {  /* body */\n  p[0] = 1;   // store\n}\n"
+    (tmp_path / "a.hip").write_text(src)
+    h0 = bench.kernel_source_hash(str(tmp_path))
+    (tmp_path / "a.hip").write_text(src.replace("// store", "// the store").replace("header", "x"))
+    assert bench.kernel_source_hash(str(tmp_path)) == h0
+    (tmp_path / "a.hip").write_text(src.replace("p[0] = 1", "p[0] = 2"))
+    assert bench.kernel_source_hash(str(tmp_path)) != h0
