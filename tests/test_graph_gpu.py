@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as W
-from harness import compare, dev, download, exact_diffs, expected, launch, upload
+from harness import compare, dev, download, expected, launch, upload
 
 pytestmark = pytest.mark.gpu
 

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from harness import dev, download, expected, host16, launch, upload
+from harness import dev, download, expected, launch, upload
 
 pytestmark = pytest.mark.gpu
 

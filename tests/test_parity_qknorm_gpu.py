@@ -10,7 +10,6 @@ one code step.
 """
 import numpy as np
 import pytest
-import torch
 
 import workloads as W
 from harness import compare, exact_diffs, expected, run_gpu
