@@ -57,8 +57,12 @@
 extern "C" {
 #endif
 
+/* A HIP stream.  This is the same type as HIP's hipStream_t, declared here
+ * under its own name so that C callers need no HIP header and may include
+ * hip_runtime_api.h before or after this one (C99 forbids a second typedef
+ * of the same name). */
 struct ihipStream_t;
-typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipStream_t* rkv_stream_t;
 
 typedef enum {
   RKV_OK = 0,
@@ -111,7 +115,7 @@ typedef struct {
  * be >= 0.  B = 0 or S = 0 is a valid call that enqueues nothing. */
 rkv_status rkv_apply_rope_write_kv_packed_qkv(const rkv_tensor* cosSinCache, rkv_tensor* qkv,
                                               rkv_tensor* kvCache, int32_t ropeStyle,
-                                              hipStream_t stream);
+                                              rkv_stream_t stream);
 
 /* Call 2 -- write into a non-empty cache, rotated Q to a separate tensor.
  * (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV",
@@ -130,7 +134,7 @@ rkv_status rkv_apply_rope_write_kv_continuous(const rkv_tensor* cosSinCache,
                                               const rkv_tensor* kvCacheEndLens,
                                               const rkv_tensor* qkv, rkv_tensor* kvCache,
                                               rkv_tensor* qOut, int32_t ropeStyle,
-                                              hipStream_t stream);
+                                              rkv_stream_t stream);
 
 /* Call 3 -- tree-decoding write for speculative decoding.
  * (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV",
@@ -144,7 +148,7 @@ rkv_status rkv_apply_rope_write_kv_tree(const rkv_tensor* cosSinCache,
                                         const rkv_tensor* kvCacheEndLens,
                                         const rkv_tensor* tokenPosIds, const rkv_tensor* qkv,
                                         rkv_tensor* kvCache, rkv_tensor* qOut,
-                                        int32_t ropeStyle, hipStream_t stream);
+                                        int32_t ropeStyle, rkv_stream_t stream);
 
 /* Call 4 -- paged delta update.
  * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
@@ -173,7 +177,7 @@ rkv_status rkv_dflash_target_kv_cache_update(
     const float* tokenAlignedCosSin, const int32_t* deltaPositions,
     const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
     int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim,
-    int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
+    int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle, rkv_stream_t stream);
 
 /* Call 4 with the cos/sin gather fused in (the page's
  * launchDFlashGatherDeltaRope builds tokenAlignedCosSin from a rope table;
@@ -193,7 +197,7 @@ rkv_status rkv_dflash_target_kv_cache_update_gather_rope(
     const int32_t* deltaPositions, const int32_t* deltaTokenToSequence, const int32_t* pageTable,
     int32_t numDeltaTokens, int32_t batchSize, int32_t numKVHeads, int32_t headDim,
     int32_t rotaryDim, int32_t numPages, int32_t maxPagesPerSeq, int32_t ropeStyle,
-    hipStream_t stream);
+    rkv_stream_t stream);
 
 /* fp8 (E4M3) KV cache
  * ---------------------
@@ -224,28 +228,28 @@ rkv_status rkv_dflash_target_kv_cache_update_gather_rope(
 rkv_status rkv_apply_rope_write_kv_packed_qkv_fp8(const rkv_tensor* cosSinCache, rkv_tensor* qkv,
                                                   rkv_tensor* kvCache, const float* kScale,
                                                   const float* vScale, int32_t ropeStyle,
-                                                  hipStream_t stream);
+                                                  rkv_stream_t stream);
 
 rkv_status rkv_apply_rope_write_kv_continuous_fp8(const rkv_tensor* cosSinCache,
                                                   const rkv_tensor* kvCacheEndLens,
                                                   const rkv_tensor* qkv, rkv_tensor* kvCache,
                                                   rkv_tensor* qOut, const float* kScale,
                                                   const float* vScale, int32_t ropeStyle,
-                                                  hipStream_t stream);
+                                                  rkv_stream_t stream);
 
 rkv_status rkv_apply_rope_write_kv_tree_fp8(const rkv_tensor* cosSinCache,
                                             const rkv_tensor* kvCacheEndLens,
                                             const rkv_tensor* tokenPosIds, const rkv_tensor* qkv,
                                             rkv_tensor* kvCache, rkv_tensor* qOut,
                                             const float* kScale, const float* vScale,
-                                            int32_t ropeStyle, hipStream_t stream);
+                                            int32_t ropeStyle, rkv_stream_t stream);
 
 rkv_status rkv_dflash_target_kv_cache_update_fp8(
     const uint16_t* kDelta, const uint16_t* vDelta, uint8_t* kvCache, const float* kScale,
     const float* vScale, const float* tokenAlignedCosSin, const int32_t* deltaPositions,
     const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
     int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
-    int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
+    int32_t maxPagesPerSeq, int32_t ropeStyle, rkv_stream_t stream);
 
 rkv_status rkv_dflash_target_kv_cache_update_gather_rope_fp8(
     const uint16_t* kDelta, const uint16_t* vDelta, uint8_t* kvCache, const float* kScale,
@@ -253,7 +257,7 @@ rkv_status rkv_dflash_target_kv_cache_update_gather_rope_fp8(
     const int32_t* stateIndices, const int32_t* deltaPositions,
     const int32_t* deltaTokenToSequence, const int32_t* pageTable, int32_t numDeltaTokens,
     int32_t batchSize, int32_t numKVHeads, int32_t headDim, int32_t rotaryDim, int32_t numPages,
-    int32_t maxPagesPerSeq, int32_t ropeStyle, hipStream_t stream);
+    int32_t maxPagesPerSeq, int32_t ropeStyle, rkv_stream_t stream);
 
 /* Q/K RMS norm fused before the rotation
  * ---------------------------------------
@@ -287,19 +291,19 @@ rkv_status rkv_apply_rope_write_kv_packed_qkv_qknorm(const rkv_tensor* cosSinCac
                                                      const float* qNormWeight,
                                                      const float* kNormWeight, float epsilon,
                                                      const float* kScale, const float* vScale,
-                                                     int32_t ropeStyle, hipStream_t stream);
+                                                     int32_t ropeStyle, rkv_stream_t stream);
 
 rkv_status rkv_apply_rope_write_kv_continuous_qknorm(
     const rkv_tensor* cosSinCache, const rkv_tensor* kvCacheEndLens, const rkv_tensor* qkv,
     rkv_tensor* kvCache, rkv_tensor* qOut, const float* qNormWeight, const float* kNormWeight,
     float epsilon, const float* kScale, const float* vScale, int32_t ropeStyle,
-    hipStream_t stream);
+    rkv_stream_t stream);
 
 rkv_status rkv_apply_rope_write_kv_tree_qknorm(
     const rkv_tensor* cosSinCache, const rkv_tensor* kvCacheEndLens,
     const rkv_tensor* tokenPosIds, const rkv_tensor* qkv, rkv_tensor* kvCache, rkv_tensor* qOut,
     const float* qNormWeight, const float* kNormWeight, float epsilon, const float* kScale,
-    const float* vScale, int32_t ropeStyle, hipStream_t stream);
+    const float* vScale, int32_t ropeStyle, rkv_stream_t stream);
 
 /* Device metadata builders
  * ------------------------
@@ -322,7 +326,7 @@ rkv_status rkv_dflash_prepare_delta_metadata(const int32_t* oldDraftCacheLengths
                                              const int32_t* deltaLengths, int32_t deltaWidth,
                                              int32_t* deltaPositions,
                                              int32_t* deltaTokenToSequence, int32_t batchSize,
-                                             hipStream_t stream);
+                                             rkv_stream_t stream);
 
 /* Tree metadata of a linear verification path (same page,
  * launchDFlashBuildLinearTreeMetadata): for every sequence, node 0 is the
@@ -333,7 +337,7 @@ rkv_status rkv_dflash_prepare_delta_metadata(const int32_t* oldDraftCacheLengths
  * exactly what call 2 writes. */
 rkv_status rkv_dflash_build_linear_tree_metadata(int32_t* treeParentIds, int32_t* treeDepths,
                                                  int32_t batchSize, int32_t verifySize,
-                                                 hipStream_t stream);
+                                                 rkv_stream_t stream);
 
 /* Host-only capacity check.
  * (TensorRT-Edge-LLM C++ API, "Dflash Runtime Kernels",
