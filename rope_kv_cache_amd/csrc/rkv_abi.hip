@@ -386,10 +386,14 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.num_pages = numPages;
   p.max_pages = maxPagesPerSeq;
   const long long rows_per_group = 512 / D;
+  const long long groups_per_row = (2 * Hkv + rows_per_group - 1) / rows_per_group;
   const int g_start =
       (exact_of(ropeStyle) || fp8 || layout_of(ropeStyle) == RKV_ROPE_NEOX) ? 2 : 1;
-  const Split sp = pick_split(N, (2 * Hkv + rows_per_group - 1) / rows_per_group, g_start,
-                              g_start);
+  const Split sp = pick_split(N, groups_per_row, g_start, g_start);
+  // non-temporal delta loads and pool stores for large launches (small fp16
+  // ones run faster when the caches absorb the pool writes); E4M3 pools
+  // always take them
+  const bool streaming = fp8 || N * groups_per_row > kStreamingGroups;
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_row = sp.waves_per_item;
@@ -397,9 +401,9 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
   g_last_groups = p.groups_per_wave;
   return launched(fp8 ? rkv::launch_paged_fp8(p, headDim, layout_of(ropeStyle),
-                                              exact_of(ropeStyle), gather, stream)
+                                              exact_of(ropeStyle), gather, streaming, stream)
                       : rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle),
-                                          gather, stream));
+                                          gather, streaming, stream));
 }
 
 }  // namespace

@@ -215,17 +215,24 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
 // launchDFlashTargetKVCacheUpdate).  Delta row i has 2*Hkv head rows: K
 // heads first, then V heads; a wave owns G row groups of one delta row.
 // The pool is addressed as [2*numPages][64][Hkv][D] by canonical page id,
-// in 64-bit.  The delta rows and the row's cos/sin values do not depend on
-// the index metadata, so they are requested first; the position/sequence
-// loads and then the page-table loads overlap with them, and only the
-// stores wait for the page ids.
+// in 64-bit.  Two access plans, chosen by the host as kStream:
+//  - small fp16 launches (latency-bound): the delta rows and cos/sin values
+//    are requested first, the index loads overlap with them, only the stores
+//    wait for the page ids; ordinary accesses, whose pool writes the caches
+//    absorb;
+//  - large launches and E4M3 pools (bandwidth-bound): the delta rows are
+//    loaded once the position, sequence and page ids are known, and only
+//    those that will be written (padding rows and rows of unmapped pages move
+//    no bytes), with non-temporal loads and stores.  Measured on MI355X: a
+//    65,536-row update 98 -> 81 us, the 4,096-row E4M3 update 11.4 -> 10.6 us
+//    (by events).
 //
 // kGather fuses the page's cos/sin gather (launchDFlashGatherDeltaRope)
 // into the update: the row's cos/sin values come from the rope table row of
 // (state of its sequence, its position), read once the position and
 // sequence are known (in parallel with the page-table lookup); a row with
 // no such table row writes no K.
-template <int D, int kStyle, bool kExact, int G, bool kGather, bool kFp8>
+template <int D, int kStyle, bool kExact, int G, bool kGather, bool kFp8, bool kStream>
 __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
@@ -243,17 +250,20 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   const int rows = 2 * p.Hkv;
   const size_t delta_row = (size_t)i * p.Hkv;
 
-  uint4 x[G];
   int row[G];
+  uint4 x[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int r = (part * G + g) * kRowsPerGroup + row_in_group;
     row[g] = r;
     x[g] = make_uint4(0, 0, 0, 0);
-    if (r < p.Hkv)
-      x[g] = ld16(p.k_delta + (delta_row + r) * D + 8 * c);
-    else if (r < rows)
-      x[g] = ld16(p.v_delta + (delta_row + (r - p.Hkv)) * D + 8 * c);
+    // small launches are latency-bound: request every row before the index loads
+    if constexpr (!kStream) {
+      if (r < p.Hkv)
+        x[g] = ld16(p.k_delta + (delta_row + r) * D + 8 * c);
+      else if (r < rows)
+        x[g] = ld16(p.v_delta + (delta_row + (r - p.Hkv)) * D + 8 * c);
+    }
   }
   float cs[8], sn[8];
   const bool has_k = part * G * kRowsPerGroup < p.Hkv;   // wave-uniform
@@ -283,7 +293,19 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
                              sn);
     }
   }
-  // fp8: the scales, read while the row, cos/sin and page-table loads are in flight
+  // large launches are bandwidth-bound: load only the rows that will be written
+  if constexpr (kStream) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int r = row[g];
+      if (r < p.Hkv ? k_ok : (r < rows && v_ok)) {
+        const uint16_t* src = r < p.Hkv ? p.k_delta + (delta_row + r) * D
+                                        : p.v_delta + (delta_row + (r - p.Hkv)) * D;
+        x[g] = ld16_stream(src + 8 * c);
+      }
+    }
+  }
+  // fp8: the scales, read while the row and cos/sin loads are in flight
   float k_rcp = 1.f, v_rcp = 1.f;
   if constexpr (kFp8) load_reciprocal_scales(p.k_scale, p.v_scale, k_rcp, v_rcp);
 
@@ -298,11 +320,14 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
       WideT<kExact> w[8];
       rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn, w);
       if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-      st8(p.pool8 + pool_row * D + 8 * c, to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp));
+      uint8_t* const dst = p.pool8 + pool_row * D + 8 * c;
+      const uint2 b = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
+      if constexpr (kStream) st8_stream(dst, b); else st8(dst, b);
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn);
       if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-      st16(p.pool + pool_row * D + 8 * c, y);
+      if constexpr (kStream) st16_stream(p.pool + pool_row * D + 8 * c, y);
+      else st16(p.pool + pool_row * D + 8 * c, y);
     }
   }
 }
@@ -374,7 +399,7 @@ hipError_t launch_contig_t(const ContigParams& p, int call, int D, int style, bo
   }
 }
 
-template <bool kGather, bool kFp8>
+template <bool kGather, bool kFp8, bool kStream>
 hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
                           hipStream_t stream) {
   return with_d(D, [&](auto d) {
@@ -382,7 +407,7 @@ hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
       return with_groups(p.groups_per_wave, [&](auto g) {
         hipLaunchKernelGGL((paged_kernel<decltype(d)::value, decltype(st)::value,
                                          decltype(ex)::value != 0, decltype(g)::value, kGather,
-                                         kFp8>),
+                                         kFp8, kStream>),
                            dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p);
         return hipGetLastError();
       });
@@ -390,11 +415,20 @@ hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
   });
 }
 
+// E4M3 pools always take non-temporal accesses; fp16 pools when `streaming`.
 template <bool kFp8>
 hipError_t launch_paged_t(const PagedParams& p, int D, int style, bool exact, bool gather,
-                          hipStream_t stream) {
-  return gather ? launch_paged_g<true, kFp8>(p, D, style, exact, stream)
-                : launch_paged_g<false, kFp8>(p, D, style, exact, stream);
+                          bool streaming, hipStream_t stream) {
+  if constexpr (kFp8) {
+    return gather ? launch_paged_g<true, true, true>(p, D, style, exact, stream)
+                  : launch_paged_g<false, true, true>(p, D, style, exact, stream);
+  } else {
+    if (streaming)
+      return gather ? launch_paged_g<true, false, true>(p, D, style, exact, stream)
+                    : launch_paged_g<false, false, true>(p, D, style, exact, stream);
+    return gather ? launch_paged_g<true, false, false>(p, D, style, exact, stream)
+                  : launch_paged_g<false, false, false>(p, D, style, exact, stream);
+  }
 }
 
 }  // namespace detail

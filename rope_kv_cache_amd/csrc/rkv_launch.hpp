@@ -83,8 +83,10 @@ struct PagedParams {
 
 hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool exact,
                          hipStream_t stream);
+// streaming: non-temporal delta loads and pool stores (the fp8 launcher
+// always uses them).
 hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool gather,
-                        hipStream_t stream);
+                        bool streaming, hipStream_t stream);
 hipError_t launch_contig_fp8(const ContigParams& p, int call, int D, int style, bool exact,
                              hipStream_t stream);
 hipError_t launch_contig_norm(const ContigParams& p, int call, int D, int style, bool exact,
@@ -92,7 +94,7 @@ hipError_t launch_contig_norm(const ContigParams& p, int call, int D, int style,
 hipError_t launch_contig_norm_fp8(const ContigParams& p, int call, int D, int style, bool exact,
                                   hipStream_t stream);
 hipError_t launch_paged_fp8(const PagedParams& p, int D, int style, bool exact, bool gather,
-                            hipStream_t stream);
+                            bool streaming, hipStream_t stream);
 
 // Index builders (rkv_meta.hip): rows = batch * width > 0, nodes = batch *
 // verify > 0, all pointers valid device arrays of that many int32.
