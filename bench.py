@@ -551,6 +551,27 @@ def main():
             del tx, x
             torch.cuda.empty_cache()
         del flush_buf
+        torch.cuda.empty_cache()
+        # the paged update at a size where bandwidth, not the launch, bounds it:
+        # 65,536 delta rows (0.27 GB of deltas, beyond the 256 MB MALL) into the 2 GiB pool
+        log("[bench] generating paged_delta_large")
+        x = W.paged(65536, 64, 8, 128, 128, 8192, 128, W.NEOX, 1044, pool_fill="none",
+                    name="paged_delta_n65536_p8192")
+        xb = algorithmic_bytes(x)
+        tx = upload(x)
+        # the 2 GiB pool is filled on the device (its contents do not change the work)
+        tx["pool"] = torch.zeros((2, x.num_pages, W.TOKENS_PER_PAGE, x.Hkv, x.D),
+                                 dtype=torch.float16, device="cuda")
+        k_ms, _ = time_launches(x, tx, max(10, args.steps // 2), 3)
+        gbs = xb / (k_ms * 1e-3) / 1e9
+        extra["paged_delta_large"] = {
+            "workload": x.name, "kernel_us": k_ms * 1e3, "GB/s": gbs,
+            "frac": gbs / PEAK_HBM_GBS, "tokens_per_s": x.tokens / (k_ms * 1e-3),
+            "algorithmic_bytes": xb, "note": "launches back to back, event span / count"}
+        log(f"[bench] paged_delta_large: {k_ms * 1e3:.1f} us, {gbs:.0f} GB/s "
+            f"({gbs / PEAK_HBM_GBS:.1%})")
+        del tx, x
+        torch.cuda.empty_cache()
         meta = metadata_builders(max(10, args.steps // 2))
         for k, v in meta.items():
             log(f"[bench] {k}: {v['kernel_us_events']:.2f} us")
