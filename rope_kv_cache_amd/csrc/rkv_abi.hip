@@ -287,8 +287,9 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
   const bool neox = layout_of(style) == RKV_ROPE_NEOX;
   const int g_large = norm ? ((neox || fp8) ? 4 : 2) : ((heavy || neox) ? 2 : 1);
-  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, g_large,
-                              norm ? 4 : (heavy ? 2 : 1));
+  const long long groups_per_token = (H + rows_per_group - 1) / rows_per_group;
+  const Split sp = pick_split(tokens, groups_per_token, g_large, norm ? 4 : (heavy ? 2 : 1));
+  p.stream_cache8 = tokens * groups_per_token <= kStreamingGroups ? 1 : 0;
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_token = sp.waves_per_item;
