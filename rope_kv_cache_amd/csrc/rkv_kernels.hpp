@@ -19,10 +19,8 @@
 // unrounded, writes Q (and call 1's in-place K) as fp16 and the cache row
 // chunk as 8 E4M3 bytes of value * (1/scale), the per-tensor scales read
 // from device memory (sglang rope_cache.py, HAVE_K_SCALE / HAVE_V_SCALE).
-// The 128-byte E4M3 rows of consecutive tokens are neighbours in the cache,
-// and in large launches ordinary stores, which the caches merge before they
-// reach HBM, beat non-temporal ones (large prefill 219 -> 209 us on MI355X);
-// small launches keep non-temporal stores (about 1% faster there).
+// Cache rows take ordinary stores in large launches and non-temporal ones in
+// small launches, as the fp16 ones do (store_cache_row).
 //
 // Q/K RMS norm (kNorm, calls 1-3).  Same decomposition; each Q or K row
 // with a weight vector is normalised before its rotation: the lanes of a row
@@ -71,6 +69,15 @@ __device__ __forceinline__ void st16_stream(uint16_t* p, uint4 v) {
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// A chunk of a cache row (calls 1-3).  The rows of consecutive tokens are
+// neighbours in the cache (one stream per (plane, head)), and in large
+// launches ordinary stores, which the caches merge into long runs before
+// they reach HBM, beat non-temporal ones; small launches keep non-temporal
+// stores.  `streaming` is uniform across the launch.
+__device__ __forceinline__ void store_cache_row(uint16_t* p, uint4 v, int32_t streaming) {
+  if (streaming) st16_stream(p, v); else st16(p, v);
+}
 
 // 8-byte stores of E4M3 cache chunks.
 __device__ __forceinline__ void st8(uint8_t* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
@@ -194,12 +201,12 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
       } else if constexpr (kFp8) {
         uint8_t* const dst = p.cache8 + cache_row * D + 8 * c;
         const uint2 b8 = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
-        if (p.stream_cache8) st8_stream(dst, b8); else st8(dst, b8);
+        if (p.stream_cache) st8_stream(dst, b8); else st8(dst, b8);
         if (kCall == kCallPacked && is_k)
           st16_stream(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
       } else {
         const uint4 y = narrow_chunk<kExact>(w, x[g], comp);
-        st16_stream(p.cache + cache_row * D + 8 * c, y);
+        store_cache_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
         if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
       }
     } else {
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
       if (is_q) {
         st16_stream(q_dst + 8 * c, y);
       } else {
-        st16_stream(p.cache + cache_row * D + 8 * c, y);
+        store_cache_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
         if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
       }
     }
