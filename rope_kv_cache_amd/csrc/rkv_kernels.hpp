@@ -231,14 +231,16 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
 // in 64-bit.  Two access plans, chosen by the host as kStream:
 //  - small fp16 launches (latency-bound): the delta rows and cos/sin values
 //    are requested first, the index loads overlap with them, only the stores
-//    wait for the page ids; ordinary accesses, whose pool writes the caches
-//    absorb;
+//    wait for the page ids; ordinary loads;
 //  - large launches and E4M3 pools (bandwidth-bound): the delta rows are
 //    loaded once the position, sequence and page ids are known, and only
 //    those that will be written (padding rows and rows of unmapped pages move
-//    no bytes), with non-temporal loads and stores.  Measured on MI355X: a
-//    65,536-row update 98 -> 81 us, the 4,096-row E4M3 update 11.4 -> 10.6 us
-//    (by events).
+//    no bytes), with non-temporal loads.
+// fp16 pool rows are written by ordinary stores, which the caches gather
+// into page-long runs (64 slots of a page are neighbours); E4M3 pool rows by
+// non-temporal stores, which measured faster for them.  Measured on MI355X
+// (by events): a 65,536-row update 98 -> 76 us, the 4,096-row E4M3 update
+// 11.4 -> 10.6 us.
 //
 // kGather fuses the page's cos/sin gather (launchDFlashGatherDeltaRope)
 // into the update: the row's cos/sin values come from the rope table row of
@@ -339,8 +341,7 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn);
       if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-      if constexpr (kStream) st16_stream(p.pool + pool_row * D + 8 * c, y);
-      else st16(p.pool + pool_row * D + 8 * c, y);
+      st16(p.pool + pool_row * D + 8 * c, y);
     }
   }
 }
