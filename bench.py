@@ -10,8 +10,9 @@ duration for the roofline.  The same workload in the library's RKV_ROUND_EXACT m
 other workloads (continuous write, tree write, paged delta update, the
 paged update with the cos/sin gather fused in, the prefill, continuous
 and paged calls into an E4M3 cache, the prefill and continuous calls
-with Q/K RMS norm, and the two device index builders) are reported under
-"workloads".  The small workloads' inputs fit the 256 MB
+with Q/K RMS norm, the prefill in the NeoX layout, a 65,536-row paged update,
+and the two device index builders) are reported under "workloads".  The
+small workloads' inputs fit the 256 MB
 MALL, so a 1 GiB buffer is read before each of their timed launches to push
 them back to HBM (a read leaves clean lines, so the timed kernel inherits no
 write-back); their event-bracketed times include the events' own overhead
@@ -20,7 +21,7 @@ of a few microseconds, so rocprofv3's kernel trace is the reference there.
 Prints one JSON line on stdout; progress goes to stderr.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-                      [--calib] [--floors]
+                      [--calib] [--floors] [--paged-large]
 """
 from __future__ import annotations
 
@@ -237,6 +238,45 @@ def metadata_builders(steps):
     }
 
 
+def calibration_copy():
+    """The counter runs' reference: torch.mul(src, 1.0, out=dst) on 1 GiB fp16
+    tensors (1 GiB read, 1 GiB written per launch), three launches."""
+    import torch
+    src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def paged_large(steps, warmup=3):
+    """The paged update at a size where bandwidth, not the launch, bounds
+    it: 65,536 delta rows of the paged workload's shape (0.27 GB of deltas,
+    beyond the 256 MB MALL) into the 2 GiB pool, launches back to back."""
+    import torch
+    import workloads as W
+    from harness import upload
+    log("[bench] generating paged_delta_large")
+    x = W.paged(65536, 64, 8, 128, 128, 8192, 128, W.NEOX, 1044, pool_fill="none",
+                name="paged_delta_n65536_p8192")
+    xb = algorithmic_bytes(x)
+    tx = upload(x)
+    # the 2 GiB pool is filled on the device (its contents do not change the work)
+    tx["pool"] = torch.zeros((2, x.num_pages, W.TOKENS_PER_PAGE, x.Hkv, x.D),
+                             dtype=torch.float16, device="cuda")
+    k_ms, _ = time_launches(x, tx, steps, warmup)
+    gbs = xb / (k_ms * 1e-3) / 1e9
+    log(f"[bench] paged_delta_large: {k_ms * 1e3:.1f} us, {gbs:.0f} GB/s "
+        f"({gbs / PEAK_HBM_GBS:.1%})")
+    del tx, x
+    torch.cuda.empty_cache()
+    return {"workload": "paged_delta_n65536_p8192", "kernel_us": k_ms * 1e3, "GB/s": gbs,
+            "frac": gbs / PEAK_HBM_GBS, "tokens_per_s": 65536 / (k_ms * 1e-3),
+            "algorithmic_bytes": xb, "note": "launches back to back, event span / count"}
+
+
 def floors(steps):
     """Lower bounds for the small workloads on this chip, timed like them (a
     1 GiB read before each launch pushes the inputs out of the MALL): a
@@ -381,6 +421,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--paged-large", action="store_true",
+                    help="time only the 65,536-row paged update (for counter runs)")
     ap.add_argument("--floors", action="store_true",
                     help="only time the floors of the small workloads: a torch copy moving the "
                          "paged workload's bytes and a near-empty kernel, each after the same "
@@ -405,6 +447,12 @@ def main():
     log(f"[bench] device: {torch.cuda.get_device_name(0)}")
     if args.floors:
         print(json.dumps(floors(max(10, args.steps // 2))), flush=True)
+        return
+    if args.paged_large:
+        res = paged_large(args.steps, args.warmup)
+        if args.calib:
+            calibration_copy()
+        print(json.dumps(res), flush=True)
         return
 
     log("[bench] generating the headline workload")
@@ -504,13 +552,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.calib:
-        src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-        torch.cuda.empty_cache()
+        calibration_copy()
 
     if not args.no_extra:
         flush_buf = torch.ones(1 << 29, dtype=torch.float16, device="cuda")   # 1 GiB
@@ -552,26 +594,7 @@ def main():
             torch.cuda.empty_cache()
         del flush_buf
         torch.cuda.empty_cache()
-        # the paged update at a size where bandwidth, not the launch, bounds it:
-        # 65,536 delta rows (0.27 GB of deltas, beyond the 256 MB MALL) into the 2 GiB pool
-        log("[bench] generating paged_delta_large")
-        x = W.paged(65536, 64, 8, 128, 128, 8192, 128, W.NEOX, 1044, pool_fill="none",
-                    name="paged_delta_n65536_p8192")
-        xb = algorithmic_bytes(x)
-        tx = upload(x)
-        # the 2 GiB pool is filled on the device (its contents do not change the work)
-        tx["pool"] = torch.zeros((2, x.num_pages, W.TOKENS_PER_PAGE, x.Hkv, x.D),
-                                 dtype=torch.float16, device="cuda")
-        k_ms, _ = time_launches(x, tx, max(10, args.steps // 2), 3)
-        gbs = xb / (k_ms * 1e-3) / 1e9
-        extra["paged_delta_large"] = {
-            "workload": x.name, "kernel_us": k_ms * 1e3, "GB/s": gbs,
-            "frac": gbs / PEAK_HBM_GBS, "tokens_per_s": x.tokens / (k_ms * 1e-3),
-            "algorithmic_bytes": xb, "note": "launches back to back, event span / count"}
-        log(f"[bench] paged_delta_large: {k_ms * 1e3:.1f} us, {gbs:.0f} GB/s "
-            f"({gbs / PEAK_HBM_GBS:.1%})")
-        del tx, x
-        torch.cuda.empty_cache()
+        extra["paged_delta_large"] = paged_large(max(10, args.steps // 2))
         meta = metadata_builders(max(10, args.steps // 2))
         for k, v in meta.items():
             log(f"[bench] {k}: {v['kernel_us_events']:.2f} us")
