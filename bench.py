@@ -11,7 +11,8 @@ other workloads (continuous write, tree write, paged delta update, the
 paged update with the cos/sin gather fused in, the prefill, continuous
 and paged calls into an E4M3 cache, the prefill and continuous calls
 with Q/K RMS norm, the prefill in the NeoX layout, a 65,536-row paged update,
-and the two device index builders) are reported under "workloads".  The
+a 16-sequence continuous write, and the two device index builders) are
+reported under "workloads".  The
 small workloads' inputs fit the 256 MB
 MALL, so a 1 GiB buffer is read before each of their timed launches to push
 them back to HBM (a read leaves clean lines, so the timed kernel inherits no
@@ -595,6 +596,24 @@ def main():
         del flush_buf
         torch.cuda.empty_cache()
         extra["paged_delta_large"] = paged_large(max(10, args.steps // 2))
+        # call 2 at a size where bandwidth bounds it: 16 sequences x 1024 new tokens
+        # (0.4 GB moved, beyond the 256 MB MALL)
+        log("[bench] generating continuous_large")
+        x = W.continuous(16, 1024, 32, 8, 128, 128, 2048, W.NEOX, 1062, 1024, 2048,
+                         theta=500000.0, cache_fill="sentinel",
+                         name="continuous_b16_s1024_d128_neox")
+        xb = algorithmic_bytes(x)
+        tx = upload(x)
+        c_ms, _ = time_launches(x, tx, max(10, args.steps // 2), 3)
+        gbs = xb / (c_ms * 1e-3) / 1e9
+        extra["continuous_large"] = {
+            "workload": x.name, "kernel_us": c_ms * 1e3, "GB/s": gbs,
+            "frac": gbs / PEAK_HBM_GBS, "tokens_per_s": x.tokens / (c_ms * 1e-3),
+            "algorithmic_bytes": xb, "note": "launches back to back, event span / count"}
+        log(f"[bench] continuous_large: {c_ms * 1e3:.1f} us, {gbs:.0f} GB/s "
+            f"({gbs / PEAK_HBM_GBS:.1%})")
+        del tx, x
+        torch.cuda.empty_cache()
         meta = metadata_builders(max(10, args.steps // 2))
         for k, v in meta.items():
             log(f"[bench] {k}: {v['kernel_us_events']:.2f} us")

@@ -33,10 +33,12 @@ void clear_error() {
 // the cos/sin values (and norm weights) once for all of them.  Large
 // launches are bandwidth-bound: they run with two row groups per wave
 // (measured on MI355X, with the cache rows written by ordinary stores: large
-// GPT-J prefill 225 -> 212 us against one; a NeoX lane needs twice the
-// cos/sin values of a GPT-J lane, so NeoX gains more), the Q/K-norm and
-// exact-mode kernels, with more arithmetic between load and store, with four
-// (large prefill with Q/K norm 243 -> 229 us, exact 265 -> 245 us).  Small
+// GPT-J prefill 225 -> 212 us against one), the Q/K-norm and exact-mode
+// kernels, with more arithmetic between load and store, with four (large
+// prefill with Q/K norm 243 -> 229 us, exact 265 -> 245 us), and so does the
+// plain NeoX kernel, whose lanes need twice the cos/sin values of GPT-J
+// lanes (a 16 x 1024-token continuous write 69 -> 66.5 us, 32 x 1024
+// 129 -> 123 us).  Small
 // launches are latency-bound, so they take G = 2 or 4 when that keeps every
 // wave resident at once (256 CUs x 4 SIMDs x 8 waves); there the Q/K-norm
 // kernel, with the longest chain between load and store, starts from four
@@ -280,7 +282,8 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.R = (int32_t)R;
   const long long rows_per_group = 512 / D;
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
-  const int g_large = (norm || exact_of(style)) ? 4 : 2;
+  const bool neox_fp16 = layout_of(style) == RKV_ROPE_NEOX && !fp8;
+  const int g_large = (norm || exact_of(style) || neox_fp16) ? 4 : 2;
   const long long groups_per_token = (H + rows_per_group - 1) / rows_per_group;
   const Split sp = pick_split(tokens, groups_per_token, g_large, norm ? 4 : (heavy ? 2 : 1));
   p.stream_cache = tokens * groups_per_token <= kStreamingGroups ? 1 : 0;
