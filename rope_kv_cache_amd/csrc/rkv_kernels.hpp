@@ -70,12 +70,13 @@ __device__ __forceinline__ void st16_stream(uint16_t* p, uint4 v) {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// A chunk of a cache row (calls 1-3).  The rows of consecutive tokens are
-// neighbours in the cache (one stream per (plane, head)), and in large
-// launches ordinary stores, which the caches merge into long runs before
-// they reach HBM, beat non-temporal ones; small launches keep non-temporal
+// A chunk of a K or V row (calls 1-3): a cache row, or call 1's in-place K
+// row.  The cache rows of consecutive tokens are neighbours (one stream per
+// plane and head), and in large launches ordinary stores, which the caches
+// merge into long runs before they reach HBM, beat non-temporal ones (the
+// in-place K rows gain a little too); small launches keep non-temporal
 // stores.  `streaming` is uniform across the launch.
-__device__ __forceinline__ void store_cache_row(uint16_t* p, uint4 v, int32_t streaming) {
+__device__ __forceinline__ void store_kv_row(uint16_t* p, uint4 v, int32_t streaming) {
   if (streaming) st16_stream(p, v); else st16(p, v);
 }
 
@@ -203,11 +204,13 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
         const uint2 b8 = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
         if (p.stream_cache) st8_stream(dst, b8); else st8(dst, b8);
         if (kCall == kCallPacked && is_k)
-          st16_stream(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
+          store_kv_row(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], comp),
+                       p.stream_cache);
       } else {
         const uint4 y = narrow_chunk<kExact>(w, x[g], comp);
-        store_cache_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
-        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
+        store_kv_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
+        if (kCall == kCallPacked && is_k)
+          store_kv_row(tok_base + (size_t)r * D + 8 * c, y, p.stream_cache);
       }
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn);
@@ -215,8 +218,9 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
       if (is_q) {
         st16_stream(q_dst + 8 * c, y);
       } else {
-        store_cache_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
-        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
+        store_kv_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
+        if (kCall == kCallPacked && is_k)
+          store_kv_row(tok_base + (size_t)r * D + 8 * c, y, p.stream_cache);
       }
     }
   }
