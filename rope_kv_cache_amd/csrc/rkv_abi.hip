@@ -29,16 +29,19 @@ void clear_error() {
 }
 
 // Launch shape.  A wave handles G row groups (512/D rows each) of one work
-// item; its loads for all G groups are in flight together, and it fetches
-// the cos/sin values (and norm weights) once for all of them.  Large
-// launches are bandwidth-bound: they run with two row groups per wave
-// (measured on MI355X, with the cache rows written by ordinary stores: large
-// GPT-J prefill 225 -> 212 us against one), the Q/K-norm and exact-mode
-// kernels, with more arithmetic between load and store, with four (large
-// prefill with Q/K norm 243 -> 229 us, exact 265 -> 245 us), and so does the
-// plain NeoX kernel, whose lanes need twice the cos/sin values of GPT-J
-// lanes (a 16 x 1024-token continuous write 69 -> 66.5 us, 32 x 1024
-// 129 -> 123 us).  Small
+// item.  Large launches are bandwidth-bound: the plain binary32 kernel runs
+// fastest with one row group per wave, while the kernels with more
+// arithmetic per byte (exact mode, E4M3 cache, Q/K norm) run faster with at
+// least two, whose loads are in flight together while the wave computes
+// (measured on the large prefill: 236 -> 221 us with an E4M3 cache, 266 ->
+// 241 us with Q/K norm, 272 -> 247 us exact; four were no better).  A wave
+// fetches its cos/sin values once for all its row groups, and a NeoX lane
+// needs twice as many as a GPT-J lane (8 frequencies instead of 4), so the
+// NeoX kernels take one step more: two row groups for the plain kernel
+// (large NeoX prefill 245-251 -> 236 us), four with Q/K norm (254 -> 244
+// us); the paged update takes two for NeoX as for its heavier kernels.  Q/K
+// norm into an E4M3 cache takes four in both layouts (GPT-J 242 -> 231 us,
+// NeoX 266 -> 248 us).  Small
 // launches are latency-bound, so they take G = 2 or 4 when that keeps every
 // wave resident at once (256 CUs x 4 SIMDs x 8 waves); there the Q/K-norm
 // kernel, with the longest chain between load and store, starts from four
@@ -282,11 +285,10 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.R = (int32_t)R;
   const long long rows_per_group = 512 / D;
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
-  const bool neox_fp16 = layout_of(style) == RKV_ROPE_NEOX && !fp8;
-  const int g_large = (norm || exact_of(style) || neox_fp16) ? 4 : 2;
-  const long long groups_per_token = (H + rows_per_group - 1) / rows_per_group;
-  const Split sp = pick_split(tokens, groups_per_token, g_large, norm ? 4 : (heavy ? 2 : 1));
-  p.stream_cache = tokens * groups_per_token <= kStreamingGroups ? 1 : 0;
+  const bool neox = layout_of(style) == RKV_ROPE_NEOX;
+  const int g_large = norm ? ((neox || fp8) ? 4 : 2) : ((heavy || neox) ? 2 : 1);
+  const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, g_large,
+                              norm ? 4 : (heavy ? 2 : 1));
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_token = sp.waves_per_item;

@@ -19,8 +19,6 @@
 // unrounded, writes Q (and call 1's in-place K) as fp16 and the cache row
 // chunk as 8 E4M3 bytes of value * (1/scale), the per-tensor scales read
 // from device memory (sglang rope_cache.py, HAVE_K_SCALE / HAVE_V_SCALE).
-// Cache rows take ordinary stores in large launches and non-temporal ones in
-// small launches, as the fp16 ones do (store_cache_row).
 //
 // Q/K RMS norm (kNorm, calls 1-3).  Same decomposition; each Q or K row
 // with a weight vector is normalised before its rotation: the lanes of a row
@@ -69,16 +67,6 @@ __device__ __forceinline__ void st16_stream(uint16_t* p, uint4 v) {
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// A chunk of a K or V row (calls 1-3): a cache row, or call 1's in-place K
-// row.  The cache rows of consecutive tokens are neighbours (one stream per
-// plane and head), and in large launches ordinary stores, which the caches
-// merge into long runs before they reach HBM, beat non-temporal ones (the
-// in-place K rows gain a little too); small launches keep non-temporal
-// stores.  `streaming` is uniform across the launch.
-__device__ __forceinline__ void store_kv_row(uint16_t* p, uint4 v, int32_t streaming) {
-  if (streaming) st16_stream(p, v); else st16(p, v);
-}
 
 // 8-byte stores of E4M3 cache chunks.
 __device__ __forceinline__ void st8(uint8_t* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
@@ -200,17 +188,13 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
       if (is_q) {
         st16_stream(q_dst + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
       } else if constexpr (kFp8) {
-        uint8_t* const dst = p.cache8 + cache_row * D + 8 * c;
-        const uint2 b8 = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
-        if (p.stream_cache) st8_stream(dst, b8); else st8(dst, b8);
+        st8_stream(p.cache8 + cache_row * D + 8 * c, to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp));
         if (kCall == kCallPacked && is_k)
-          store_kv_row(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], comp),
-                       p.stream_cache);
+          st16_stream(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
       } else {
         const uint4 y = narrow_chunk<kExact>(w, x[g], comp);
-        store_kv_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
-        if (kCall == kCallPacked && is_k)
-          store_kv_row(tok_base + (size_t)r * D + 8 * c, y, p.stream_cache);
+        st16_stream(p.cache + cache_row * D + 8 * c, y);
+        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
       }
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn);
@@ -218,9 +202,8 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
       if (is_q) {
         st16_stream(q_dst + 8 * c, y);
       } else {
-        store_kv_row(p.cache + cache_row * D + 8 * c, y, p.stream_cache);
-        if (kCall == kCallPacked && is_k)
-          store_kv_row(tok_base + (size_t)r * D + 8 * c, y, p.stream_cache);
+        st16_stream(p.cache + cache_row * D + 8 * c, y);
+        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
       }
     }
   }
@@ -235,16 +218,14 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
 // in 64-bit.  Two access plans, chosen by the host as kStream:
 //  - small fp16 launches (latency-bound): the delta rows and cos/sin values
 //    are requested first, the index loads overlap with them, only the stores
-//    wait for the page ids; ordinary loads;
+//    wait for the page ids; ordinary accesses, whose pool writes the caches
+//    absorb;
 //  - large launches and E4M3 pools (bandwidth-bound): the delta rows are
 //    loaded once the position, sequence and page ids are known, and only
 //    those that will be written (padding rows and rows of unmapped pages move
-//    no bytes), with non-temporal loads.
-// fp16 pool rows are written by ordinary stores, which the caches gather
-// into page-long runs (64 slots of a page are neighbours); E4M3 pool rows by
-// non-temporal stores, which measured faster for them.  Measured on MI355X
-// (by events): a 65,536-row update 98 -> 76 us, the 4,096-row E4M3 update
-// 11.4 -> 10.6 us.
+//    no bytes), with non-temporal loads and stores.  Measured on MI355X: a
+//    65,536-row update 98 -> 81 us, the 4,096-row E4M3 update 11.4 -> 10.6 us
+//    (by events).
 //
 // kGather fuses the page's cos/sin gather (launchDFlashGatherDeltaRope)
 // into the update: the row's cos/sin values come from the rope table row of
@@ -345,7 +326,8 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn);
       if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-      st16(p.pool + pool_row * D + 8 * c, y);
+      if constexpr (kStream) st16_stream(p.pool + pool_row * D + 8 * c, y);
+      else st16(p.pool + pool_row * D + 8 * c, y);
     }
   }
 }

@@ -48,7 +48,6 @@ struct ContigParams {
   const float* q_norm_w;    // Q/K norm: per-dimension weights [D] of Q and K heads,
   const float* k_norm_w;    //   or null (those heads are not normalised)
   float eps;                // Q/K norm: added to the mean square
-  int32_t stream_cache;     // K/V-row stores: non-temporal (small launches) or ordinary (0)
   uint16_t* q_out;          // [B, S, Hq, D]; calls 2 and 3
   const int32_t* end_lens;  // [B]; calls 2 and 3
   const int32_t* pos_ids;   // [B, S]; call 3
