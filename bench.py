@@ -571,7 +571,10 @@ def main():
                   lambda: W.with_fp8_cache(W.config(2, W.NEOX), 7002, fill="sentinel")),
                  ("paged_delta_fp8_cache",
                   lambda: W.with_fp8_cache(W.config(4), 7004, fill="sentinel")),
-                 ("continuous_neox_qknorm", lambda: W.with_qk_norm(W.config(2, W.NEOX), 7102))]
+                 ("continuous_neox_qknorm", lambda: W.with_qk_norm(W.config(2, W.NEOX), 7102)),
+                 # one GPU's share of the large prefill under 8-way tensor parallelism
+                 # (8 Q heads, 1 KV head; 193 MB, within the 256 MB MALL, hence flushed)
+                 ("prefill_tp8_shard", lambda: W.prefill_tp_shard(8))]
         for label, make in cases:
             log(f"[bench] generating {label}")
             x = make()

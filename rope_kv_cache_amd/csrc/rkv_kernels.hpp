@@ -117,19 +117,41 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
   const int H = p.Hq + 2 * p.Hkv;
   uint16_t* const tok_base = p.qkv + (size_t)token * H * D;
 
-  // Row loads first: they do not depend on the slot or the position.
+  // Calls 2 and 3: the token's end length (and position id) are requested
+  // first, as scalar loads, so that their wait does not include the row
+  // loads (vector loads complete in order).
+  int end_len = 0, pos_id = 0;
+  if constexpr (kCall != kCallPacked) {
+    end_len = p.end_lens[b];
+    if constexpr (kCall == kCallTree) pos_id = p.pos_ids[token];
+  }
+
+  // Row loads next: they do not depend on the slot or the position.  In
+  // calls 2 and 3, lanes past the token's last row (only in its last group)
+  // load that row again (same addresses, no extra traffic) and store
+  // nothing: a branch around the load makes the compiler wait for every row
+  // load before the cos/sin loads can be issued.  The empty asm keeps it
+  // from sinking the loads below the range check of the slot (it waits for
+  // nothing: no register of the loads is named).  Measured on MI355X: no
+  // change for NeoX, about 1.5% on a large GPT-J continuous write.
   uint4 x[G];
   int row[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     row[g] = (part * G + g) * kRowsPerGroup + row_in_group;
-    x[g] = row[g] < H ? ld16_stream(tok_base + (size_t)row[g] * D + 8 * c) : make_uint4(0, 0, 0, 0);
+    if constexpr (kCall == kCallPacked) {
+      x[g] = row[g] < H ? ld16_stream(tok_base + (size_t)row[g] * D + 8 * c)
+                        : make_uint4(0, 0, 0, 0);
+    } else {
+      x[g] = ld16_stream(tok_base + (size_t)(row[g] < H ? row[g] : H - 1) * D + 8 * c);
+    }
   }
+  if constexpr (kCall != kCallPacked) asm volatile("" ::: "memory");
 
   int slot = s, pos = s;
   if constexpr (kCall != kCallPacked) {
-    const long long slot64 = (long long)p.end_lens[b] - p.S + s;
-    const long long pos64 = (kCall == kCallTree) ? (long long)p.pos_ids[token] : slot64;
+    const long long slot64 = (long long)end_len - p.S + s;
+    const long long pos64 = (kCall == kCallTree) ? (long long)pos_id : slot64;
     if (slot64 < 0 || slot64 >= p.cap || pos64 < 0 || pos64 >= p.table_len) return;
     slot = (int)slot64;
     pos = (int)pos64;

@@ -57,6 +57,14 @@ def test_config(idx, style):
     check(w)
 
 
+@pytest.mark.parametrize("tp", [4, 8])
+def test_prefill_tensor_parallel_shard(tp):
+    """One GPU's share of the large prefill under tensor parallelism: Hq/tp
+    and Hkv/tp heads at the full batch and length, launched as the benchmark
+    launches it."""
+    check(W.prefill_tp_shard(tp))
+
+
 def test_config4_gptj():
     w = W.paged(4096, 32, 8, 128, 128, 8192, 128, GPTJ, 1014, name="paged_delta_gptj")
     check(w)

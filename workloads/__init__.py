@@ -375,3 +375,15 @@ def config(idx: int, style: int | None = None):
         return packed(4, 8192, 64, 8, 128, 128, 16384, GPTJ, 1005, table_batch=4,
                       table_len=8192, offsets=offs, name="prefill_b4_s8192_h64_d128")
     raise ValueError(idx)
+
+
+def prefill_tp_shard(tp: int):
+    """One GPU's share of the large prefill under tensor parallelism of degree
+    ``tp``: the same sequences, positions and tables, Hq/tp query heads and
+    Hkv/tp KV heads (the cache is head-sharded the same way)."""
+    assert 64 % tp == 0 and 8 % tp == 0, tp
+    r = rng(10050)
+    offs = np.concatenate([[0], r.integers(1, 8193, size=3)])
+    return packed(4, 8192, 64 // tp, 8 // tp, 128, 128, 16384, GPTJ, 1005 + 10 * tp,
+                  table_batch=4, table_len=8192, offsets=offs,
+                  name=f"prefill_tp{tp}_shard_b4_s8192_h{64 // tp}_kv{8 // tp}_d128")
