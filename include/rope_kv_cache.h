@@ -32,7 +32,11 @@
  *   launches that would need more waves than one dispatch holds (2^32 - 1
  *   work-items, 2^26 waves).  A wave handles up to four 1 KB row groups of
  *   one token or delta row (512/headDim head rows each), so the limit is
- *   about 2^28 row groups, and lower when tokens have few heads.
+ *   about 2^28 row groups, and lower when tokens have few heads.  A token's
+ *   head rows, and a delta row's K and V head rows, are addressed by 32-bit
+ *   byte offsets: (heads + 64) * headDim must stay below 2^31 (calls 1-3,
+ *   heads = Hq + 2*Hkv) and (2*numKVHeads + 64) * headDim below 2^30
+ *   (paged calls); beyond that the calls return RKV_ERR_UNSUPPORTED.
  * Rotation.  For frequency i < rotaryDim/2 with c = row[i] and
  *   s = row[rotaryDim/2 + i] of the token's cos/sin row, the pair (u, v)
  *   becomes (x_u*c - x_v*s, x_v*c + x_u*s), rounded to fp16 to nearest-even.

@@ -256,8 +256,10 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   }
   const long long tokens = B * S;
   if (tokens > INT32_MAX) return fail(RKV_ERR_UNSUPPORTED, "B*S=%lld exceeds 2^31-1", tokens);
-  if (H > INT32_MAX - 64)   // a token's head rows are indexed in int32
-    return fail(RKV_ERR_UNSUPPORTED, "%lld heads per token is too many", H);
+  // a token's head rows (and the padding rows of its last wave) are
+  // addressed by 32-bit byte offsets from the token's first row
+  if ((H + 64) * D >= (1LL << 31))
+    return fail(RKV_ERR_UNSUPPORTED, "%lld heads of %lld values per token is too many", H, D);
   if (tokens == 0 || H == 0) return RKV_OK;
 
   rkv::ContigParams p{};
@@ -280,6 +282,11 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   p.Hq = (int32_t)Hq;
   p.Hkv = (int32_t)Hkv;
   p.cap = (int32_t)cap;
+  // one batch's cache slice; stored through a buffer resource when its byte
+  // count fits the resource's 32-bit size
+  const unsigned long long slice = 2ull * (unsigned long long)Hkv * (unsigned long long)cap *
+                                   (unsigned long long)D * (fp8 ? 1u : 2u);
+  p.cache_b_bytes = slice <= 0xFFFFFFFFull ? (uint32_t)slice : 0u;
   p.table_batch = (int32_t)TB;
   p.table_len = (int32_t)TL;
   p.R = (int32_t)R;
@@ -333,7 +340,9 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
       !mul_ok(gather ? (long long)ropeStates * ropeRows : N, R, &cs_elems) ||
       pool_elems > (INT64_MAX / 2))
     return fail(RKV_ERR_SHAPE, "sizes overflow");
-  if (2 * Hkv > INT32_MAX - 64)   // a delta row's 2*Hkv head rows are indexed in int32
+  // a delta row's 2*Hkv head rows (and the padding rows of its last wave)
+  // are addressed by 32-bit byte offsets below 2^31
+  if ((2 * Hkv + 64) * D * 2 >= (1LL << 31))
     return fail(RKV_ERR_UNSUPPORTED, "numKVHeads %lld too large", Hkv);
   if (N == 0 || Hkv == 0) return RKV_OK;
   const float* cs = gather ? rope : tokenAlignedCosSin;

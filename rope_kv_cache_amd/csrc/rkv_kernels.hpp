@@ -75,6 +75,38 @@ __device__ __forceinline__ void st8_stream(uint8_t* p, uint2 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2*>(p));
 }
 
+// Buffer accesses: a resource (base address and size, wave-uniform, in
+// SGPRs) and a 32-bit byte offset per lane.  A load at or past the size
+// reads zeros without touching memory; a store there is dropped.  Their
+// cache-policy bits reach what the generic non-temporal builtins do not:
+// row stores are non-temporal at device scope (nt sc1).  Measured on MI355X
+// against non-temporal global stores, written buffers rotated so that no
+// launch rewrites lines the previous one left: the large GPT-J prefill
+// 228.8-229.1 -> 225.2-226.3 us, NeoX 237.6-238.3 -> 232.6-233.1 us;
+// without nt the stores are 8% slower.
+constexpr int kBufLoadStream = 2;        // nt
+constexpr int kBufStoreStream = 2 | 16;  // nt sc1
+constexpr int kBufDescWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+__device__ __forceinline__ BufRes buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kBufDescWord3);
+}
+
+__device__ __forceinline__ uint4 ld16_buf(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufLoadStream));
+}
+
+__device__ __forceinline__ void st16_buf(BufRes r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kBufStoreStream);
+}
+
+__device__ __forceinline__ void st8_buf(BufRes r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kBufStoreStream);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2.  Renumber them so that XCD x works through one contiguous range of
 // work items: neighbouring tokens then share an L2.
@@ -126,25 +158,21 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
     if constexpr (kCall == kCallTree) pos_id = p.pos_ids[token];
   }
 
-  // Row loads next: they do not depend on the slot or the position.  In
-  // calls 2 and 3, lanes past the token's last row (only in its last group)
-  // load that row again (same addresses, no extra traffic) and store
-  // nothing: a branch around the load makes the compiler wait for every row
-  // load before the cos/sin loads can be issued.  The empty asm keeps it
-  // from sinking the loads below the range check of the slot (it waits for
-  // nothing: no register of the loads is named).  Measured on MI355X: no
-  // change for NeoX, about 1.5% on a large GPT-J continuous write.
+  // Row loads next: they do not depend on the slot or the position.  They go
+  // through a buffer over the token's H rows: lanes past its last row (only
+  // in its last group) read zeros without touching memory and store
+  // nothing.  No branch surrounds the load: one made the compiler wait for
+  // every row load before the cos/sin loads of calls 2 and 3 could be
+  // issued.  For those calls the empty asm keeps it from sinking the loads
+  // below the range check of the slot (it waits for nothing: no register of
+  // the loads is named).  The host keeps H * D * 2 below 2^32.
+  const BufRes tok_buf = buffer_of(tok_base, (uint32_t)H * D * 2);
   uint4 x[G];
   int row[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     row[g] = (part * G + g) * kRowsPerGroup + row_in_group;
-    if constexpr (kCall == kCallPacked) {
-      x[g] = row[g] < H ? ld16_stream(tok_base + (size_t)row[g] * D + 8 * c)
-                        : make_uint4(0, 0, 0, 0);
-    } else {
-      x[g] = ld16_stream(tok_base + (size_t)(row[g] < H ? row[g] : H - 1) * D + 8 * c);
-    }
+    x[g] = ld16_buf(tok_buf, (uint32_t)(row[g] * D + 8 * c) * 2);
   }
   if constexpr (kCall != kCallPacked) asm volatile("" ::: "memory");
 
@@ -185,16 +213,29 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
   float k_rcp = 1.f, v_rcp = 1.f;
   if constexpr (kFp8) load_reciprocal_scales(p.k_scale, p.v_scale, k_rcp, v_rcp);
 
+  // Stores: Q rows (in place for call 1, to qOut for calls 2 and 3) and call
+  // 1's in-place K rows through buffers over the token's rows; cache rows
+  // through a buffer over batch b's two planes, or, when those reach 4 GB
+  // (cache_b_bytes == 0), by non-temporal global stores.
+  const BufRes q_buf = (kCall == kCallPacked)
+                           ? tok_buf
+                           : buffer_of(p.q_out + (size_t)token * p.Hq * D, (uint32_t)p.Hq * D * 2);
+  const size_t cache_b = (size_t)b * 2 * p.Hkv * p.cap * D;   // first element of batch b
+  const bool cache_buffered = p.cache_b_bytes != 0;
+  const BufRes cache_buf = kFp8 ? buffer_of(p.cache8 + cache_b, p.cache_b_bytes)
+                                : buffer_of(p.cache + cache_b, p.cache_b_bytes);
+
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int r = row[g];
     const bool is_q = r < p.Hq;
     const bool is_k = !is_q && r < p.Hq + p.Hkv;
     const int h = is_k ? r - p.Hq : r - p.Hq - p.Hkv;
-    const size_t cache_row =
-        (((size_t)b * 2 + (is_k ? 0 : 1)) * p.Hkv + h) * (size_t)p.cap + slot;
-    uint16_t* const q_dst = (kCall == kCallPacked) ? tok_base + (size_t)r * D
-                                                   : p.q_out + ((size_t)token * p.Hq + r) * D;
+    // element offset of the lane's chunk within batch b's cache, and byte
+    // offset of the row's chunk within the token's rows (Q and in-place K)
+    const size_t cache_el =
+        (((size_t)(is_k ? 0 : 1) * p.Hkv + h) * (size_t)p.cap + slot) * D + 8 * c;
+    const uint32_t row_off = (uint32_t)(r * D + 8 * c) * 2;
     if constexpr (kFp8 || kNorm) {
       // the unrounded row values, then fp16 and / or E4M3 from them
       WideT<kExact> w[8];
@@ -208,24 +249,28 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
       }
       if (r >= H) continue;
       if (is_q) {
-        st16_stream(q_dst + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
+        st16_buf(q_buf, row_off, narrow_chunk<kExact>(w, x[g], comp));
       } else if constexpr (kFp8) {
-        st8_stream(p.cache8 + cache_row * D + 8 * c, to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp));
+        const uint2 e = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
+        if (cache_buffered) st8_buf(cache_buf, (uint32_t)cache_el, e);
+        else st8_stream(p.cache8 + cache_b + cache_el, e);
         if (kCall == kCallPacked && is_k)
-          st16_stream(tok_base + (size_t)r * D + 8 * c, narrow_chunk<kExact>(w, x[g], comp));
+          st16_buf(tok_buf, row_off, narrow_chunk<kExact>(w, x[g], comp));
       } else {
         const uint4 y = narrow_chunk<kExact>(w, x[g], comp);
-        st16_stream(p.cache + cache_row * D + 8 * c, y);
-        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
+        if (cache_buffered) st16_buf(cache_buf, (uint32_t)cache_el * 2, y);
+        else st16_stream(p.cache + cache_b + cache_el, y);
+        if (kCall == kCallPacked && is_k) st16_buf(tok_buf, row_off, y);
       }
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_q || is_k, cs, sn);
       if (r >= H) continue;
       if (is_q) {
-        st16_stream(q_dst + 8 * c, y);
+        st16_buf(q_buf, row_off, y);
       } else {
-        st16_stream(p.cache + cache_row * D + 8 * c, y);
-        if (kCall == kCallPacked && is_k) st16_stream(tok_base + (size_t)r * D + 8 * c, y);
+        if (cache_buffered) st16_buf(cache_buf, (uint32_t)cache_el * 2, y);
+        else st16_stream(p.cache + cache_b + cache_el, y);
+        if (kCall == kCallPacked && is_k) st16_buf(tok_buf, row_off, y);
       }
     }
   }
@@ -315,7 +360,10 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
                              sn);
     }
   }
-  // large launches are bandwidth-bound: load only the rows that will be written
+  // Large launches are bandwidth-bound: load only the rows that will be
+  // written.  (Loads from buffers over the row's K and V heads, each lane
+  // issuing both with the wrong one out of range, measured 4% slower on a
+  // 65,536-row update than these branches.)
   if constexpr (kStream) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -331,6 +379,22 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   float k_rcp = 1.f, v_rcp = 1.f;
   if constexpr (kFp8) load_reciprocal_scales(p.k_scale, p.v_scale, k_rcp, v_rcp);
 
+  // Large launches store through buffers over the K page row and the V page
+  // row of the delta row's slot (empty when unmapped), non-temporally at
+  // device scope; a group's store into a plane is skipped when none of its
+  // rows belongs to that plane (a wave-uniform test), and a lane's offset in
+  // the other plane is kNowhere, past the end of every buffer.  The host
+  // keeps 4 * Hkv * D below 2^31.  Measured on MI355X, a 65,536-row fp16
+  // update with the pool rotated among four buffers: 79.6-84.9 -> 77.9-78.2 us.
+  constexpr uint32_t kNowhere = 0x80000000u;
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * (kFp8 ? 1 : 2);   // one plane's page row
+  const size_t k_slot = ((size_t)(k_ok ? kid : 0) * kTpp + off) * p.Hkv * D;
+  const size_t v_slot = ((size_t)(v_ok ? vid : 0) * kTpp + off) * p.Hkv * D;
+  const BufRes kp = kFp8 ? buffer_of(p.pool8 + k_slot, k_ok ? row_bytes : 0u)
+                         : buffer_of(p.pool + k_slot, k_ok ? row_bytes : 0u);
+  const BufRes vp = kFp8 ? buffer_of(p.pool8 + v_slot, v_ok ? row_bytes : 0u)
+                         : buffer_of(p.pool + v_slot, v_ok ? row_bytes : 0u);
+
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int r = row[g];
@@ -338,18 +402,29 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
     const int h = is_k ? r : r - p.Hkv;
     const size_t page = (size_t)(is_k ? kid : vid);
     const size_t pool_row = (page * kTpp + off) * p.Hkv + h;
+    const int g0 = (part * G + g) * kRowsPerGroup;   // the group's first row (wave-uniform)
+    const uint32_t el_k = r < p.Hkv ? (uint32_t)(r * D + 8 * c) : kNowhere;
+    const uint32_t el_v = r >= p.Hkv ? (uint32_t)((r - p.Hkv) * D + 8 * c) : kNowhere;
     if constexpr (kFp8) {
       WideT<kExact> w[8];
       rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn, w);
-      if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-      uint8_t* const dst = p.pool8 + pool_row * D + 8 * c;
       const uint2 b = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
-      if constexpr (kStream) st8_stream(dst, b); else st8(dst, b);
+      if constexpr (kStream) {
+        if (g0 < p.Hkv) st8_buf(kp, el_k, b);
+        if (g0 + kRowsPerGroup > p.Hkv) st8_buf(vp, el_v, b);
+      } else {
+        if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
+        st8(p.pool8 + pool_row * D + 8 * c, b);
+      }
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn);
-      if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-      if constexpr (kStream) st16_stream(p.pool + pool_row * D + 8 * c, y);
-      else st16(p.pool + pool_row * D + 8 * c, y);
+      if constexpr (kStream) {
+        if (g0 < p.Hkv) st16_buf(kp, el_k == kNowhere ? kNowhere : el_k * 2, y);
+        if (g0 + kRowsPerGroup > p.Hkv) st16_buf(vp, el_v == kNowhere ? kNowhere : el_v * 2, y);
+      } else {
+        if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
+        st16(p.pool + pool_row * D + 8 * c, y);
+      }
     }
   }
 }

@@ -53,6 +53,8 @@ struct ContigParams {
   const int32_t* pos_ids;   // [B, S]; call 3
   int32_t B, S, Hq, Hkv, cap;
   int32_t table_batch, table_len, R;
+  uint32_t cache_b_bytes;   // bytes of one batch's cache slice (2 * Hkv * cap * D
+                            //   elements), or 0 when it reaches 2^32
   int32_t groups_per_wave;  // G: row groups of 512/D rows handled by one wave (1, 2 or 4)
   int32_t waves_per_token;  // ceil(row groups per token / G)
   int32_t total_waves;      // B * S * waves_per_token

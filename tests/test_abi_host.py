@@ -227,6 +227,19 @@ def test_more_waves_than_one_dispatch_is_unsupported():
     assert b"too many rows" in L.rkv_last_error()
 
 
+@no_gpu
+def test_token_rows_beyond_32bit_offsets_are_unsupported():
+    """A token's head rows are addressed by 32-bit byte offsets: 2^23 heads
+    of 256 values (4 GiB per token) are refused before any launch."""
+    H = 1 << 23
+    cs = fake(F32, 1, 4, 256, addr=1 << 42)
+    qkv = fake(F16, 1, 1, H, 256, addr=2 << 42)
+    cache = fake(F16, 1, 2, 1, 4, 256, addr=3 << 42)
+    st = call_packed(cs, qkv, cache, style=1)
+    assert st == rkv.ERR_UNSUPPORTED, (rkv.status_string(st), L.rkv_last_error())
+    assert b"heads of 256 values per token" in L.rkv_last_error()
+
+
 # -------------------------------------------------------- calls 2 and 3 ---
 
 @no_gpu

@@ -81,3 +81,28 @@ def test_kernel_source_hash_ignores_comments_only(tmp_path):
     assert bench.kernel_source_hash(str(tmp_path)) == h0
     (tmp_path / "a.hip").write_text(src.replace("p[0] = 1", "p[0] = 2"))
     assert bench.kernel_source_hash(str(tmp_path)) != h0
+
+
+def test_rotated_copies_only_the_written_tensors():
+    """Back-to-back timings cycle through copies of what a call writes: call 1
+    writes qkv and the cache, calls 2-3 the cache and qOut, call 4 the pool;
+    everything else is shared."""
+    import torch
+    from harness import upload
+    cases = [(W.config(1), ("qkv", "cache")), (W.config(2), ("cache", "q_out")),
+             (W.config(3), ("cache", "q_out"))]
+    for w, keys in cases:
+        t = upload(w, device="cpu")
+        sets = bench.rotated(w, t, 3)
+        assert len(sets) == 3 and sets[0] is t
+        assert bench.written_keys(w) == keys
+        for u in sets[1:]:
+            assert set(u) == set(t)
+            for k, v in u.items():
+                if k in keys:
+                    assert v is not t[k] and v.data_ptr() != t[k].data_ptr()
+                    assert torch.equal(v.view(torch.int16), t[k].view(torch.int16))
+                else:
+                    assert v is t[k]
+    p = W.paged(64, 2, 2, 64, 64, 8, 4, W.NEOX, 5, name="p")
+    assert bench.written_keys(p) == ("pool",)

@@ -240,10 +240,15 @@ def test_paged_pool_beyond_4g_elements():
     torch.cuda.empty_cache()
 
 
-def test_contiguous_cache_beyond_4g_elements():
-    """An 8 GiB cache [8, 2, 8, 262144, 128] (2^32 elements) written near its
-    end: the last rows lie beyond 2^31 and close to 2^32 elements."""
-    B, S, Hq, Hkv, D, cap = 8, 16, 4, 8, 128, 1 << 18
+@pytest.mark.parametrize("B,cap", [(8, 1 << 18), (2, 1 << 20)],
+                         ids=["slice_1GiB_buffer_stores", "slice_4GiB_global_stores"])
+def test_contiguous_cache_beyond_4g_elements(B, cap):
+    """An 8 GiB cache [B, 2, 8, cap, 128] (2^32 elements) written near its
+    end: the last rows lie beyond 2^31 and close to 2^32 elements.  With
+    B = 8 each batch's slice is 1 GiB and its rows are stored through a
+    buffer resource; with B = 2 a slice is 4 GiB, past a resource's 32-bit
+    size, and the kernel stores the rows with global stores instead."""
+    S, Hq, Hkv, D = 16, 4, 8, 128
     r = np.random.default_rng(91)
     qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
     end = (cap - np.arange(B) * 1000).astype(np.int32)
@@ -256,7 +261,7 @@ def test_contiguous_cache_beyond_4g_elements():
                        q_out=W.sentinel_f16((B, S, Hq, D)), end_lens=(end - lo).astype(np.int32),
                        name="continuous_cache_8GiB_compact")
     want = expected(w_small)
-    _say("[parity] contiguous cache 8 GiB")
+    _say(f"[parity] contiguous cache 8 GiB, B={B}, cap={cap}")
     cache = torch.empty((B, 2, Hkv, cap, D), dtype=torch.float16, device="cuda")
     cache.view(torch.int16).fill_(W.SENTINEL)
     import rope_kv_cache_amd as rkv
