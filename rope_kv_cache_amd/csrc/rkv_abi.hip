@@ -396,9 +396,12 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.max_pages = maxPagesPerSeq;
   const long long rows_per_group = 512 / D;
   const long long groups_per_row = (2 * Hkv + rows_per_group - 1) / rows_per_group;
-  const int g_start =
+  // row groups per wave: E4M3 pools take four in large launches (65,536
+  // rows: 72-74 -> 64-65 us on MI355X), NeoX, exact and E4M3 two otherwise
+  const int g_small =
       (exact_of(ropeStyle) || fp8 || layout_of(ropeStyle) == RKV_ROPE_NEOX) ? 2 : 1;
-  const Split sp = pick_split(N, groups_per_row, g_start, g_start);
+  const int g_large = fp8 ? 4 : g_small;
+  const Split sp = pick_split(N, groups_per_row, g_large, g_small);
   // non-temporal delta loads and pool stores for large launches (small fp16
   // ones run faster when the caches absorb the pool writes); E4M3 pools
   // always take them
