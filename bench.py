@@ -284,28 +284,33 @@ def calibration_copy():
     torch.cuda.empty_cache()
 
 
-def paged_large(steps, warmup=3):
+def paged_large(steps, warmup=3, fp8=False):
     """The paged update at a size where bandwidth, not the launch, bounds
     it: 65,536 delta rows of the paged workload's shape (0.27 GB of deltas,
-    beyond the 256 MB MALL) into the 2 GiB pool, launches back to back."""
+    beyond the 256 MB MALL) into the 2 GiB pool (1 GiB with `fp8`: an E4M3
+    pool with per-tensor scales), launches back to back."""
     import torch
     import workloads as W
     from harness import upload
-    log("[bench] generating paged_delta_large")
+    label = "paged_delta_large_fp8" if fp8 else "paged_delta_large"
+    log(f"[bench] generating {label}")
     x = W.paged(65536, 64, 8, 128, 128, 8192, 128, W.NEOX, 1044, pool_fill="none",
                 name="paged_delta_n65536_p8192")
+    if fp8:
+        W.with_fp8_cache(x, 7044, fill="sentinel")
     xb = algorithmic_bytes(x)
     tx = upload(x)
-    # the 2 GiB pool is filled on the device (its contents do not change the work)
+    # the pool is filled on the device (its contents do not change the work)
     tx["pool"] = torch.zeros((2, x.num_pages, W.TOKENS_PER_PAGE, x.Hkv, x.D),
-                             dtype=torch.float16, device="cuda")
+                             dtype=torch.uint8 if fp8 else torch.float16, device="cuda")
     k_ms, _ = time_launches(x, tx, steps, warmup)
     gbs = xb / (k_ms * 1e-3) / 1e9
-    log(f"[bench] paged_delta_large: {k_ms * 1e3:.1f} us, {gbs:.0f} GB/s "
+    log(f"[bench] {label}: {k_ms * 1e3:.1f} us, {gbs:.0f} GB/s "
         f"({gbs / PEAK_HBM_GBS:.1%})")
     del tx, x
     torch.cuda.empty_cache()
-    return {"workload": "paged_delta_n65536_p8192", "kernel_us": k_ms * 1e3, "GB/s": gbs,
+    return {"workload": "paged_delta_n65536_p8192" + ("_fp8" if fp8 else ""),
+            "kernel_us": k_ms * 1e3, "GB/s": gbs,
             "frac": gbs / PEAK_HBM_GBS, "tokens_per_s": 65536 / (k_ms * 1e-3),
             "algorithmic_bytes": xb, "note": "launches back to back over 4 copies of the written tensors, event span / count"}
 
@@ -633,6 +638,7 @@ def main():
         del flush_buf
         torch.cuda.empty_cache()
         extra["paged_delta_large"] = paged_large(max(10, args.steps // 2))
+        extra["paged_delta_large_fp8"] = paged_large(max(10, args.steps // 2), fp8=True)
         # call 2 at a size where bandwidth bounds it: 16 sequences x 1024 new tokens
         # (0.4 GB moved, beyond the 256 MB MALL)
         log("[bench] generating continuous_large")

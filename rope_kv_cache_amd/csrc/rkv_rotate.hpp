@@ -199,27 +199,6 @@ __device__ __forceinline__ ChunkRole chunk_role(int c, int R) {
   return r;
 }
 
-// The cos/sin values a rotary lane needs from one table row [cos | sin]:
-// NeoX: 8 frequencies from freq0; GPT-J: 4 frequencies from freq0 (c[0..3]).
-template <int kStyle>
-__device__ __forceinline__ void load_cos_sin(const float* row, int freq0, int R, float (&c)[8],
-                                             float (&s)[8]) {
-  const int half = R >> 1;
-  const float4 c0 = *reinterpret_cast<const float4*>(row + freq0);
-  const float4 s0 = *reinterpret_cast<const float4*>(row + half + freq0);
-  c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
-  s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
-  if constexpr (kStyle == kNeox) {
-    const float4 c1 = *reinterpret_cast<const float4*>(row + freq0 + 4);
-    const float4 s1 = *reinterpret_cast<const float4*>(row + half + freq0 + 4);
-    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
-    s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-  } else {
-#pragma unroll
-    for (int k = 4; k < 8; ++k) { c[k] = 0.f; s[k] = 0.f; }
-  }
-}
-
 // Rotate (or pass through) one chunk.  Must be called by every lane of the
 // wave with the same control flow (the NeoX partner fetch is a wave-wide
 // permute); lanes whose row is not rotated simply keep their value.
