@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from harness import (compare, dev, download, exact_diffs, expected, host8, launch, run_gpu,
+from harness import (compare, dev, download, exact_diffs, expected, host8, host16, launch, run_gpu,
                      upload)
 
 pytestmark = pytest.mark.gpu
@@ -221,4 +221,41 @@ def test_fp8_pool_beyond_4g_elements():
             g = host8(pool.view(2 * P, 64, Hkv, D)[pid])
             assert np.array_equal(g, wflat[plane * nc + rank]), (plane, pid)
     del pool
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,cap", [(2, 1 << 20), (1, 1 << 21)],
+                         ids=["slice_2GiB_buffer_stores", "slice_4GiB_global_stores"])
+def test_fp8_cache_beyond_4g_elements(B, cap):
+    """A 4 GiB E4M3 cache [B, 2, 8, cap, 128] (2^32 elements) written near
+    its end.  With B = 2 each batch's slice is 2 GiB and its rows are stored
+    through a buffer resource; with B = 1 the slice is 4 GiB, past a
+    resource's 32-bit size, and the kernel stores the rows with global stores
+    instead.  The oracle runs on a compact cache of the last slots."""
+    import rope_kv_cache_amd as rkv
+    S, Hq, Hkv, D = 16, 4, 8, 128
+    r = np.random.default_rng(93)
+    qkv = W.normal_f16(r, (B, S, Hq + 2 * Hkv, D))
+    end = (cap - np.arange(B) * 1000).astype(np.int32)
+    cs_full = W.rope_table(1, cap, D, 10000.0)
+    lo = int(end.min()) - S
+    w_small = W.Contig("continuous", GPTJ, B, S, Hq, Hkv, D, D, cap - lo, cs_full[:, lo:], qkv,
+                       np.full((B, 2, Hkv, cap - lo, D), W.SENTINEL8, np.uint8),
+                       q_out=W.sentinel_f16((B, S, Hq, D)), end_lens=(end - lo).astype(np.int32),
+                       name="continuous_fp8_cache_compact")
+    w_small.extra["fp8"] = {"k_scale": np.float32(W.K_SCALE), "v_scale": np.float32(W.V_SCALE)}
+    want = expected(w_small)
+    _say(f"[parity-fp8] E4M3 cache 4 GiB, B={B}, cap={cap}")
+    cache = torch.full((B, 2, Hkv, cap, D), W.SENTINEL8, dtype=torch.uint8, device="cuda")
+    q_out = dev(W.sentinel_f16((B, S, Hq, D)))
+    ks = torch.tensor([W.K_SCALE], dtype=torch.float32, device="cuda")
+    vs = torch.tensor([W.V_SCALE], dtype=torch.float32, device="cuda")
+    rkv.apply_rope_write_kv_continuous_fp8(dev(cs_full), dev(end), dev(qkv), cache, q_out, ks, vs,
+                                           GPTJ | rkv.ROUND_EXACT)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(q_out), want["q_out"])
+    assert np.array_equal(host8(cache[:, :, :, lo:]), want["cache"])
+    written = (cache != W.SENTINEL8).any(dim=-1).sum().item()
+    assert written == B * S * 2 * Hkv
+    del cache
     torch.cuda.empty_cache()
