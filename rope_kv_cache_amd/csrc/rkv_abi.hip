@@ -304,6 +304,9 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_token = sp.waves_per_item;
+  // large launches: the XCDs take chunks of 128 workgroups in turn
+  const long long groups = tokens * ((H + rows_per_group - 1) / rows_per_group);
+  p.xcd_chunk_log2 = groups > kStreamingGroups ? 7 : 0;
   p.total_waves = (int32_t)(tokens * p.waves_per_token);
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_token);
   p.div_seq = rkv::make_fastdiv((uint32_t)S);

@@ -180,16 +180,40 @@ __device__ __forceinline__ void spread_cos_sin(const CosSinRaw& raw, float (&c)[
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
-// L2.  Renumber them so that XCD x works through one contiguous range of
-// work items: neighbouring tokens then share an L2.
-__device__ __forceinline__ int block_id_xcd_major() {
-  const int n = (int)gridDim.x, bid = (int)blockIdx.x;
+// L2: workgroup bid runs on XCD bid % 8.  Renumbering them sets which work
+// items share an L2 and how the XCDs move through memory together.
+//  chunk_log2 == 0: XCD x works through one contiguous eighth of the items.
+//  chunk_log2 > 0: the XCDs take chunks of 2^chunk_log2 workgroups in turn
+//   (XCD x gets chunks x, x + 8, ...), so all eight sweep the tensors side by
+//   side; the blocks past the last whole round of 8 chunks are numbered as
+//   for 0.  Both numberings are permutations of [0, gridDim.x).
+// Measured on MI355X with the written buffers rotated, chunks of 128
+// workgroups against contiguous eighths: the 16 x 1024-token NeoX continuous
+// write 72.7-72.9 -> 66.4-66.5 us, the large prefill with Q/K norm
+// 231.3-232.8 -> 224.9-225.2 us, NeoX 229.9-230.1 -> 223.6-224.4 us, GPT-J
+// 225.9-227.2 -> 224.4-225.0 us; the paged update was 2-4% slower with them
+// and small launches (all waves resident at once) 1-2%: those keep
+// contiguous eighths.  chunk_log2 is wave-uniform (a launch parameter).
+__device__ __forceinline__ int xcd_contiguous(int bid, int n) {
   const int x = bid & 7, q = n >> 3, r = n & 7;
   return x * q + (x < r ? x : r) + (bid >> 3);
 }
 
-__device__ __forceinline__ int wave_id_uniform() {
-  return __builtin_amdgcn_readfirstlane(block_id_xcd_major() * kWavesPerBlock +
+__device__ __forceinline__ int block_id_xcd(int chunk_log2) {
+  const int n = (int)gridDim.x, bid = (int)blockIdx.x;
+  if (chunk_log2 == 0) return xcd_contiguous(bid, n);
+  // blocks in whole rounds of 8 chunks (a power of two: no division, which
+  // would put some 30 instructions before every wave's first load)
+  const int full = n & ~((8 << chunk_log2) - 1);
+  if (bid < full) {
+    const int k = bid >> 3, mask = (1 << chunk_log2) - 1;
+    return ((((k >> chunk_log2) << 3) + (bid & 7)) << chunk_log2) + (k & mask);
+  }
+  return full + xcd_contiguous(bid - full, n - full);
+}
+
+__device__ __forceinline__ int wave_id_uniform(int chunk_log2) {
+  return __builtin_amdgcn_readfirstlane(block_id_xcd(chunk_log2) * kWavesPerBlock +
                                         (int)(threadIdx.x >> 6));
 }
 
@@ -206,7 +230,7 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
 
-  const int wave = wave_id_uniform();
+  const int wave = wave_id_uniform(p.xcd_chunk_log2);
   if (wave >= p.total_waves) return;
   const int token = (int)fast_div((uint32_t)wave, p.div_waves);
   const int part = wave - token * p.waves_per_token;
@@ -377,7 +401,7 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
   constexpr int kTpp = kTokensPerPage;
 
-  const int wave = wave_id_uniform();
+  const int wave = wave_id_uniform(0);
   if (wave >= p.total_waves) return;
   const int i = (int)fast_div((uint32_t)wave, p.div_waves);
   const int part = wave - i * p.waves_per_row;

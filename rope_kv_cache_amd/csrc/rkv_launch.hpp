@@ -55,6 +55,8 @@ struct ContigParams {
   int32_t table_batch, table_len, R;
   uint32_t cache_b_bytes;   // bytes of one batch's cache slice (2 * Hkv * cap * D
                             //   elements), or 0 when it reaches 2^32
+  int32_t xcd_chunk_log2;   // workgroup numbering: 0 contiguous eighths per XCD,
+                            //   else chunks of 2^xcd_chunk_log2 taken in turn
   int32_t groups_per_wave;  // G: row groups of 512/D rows handled by one wave (1, 2 or 4)
   int32_t waves_per_token;  // ceil(row groups per token / G)
   int32_t total_waves;      // B * S * waves_per_token
