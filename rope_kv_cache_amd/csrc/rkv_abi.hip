@@ -294,13 +294,12 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
   const bool neox = layout_of(style) == RKV_ROPE_NEOX;
   // large launches (measured on MI355X with the written buffers rotated):
-  // two row groups per wave, four for the exact mode of the NeoX layout and
-  // of the E4M3 cache (272 -> 258 us and 274 -> 262 us on a 1.4 GB prefill)
-  // and for the Q/K norm in the NeoX layout or into an E4M3 cache.  (Plain
-  // GPT-J took one until the XCDs took chunks in turn; then two: 222-224 ->
-  // 220-221 us on the 1.4 GB prefill, -5% on its TP=8 shard.)
-  const bool exact = exact_of(style);
-  const int g_large = norm ? ((neox || fp8) ? 4 : 2) : ((exact && (neox || fp8)) ? 4 : 2);
+  // two row groups per wave; four for the exact mode (1.4 GB prefill: NeoX
+  // 272 -> 258 us, E4M3 274 -> 262 us, GPT-J 235-240 -> 230 us) and for the
+  // Q/K norm in the NeoX layout or into an E4M3 cache.  (Plain GPT-J took one
+  // until the XCDs took chunks in turn; then two: 222-224 -> 220-221 us on
+  // the 1.4 GB prefill, -5% on its TP=8 shard.)
+  const int g_large = norm ? ((neox || fp8) ? 4 : 2) : (exact_of(style) ? 4 : 2);
   const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, g_large,
                               norm ? 4 : (heavy ? 2 : 1));
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
