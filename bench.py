@@ -6,23 +6,30 @@ per-sequence cos/sin tables (1.43 GB of algorithmic traffic).  Inputs are
 seeded synthetic data already resident in HBM.  W warm-up steps, then K timed
 steps back to back, bracketed by device synchronisation and by one pair of
 HIP events on the launch stream, whose span / K is the kernel's average
-duration for the roofline.  The same workload in the library's RKV_ROUND_EXACT mode and the
-other workloads (continuous write, tree write, paged delta update, the
-paged update with the cos/sin gather fused in, the prefill, continuous
-and paged calls into an E4M3 cache, the prefill and continuous calls
-with Q/K RMS norm, the prefill in the NeoX layout, a 65,536-row paged update,
-a 16-sequence continuous write, and the two device index builders) are
-reported under "workloads".  The
-small workloads' inputs fit the 256 MB
-MALL, so a 1 GiB buffer is read before each of their timed launches to push
-them back to HBM (a read leaves clean lines, so the timed kernel inherits no
-write-back); their event-bracketed times include the events' own overhead
-of a few microseconds, so rocprofv3's kernel trace is the reference there.
+duration for the roofline.  The same workload in the library's
+RKV_ROUND_EXACT mode, the NeoX layout, into an E4M3 cache and with Q/K RMS
+norm, and the other workloads (continuous write, tree write, paged delta
+update, the paged update with the cos/sin gather fused in, the continuous
+and paged calls into an E4M3 cache, the continuous call with Q/K RMS norm,
+the prefill's TP=8 shard, a 65,536-row paged update, a 16-sequence
+continuous write, and the two device index builders) are reported under
+"workloads".  The small workloads' inputs fit the 256 MB MALL: they are
+timed cold (``time_cold``: each launch after a 1 GiB read that evicts its
+inputs, all work queued behind a GPU spin, the median event pair around the
+launch minus the median event pair around nothing) and back to back; their
+figure of record is timed like the headline, back to back, cycling through
+enough full copies of every tensor they touch that each launch reads from
+and writes back to HBM (``full_copies``, ``time_rotated``).
+
+``--workload NAME`` times single small workloads and ``--ceilings`` the
+measurement kernels of ``ceilings/`` (stream ceilings, empty kernels, an
+index-free floor of the paged update, the LDS-staged prefill) beside the
+library's kernels; both exist for rocprofv3 runs.
 
 Prints one JSON line on stdout; progress goes to stderr.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-                      [--calib] [--floors] [--paged-large]
+                      [--calib] [--paged-large] [--workload NAME]... [--ceilings]
 """
 from __future__ import annotations
 
@@ -174,76 +181,183 @@ def rotated(w, t, n):
     return sets
 
 
-def time_launches(w, t, steps, warmup, flush=None, exact=False, queue_ahead=False):
-    """Kernel duration and wall time of `steps` launches.
-
-    Without `flush`: the launches run back to back on the current stream,
-    bracketed by one pair of HIP events and by device synchronisations, so
-    that nothing but the launches is timed; the kernel duration is the
-    events' span divided by the launch count (the gaps between back-to-back
-    launches, about a microsecond, are included).  They cycle through
-    ROTATIONS copies of the written tensors (`rotated`), except with
-    `queue_ahead`, which times warm launches on purpose.  With `flush` (small
-    workloads): a flush runs before each launch, so each launch has its own
-    pair of events (their overhead included).  `queue_ahead` (short
-    kernels, back to back): the GPU first spins long enough for the host to
-    queue every launch, so the span measures the kernels, not the host's
-    launch rate."""
+def time_launches(w, t, steps, warmup, exact=False):
+    """Kernel duration and wall time of `steps` launches back to back on the
+    current stream, bracketed by one pair of HIP events and by device
+    synchronisations, so that nothing but the launches is timed; the kernel
+    duration is the events' span divided by the launch count (the gaps
+    between back-to-back launches, a few tenths of a microsecond, are
+    included).  They cycle through ROTATIONS copies of the written tensors
+    (`rotated`)."""
     import torch
-    from harness import launch as launch_exact
-
-    def launch(w, t):
-        launch_exact(w, t, exact)
+    from harness import launch
 
     stream = torch.cuda.current_stream()
-    sets = rotated(w, t, ROTATIONS) if flush is None and not queue_ahead else [t]
+    sets = rotated(w, t, ROTATIONS)
     for k in range(warmup):
-        if flush is not None:
-            flush()
-        launch(w, sets[k % len(sets)])
+        launch(w, sets[k % len(sets)], exact)
     torch.cuda.synchronize()
-    wall = 0.0
-    if flush is None:
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        if queue_ahead:
-            gpu_busy_wait(2000 + 50 * steps)
-        t0 = time.perf_counter()
-        start.record(stream)
-        for k in range(steps):
-            launch(w, sets[k % len(sets)])
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        del sets
-        return start.elapsed_time(end) / steps, wall
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
     for k in range(steps):
-        flush()
-        starts[k].record(stream)
-        launch(w, t)
-        ends[k].record(stream)
+        launch(w, sets[k % len(sets)], exact)
+    end.record(stream)
     torch.cuda.synchronize()
-    kernel_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
-    return kernel_ms, wall
+    wall = time.perf_counter() - t0
+    del sets
+    return start.elapsed_time(end) / steps, wall
 
 
-def time_calls(fn, steps, warmup=3):
-    """Average duration of fn()'s launch, events on the current stream."""
+def time_flushed(launch, flush, steps, pairs=5):
+    """Cost of one launch whose inputs start in HBM, write-back included.
+
+    Two series run back to back on the current stream, each between one
+    pair of HIP events: `steps` x (flush, launch) and `steps` x flush alone;
+    their difference / `steps` is the launch's cost.  The flush (a 1 GiB
+    read) evicts the launch's inputs from L2 and MALL before it, and the
+    next flush pays for writing back whatever lines the launch left dirty,
+    so the figure covers the launch's writes reaching memory; it also
+    covers the dispatch gap between two queued kernels (a few tenths of a
+    microsecond).  Median over `pairs` pairs of series.  Returns ms."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        flush()
+        launch()
+    torch.cuda.synchronize()
+    diffs = []
+    for _ in range(pairs):
+        spans = []
+        for with_launch in (True, False):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps):
+                flush()
+                if with_launch:
+                    launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            spans.append(a.elapsed_time(b))
+        diffs.append((spans[0] - spans[1]) / steps)
+    return float(np.median(diffs))
+
+
+def time_cold(launch, flush, steps):
+    """Duration of one launch whose inputs start in HBM, without the timer's
+    own cost (ms), and that cost.
+
+    Everything is queued behind a GPU spin, so the host's launch rate is not
+    timed: `steps` x (flush, event A, launch, event B, flush, event C,
+    event D).  B - A covers the launch and the processing of one event; D - C
+    the processing of one event alone, under the same conditions; the
+    launch's duration is median(B - A) - median(D - C).  The flush (a 1 GiB
+    read) evicts the launch's inputs from L2 and MALL; the launch's stores
+    have left L2 when it completes (rocprofv3's WRITE_SIZE over a dispatch
+    equals the bytes the kernel writes)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        flush()
+        launch()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    gpu_busy_wait(500)
+    for a, b, c, d in ev:
+        flush()
+        a.record(stream)
+        launch()
+        b.record(stream)
+        flush()
+        c.record(stream)
+        d.record(stream)
+    torch.cuda.synchronize()
+    with_launch = float(np.median([a.elapsed_time(b) for a, b, _, _ in ev]))
+    alone = float(np.median([c.elapsed_time(d) for _, _, c, d in ev]))
+    return with_launch - alone, alone
+
+
+MALL_BYTES = 256 << 20
+
+
+def full_copies(t, nbytes_per_launch, min_span=3 * MALL_BYTES, most=64):
+    """Copies of every tensor a launch touches (inputs and outputs), enough
+    of them that consecutive uses of one copy are separated by at least
+    `min_span` bytes of other launches' traffic (three times the 256 MB
+    MALL): cycling through them, no launch finds its inputs in the caches
+    and every launch's writes are written back to HBM in steady state."""
+    n = max(2, min(most, -(-min_span // max(nbytes_per_launch, 1)) + 1))
+    return [t] + [{k: (None if v is None else v.clone()) for k, v in t.items()}
+                  for _ in range(n - 1)]
+
+
+def time_rotated(launch_set, sets, steps, warmup=None):
+    """Steady state of back-to-back launches that cycle through `sets`: the
+    GPU first spins long enough for the host to queue every launch, then
+    the launches run; event span / count (ms).  With `full_copies` sets this
+    is the HBM-bound cost per launch, as the headline is timed."""
+    import torch
+    stream = torch.cuda.current_stream()
+    warmup = len(sets) if warmup is None else warmup
+    for k in range(warmup):
+        launch_set(sets[k % len(sets)])
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    gpu_busy_wait(2000 + 50 * steps)
+    a.record(stream)
+    for k in range(steps):
+        launch_set(sets[(warmup + k) % len(sets)])
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def time_queued(launch, steps, warmup=3):
+    """Back to back: the GPU first spins long enough for the host to queue
+    every launch, then the launches run; event span / count (ms)."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        fn()
+        launch()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for k in range(steps):
-        starts[k].record(stream)
-        fn()
-        ends[k].record(stream)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    gpu_busy_wait(2000 + 50 * steps)
+    a.record(stream)
+    for _ in range(steps):
+        launch()
+    b.record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    return a.elapsed_time(b) / steps
+
+
+def make_flush():
+    """A 1 GiB read (torch's sum into one float): leaves L2 and the 256 MB
+    MALL holding clean lines of its own buffer."""
+    import torch
+    buf = torch.ones(1 << 29, dtype=torch.float16, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        torch.sum(buf, dim=0, dtype=torch.float32, out=sink)
+    return flush
+
+
+ROTATED_PROTOCOL = ("rotated: launches back to back, queued ahead behind a GPU spin, cycling "
+                    "through full copies of every tensor the call reads or writes (at least 768 "
+                    "MB of traffic between two uses of a copy, three times the MALL), event "
+                    "span / count: every input comes from HBM and every write reaches HBM in "
+                    "steady state, as for the headline")
+COLD_PROTOCOL = ("cold: every launch follows a 1 GiB read that evicts its inputs from L2 and "
+                 "MALL; all work queued behind a GPU spin; median over K launches of the event "
+                 "pair around the launch minus the median of an event pair around nothing, "
+                 "recorded the same way")
+MARGINAL_PROTOCOL = ("marginal: span of K x (1 GiB read, launch) minus span of K x (1 GiB "
+                     "read), / K: the time one launch adds to a stream of HBM-bound work, its "
+                     "dispatch and the write-back of the lines it leaves dirty included")
 
 
 def metadata_builders(steps):
@@ -257,17 +371,18 @@ def metadata_builders(steps):
     dl = torch.from_numpy(r.integers(100, 129, B).astype(np.int32)).cuda()
     pos = torch.empty(B * width, dtype=torch.int32, device="cuda")
     seq = torch.empty_like(pos)
-    d_ms = time_calls(lambda: rkv.dflash_prepare_delta_metadata(old, dl, width, pos, seq), steps)
+    d_ms = time_queued(lambda: rkv.dflash_prepare_delta_metadata(old, dl, width, pos, seq), steps)
     par = torch.empty((16, 64), dtype=torch.int32, device="cuda")
     dep = torch.empty_like(par)
-    t_ms = time_calls(lambda: rkv.dflash_build_linear_tree_metadata(par, dep), steps)
+    t_ms = time_queued(lambda: rkv.dflash_build_linear_tree_metadata(par, dep), steps)
+    note = "launch-bound; launches queued ahead and run back to back, event span / count"
     return {
-        "delta_metadata_b32_w128": {"kernel_us_events": d_ms * 1e3,
+        "delta_metadata_b32_w128": {"kernel_us": d_ms * 1e3,
                                     "algorithmic_bytes": 2 * B * 4 + 2 * B * width * 4,
-                                    "note": "launch-bound: 32 KB of output"},
-        "linear_tree_b16_v64": {"kernel_us_events": t_ms * 1e3,
+                                    "note": "32 KB of output; " + note},
+        "linear_tree_b16_v64": {"kernel_us": t_ms * 1e3,
                                 "algorithmic_bytes": 2 * 16 * 64 * 4,
-                                "note": "launch-bound: 8 KB of output"},
+                                "note": "8 KB of output; " + note},
     }
 
 
@@ -315,45 +430,248 @@ def paged_large(steps, warmup=3, fp8=False):
             "algorithmic_bytes": xb, "note": "launches back to back over 4 copies of the written tensors, event span / count"}
 
 
-def floors(steps):
-    """Lower bounds for the small workloads on this chip, timed like them (a
-    1 GiB read before each launch pushes the inputs out of the MALL): a
-    plain device copy moving the paged workload's bytes (15.2 MB read, 15.2
-    MB written) and a near-empty kernel (one fp32 zeroed)."""
+def small_cases():
+    """The workloads whose inputs fit the 256 MB MALL, by label."""
+    import workloads as W
+    return {
+        "continuous_neox": lambda: W.config(2, W.NEOX),
+        "continuous_gptj": lambda: W.config(2, W.GPTJ),
+        "tree": lambda: W.config(3),
+        "paged_delta": lambda: W.config(4),
+        "paged_delta_gather_fused": lambda: W.config(41),
+        "continuous_neox_fp8_cache":
+            lambda: W.with_fp8_cache(W.config(2, W.NEOX), 7002, fill="sentinel"),
+        "paged_delta_fp8_cache": lambda: W.with_fp8_cache(W.config(4), 7004, fill="sentinel"),
+        "continuous_neox_qknorm": lambda: W.with_qk_norm(W.config(2, W.NEOX), 7102),
+        # one GPU's share of the large prefill under 8-way tensor parallelism
+        # (8 Q heads, 1 KV head; 193 MB, within the 256 MB MALL, hence flushed)
+        "prefill_tp8_shard": lambda: W.prefill_tp_shard(8),
+    }
+
+
+def small_workload(label, make, steps, flush):
+    """One small workload: rotated (HBM steady state, the figure of record),
+    cold (one isolated launch after a flush) and back-to-back warm times."""
+    import torch
+    from harness import launch, upload
+    log(f"[bench] generating {label}")
+    x = make()
+    xb = algorithmic_bytes(x)
+    tx = upload(x)
+    sets = full_copies(tx, xb)
+    r_ms = time_rotated(lambda s: launch(x, s), sets, steps)
+    del sets
+    torch.cuda.empty_cache()
+    c_ms, ev_ms = time_cold(lambda: launch(x, tx), flush, steps)
+    h_ms = time_queued(lambda: launch(x, tx), steps)
+    gbs = xb / (r_ms * 1e-3) / 1e9
+    log(f"[bench] {label}: {r_ms * 1e3:.2f} us rotated, {gbs:.0f} GB/s "
+        f"({gbs / PEAK_HBM_GBS:.1%}); cold {c_ms * 1e3:.2f} us, back to back {h_ms * 1e3:.2f} us")
+    name, tokens = x.name, x.tokens
+    del tx, x
+    torch.cuda.empty_cache()
+    return {"workload": name, "kernel_us": r_ms * 1e3, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS,
+            "tokens_per_s": tokens / (r_ms * 1e-3), "algorithmic_bytes": xb,
+            "protocol": ROTATED_PROTOCOL,
+            "cold_us": c_ms * 1e3, "cold_protocol": COLD_PROTOCOL, "event_pair_us": ev_ms * 1e3,
+            "hot_kernel_us": h_ms * 1e3,
+            "hot_note": "not flushed: launches queued ahead and run back to back on the same "
+                        "tensors (inputs left in MALL / L2 by the previous launch), event span / "
+                        "count"}
+
+
+def _device_paged(x):
+    """Upload a paged workload whose pool is created on the device (its
+    contents do not change the work)."""
     import torch
     import workloads as W
-    flush_buf = torch.ones(1 << 29, dtype=torch.float16, device="cuda")
-    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
+    from harness import upload
+    t = upload(x)
+    t["pool"] = torch.zeros((2, x.num_pages, W.TOKENS_PER_PAGE, x.Hkv, x.D),
+                            dtype=torch.float16, device="cuda")
+    return t
 
-    def flush():
-        torch.sum(flush_buf, dim=0, dtype=torch.float32, out=flush_sink)
 
-    half = algorithmic_bytes(W.config(4)) // 2
-    src = torch.ones(half // 2, dtype=torch.float16, device="cuda")
-    dst = torch.empty_like(src)
-    tiny = torch.ones(1, dtype=torch.float32, device="cuda")
+CEILING_PARTS = ("streams", "empty", "paged", "prefill")
+
+
+def ceilings_leg(steps, parts=CEILING_PARTS):
+    """Ceilings and floors on this chip, from the kernels in ceilings/ timed
+    beside the library's (rocprofv3's kernel trace of this run is the
+    reference for the short ones):
+
+    * copy and in-place streams over 1 GiB buffers, four buffers cycled, with
+      the library's load and store policy (buffer loads nt, buffer stores nt
+      sc1) and with plain accesses, XCDs taking 128-workgroup chunks in turn
+      or contiguous eighths;
+    * an empty kernel of 1 and of 2048 workgroups (the paged workload's
+      grid), flushed and back to back;
+    * the paged workload's shape (4096 delta rows, 8 KV heads, D = R = 128,
+      NeoX, sequences of 128 rows of which 115 are written) moved by an
+      index-free floor (every address computed from the row number), into
+      contiguous rows and scattered over pool pages, in both access plans,
+      beside the library's paged update on the paged workload;
+    * the large prefill with its cos/sin row staged in LDS (one workgroup per
+      token, 2 or 4 row groups per wave) beside the library's kernel."""
     out = {}
-    for label, fn, nbytes in (("copy_paged_bytes", lambda: dst.copy_(src), 2 * src.numel() * 2),
-                              ("near_empty_kernel", lambda: tiny.zero_(), 4)):
-        stream = torch.cuda.current_stream()
-        for _ in range(3):
-            flush()
-            fn()
-        torch.cuda.synchronize()
-        st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        for k in range(steps):
-            flush()
-            st[k].record(stream)
-            fn()
-            en[k].record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in zip(st, en)]))
-        out[label] = {"kernel_us_events": ms * 1e3, "bytes": nbytes,
-                      "GB/s": nbytes / (ms * 1e-3) / 1e9}
-        log(f"[bench] floor {label}: {ms * 1e3:.2f} us by events")
-    return {"floors": out, "note": "event-bracketed single launches after a 1 GiB read; "
-                                   "rocprofv3 kernel durations are the reference"}
+    flush = make_flush()
+    if "streams" in parts:
+        out.update(_stream_ceilings(steps))
+    if "empty" in parts:
+        out.update(_empty_kernels(steps, flush))
+    if "paged" in parts:
+        out.update(_paged_floors(steps, flush))
+    if "prefill" in parts:
+        out.update(_prefill_lds(steps))
+    return out
+
+
+def _stream_ceilings(steps):
+    import torch
+    import ceilings as C
+    out = {}
+    GiB = 1 << 30
+    bufs = [torch.ones(GiB // 2, dtype=torch.float16, device="cuda") for _ in range(8)]
+    for policy, pname in ((1, "library policy (nt loads, nt sc1 stores)"), (0, "plain")):
+        for chunk in (7, 0):
+            tag = f"{'lib' if policy else 'plain'}_xcd{'chunk128' if chunk else 'eighths'}"
+            for kind in ("copy", "inplace"):
+                k = [0]
+
+                def run():
+                    i = k[0] % 4
+                    k[0] += 1
+                    if kind == "copy":
+                        C.stream_copy(bufs[i], bufs[4 + i], policy, chunk)
+                    else:
+                        C.stream_inplace(bufs[i], policy, chunk)
+                for _ in range(4):
+                    run()
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(steps):
+                    run()
+                b.record()
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) / steps * 1e3
+                gbs = 2 * GiB / (us * 1e-6) / 1e9
+                out[f"stream_{kind}_{tag}"] = {"kernel_us": us, "bytes": 2 * GiB, "GB/s": gbs,
+                                               "frac": gbs / PEAK_HBM_GBS, "policy": pname,
+                                               "timing": "back to back over 4 buffers"}
+                log(f"[bench] ceiling stream_{kind}_{tag}: {us:.1f} us, {gbs:.0f} GB/s")
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def _four_ways(run_set, t, nbytes, flush, steps):
+    """rotated (time_rotated over full copies of `t`), cold (time_cold),
+    marginal (time_flushed) and back-to-back warm times of run_set(t), us."""
+    import torch
+    sets = full_copies(t, nbytes)
+    r_ms = time_rotated(run_set, sets, steps)
+    del sets
+    torch.cuda.empty_cache()
+    c_ms, ev_ms = time_cold(lambda: run_set(t), flush, steps)
+    m_ms = time_flushed(lambda: run_set(t), flush, steps)
+    h_ms = time_queued(lambda: run_set(t), steps)
+    return {"kernel_us": r_ms * 1e3, "protocol": ROTATED_PROTOCOL, "cold_us": c_ms * 1e3,
+            "event_pair_us": ev_ms * 1e3, "marginal_us": m_ms * 1e3, "hot_kernel_us": h_ms * 1e3,
+            "cold_protocol": COLD_PROTOCOL, "marginal_protocol": MARGINAL_PROTOCOL}
+
+
+def _empty_kernels(steps, flush):
+    import ceilings as C
+    out = {}
+    for wg in (1, 2048):
+        r = _four_ways(lambda t: C.empty(wg), {}, 1, flush, steps)
+        out[f"empty_kernel_{wg}wg"] = r
+        log(f"[bench] ceiling empty kernel {wg} workgroups: {r['kernel_us']:.2f} us back to back "
+            f"(rotated protocol), {r['cold_us']:.2f} us cold, {r['marginal_us']:.2f} us marginal")
+    return out
+
+
+def _paged_floors(steps, flush):
+    import torch
+    import ceilings as C
+    import workloads as W
+    from harness import launch
+    out = {}
+    x = W.paged(4096, 32, 8, 128, 128, 8192, 128, W.NEOX, 1004, pool_fill="none",
+                name="paged_delta_n4096_p8192")
+    xb = algorithmic_bytes(x)
+    tx = _device_paged(x)
+    r = _four_ways(lambda t: launch(x, t), tx, xb, flush, steps)
+    r.update(bytes=xb, **{"GB/s": xb / (r["kernel_us"] * 1e-6) / 1e9})
+    out["paged_delta_library"] = r
+    log(f"[bench] paged update (library): {r['kernel_us']:.2f} us rotated, {r['cold_us']:.2f} us "
+        f"cold, {r['marginal_us']:.2f} us marginal, {r['hot_kernel_us']:.2f} us back to back")
+    live, rows_log2 = 115, 7
+    n_live = sum(min(live, 128) for _ in range(4096 // 128))
+    floor_bytes = n_live * (8 * 128 * 2 * 4 + 128 * 4)
+    for scatter in (0, 1):
+        for plan in (0, 1):
+            def run(t, scatter=scatter, plan=plan):
+                C.paged_floor(t["k_delta"], t["v_delta"], t["pool"], t["cos_sin"],
+                              x.num_pages, rows_log2, live, scatter, 2, plan)
+            r = _four_ways(run, tx, floor_bytes, flush, steps)
+            r.update(bytes=floor_bytes, **{"GB/s": floor_bytes / (r["kernel_us"] * 1e-6) / 1e9})
+            name = (f"paged_floor_{'scatter' if scatter else 'contiguous'}_"
+                    f"{'streaming' if plan else 'early_loads'}")
+            out[name] = r
+            log(f"[bench] {name}: {r['kernel_us']:.2f} us rotated ({r['GB/s']:.0f} GB/s), "
+                f"{r['cold_us']:.2f} us cold, {r['marginal_us']:.2f} us marginal, "
+                f"{r['hot_kernel_us']:.2f} us back to back")
+    del tx, x
+    torch.cuda.empty_cache()
+    return out
+
+
+def _prefill_lds(steps):
+    import torch
+    import ceilings as C
+    import workloads as W
+    from harness import launch, upload
+    out = {}
+    w = W.config(HEADLINE)
+    nbytes = algorithmic_bytes(w)
+    t = upload(w)
+    sets = rotated(w, t, ROTATIONS)
+    variants = [("library", None, None)] + [(f"lds_g{g}_xcd{c}", g, c)
+                                            for g in (2, 4) for c in (5, 0)]
+    for rep in range(2):
+        for name, g, c in variants:
+            k = [0]
+
+            def run(g=g, c=c):
+                s = sets[k[0] % len(sets)]
+                k[0] += 1
+                if g is None:
+                    launch(w, s)
+                else:
+                    C.prefill_lds(s["cos_sin"], s["qkv"], s["cache"], w.style, g, c)
+            for _ in range(4):
+                run()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                run()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / steps * 1e3
+            key = f"prefill_{name}"
+            prev = out.get(key, {}).get("kernel_us_series", [])
+            out[key] = {"kernel_us_series": prev + [us], "bytes": nbytes,
+                        "timing": "back to back over 4 copies of the written tensors; two "
+                                  "interleaved series"}
+            log(f"[bench] {key}: {us:.1f} us ({nbytes / (us * 1e-6) / 1e9:.0f} GB/s)")
+    del sets, t
+    torch.cuda.empty_cache()
+    return out
 
 
 def traffic_from_profile(kernel_name: str):
@@ -386,70 +704,97 @@ def kernel_source_hash(d=None) -> str:
     return hsh.hexdigest()
 
 
-def _oracle_parts(w, batches):
-    """Per-sequence copies of the headline inputs, made once, outside any
-    timed region: (table rows, qkv, cache) of each listed sequence."""
+def host_cpus():
+    """(threads to use, logical CPUs of the host, CPUs this process may run
+    on, CPU model).  The threads are the CPUs this process may run on,
+    capped by OMP_NUM_THREADS when the environment sets it (a machine's CPU
+    share for this job)."""
+    host = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = host
+    use = allowed
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        use = min(use, int(env))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return use, host, allowed, model
+
+
+def _oracle_parts(w, ranges):
+    """Inputs of the oracle's call 1 for token ranges [t0, t1) of sequences
+    b, made once, outside any timed region: the range's table rows (so that
+    its first token sits at position t0, as in the whole call), its qkv rows
+    and a cache of its own of capacity t1 - t0 that receives its K and V
+    rows.  Each part computes exactly the values the whole call computes for
+    those tokens."""
     tb = w.cos_sin.shape[0]
-    return [(np.ascontiguousarray(w.cos_sin[b:b + 1] if tb > 1 else w.cos_sin),
-             np.array(w.qkv[b:b + 1], order="C"), np.array(w.cache[b:b + 1], order="C"))
-            for b in batches]
+    parts = []
+    for b, t0, t1 in ranges:
+        table = np.ascontiguousarray(w.cos_sin[b if tb > 1 else 0, t0:t1][None])
+        qkv = np.array(w.qkv[b:b + 1, t0:t1], order="C")
+        cache = np.empty((1, 2, w.Hkv, t1 - t0, w.D), dtype=np.uint16)
+        parts.append((table, qkv, cache))
+    return parts
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The oracle as it is (single-threaded C) on a bounded sample of the
-    headline workload: sequence 0 (8192 tokens, all 80 heads), called on
-    arrays prepared once (qkv is rotated in place again by each call, as on
-    the GPU), repeated until the budget is spent."""
-    import oracle
-    oracle.lib()
-    part = _oracle_parts(w, [0])[0]
-    n, t_total = 0, 0.0
-    while t_total < budget_s:
-        t0 = time.perf_counter()
-        oracle.packed_qkv_in_place(*part, w.style)
-        t_total += time.perf_counter() - t0
-        n += 1
-    tokens = n * w.S
-    return {"value": tokens / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"sequence 0 of the workload ({w.S} tokens x {w.Hq + 2 * w.Hkv} heads), "
-                      f"{n} oracle calls in place, {t_total:.1f} s"}
+def _token_ranges(w, n_parts):
+    """Split every sequence into ceil(n_parts / B) contiguous token ranges."""
+    per_seq = max(1, -(-n_parts // w.B))
+    step = -(-w.S // per_seq)
+    return [(b, t0, min(w.S, t0 + step)) for b in range(w.B) for t0 in range(0, w.S, step)]
 
 
-def cpu_baseline_threads(w, budget_s=10.0):
-    """The same oracle call on all sequences of the headline workload at
-    once, one host thread per sequence (call 1 places each sequence's tokens
-    from slot 0, so a sequence is its smallest independent piece), repeated
-    until the budget is spent.  The oracle's C code runs outside Python's
-    interpreter lock, so the threads run in parallel."""
-    import threading
+def _time_parts(w, parts, threads, budget_s):
+    """Rounds of every part's oracle call (in place) on a pool of `threads`
+    host threads until the budget is spent; the oracle's C code runs outside
+    Python's interpreter lock.  Returns (tokens per second, rounds, seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     oracle.lib()
-    parts = _oracle_parts(w, range(w.B))
-    errors = []
-
-    def work(part):
-        try:
-            oracle.packed_qkv_in_place(*part, w.style)
-        except Exception as e:      # surfaced after the join
-            errors.append(e)
-
+    tokens = sum(p[1].shape[1] for p in parts)
     n, t_total = 0, 0.0
-    while t_total < budget_s:
-        threads = [threading.Thread(target=work, args=(part,)) for part in parts]
-        t0 = time.perf_counter()
-        for th in threads:
-            th.start()
-        for th in threads:
-            th.join()
-        t_total += time.perf_counter() - t0
-        if errors:
-            raise errors[0]
-        n += 1
-    tokens = n * w.B * w.S
-    return {"value": tokens / t_total, "unit": "tokens/s", "cores": len(parts), "kind": "oracle",
-            "sample": f"all {w.B} sequences of the workload, one thread each, {n} rounds of "
-                      f"in-place calls, {t_total:.1f} s wall"}
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        while t_total < budget_s:
+            t0 = time.perf_counter()
+            list(pool.map(lambda p: oracle.packed_qkv_in_place(*p, w.style), parts))
+            t_total += time.perf_counter() - t0
+            n += 1
+    return n * tokens / t_total, n, t_total
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle as it is (plain C, one call-1 evaluation per token range),
+    partitioned over every CPU this process may use: all B x S tokens of the
+    headline workload in contiguous token ranges, at least one per thread,
+    repeated until the budget is spent."""
+    use, host, allowed, model = host_cpus()
+    parts = _oracle_parts(w, _token_ranges(w, use))
+    rate, n, secs = _time_parts(w, parts, use, budget_s)
+    return {"value": rate, "unit": "tokens/s", "cores": use, "kind": "oracle",
+            "host_logical_cpus": host, "cpus_allowed": allowed, "cpu_model": model,
+            "sample": f"all {w.B * w.S} tokens of the workload in {len(parts)} token ranges on "
+                      f"{use} threads, {n} rounds of in-place oracle calls, {secs:.1f} s wall"}
+
+
+def cpu_baseline_single(w, budget_s=10.0):
+    """The same oracle on one thread: sequence 0's first 2048 tokens, called
+    in place repeatedly until the budget is spent."""
+    parts = _oracle_parts(w, [(0, 0, min(w.S, 2048))])
+    rate, n, secs = _time_parts(w, parts, 1, budget_s)
+    return {"value": rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"tokens 0-{parts[0][1].shape[1] - 1} of sequence 0, {n} in-place oracle "
+                      f"calls, {secs:.1f} s"}
 
 
 def main():
@@ -461,10 +806,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--paged-large", action="store_true",
                     help="time only the 65,536-row paged update (for counter runs)")
-    ap.add_argument("--floors", action="store_true",
-                    help="only time the floors of the small workloads: a torch copy moving the "
-                         "paged workload's bytes and a near-empty kernel, each after the same "
-                         "MALL flush")
+    ap.add_argument("--workload", action="append", default=[], metavar="NAME",
+                    help="time only this small workload (repeatable; for counter and trace "
+                         "runs): " + ", ".join(small_cases()))
+    ap.add_argument("--ceilings", nargs="?", const=",".join(CEILING_PARTS), default=None,
+                    metavar="PARTS",
+                    help="time only the ceilings and floors of ceilings/ beside the library's "
+                         "kernels: a comma list of " + ", ".join(CEILING_PARTS) + " (default: all)")
     ap.add_argument("--calib", action="store_true",
                     help="also run a 1 GiB elementwise copy (1 GiB read + 1 GiB written per "
                          "launch) to scale HBM byte counters")
@@ -483,8 +831,25 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     log(f"[bench] device: {torch.cuda.get_device_name(0)}")
-    if args.floors:
-        print(json.dumps(floors(max(10, args.steps // 2))), flush=True)
+    if args.ceilings is not None or args.workload:
+        cases = small_cases()
+        unknown = [n for n in args.workload if n not in cases]
+        parts = [p for p in (args.ceilings or "").split(",") if p]
+        unknown += [p for p in parts if p not in CEILING_PARTS]
+        if unknown:
+            sys.exit(f"unknown workload(s) or ceiling part(s) {unknown}; choose from "
+                     f"{list(cases)} and {list(CEILING_PARTS)}")
+        res = {}
+        if args.workload:
+            flush = make_flush()
+            res["workloads"] = {n: small_workload(n, cases[n], args.steps, flush)
+                                for n in args.workload}
+            del flush
+        if parts:
+            res["ceilings"] = ceilings_leg(args.steps, parts)
+        if args.calib:
+            calibration_copy()
+        print(json.dumps(res), flush=True)
         return
     if args.paged_large:
         res = paged_large(args.steps, args.warmup)
@@ -595,47 +960,10 @@ def main():
         calibration_copy()
 
     if not args.no_extra:
-        flush_buf = torch.ones(1 << 29, dtype=torch.float16, device="cuda")   # 1 GiB
-        flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
-
-        def flush():
-            torch.sum(flush_buf, dim=0, dtype=torch.float32, out=flush_sink)
-
-        cases = [("continuous_neox", lambda: W.config(2, W.NEOX)),
-                 ("continuous_gptj", lambda: W.config(2, W.GPTJ)),
-                 ("tree", lambda: W.config(3)),
-                 ("paged_delta", lambda: W.config(4)),
-                 ("paged_delta_gather_fused", lambda: W.config(41)),
-                 ("continuous_neox_fp8_cache",
-                  lambda: W.with_fp8_cache(W.config(2, W.NEOX), 7002, fill="sentinel")),
-                 ("paged_delta_fp8_cache",
-                  lambda: W.with_fp8_cache(W.config(4), 7004, fill="sentinel")),
-                 ("continuous_neox_qknorm", lambda: W.with_qk_norm(W.config(2, W.NEOX), 7102)),
-                 # one GPU's share of the large prefill under 8-way tensor parallelism
-                 # (8 Q heads, 1 KV head; 193 MB, within the 256 MB MALL, hence flushed)
-                 ("prefill_tp8_shard", lambda: W.prefill_tp_shard(8))]
-        for label, make in cases:
-            log(f"[bench] generating {label}")
-            x = make()
-            xb = algorithmic_bytes(x)
-            tx = upload(x)
-            steps = max(5, min(args.steps, 50))
-            k_ms, _ = time_launches(x, tx, steps, 3, flush=flush)
-            gbs = xb / (k_ms * 1e-3) / 1e9
-            # hot: the same launches back to back, inputs left in MALL / L2 by the previous one
-            h_ms, _ = time_launches(x, tx, steps, 3, queue_ahead=True)
-            extra[label] = {"workload": x.name, "kernel_us_events": k_ms * 1e3, "GB/s": gbs,
-                            "frac": gbs / PEAK_HBM_GBS, "tokens_per_s": x.tokens / (k_ms * 1e-3),
-                            "algorithmic_bytes": xb, "mall_flushed": True,
-                            "note": "event-bracketed single launches: includes event overhead",
-                            "hot_kernel_us": h_ms * 1e3,
-                            "hot_note": "not flushed: launches queued ahead and run back to "
-                                        "back, event span / count"}
-            log(f"[bench] {label}: {k_ms * 1e3:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%}); "
-                f"hot {h_ms * 1e3:.2f} us")
-            del tx, x
-            torch.cuda.empty_cache()
-        del flush_buf
+        flush = make_flush()
+        for label, make in small_cases().items():
+            extra[label] = small_workload(label, make, max(20, args.steps), flush)
+        del flush
         torch.cuda.empty_cache()
         extra["paged_delta_large"] = paged_large(max(10, args.steps // 2))
         extra["paged_delta_large_fp8"] = paged_large(max(10, args.steps // 2), fp8=True)
@@ -659,17 +987,20 @@ def main():
         torch.cuda.empty_cache()
         meta = metadata_builders(max(10, args.steps // 2))
         for k, v in meta.items():
-            log(f"[bench] {k}: {v['kernel_us_events']:.2f} us")
+            log(f"[bench] {k}: {v['kernel_us']:.2f} us")
         extra.update(meta)
         result["workloads"] = extra
 
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a sample")
+        w = W.config(HEADLINE)
         result["cpu_baseline"] = cpu_baseline(w)
-        log(f"[bench] cpu oracle {result['cpu_baseline']['value']:.3e} tokens/s")
-        result["cpu_baseline_threads"] = cpu_baseline_threads(w)
-        log(f"[bench] cpu oracle, {result['cpu_baseline_threads']['cores']} threads: "
-            f"{result['cpu_baseline_threads']['value']:.3e} tokens/s")
+        cb = result["cpu_baseline"]
+        log(f"[bench] cpu oracle, {cb['cores']} threads ({cb['cpu_model']}, "
+            f"{cb['host_logical_cpus']} logical CPUs): {cb['value']:.3e} tokens/s")
+        result["cpu_baseline_single_thread"] = cpu_baseline_single(w)
+        log(f"[bench] cpu oracle, 1 thread: "
+            f"{result['cpu_baseline_single_thread']['value']:.3e} tokens/s")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -2,7 +2,9 @@
 
 The library is built in-tree, next to this file.  Packed-FP32 instructions
 are disabled for all device code (``-packed-fp32-ops``); the host pass of
-hipcc warns that it does not know that feature, which is harmless.
+hipcc warns that it does not know that feature, which is harmless.  The
+kernels take the values a wave needs first as leading scalar arguments, and
+the build asks for them to be preloaded into SGPRs at wave start.
 """
 from __future__ import annotations
 
@@ -19,8 +21,11 @@ SOURCES = [os.path.join(CSRC, f) for f in ("rkv_abi.hip", "rkv_kernels.hip",
                                             "rkv_kernels_norm_fp8.hip", "rkv_meta.hip")]
 OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Kernel-argument preloading: the leading scalar arguments of every kernel
+# (up to 14 dwords) are written into SGPRs when a wave starts.
+PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=10"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *PRELOAD,
          "-Wall", "-Wno-unused-command-line-argument"]
 
 

@@ -411,10 +411,11 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
       (exact_of(ropeStyle) || fp8 || layout_of(ropeStyle) == RKV_ROPE_NEOX) ? 2 : 1;
   const int g_large = fp8 ? 4 : g_small;
   const Split sp = pick_split(N, groups_per_row, g_large, g_small);
-  // non-temporal delta loads and pool stores for large launches (small fp16
-  // ones run faster when the caches absorb the pool writes); E4M3 pools
-  // always take them
-  const bool streaming = fp8 || N * groups_per_row > kStreamingGroups;
+  // large launches and E4M3 pools load a delta row once its page ids are
+  // known (only rows that are written move bytes); small fp16 ones request
+  // every row with the index loads, so that the reads overlap the two
+  // dependent index round trips
+  const bool late_loads = fp8 || N * groups_per_row > kStreamingGroups;
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_row = sp.waves_per_item;
@@ -422,9 +423,9 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
   g_last_groups = p.groups_per_wave;
   return launched(fp8 ? rkv::launch_paged_fp8(p, headDim, layout_of(ropeStyle),
-                                              exact_of(ropeStyle), gather, streaming, stream)
+                                              exact_of(ropeStyle), gather, late_loads, stream)
                       : rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle),
-                                          gather, streaming, stream));
+                                          gather, late_loads, stream));
 }
 
 }  // namespace

@@ -9,8 +9,8 @@ hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool
 }
 
 hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool gather,
-                        bool streaming, hipStream_t stream) {
-  return detail::launch_paged_t<false>(p, D, style, exact, gather, streaming, stream);
+                        bool late_loads, hipStream_t stream) {
+  return detail::launch_paged_t<false>(p, D, style, exact, gather, late_loads, stream);
 }
 
 }  // namespace rkv

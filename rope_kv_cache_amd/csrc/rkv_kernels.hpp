@@ -199,8 +199,10 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
   return x * q + (x < r ? x : r) + (bid >> 3);
 }
 
-__device__ __forceinline__ int block_id_xcd(int chunk_log2) {
-  const int n = (int)gridDim.x, bid = (int)blockIdx.x;
+// n: the grid's workgroup count (passed in: reading gridDim would cost a
+// kernel-argument load before the first row load).
+__device__ __forceinline__ int block_id_xcd(int chunk_log2, int n) {
+  const int bid = (int)blockIdx.x;
   if (chunk_log2 == 0) return xcd_contiguous(bid, n);
   // blocks in whole rounds of 8 chunks (a power of two: no division, which
   // would put some 30 instructions before every wave's first load)
@@ -212,10 +214,24 @@ __device__ __forceinline__ int block_id_xcd(int chunk_log2) {
   return full + xcd_contiguous(bid - full, n - full);
 }
 
-__device__ __forceinline__ int wave_id_uniform(int chunk_log2) {
-  return __builtin_amdgcn_readfirstlane(block_id_xcd(chunk_log2) * kWavesPerBlock +
+// The wave's work item among `waves` (the grid has ceil(waves / 4)
+// workgroups of four waves).
+__device__ __forceinline__ int wave_id_uniform(int chunk_log2, int waves) {
+  const int n = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  return __builtin_amdgcn_readfirstlane(block_id_xcd(chunk_log2, n) * kWavesPerBlock +
                                         (int)(threadIdx.x >> 6));
 }
+
+// Kernel arguments.  The values a wave needs before its first loads are
+// separate scalar arguments ahead of the parameter block: the library is
+// built with kernel-argument preloading (-amdgpu-kernarg-preload-count), so
+// the hardware writes them into SGPRs when the wave starts, instead of every
+// wave fetching them from the kernel-argument segment before it can compute
+// its first addresses (the compiler issued two or three dependent fetches of
+// parameter-block fields ahead of the first row load).  At most 14 dwords
+// are preloaded.  The rest of the block is fetched once the row loads are in
+// flight.  Measured on MI355X (paged workload, launches back to back over
+// full copies of its tensors): 9.7 -> 9.2 us; a 65,536-row update unchanged.
 
 // ------------------------------------------------------------ calls 1-3 --
 //
@@ -225,33 +241,42 @@ __device__ __forceinline__ int wave_id_uniform(int chunk_log2) {
 // Call 3 (tree): slot = endLens[b] - S + s, position = tokenPosIds[b, s].
 // Calls 2 and 3 skip a token whose slot or position is out of range.
 // (TensorRT-Edge-LLM C++ API, "Apply Rope Write KV".)
+//
+// Preloaded arguments (see "Kernel arguments" above): the launch's wave
+// count, the multipliers of the divisions by waves per token and by S, the
+// three shifts packed in one dword (bits 0-7 waves per token, 8-15 S, 16-23
+// the XCD chunk order), H = Hq + 2 Hkv, and the qkv, end-length and
+// position-id pointers (the last two null for call 1, the last for call 2).
 template <int D, int kCall, int kStyle, bool kExact, int G, bool kFp8, bool kNorm>
-__global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
+__global__ __launch_bounds__(kBlock) void contig_kernel(
+    int32_t total_waves, uint32_t waves_div_m, int32_t waves_per_token, uint32_t seq_div_m,
+    int32_t S, int32_t H, uint32_t shifts, uint16_t* qkv, const int32_t* __restrict__ end_lens,
+    const int32_t* __restrict__ pos_ids, ContigParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
 
-  const int wave = wave_id_uniform(p.xcd_chunk_log2);
-  if (wave >= p.total_waves) return;
-  const int token = (int)fast_div((uint32_t)wave, p.div_waves);
-  const int part = wave - token * p.waves_per_token;
-  const int b = (int)fast_div((uint32_t)token, p.div_seq);
-  const int s = token - b * p.S;
+  const int wave = wave_id_uniform((int)((shifts >> 16) & 0xffu), total_waves);
+  if (wave >= total_waves) return;
+  const FastDiv div_waves{(uint32_t)waves_per_token, waves_div_m, shifts & 0xffu};
+  const FastDiv div_seq{(uint32_t)S, seq_div_m, (shifts >> 8) & 0xffu};
+  const int token = (int)fast_div((uint32_t)wave, div_waves);
+  const int part = wave - token * waves_per_token;
+  const int b = (int)fast_div((uint32_t)token, div_seq);
+  const int s = token - b * S;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % kLanesPerRow;
   const int row_in_group = lane / kLanesPerRow;
-  const ChunkRole role = chunk_role<kStyle>(c, p.R);
 
-  const int H = p.Hq + 2 * p.Hkv;
-  uint16_t* const tok_base = p.qkv + (size_t)token * H * D;
+  uint16_t* const tok_base = qkv + (size_t)token * H * D;
 
   // Calls 2 and 3: the token's end length (and position id) are requested
   // first, as scalar loads, so that their wait does not include the row
   // loads (vector loads complete in order).
   int end_len = 0, pos_id = 0;
   if constexpr (kCall != kCallPacked) {
-    end_len = p.end_lens[b];
-    if constexpr (kCall == kCallTree) pos_id = p.pos_ids[token];
+    end_len = end_lens[b];
+    if constexpr (kCall == kCallTree) pos_id = pos_ids[token];
   }
 
   // Row loads next: they do not depend on the slot or the position.  They go
@@ -274,13 +299,14 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
 
   int slot = s, pos = s;
   if constexpr (kCall != kCallPacked) {
-    const long long slot64 = (long long)end_len - p.S + s;
+    const long long slot64 = (long long)end_len - S + s;
     const long long pos64 = (kCall == kCallTree) ? (long long)pos_id : slot64;
     if (slot64 < 0 || slot64 >= p.cap || pos64 < 0 || pos64 >= p.table_len) return;
     slot = (int)slot64;
     pos = (int)pos64;
   }
 
+  const ChunkRole role = chunk_role<kStyle>(c, p.R);
   const int tb = (p.table_batch == 1) ? 0 : b;
   const CosSinRaw csr =
       load_cos_sin<kStyle>(p.cos_sin + ((size_t)tb * p.table_len + pos) * p.R, role.freq0, p.R, lane);
@@ -378,40 +404,57 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(ContigParams p) {
 // launchDFlashTargetKVCacheUpdate).  Delta row i has 2*Hkv head rows: K
 // heads first, then V heads; a wave owns G row groups of one delta row.
 // The pool is addressed as [2*numPages][64][Hkv][D] by canonical page id,
-// in 64-bit.  Two access plans, chosen by the host as kStream:
-//  - small fp16 launches (latency-bound): the delta rows and cos/sin values
-//    are requested first, the index loads overlap with them, only the stores
-//    wait for the page ids; ordinary accesses, whose pool writes the caches
-//    absorb;
-//  - large launches and E4M3 pools (bandwidth-bound): the delta rows are
-//    loaded once the position, sequence and page ids are known, and only
-//    those that will be written (padding rows and rows of unmapped pages move
-//    no bytes), with non-temporal loads and stores.  Measured on MI355X: a
-//    65,536-row update 98 -> 81 us, the 4,096-row E4M3 update 11.4 -> 10.6 us
-//    (by events).
+// in 64-bit.  The row's position and sequence are requested first; the page
+// ids depend on them.  Two load plans, chosen by the host as kLateLoads:
+//  - small launches (all waves resident at once, so the two dependent index
+//    round trips are the kernel's critical path): every delta row of the
+//    wave is requested at once, with the index loads, so that the reads
+//    overlap both round trips; rows that turn out to be padding or to have
+//    no page are read and dropped (about 9% more reads on the paged
+//    workload);
+//  - large launches and E4M3 pools: a delta row is loaded once its position,
+//    sequence and page ids are known, and only if it will be written.
+// Both read non-temporally and store through buffers over the slot's K and
+// V page rows with nt sc1.  Measured on MI355X, launches back to back over
+// full copies of the paged workload's tensors (every byte from and back to
+// HBM), with preloaded arguments: early loads with ordinary accesses 9.2 us,
+// late loads 8.1 us, early loads non-temporal 8.2 us (the fused gather:
+// 8.4 and 7.5 us for the last two).  A 65,536-row update takes 78 us with
+// late loads (98 us with early ordinary ones).
 //
 // kGather fuses the page's cos/sin gather (launchDFlashGatherDeltaRope)
 // into the update: the row's cos/sin values come from the rope table row of
 // (state of its sequence, its position), read once the position and
 // sequence are known (in parallel with the page-table lookup); a row with
 // no such table row writes no K.
-template <int D, int kStyle, bool kExact, int G, bool kGather, bool kFp8, bool kStream>
-__global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
+//
+// Preloaded arguments (see "Kernel arguments" above): the launch's wave
+// count, the division by waves per row (multiplier and shift), waves per
+// row, Hkv, R, and the K-delta, V-delta, position and sequence pointers.
+template <int D, int kStyle, bool kExact, int G, bool kGather, bool kFp8, bool kLateLoads>
+__global__ __launch_bounds__(kBlock) void paged_kernel(
+    int32_t total_waves, uint32_t waves_div_m, uint32_t waves_div_l, int32_t waves_per_row,
+    int32_t Hkv, int32_t R, const uint16_t* __restrict__ k_delta,
+    const uint16_t* __restrict__ v_delta, const int32_t* __restrict__ positions,
+    const int32_t* __restrict__ seqs, PagedParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
   constexpr int kTpp = kTokensPerPage;
 
-  const int wave = wave_id_uniform(0);
-  if (wave >= p.total_waves) return;
-  const int i = (int)fast_div((uint32_t)wave, p.div_waves);
-  const int part = wave - i * p.waves_per_row;
+  const int wave = wave_id_uniform(0, total_waves);
+  if (wave >= total_waves) return;
+  const FastDiv div_waves{(uint32_t)waves_per_row, waves_div_m, waves_div_l};
+  const int i = (int)fast_div((uint32_t)wave, div_waves);
+  const int part = wave - i * waves_per_row;
+  const int pos = positions[i];
+  const int seq = seqs[i];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % kLanesPerRow;
   const int row_in_group = lane / kLanesPerRow;
-  const ChunkRole role = chunk_role<kStyle>(c, p.R);
-  const int rows = 2 * p.Hkv;
-  const size_t delta_row = (size_t)i * p.Hkv;
+  const ChunkRole role = chunk_role<kStyle>(c, R);
+  const int rows = 2 * Hkv;
+  const size_t delta_row = (size_t)i * Hkv;
 
   int row[G];
   uint4 x[G];
@@ -420,23 +463,21 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
     const int r = (part * G + g) * kRowsPerGroup + row_in_group;
     row[g] = r;
     x[g] = make_uint4(0, 0, 0, 0);
-    // small launches are latency-bound: request every row before the index loads
-    if constexpr (!kStream) {
-      if (r < p.Hkv)
-        x[g] = ld16(p.k_delta + (delta_row + r) * D + 8 * c);
+    // small launches: request every row now, with the index loads
+    if constexpr (!kLateLoads) {
+      if (r < Hkv)
+        x[g] = ld16_stream(k_delta + (delta_row + r) * D + 8 * c);
       else if (r < rows)
-        x[g] = ld16(p.v_delta + (delta_row + (r - p.Hkv)) * D + 8 * c);
+        x[g] = ld16_stream(v_delta + (delta_row + (r - Hkv)) * D + 8 * c);
     }
   }
   float cs[8], sn[8];
-  const bool has_k = part * G * kRowsPerGroup < p.Hkv;   // wave-uniform
+  const bool has_k = part * G * kRowsPerGroup < Hkv;   // wave-uniform
   if constexpr (!kGather) {
     if (has_k && role.rotary)
-      load_cos_sin_direct<kStyle>(p.cos_sin + (size_t)i * p.R, role.freq0, p.R, cs, sn);
+      load_cos_sin_direct<kStyle>(p.cos_sin + (size_t)i * R, role.freq0, R, cs, sn);
   }
 
-  const int pos = p.positions[i];
-  const int seq = p.seq[i];
   if (pos < 0 || seq < 0 || seq >= p.batch || (long long)pos >= (long long)p.max_pages * kTpp)
     return;
   const int lp = pos / kTpp;
@@ -452,21 +493,21 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
       const bool rope_ok = st >= 0 && st < p.rope_states && pos < p.rope_rows;
       k_ok = k_ok && rope_ok;
       if (rope_ok && role.rotary)
-        load_cos_sin_direct<kStyle>(p.rope + ((size_t)st * p.rope_rows + pos) * p.R, role.freq0,
-                                    p.R, cs, sn);
+        load_cos_sin_direct<kStyle>(p.rope + ((size_t)st * p.rope_rows + pos) * R, role.freq0,
+                                    R, cs, sn);
     }
   }
-  // Large launches are bandwidth-bound: load only the rows that will be
-  // written.  (Loads from buffers over the row's K and V heads, each lane
-  // issuing both with the wrong one out of range, measured 4% slower on a
-  // 65,536-row update than these branches.)
-  if constexpr (kStream) {
+  // Large launches: load only the rows that will be written.  (Loads from
+  // buffers over the row's K and V heads, each lane issuing both with the
+  // wrong one out of range, measured 4% slower on a 65,536-row update than
+  // these branches.)
+  if constexpr (kLateLoads) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int r = row[g];
-      if (r < p.Hkv ? k_ok : (r < rows && v_ok)) {
-        const uint16_t* src = r < p.Hkv ? p.k_delta + (delta_row + r) * D
-                                        : p.v_delta + (delta_row + (r - p.Hkv)) * D;
+      if (r < Hkv ? k_ok : (r < rows && v_ok)) {
+        const uint16_t* src =
+            r < Hkv ? k_delta + (delta_row + r) * D : v_delta + (delta_row + (r - Hkv)) * D;
         x[g] = ld16_stream(src + 8 * c);
       }
     }
@@ -475,17 +516,18 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
   float k_rcp = 1.f, v_rcp = 1.f;
   if constexpr (kFp8) load_reciprocal_scales(p.k_scale, p.v_scale, k_rcp, v_rcp);
 
-  // Large launches store through buffers over the K page row and the V page
-  // row of the delta row's slot (empty when unmapped), non-temporally at
-  // device scope; a group's store into a plane is skipped when none of its
-  // rows belongs to that plane (a wave-uniform test), and a lane's offset in
-  // the other plane is kNowhere, past the end of every buffer.  The host
-  // keeps 4 * Hkv * D below 2^31.  Measured on MI355X, a 65,536-row fp16
-  // update with the pool rotated among four buffers: 79.6-84.9 -> 77.9-78.2 us.
+  // Stores go through buffers over the K page row and the V page row of the
+  // delta row's slot (empty when unmapped), non-temporally at device scope;
+  // a group's store into a plane is skipped when none of its rows belongs to
+  // that plane (a wave-uniform test), and a lane's offset in the other plane
+  // is kNowhere, past the end of every buffer, as is that of a lane past the
+  // row's last head.  The host keeps 4 * Hkv * D below 2^31.  Measured on
+  // MI355X, a 65,536-row fp16 update with the pool rotated among four
+  // buffers: 79.6-84.9 -> 77.9-78.2 us against non-temporal global stores.
   constexpr uint32_t kNowhere = 0x80000000u;
-  const uint32_t row_bytes = (uint32_t)p.Hkv * D * (kFp8 ? 1 : 2);   // one plane's page row
-  const size_t k_slot = ((size_t)(k_ok ? kid : 0) * kTpp + off) * p.Hkv * D;
-  const size_t v_slot = ((size_t)(v_ok ? vid : 0) * kTpp + off) * p.Hkv * D;
+  const uint32_t row_bytes = (uint32_t)Hkv * D * (kFp8 ? 1 : 2);   // one plane's page row
+  const size_t k_slot = ((size_t)(k_ok ? kid : 0) * kTpp + off) * Hkv * D;
+  const size_t v_slot = ((size_t)(v_ok ? vid : 0) * kTpp + off) * Hkv * D;
   const BufRes kp = kFp8 ? buffer_of(p.pool8 + k_slot, k_ok ? row_bytes : 0u)
                          : buffer_of(p.pool + k_slot, k_ok ? row_bytes : 0u);
   const BufRes vp = kFp8 ? buffer_of(p.pool8 + v_slot, v_ok ? row_bytes : 0u)
@@ -494,33 +536,20 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(PagedParams p) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int r = row[g];
-    const bool is_k = r < p.Hkv;
-    const int h = is_k ? r : r - p.Hkv;
-    const size_t page = (size_t)(is_k ? kid : vid);
-    const size_t pool_row = (page * kTpp + off) * p.Hkv + h;
+    const bool is_k = r < Hkv;
     const int g0 = (part * G + g) * kRowsPerGroup;   // the group's first row (wave-uniform)
-    const uint32_t el_k = r < p.Hkv ? (uint32_t)(r * D + 8 * c) : kNowhere;
-    const uint32_t el_v = r >= p.Hkv ? (uint32_t)((r - p.Hkv) * D + 8 * c) : kNowhere;
+    const uint32_t el_k = r < Hkv ? (uint32_t)(r * D + 8 * c) : kNowhere;
+    const uint32_t el_v = r >= Hkv && r < rows ? (uint32_t)((r - Hkv) * D + 8 * c) : kNowhere;
     if constexpr (kFp8) {
       WideT<kExact> w[8];
       rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn, w);
       const uint2 b = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
-      if constexpr (kStream) {
-        if (g0 < p.Hkv) st8_buf(kp, el_k, b);
-        if (g0 + kRowsPerGroup > p.Hkv) st8_buf(vp, el_v, b);
-      } else {
-        if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-        st8(p.pool8 + pool_row * D + 8 * c, b);
-      }
+      if (g0 < Hkv) st8_buf(kp, el_k, b);
+      if (g0 + kRowsPerGroup > Hkv) st8_buf(vp, el_v, b);
     } else {
       const uint4 y = rotate_chunk<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn);
-      if constexpr (kStream) {
-        if (g0 < p.Hkv) st16_buf(kp, el_k == kNowhere ? kNowhere : el_k * 2, y);
-        if (g0 + kRowsPerGroup > p.Hkv) st16_buf(vp, el_v == kNowhere ? kNowhere : el_v * 2, y);
-      } else {
-        if (r >= rows || (is_k ? !k_ok : !v_ok)) continue;
-        st16(p.pool + pool_row * D + 8 * c, y);
-      }
+      if (g0 < Hkv) st16_buf(kp, el_k == kNowhere ? kNowhere : el_k * 2, y);
+      if (g0 + kRowsPerGroup > Hkv) st16_buf(vp, el_v == kNowhere ? kNowhere : el_v * 2, y);
     }
   }
 }
@@ -566,13 +595,17 @@ inline unsigned blocks_for(int32_t waves) {
 template <int kCall, bool kFp8, bool kNorm>
 hipError_t launch_contig_call(const ContigParams& p, int D, int style, bool exact,
                               hipStream_t stream) {
+  const uint32_t shifts = p.div_waves.l | (p.div_seq.l << 8) | ((uint32_t)p.xcd_chunk_log2 << 16);
+  const int32_t H = p.Hq + 2 * p.Hkv;
   return with_d(D, [&](auto d) {
     return with_style_exact(style, exact, [&](auto st, auto ex) {
       return with_groups(p.groups_per_wave, [&](auto g) {
         hipLaunchKernelGGL(
             (contig_kernel<decltype(d)::value, kCall, decltype(st)::value, decltype(ex)::value != 0,
                            decltype(g)::value, kFp8, kNorm>),
-            dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p);
+            dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p.total_waves,
+            p.div_waves.m, p.waves_per_token, p.div_seq.m, p.S, H, shifts, p.qkv, p.end_lens,
+            p.pos_ids, p);
         return hipGetLastError();
       });
     });
@@ -592,7 +625,7 @@ hipError_t launch_contig_t(const ContigParams& p, int call, int D, int style, bo
   }
 }
 
-template <bool kGather, bool kFp8, bool kStream>
+template <bool kGather, bool kFp8, bool kLateLoads>
 hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
                           hipStream_t stream) {
   return with_d(D, [&](auto d) {
@@ -600,23 +633,25 @@ hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
       return with_groups(p.groups_per_wave, [&](auto g) {
         hipLaunchKernelGGL((paged_kernel<decltype(d)::value, decltype(st)::value,
                                          decltype(ex)::value != 0, decltype(g)::value, kGather,
-                                         kFp8, kStream>),
-                           dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream, p);
+                                         kFp8, kLateLoads>),
+                           dim3(blocks_for(p.total_waves)), dim3(kBlock), 0, stream,
+                           p.total_waves, p.div_waves.m, p.div_waves.l, p.waves_per_row, p.Hkv,
+                           p.R, p.k_delta, p.v_delta, p.positions, p.seq, p);
         return hipGetLastError();
       });
     });
   });
 }
 
-// E4M3 pools always take non-temporal accesses; fp16 pools when `streaming`.
+// E4M3 pools always load late; fp16 pools when `late_loads`.
 template <bool kFp8>
 hipError_t launch_paged_t(const PagedParams& p, int D, int style, bool exact, bool gather,
-                          bool streaming, hipStream_t stream) {
+                          bool late_loads, hipStream_t stream) {
   if constexpr (kFp8) {
     return gather ? launch_paged_g<true, true, true>(p, D, style, exact, stream)
                   : launch_paged_g<false, true, true>(p, D, style, exact, stream);
   } else {
-    if (streaming)
+    if (late_loads)
       return gather ? launch_paged_g<true, false, true>(p, D, style, exact, stream)
                     : launch_paged_g<false, false, true>(p, D, style, exact, stream);
     return gather ? launch_paged_g<true, false, false>(p, D, style, exact, stream)

@@ -9,8 +9,8 @@ hipError_t launch_contig_fp8(const ContigParams& p, int call, int D, int style, 
 }
 
 hipError_t launch_paged_fp8(const PagedParams& p, int D, int style, bool exact, bool gather,
-                            bool streaming, hipStream_t stream) {
-  return detail::launch_paged_t<true>(p, D, style, exact, gather, streaming, stream);
+                            bool late_loads, hipStream_t stream) {
+  return detail::launch_paged_t<true>(p, D, style, exact, gather, late_loads, stream);
 }
 
 }  // namespace rkv

@@ -87,10 +87,11 @@ struct PagedParams {
 
 hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool exact,
                          hipStream_t stream);
-// streaming: non-temporal delta loads and pool stores (the fp8 launcher
-// always uses them).
+// late_loads: a delta row is loaded once its page ids are known, and only if
+// it is written; otherwise every row is requested with the index loads (the
+// fp8 launcher always loads late).
 hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool gather,
-                        bool streaming, hipStream_t stream);
+                        bool late_loads, hipStream_t stream);
 hipError_t launch_contig_fp8(const ContigParams& p, int call, int D, int style, bool exact,
                              hipStream_t stream);
 hipError_t launch_contig_norm(const ContigParams& p, int call, int D, int style, bool exact,
@@ -98,7 +99,7 @@ hipError_t launch_contig_norm(const ContigParams& p, int call, int D, int style,
 hipError_t launch_contig_norm_fp8(const ContigParams& p, int call, int D, int style, bool exact,
                                   hipStream_t stream);
 hipError_t launch_paged_fp8(const PagedParams& p, int D, int style, bool exact, bool gather,
-                            bool streaming, hipStream_t stream);
+                            bool late_loads, hipStream_t stream);
 
 // Index builders (rkv_meta.hip): rows = batch * width > 0, nodes = batch *
 // verify > 0, all pointers valid device arrays of that many int32.

@@ -106,3 +106,45 @@ def test_rotated_copies_only_the_written_tensors():
                     assert v is t[k]
     p = W.paged(64, 2, 2, 64, 64, 8, 4, W.NEOX, 5, name="p")
     assert bench.written_keys(p) == ("pool",)
+
+
+def test_token_ranges_cover_every_token_once():
+    w = _headline()
+    for parts in (1, 3, 4, 16, 100, 257):
+        ranges = bench._token_ranges(w, parts)
+        assert len(ranges) >= min(parts, w.B * w.S)
+        seen = np.zeros((w.B, w.S), dtype=np.int32)
+        for b, t0, t1 in ranges:
+            assert 0 <= t0 < t1 <= w.S
+            seen[b, t0:t1] += 1
+        assert (seen == 1).all()
+
+
+def test_cpu_baseline_parts_reproduce_the_whole_call():
+    """The CPU baseline's token-range parts compute exactly what one call on
+    the whole workload computes: every part's in-place qkv rows and its own
+    cache rows equal the whole call's, bit for bit."""
+    import oracle
+    w = W.packed(2, 40, 4, 2, 128, 128, 48, W.GPTJ, 77, table_batch=2, table_len=48,
+                 offsets=np.array([0, 9]), name="t")
+    whole_qkv, whole_cache = oracle.packed_qkv(w.cos_sin, w.qkv, w.cache, w.style)
+    ranges = bench._token_ranges(w, 7)
+    parts = bench._oracle_parts(w, ranges)
+    for (b, t0, t1), (table, qkv, cache) in zip(ranges, parts):
+        oracle.packed_qkv_in_place(table, qkv, cache, w.style)
+        assert np.array_equal(qkv[0], whole_qkv[b, t0:t1])
+        assert np.array_equal(cache[0], whole_cache[b, :, :, t0:t1])
+
+
+def test_host_cpus():
+    use, host, allowed, model = bench.host_cpus()
+    assert 1 <= use <= allowed <= host and isinstance(model, str) and model
+
+
+def test_ceilings_library_loads():
+    """The measurement kernels' library is built and exports its entry points
+    (no kernel is launched here)."""
+    import ceilings as C
+    for name in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_empty", "rkvc_paged_floor",
+                 "rkvc_prefill_lds"):
+        assert hasattr(C._L, name)

@@ -1,0 +1,110 @@
+"""The measurement kernels of ceilings/ do the work they stand in for.
+
+bench.py --ceilings times them beside the library's kernels, so each must
+move exactly what it claims: the streams copy (or xor in place) every byte;
+the index-free paged floor writes the pool that the library's paged update
+writes when its positions, sequences and page table encode the floor's
+address arithmetic; the LDS-staged prefill produces the library's call-1
+output bit for bit (both use the library's default arithmetic).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import ceilings as C
+    import rope_kv_cache_amd as rkv
+    return C, rkv
+
+
+def test_streams_move_every_byte():
+    C, _ = _lib()
+    n = 1 << 22   # 8 MiB of fp16
+    src = torch.from_numpy(W.normal_f16(W.rng(3), (n,)).view(np.float16)).cuda()
+    for policy in (1, 0):
+        for chunk in (7, 0):
+            dst = torch.zeros_like(src)
+            C.stream_copy(src, dst, policy, chunk)
+            torch.cuda.synchronize()
+            assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
+            buf = src.clone()
+            C.stream_inplace(buf, policy, chunk, key=0x00010001)
+            torch.cuda.synchronize()
+            want = src.view(torch.int32) ^ 0x00010001
+            assert torch.equal(buf.view(torch.int32), want)
+
+
+def _floor_as_paged(N, Hkv, num_pages, rows_log2, live, scatter, seed):
+    """Delta rows, cos/sin rows, and the positions, sequences and page table
+    under which the library's paged update writes what the floor writes."""
+    r = W.rng(seed)
+    per = 1 << rows_log2
+    seqs = N // per
+    i = np.arange(N)
+    q, j = i >> rows_log2, i & (per - 1)
+    live_row = j < live
+    if scatter:
+        pos = ((q * 37) & 63) + j
+    else:
+        pos = j
+    positions = np.where(live_row, pos, -1).astype(np.int32)
+    seq = np.where(live_row, q, -1).astype(np.int32)
+    max_pages = 4
+    pt = np.zeros((seqs, 2, max_pages), dtype=np.int32)
+    for s in range(seqs):
+        for lp in range(max_pages):
+            if scatter:
+                key = 4 * s + lp
+                pt[s, 0, lp] = (key * 1021) & (num_pages - 1)
+                pt[s, 1, lp] = num_pages + ((key * 2053) & (num_pages - 1))
+            else:
+                pt[s, 0, lp] = (per // 64) * s + lp
+                pt[s, 1, lp] = num_pages + (per // 64) * s + lp
+    k = W.normal_f16(r, (N, Hkv, 128))
+    v = W.normal_f16(r, (N, Hkv, 128))
+    cs = W.rope_rows(np.where(live_row, pos, 0), 128, 10000.0)
+    return k, v, cs, positions, seq, pt, seqs, max_pages
+
+
+@pytest.mark.parametrize("scatter", [0, 1])
+@pytest.mark.parametrize("plan", [0, 1])
+@pytest.mark.parametrize("groups", [1, 2, 4])
+def test_paged_floor_equals_library_update(scatter, plan, groups):
+    C, rkv = _lib()
+    from harness import dev
+    N, Hkv, num_pages, rows_log2, live = 512, 8, 64, 7, 115
+    k, v, cs, positions, seq, pt, seqs, max_pages = _floor_as_paged(
+        N, Hkv, num_pages, rows_log2, live, scatter, 40 + scatter)
+    kd, vd, csd = dev(k), dev(v), dev(cs)
+    fill = W.normal_f16(W.rng(9), (2, num_pages, 64, Hkv, 128))
+    pool_floor, pool_lib = dev(fill), dev(fill)
+    C.paged_floor(kd, vd, pool_floor, csd, num_pages, rows_log2, live, scatter, groups, plan)
+    rkv.dflash_target_kv_cache_update(kd, vd, pool_lib, csd, dev(positions), dev(seq), dev(pt),
+                                      seqs, rkv.ROPE_NEOX)
+    torch.cuda.synchronize()
+    a, b = pool_floor.view(torch.int16), pool_lib.view(torch.int16)
+    written = (b != dev(fill).view(torch.int16)).sum().item()
+    assert written > 0.9 * N * 2 * Hkv * 128 * (live / 128)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("style", [W.GPTJ, W.NEOX])
+@pytest.mark.parametrize("R", [128, 64])
+@pytest.mark.parametrize("groups", [2, 4])
+@pytest.mark.parametrize("chunk", [0, 5])
+def test_lds_prefill_equals_library_call1(style, R, groups, chunk):
+    C, rkv = _lib()
+    from harness import upload
+    w = W.packed(2, 96, 8, 2, 128, R, 128, style, 55 + R, table_batch=2, table_len=100,
+                 offsets=np.array([0, 17]), name="lds")
+    t_lib, t_lds = upload(w), upload(w)
+    rkv.apply_rope_write_kv_packed_qkv(t_lib["cos_sin"], t_lib["qkv"], t_lib["cache"], style)
+    C.prefill_lds(t_lds["cos_sin"], t_lds["qkv"], t_lds["cache"], style, groups, chunk)
+    torch.cuda.synchronize()
+    for key in ("qkv", "cache"):
+        assert torch.equal(t_lds[key].view(torch.int16), t_lib[key].view(torch.int16)), key
