@@ -5,21 +5,21 @@ Moving arrays to and from the device and calling the binding is all it does;
 every step of the computation runs in the library's kernels.
 
 Comparison rules:
-* every element that is not a rotated Q/K output (V copies, passthrough dims
-  >= R, untouched cache and pool bytes, untouched qOut rows) must match the
-  oracle bit for bit;
+* every element that is not a rotated Q/K output inside the call's write set
+  (V copies, passthrough dims >= R, every cache slot, pool row and qOut row
+  the call does not write, derived from its end lengths, position ids and
+  page ids by the skip rules: ``computed_at``) must match the oracle bit for
+  bit;
 * rotated Q/K elements must satisfy |gpu - ref| <= 2^-10*|ref| + 1e-3
   (non-finite values must match in kind);
 * ``compare`` also counts rotated elements whose bits differ and their
   largest distance in fp16 ulps, so that a test can require bit equality
   (the library's RKV_ROUND_EXACT mode) or at most one ulp (its default
   binary32 arithmetic);
-* an fp8 (E4M3) cache or pool starts filled with the E4M3 NaN code, which
-  finite inputs never produce, so the oracle's output marks the bytes it
-  wrote: everywhere else the device must leave that code; written bytes must
-  be within one code step of the oracle's (both NaN counts as equal), and
-  the count and largest step are reported so that a test can require bit
-  equality.
+* an fp8 (E4M3) cache or pool: bytes outside the write set must match the
+  oracle bit for bit; written bytes must be within one code step of the
+  oracle's (both NaN counts as equal), and the count and largest step are
+  reported so that a test can require bit equality.
 """
 from __future__ import annotations
 
@@ -28,6 +28,7 @@ import torch
 
 import workloads as W
 
+TOKENS_PER_PAGE = W.TOKENS_PER_PAGE
 TOL_REL = 2.0 ** -10
 TOL_ABS = 1e-3
 
@@ -183,23 +184,102 @@ def expected(w, L=None) -> dict:
     return want
 
 
-def rotated_mask_parts(w, key):
-    """Index expressions (tuples of slices) covering the elements of output
-    ``key`` that may hold a rotated value (with Q/K norm, every dim of a
-    normalised head is computed)."""
-    R = w.R
-    if w.extra.get("qknorm"):
-        R = w.D
+def written_tokens(w):
+    """Calls 1-3: ([B, S] bool, [B, S] int64) -- which tokens the call
+    writes and the cache slot of each.  Call 1 writes every token at slot s;
+    calls 2 and 3 place token s at end - S + s and skip it when that slot is
+    outside [0, cap) or its position outside the table (the skip rules of
+    the pages' statement, as the oracle and the kernels apply them)."""
+    tlen = w.cos_sin.shape[1]
+    if w.call == "packed":
+        slot = np.broadcast_to(np.arange(w.S, dtype=np.int64), (w.B, w.S))
+        return np.ones((w.B, w.S), dtype=bool), slot
+    slot = w.end_lens.astype(np.int64)[:, None] - w.S + np.arange(w.S, dtype=np.int64)[None, :]
+    pos = slot if w.call == "continuous" else w.pos_ids.astype(np.int64)
+    ok = (slot >= 0) & (slot < w.cap) & (pos >= 0) & (pos < tlen)
+    return ok, slot
+
+
+def written_slots(w) -> np.ndarray:
+    """Calls 1-3: [B, cap] bool, the cache slots (both planes) the call writes."""
+    ok, slot = written_tokens(w)
+    t = np.zeros((w.B, w.cap), dtype=bool)
+    b = np.broadcast_to(np.arange(w.B)[:, None], ok.shape)
+    t[b[ok], slot[ok]] = True
+    return t
+
+
+def written_pool_rows(w):
+    """Call 4: ([numPages, 64] bool, [numPages, 64] bool) -- the K-plane and
+    V-plane page slots the call writes: rows that are not padding, whose
+    sequence is active and position inside the page table, through page ids
+    inside their own plane (and, with the cos/sin gather fused in, with a
+    rope-table row for K)."""
+    P = w.num_pages
+    p = w.positions.astype(np.int64)
+    q = w.seq.astype(np.int64)
+    live = (p >= 0) & (q >= 0) & (q < w.batch) & (p < w.max_pages * TOKENS_PER_PAGE)
+    lp = np.where(live, p // TOKENS_PER_PAGE, 0)
+    qq = np.where(live, q, 0)
+    off = np.where(live, p % TOKENS_PER_PAGE, 0)
+    kid = w.page_table[qq, 0, lp].astype(np.int64)
+    vid = w.page_table[qq, 1, lp].astype(np.int64)
+    k_ok = live & (kid >= 0) & (kid < P)
+    v_ok = live & (vid >= P) & (vid < 2 * P)
+    if w.extra.get("gather"):
+        rope = w.extra["rope"]
+        si = w.extra["state_indices"]
+        st = si[qq].astype(np.int64) if si is not None else \
+            (np.zeros_like(qq) if rope.shape[0] == 1 else qq)
+        k_ok &= (st >= 0) & (st < rope.shape[0]) & (p < rope.shape[1])
+    tk = np.zeros((P, TOKENS_PER_PAGE), dtype=bool)
+    tv = np.zeros((P, TOKENS_PER_PAGE), dtype=bool)
+    tk[kid[k_ok], off[k_ok]] = True
+    tv[vid[v_ok] - P, off[v_ok]] = True
+    return tk, tv
+
+
+def _dims(w):
+    """(dims of a Q row, dims of a K row) that hold computed values: the
+    rotary dims, or all D of a head normalised by the Q/K norm."""
+    norm = w.extra.get("qknorm") or {}
+    rq = w.D if norm.get("q_weight") is not None else w.R
+    rk = w.D if norm.get("k_weight") is not None else w.R
+    return rq, rk
+
+
+def computed_at(w, key, where) -> np.ndarray:
+    """For the elements of output `key` at index arrays `where` (as returned
+    by np.nonzero), whether each holds a value the call computes rather
+    than copies: rotated (or normalised) Q and K elements inside the write
+    set, and with an E4M3 cache every cache element the call writes (V too
+    is scaled and rounded there).  Everything else -- V copies, passthrough
+    dims, slots, rows and pages the call does not write -- must match the
+    oracle bit for bit."""
+    rq, rk = _dims(w)
+    fp8 = is_fp8(w)
     if key == "pool":
-        return [(0, Ellipsis, slice(0, R))]
+        plane, page, off, _, d = where
+        tk, tv = written_pool_rows(w)
+        k_row = (plane == 0) & tk[page, off]
+        if fp8:
+            return k_row | ((plane == 1) & tv[page, off])
+        return k_row & (d < rk)
     if key == "cache":
-        return [(slice(None), 0, Ellipsis, slice(0, R))]
+        b, plane, _, slot, d = where
+        rows = written_slots(w)[b, slot]
+        if fp8:
+            return rows
+        return rows & (plane == 0) & (d < rk)
     if key == "q_out":
-        return [(Ellipsis, slice(0, R))]
+        b, s_, _, d = where
+        ok, _ = written_tokens(w)
+        return ok[b, s_] & (d < rq)
     if key == "qkv":
-        if w.call == "packed":
-            return [(slice(None), slice(None), slice(0, w.Hq + w.Hkv), slice(0, R))]
-        return []
+        if w.call != "packed":
+            return np.zeros(where[0].shape, dtype=bool)
+        _, _, h, d = where
+        return ((h < w.Hq) & (d < rq)) | ((h >= w.Hq) & (h < w.Hq + w.Hkv) & (d < rk))
     raise KeyError(key)
 
 
@@ -252,13 +332,14 @@ def _compare_fp8(w, key, g, ref, report):
     if not diff.any():
         report[key] = 0
         return
-    unwritten = ref == W.SENTINEL8
-    bad = diff & unwritten
-    if bad.any():
-        idx = tuple(int(i) for i in np.argwhere(bad)[0])
-        raise AssertionError(f"{w.name}: {key}{list(idx)} written by the device only: "
-                             f"{g[idx]:#04x} ({int(bad.sum())} such bytes)")
     where = np.nonzero(diff)
+    written = computed_at(w, key, where)
+    if not written.all():
+        k = int(np.argmin(written))
+        idx = tuple(int(a[k]) for a in where)
+        raise AssertionError(f"{w.name}: {key}{list(idx)} differs outside the bytes the call "
+                             f"writes: gpu {g[idx]:#04x} oracle {ref[idx]:#04x} "
+                             f"({int((~written).sum())} such bytes)")
     gd, rd = g[where], ref[where]
     both_nan = _is_nan8(gd) & _is_nan8(rd)
     steps = np.where(both_nan, 0, _e4m3_steps(gd, rd))
@@ -287,26 +368,27 @@ def compare(w, got: dict, want: dict) -> dict:
         if not diff.any():
             report[key] = 0
             continue
-        rot = np.zeros(ref.shape, dtype=bool)
-        for ix in rotated_mask_parts(w, key):
-            rot[ix] = True
-        bad = diff & ~rot
-        if bad.any():
-            idx = tuple(int(i) for i in np.argwhere(bad)[0])
+        where = np.nonzero(diff)
+        rot = computed_at(w, key, where)
+        if not rot.all():
+            k = int(np.argmin(rot))
+            idx = tuple(int(a[k]) for a in where)
             raise AssertionError(
-                f"{w.name}: {key}{list(idx)} differs outside rotated Q/K: gpu {g[idx]:#06x} "
-                f"oracle {ref[idx]:#06x} ({int(bad.sum())} such elements)")
+                f"{w.name}: {key}{list(idx)} differs outside the computed Q/K elements the call "
+                f"writes: gpu {g[idx]:#06x} oracle {ref[idx]:#06x} ({int((~rot).sum())} such "
+                f"elements)")
+        gd, rd = g[where], ref[where]
         # computed NaN results match as NaN: IEEE 754 leaves the sign (and
         # payload) of a NaN produced by an invalid operation unspecified
-        nan_pair = diff & _is_nan16(g) & _is_nan16(ref) & rot
+        nan_pair = _is_nan16(gd) & _is_nan16(rd)
         if nan_pair.any():
             report[key + "_nan_bits_differ"] = int(nan_pair.sum())
-            diff = diff & ~nan_pair
-            if not diff.any():
+            keep = ~nan_pair
+            where = tuple(a[keep] for a in where)
+            gd, rd = gd[keep], rd[keep]
+            if gd.size == 0:
                 report[key] = 0
                 continue
-        where = np.nonzero(diff)
-        gd, rd = g[where], ref[where]
         tol_ok = _within_tol(gd, rd)
         if not tol_ok.all():
             k = int(np.argmin(tol_ok))
