@@ -13,13 +13,11 @@ update, the paged update with the cos/sin gather fused in, the continuous
 and paged calls into an E4M3 cache, the continuous call with Q/K RMS norm,
 the prefill's TP=8 shard, a 65,536-row paged update, a 16-sequence
 continuous write, and the two device index builders) are reported under
-"workloads".  The small workloads' inputs fit the 256 MB MALL: they are
-timed cold (``time_cold``: each launch after a 1 GiB read that evicts its
-inputs, all work queued behind a GPU spin, the median event pair around the
-launch minus the median event pair around nothing) and back to back; their
-figure of record is timed like the headline, back to back, cycling through
-enough full copies of every tensor they touch that each launch reads from
-and writes back to HBM (``full_copies``, ``time_rotated``).
+"workloads".  The small workloads' inputs fit the 256 MB MALL: their figure
+of record is timed like the headline, back to back, cycling through enough
+full copies of every tensor they touch that each launch reads from and
+writes back to HBM (``full_copies``, ``time_rotated``); warm launches on the
+same tensors are reported beside it.
 
 ``--workload NAME`` times single small workloads and ``--ceilings`` the
 measurement kernels of ``ceilings/`` (stream ceilings, empty kernels, an
@@ -354,7 +352,9 @@ ROTATED_PROTOCOL = ("rotated: launches back to back, queued ahead behind a GPU s
 COLD_PROTOCOL = ("cold: every launch follows a 1 GiB read that evicts its inputs from L2 and "
                  "MALL; all work queued behind a GPU spin; median over K launches of the event "
                  "pair around the launch minus the median of an event pair around nothing, "
-                 "recorded the same way")
+                 "recorded the same way (an estimate from below: part of the pair's own cost "
+                 "overlaps the launch; rocprofv3's trace of such launches reads up to about "
+                 "2 us more)")
 MARGINAL_PROTOCOL = ("marginal: span of K x (1 GiB read, launch) minus span of K x (1 GiB "
                      "read), / K: the time one launch adds to a stream of HBM-bound work, its "
                      "dispatch and the write-back of the lines it leaves dirty included")
@@ -449,9 +449,9 @@ def small_cases():
     }
 
 
-def small_workload(label, make, steps, flush):
-    """One small workload: rotated (HBM steady state, the figure of record),
-    cold (one isolated launch after a flush) and back-to-back warm times."""
+def small_workload(label, make, steps):
+    """One small workload: rotated (HBM steady state, the figure of record)
+    and back-to-back warm times."""
     import torch
     from harness import launch, upload
     log(f"[bench] generating {label}")
@@ -462,18 +462,16 @@ def small_workload(label, make, steps, flush):
     r_ms = time_rotated(lambda s: launch(x, s), sets, steps)
     del sets
     torch.cuda.empty_cache()
-    c_ms, ev_ms = time_cold(lambda: launch(x, tx), flush, steps)
     h_ms = time_queued(lambda: launch(x, tx), steps)
     gbs = xb / (r_ms * 1e-3) / 1e9
     log(f"[bench] {label}: {r_ms * 1e3:.2f} us rotated, {gbs:.0f} GB/s "
-        f"({gbs / PEAK_HBM_GBS:.1%}); cold {c_ms * 1e3:.2f} us, back to back {h_ms * 1e3:.2f} us")
+        f"({gbs / PEAK_HBM_GBS:.1%}); warm, back to back {h_ms * 1e3:.2f} us")
     name, tokens = x.name, x.tokens
     del tx, x
     torch.cuda.empty_cache()
     return {"workload": name, "kernel_us": r_ms * 1e3, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS,
             "tokens_per_s": tokens / (r_ms * 1e-3), "algorithmic_bytes": xb,
             "protocol": ROTATED_PROTOCOL,
-            "cold_us": c_ms * 1e3, "cold_protocol": COLD_PROTOCOL, "event_pair_us": ev_ms * 1e3,
             "hot_kernel_us": h_ms * 1e3,
             "hot_note": "not flushed: launches queued ahead and run back to back on the same "
                         "tensors (inputs left in MALL / L2 by the previous launch), event span / "
@@ -841,10 +839,8 @@ def main():
                      f"{list(cases)} and {list(CEILING_PARTS)}")
         res = {}
         if args.workload:
-            flush = make_flush()
-            res["workloads"] = {n: small_workload(n, cases[n], args.steps, flush)
+            res["workloads"] = {n: small_workload(n, cases[n], args.steps)
                                 for n in args.workload}
-            del flush
         if parts:
             res["ceilings"] = ceilings_leg(args.steps, parts)
         if args.calib:
@@ -960,10 +956,8 @@ def main():
         calibration_copy()
 
     if not args.no_extra:
-        flush = make_flush()
         for label, make in small_cases().items():
-            extra[label] = small_workload(label, make, max(20, args.steps), flush)
-        del flush
+            extra[label] = small_workload(label, make, max(20, args.steps))
         torch.cuda.empty_cache()
         extra["paged_delta_large"] = paged_large(max(10, args.steps // 2))
         extra["paged_delta_large_fp8"] = paged_large(max(10, args.steps // 2), fp8=True)
