@@ -490,7 +490,7 @@ def _device_paged(x):
     return t
 
 
-CEILING_PARTS = ("streams", "empty", "paged", "prefill")
+CEILING_PARTS = ("streams", "empty", "paged", "prefill", "shapes")
 
 
 def ceilings_leg(steps, parts=CEILING_PARTS):
@@ -510,7 +510,10 @@ def ceilings_leg(steps, parts=CEILING_PARTS):
       contiguous rows and scattered over pool pages, in both access plans,
       beside the library's paged update on the paged workload;
     * the large prefill with its cos/sin row staged in LDS (one workgroup per
-      token, 2 or 4 row groups per wave) beside the library's kernel."""
+      token, 2 or 4 row groups per wave) beside the library's kernel;
+    * launch shapes: each workload under every forced number of row groups
+      per wave (and both load plans of the paged update), timed as its figure
+      of record is."""
     out = {}
     flush = make_flush()
     if "streams" in parts:
@@ -521,6 +524,8 @@ def ceilings_leg(steps, parts=CEILING_PARTS):
         out.update(_paged_floors(steps, flush))
     if "prefill" in parts:
         out.update(_prefill_lds(steps))
+    if "shapes" in parts:
+        out["launch_shapes"] = _launch_shapes(steps)
     return out
 
 
@@ -670,6 +675,88 @@ def _prefill_lds(steps):
     del sets, t
     torch.cuda.empty_cache()
     return out
+
+
+def _launch_shapes(steps):
+    """Every workload under each forced row-group count (rkv_set_launch_
+    overrides; results are identical under all of them), and the paged
+    update under both load plans: the large workloads back to back over four
+    copies of the written tensors (time_launches), the small ones back to
+    back over full copies (time_rotated).  The library's own choice is
+    reported beside them.  Returns {workload: {setting: us}}."""
+    import torch
+    import rope_kv_cache_amd as rkv
+    import workloads as W
+    from harness import launch, upload
+    out = {}
+
+    def sweep(label, w, t, large, plans=(0,), exact=False):
+        """Three rounds over the settings, each round in a rotated order (so
+        that no setting always runs first); median per setting."""
+        nb = algorithmic_bytes(w)
+        sets = None if large else full_copies(t, nb)
+        settings = [(g, plan) for plan in plans for g in (0, 1, 2, 4)]
+        times = {}
+        for rnd in range(3):
+            k = rnd * len(settings) // 3
+            for g, plan in settings[k:] + settings[:k]:
+                rkv.set_launch_overrides(g, plan)
+                try:
+                    if large:
+                        ms, _ = time_launches(w, t, max(10, steps // 2), 3, exact=exact)
+                    else:
+                        ms = time_rotated(lambda s_: launch(w, s_, exact), sets, steps)
+                    chosen = rkv.last_launch_groups_per_wave()
+                    loads = rkv.last_launch_paged_loads()
+                finally:
+                    rkv.set_launch_overrides(0, 0)
+                key = (f"G{g}" if g else f"auto(G{chosen})") + \
+                    (f"_{'early' if loads == 1 else 'late'}" if loads else "")
+                times.setdefault(key, []).append(ms * 1e3)
+        res = {k: float(np.median(v)) for k, v in times.items()}
+        log(f"[bench] shapes {label}: " + ", ".join(f"{k} {v:.2f}" for k, v in res.items()))
+        out[label] = {"median_us": res, "rounds_us": times}
+        del sets
+        torch.cuda.empty_cache()
+
+    for label, make, large, plans in (
+            ("prefill_gptj", lambda: W.config(HEADLINE), True, (0,)),
+            ("prefill_gptj_exact", lambda: W.config(HEADLINE), True, (0,)),
+            ("prefill_neox", lambda: _styled(W.config(HEADLINE), W.NEOX), True, (0,)),
+            ("prefill_fp8_cache", lambda: W.with_fp8_cache(W.config(HEADLINE), 7005, fill="sentinel"), True, (0,)),
+            ("prefill_qknorm", lambda: W.with_qk_norm(W.config(HEADLINE), 7105), True, (0,)),
+            ("prefill_qknorm_neox", lambda: _styled(W.with_qk_norm(W.config(HEADLINE), 7105), W.NEOX), True, (0,)),
+            ("prefill_neox_exact", lambda: _styled(W.config(HEADLINE), W.NEOX), True, (0,)),
+            ("prefill_fp8_cache_exact", lambda: W.with_fp8_cache(W.config(HEADLINE), 7005, fill="sentinel"), True, (0,)),
+            ("prefill_qknorm_fp8_cache", lambda: W.with_fp8_cache(W.with_qk_norm(W.config(HEADLINE), 7105), 7005, fill="sentinel"), True, (0,)),
+            ("prefill_qknorm_fp8_cache_neox", lambda: _styled(W.with_fp8_cache(W.with_qk_norm(W.config(HEADLINE), 7105), 7005, fill="sentinel"), W.NEOX), True, (0,)),
+            ("paged_delta_n65536", lambda: W.paged(65536, 64, 8, 128, 128, 8192, 128, W.NEOX, 1044,
+                                                   pool_fill="none", name="paged_delta_n65536_p8192"),
+             True, (1, 2))):
+        log(f"[bench] generating {label}")
+        w = make()
+        t = _device_paged(w) if isinstance(w, W.Paged) else upload(w)
+        sweep(label, w, t, large, plans, exact=label.endswith("_exact"))
+        del t, w
+        torch.cuda.empty_cache()
+    smalls = dict(small_cases())
+    smalls["paged_delta_gptj"] = lambda: _styled(W.config(4), W.GPTJ)
+    smalls["paged_delta_exact"] = lambda: W.config(4)
+    smalls["continuous_neox_exact"] = lambda: W.config(2, W.NEOX)
+    for label, make in smalls.items():
+        log(f"[bench] generating {label}")
+        w = make()
+        t = upload(w)
+        sweep(label, w, t, False, (1, 2) if isinstance(w, W.Paged) else (0,),
+              exact=label.endswith("_exact"))
+        del t, w
+        torch.cuda.empty_cache()
+    return out
+
+
+def _styled(w, style):
+    w.style = style
+    return w
 
 
 def traffic_from_profile(kernel_name: str):

@@ -364,6 +364,25 @@ int32_t rkv_tokens_per_page(void);
  * it is reported for tests and tuning and has no effect on results. */
 int32_t rkv_last_launch_groups_per_wave(void);
 
+/* Launch-shape overrides, for tuning and tests (no page defines such a
+ * call).  They hold for this thread's later rope / KV-cache calls until they
+ * are set again; results are the same bit for bit under every setting, only
+ * the time differs.
+ *   groupsPerWave: 0 lets the library choose; 1, 2 or 4 asks for that many
+ *     row groups per wave (fewer when a work item -- a token of calls 1-3, a
+ *     delta row of call 4 -- has fewer; more when one dispatch could not
+ *     hold the waves).
+ *   pagedLoads: 0 lets the library choose; 1 makes call 4 request every
+ *     delta row together with its index loads ("early"); 2 loads a delta
+ *     row once its page ids are known, and only if it is written ("late").
+ * Returns RKV_ERR_SHAPE and changes nothing for any other value. */
+rkv_status rkv_set_launch_overrides(int32_t groupsPerWave, int32_t pagedLoads);
+
+/* Load plan of this thread's most recent call: 1 early, 2 late (see
+ * rkv_set_launch_overrides); 0 when that call was not a paged update or
+ * launched nothing. */
+int32_t rkv_last_launch_paged_loads(void);
+
 /* Message for the last error raised on this thread ("" if none).  The
  * pointer stays valid until the next call on the same thread. */
 const char* rkv_last_error(void);

@@ -27,6 +27,7 @@ Functions (same names as the C entry points, without the ``rkv_`` prefix):
   check_rope_capacity(cos_sin_seq_len, kv_capacity)
   tokens_per_page()
   last_launch_groups_per_wave()
+  set_launch_overrides(groups_per_wave=0, paged_loads=0), last_launch_paged_loads()
 
   apply_rope_write_kv_packed_qkv_qknorm(cos_sin_cache, qkv, kv_cache, q_norm_weight, k_norm_weight,
                                         epsilon, rope_style, k_scale=None, v_scale=None)
@@ -105,6 +106,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rkv_check_rope_capacity": [i32, i32],
         "rkv_tokens_per_page": [],
         "rkv_last_launch_groups_per_wave": [],
+        "rkv_set_launch_overrides": [i32, i32],
+        "rkv_last_launch_paged_loads": [],
         "rkv_last_error": [],
         "rkv_status_string": [i32],
     }
@@ -438,3 +441,16 @@ def last_launch_groups_per_wave() -> int:
     """Row groups per wave (1, 2 or 4) of the kernel this thread's last
     rope / KV-cache call launched; 0 if it launched none."""
     return lib.rkv_last_launch_groups_per_wave()
+
+
+def set_launch_overrides(groups_per_wave: int = 0, paged_loads: int = 0) -> None:
+    """Force the row groups per wave (0 = the library's choice, 1, 2, 4) and
+    the paged update's load plan (0 = the library's choice, 1 early, 2 late)
+    for this thread's later calls."""
+    _check(lib.rkv_set_launch_overrides(int(groups_per_wave), int(paged_loads)))
+
+
+def last_launch_paged_loads() -> int:
+    """Load plan of this thread's last call: 1 early, 2 late, 0 if it was
+    not a paged update or launched nothing."""
+    return lib.rkv_last_launch_paged_loads()

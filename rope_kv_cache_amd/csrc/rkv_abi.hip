@@ -14,6 +14,9 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local int32_t g_last_groups = 0;   // row groups per wave of this thread's last launch
+thread_local int32_t g_last_loads = 0;    // paged load plan of the last launch (1 early, 2 late)
+thread_local int32_t g_force_groups = 0;  // rkv_set_launch_overrides: 0 or 1, 2, 4
+thread_local int32_t g_force_loads = 0;   // rkv_set_launch_overrides: 0, 1 early, 2 late
 
 rkv_status fail(rkv_status st, const char* fmt, ...) {
   va_list ap;
@@ -26,26 +29,34 @@ rkv_status fail(rkv_status st, const char* fmt, ...) {
 void clear_error() {
   g_err[0] = '\0';
   g_last_groups = 0;
+  g_last_loads = 0;
 }
 
 // Launch shape.  A wave handles G row groups (512/D rows each) of one work
-// item.  Large launches are bandwidth-bound: the plain binary32 kernel runs
-// fastest with one row group per wave, while the kernels with more
-// arithmetic per byte (exact mode, E4M3 cache, Q/K norm) run faster with at
-// least two, whose loads are in flight together while the wave computes
-// (measured on the large prefill: 236 -> 221 us with an E4M3 cache, 266 ->
-// 241 us with Q/K norm, 272 -> 247 us exact; four were no better).  A wave
-// fetches its cos/sin values once for all its row groups, and a NeoX lane
-// needs twice as many as a GPT-J lane (8 frequencies instead of 4), so the
-// NeoX kernels take one step more: two row groups for the plain kernel
-// (large NeoX prefill 245-251 -> 236 us), four with Q/K norm (254 -> 244
-// us); the paged update takes two for NeoX as for its heavier kernels.  Q/K
-// norm into an E4M3 cache takes four in both layouts (GPT-J 242 -> 231 us,
-// NeoX 266 -> 248 us).  Small
-// launches are latency-bound, so they take G = 2 or 4 when that keeps every
-// wave resident at once (256 CUs x 4 SIMDs x 8 waves); there the Q/K-norm
-// kernel, with the longest chain between load and store, starts from four
-// (12.8 -> 11.9 us on the continuous workload; four slowed the E4M3 ones).
+// item (a token of calls 1-3, a delta row of call 4); its loads for all G
+// groups are in flight together and it fetches its cos/sin values (and norm
+// weights) once for all of them.  The choices below come from sweeps of
+// every forced G (rkv_set_launch_overrides) on MI355X, three interleaved
+// rounds each, large launches back to back over four copies of the written
+// tensors, small ones back to back over full copies of all their tensors
+// (medians, us):
+//  - large prefill (1.43 GB): two row groups per wave for every flavour
+//    (GPT-J 217.7, one 219.0, four 227.6; E4M3 205.2 against 210.2 / 218.8;
+//    Q/K norm 218.7, NeoX Q/K norm 214.7 against 224.8 at four, Q/K norm
+//    into E4M3 204.1 against 213.0) except the exact mode of the NeoX layout
+//    and of the E4M3 cache, whose binary64 arithmetic per byte is highest
+//    and which take four (NeoX 227.4 against 231.4, E4M3 219.6 against
+//    233.4; the exact GPT-J kernel takes two, 220.8 against 228.4);
+//  - small launches are latency-bound: every wave is resident at once
+//    (256 CUs x 4 SIMDs x 8 waves), so a small launch doubles G while its
+//    waves would not all fit; the continuous and tree calls run alike at two
+//    and four (5.3-5.5), the Q/K-norm kernel starts from four;
+//  - the paged update's small fp16 launches take four, one wave per delta
+//    row, which then resolves its index chain once (NeoX 6.5 against 8.2 at
+//    two, GPT-J 6.9 against 7.8, exact 7.1 against 8.3, fused gather 6.5
+//    against 7.3); small E4M3 ones take two with late loads (7.1); large
+//    ones take two for NeoX and the exact mode, one for GPT-J, four for E4M3
+//    (65,536 rows: 77.0 at two against 81.5 / 84.1).
 constexpr long long kResidentWaves = 8192;
 constexpr long long kStreamingGroups = 65536;
 
@@ -134,13 +145,15 @@ struct Split {
 // dispatch can hold (2^32 - 1 work-items).  g_large / g_small: the row
 // groups per wave a kernel starts from in large and small launches (capped
 // by the row groups a work item has).
+// A row-group override (rkv_set_launch_overrides) replaces the starting
+// choice and skips the small-launch doubling.
 Split pick_split(long long items, long long groups_per_item, int g_large, int g_small) {
   auto waves = [&](int g) { return items * ((groups_per_item + g - 1) / g); };
   const bool small = items * groups_per_item <= kStreamingGroups;
-  const int start = small ? g_small : g_large;
+  const int start = g_force_groups ? g_force_groups : (small ? g_small : g_large);
   int g = 1;
   while (g < start && 2 * g <= groups_per_item) g *= 2;
-  if (small) {
+  if (small && !g_force_groups) {
     while (g < 4 && waves(g) > kResidentWaves) g *= 2;
   }
   while (g < 4 && waves(g) > rkv::kMaxWavesPerLaunch) g *= 2;
@@ -151,6 +164,7 @@ Split pick_split(long long items, long long groups_per_item, int g_large, int g_
 rkv_status launched(hipError_t e) {
   if (e != hipSuccess) {
     g_last_groups = 0;
+    g_last_loads = 0;
     return fail(RKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return RKV_OK;
@@ -293,13 +307,8 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   const long long rows_per_group = 512 / D;
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
   const bool neox = layout_of(style) == RKV_ROPE_NEOX;
-  // large launches (measured on MI355X with the written buffers rotated):
-  // two row groups per wave; four for the exact mode (1.4 GB prefill: NeoX
-  // 272 -> 258 us, E4M3 274 -> 262 us, GPT-J 235-240 -> 230 us) and for the
-  // Q/K norm in the NeoX layout or into an E4M3 cache.  (Plain GPT-J took one
-  // until the XCDs took chunks in turn; then two: 222-224 -> 220-221 us on
-  // the 1.4 GB prefill, -5% on its TP=8 shard.)
-  const int g_large = norm ? ((neox || fp8) ? 4 : 2) : (exact_of(style) ? 4 : 2);
+  const bool exact = exact_of(style);
+  const int g_large = (exact && (neox || fp8)) ? 4 : 2;
   const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, g_large,
                               norm ? 4 : (heavy ? 2 : 1));
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
@@ -405,23 +414,24 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   p.max_pages = maxPagesPerSeq;
   const long long rows_per_group = 512 / D;
   const long long groups_per_row = (2 * Hkv + rows_per_group - 1) / rows_per_group;
-  // row groups per wave: E4M3 pools take four in large launches (65,536
-  // rows: 72-74 -> 64-65 us on MI355X), NeoX, exact and E4M3 two otherwise
-  const int g_small =
-      (exact_of(ropeStyle) || fp8 || layout_of(ropeStyle) == RKV_ROPE_NEOX) ? 2 : 1;
-  const int g_large = fp8 ? 4 : g_small;
+  // row groups per wave (see "Launch shape" above)
+  const bool neox = layout_of(ropeStyle) == RKV_ROPE_NEOX;
+  const int g_small = fp8 ? 2 : 4;
+  const int g_large = fp8 ? 4 : ((exact_of(ropeStyle) || neox) ? 2 : 1);
   const Split sp = pick_split(N, groups_per_row, g_large, g_small);
   // large launches and E4M3 pools load a delta row once its page ids are
   // known (only rows that are written move bytes); small fp16 ones request
   // every row with the index loads, so that the reads overlap the two
   // dependent index round trips
-  const bool late_loads = fp8 || N * groups_per_row > kStreamingGroups;
+  const bool late_loads =
+      g_force_loads ? g_force_loads == 2 : (fp8 || N * groups_per_row > kStreamingGroups);
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
   p.groups_per_wave = sp.groups_per_wave;
   p.waves_per_row = sp.waves_per_item;
   p.total_waves = (int32_t)(N * p.waves_per_row);
   p.div_waves = rkv::make_fastdiv((uint32_t)p.waves_per_row);
   g_last_groups = p.groups_per_wave;
+  g_last_loads = late_loads ? 2 : 1;
   return launched(fp8 ? rkv::launch_paged_fp8(p, headDim, layout_of(ropeStyle),
                                               exact_of(ropeStyle), gather, late_loads, stream)
                       : rkv::launch_paged(p, headDim, layout_of(ropeStyle), exact_of(ropeStyle),
@@ -650,6 +660,19 @@ rkv_status rkv_check_rope_capacity(int32_t cosSinSeqLen, int32_t kvCapacity) {
 int32_t rkv_tokens_per_page(void) { return rkv::kTokensPerPage; }
 
 int32_t rkv_last_launch_groups_per_wave(void) { return g_last_groups; }
+
+rkv_status rkv_set_launch_overrides(int32_t groupsPerWave, int32_t pagedLoads) {
+  g_err[0] = '\0';
+  if (groupsPerWave != 0 && groupsPerWave != 1 && groupsPerWave != 2 && groupsPerWave != 4)
+    return fail(RKV_ERR_SHAPE, "groupsPerWave %d: must be 0, 1, 2 or 4", groupsPerWave);
+  if (pagedLoads < 0 || pagedLoads > 2)
+    return fail(RKV_ERR_SHAPE, "pagedLoads %d: must be 0, 1 or 2", pagedLoads);
+  g_force_groups = groupsPerWave;
+  g_force_loads = pagedLoads;
+  return RKV_OK;
+}
+
+int32_t rkv_last_launch_paged_loads(void) { return g_last_loads; }
 
 const char* rkv_last_error(void) { return g_err; }
 

@@ -643,20 +643,14 @@ hipError_t launch_paged_g(const PagedParams& p, int D, int style, bool exact,
   });
 }
 
-// E4M3 pools always load late; fp16 pools when `late_loads`.
 template <bool kFp8>
 hipError_t launch_paged_t(const PagedParams& p, int D, int style, bool exact, bool gather,
                           bool late_loads, hipStream_t stream) {
-  if constexpr (kFp8) {
-    return gather ? launch_paged_g<true, true, true>(p, D, style, exact, stream)
-                  : launch_paged_g<false, true, true>(p, D, style, exact, stream);
-  } else {
-    if (late_loads)
-      return gather ? launch_paged_g<true, false, true>(p, D, style, exact, stream)
-                    : launch_paged_g<false, false, true>(p, D, style, exact, stream);
-    return gather ? launch_paged_g<true, false, false>(p, D, style, exact, stream)
-                  : launch_paged_g<false, false, false>(p, D, style, exact, stream);
-  }
+  if (late_loads)
+    return gather ? launch_paged_g<true, kFp8, true>(p, D, style, exact, stream)
+                  : launch_paged_g<false, kFp8, true>(p, D, style, exact, stream);
+  return gather ? launch_paged_g<true, kFp8, false>(p, D, style, exact, stream)
+                : launch_paged_g<false, kFp8, false>(p, D, style, exact, stream);
 }
 
 }  // namespace detail

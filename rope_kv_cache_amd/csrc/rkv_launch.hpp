@@ -88,8 +88,7 @@ struct PagedParams {
 hipError_t launch_contig(const ContigParams& p, int call, int D, int style, bool exact,
                          hipStream_t stream);
 // late_loads: a delta row is loaded once its page ids are known, and only if
-// it is written; otherwise every row is requested with the index loads (the
-// fp8 launcher always loads late).
+// it is written; otherwise every row is requested with the index loads.
 hipError_t launch_paged(const PagedParams& p, int D, int style, bool exact, bool gather,
                         bool late_loads, hipStream_t stream);
 hipError_t launch_contig_fp8(const ContigParams& p, int call, int D, int style, bool exact,

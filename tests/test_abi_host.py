@@ -631,3 +631,19 @@ def test_linear_tree_validation(kw, want):
     a.update(kw)
     st = L.rkv_dflash_build_linear_tree_metadata(a["par"], a["dep"], a["B"], a["V"], None)
     assert st == want, (kw, rkv.status_string(st), L.rkv_last_error())
+
+
+def test_launch_overrides_validation():
+    """rkv_set_launch_overrides accepts 0/1/2/4 row groups and load plans 0-2,
+    rejects anything else without changing the setting; a fresh thread's
+    last-launch queries read 0."""
+    L = rkv.lib
+    assert L.rkv_last_launch_paged_loads() == 0
+    for g, p in ((0, 0), (1, 1), (2, 2), (4, 0), (0, 2)):
+        assert L.rkv_set_launch_overrides(g, p) == rkv.OK
+    for g, p in ((3, 0), (8, 0), (-1, 0), (0, 3), (0, -1)):
+        assert L.rkv_set_launch_overrides(g, p) == rkv.ERR_SHAPE
+        assert "must be" in L.rkv_last_error().decode()
+    with pytest.raises(rkv.RkvError):
+        rkv.set_launch_overrides(5, 0)
+    rkv.set_launch_overrides(0, 0)

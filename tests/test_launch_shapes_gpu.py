@@ -116,3 +116,60 @@ def test_paged_launch_shapes(gather, flavour):
     seen = _run_ladder((make(k, *row) for k, row in enumerate(PAGED_LADDER)), flavour)
     for mode in MODES:
         assert seen[mode] == {1, 2, 4}, (mode, seen)
+
+
+# ---------------------------------------------- forced launch shapes ----
+
+def _forced(workloads, flavour, plans=(0,)):
+    """Each workload under every forced row-group count (and paged load plan):
+    the library reports the forced choice and the result keeps the parity
+    bar; the override is reset afterwards."""
+    try:
+        for w in workloads:
+            want = expected(w)
+            for plan in plans:
+                for g in (1, 2, 4):
+                    rkv.set_launch_overrides(g, plan)
+                    for mode in MODES:
+                        t = upload(w)
+                        launch(w, t, exact=(mode == "exact"))
+                        got_g = rkv.last_launch_groups_per_wave()
+                        got_plan = rkv.last_launch_paged_loads()
+                        got = download(w, t)
+                        del t
+                        rep = compare(w, got, want)
+                        _say(f"[forced] {w.name} {flavour} G={g} plan={plan} {mode}: {rep}")
+                        assert got_g == g, (got_g, g)
+                        if plan:
+                            assert got_plan == plan, (got_plan, plan)
+                        if mode == "exact":
+                            assert not exact_diffs(rep), f"exact mode not bit-identical: {rep}"
+                        else:
+                            keys = ("_max_ulp_ge_2m6", "_max_code_step") if "norm" in flavour \
+                                else ("_max_ulp", "_max_code_step")
+                            assert all(v <= 1 for k, v in rep.items() if k.endswith(keys)), rep
+    finally:
+        rkv.set_launch_overrides(0, 0)
+
+
+@pytest.mark.parametrize("flavour", ["fp16", "fp8", "norm", "norm_fp8"])
+@pytest.mark.parametrize("call", ["packed", "continuous", "tree"])
+def test_contig_forced_shapes(call, flavour):
+    """Tokens of 12 row groups (the workloads' head counts): every forced
+    choice is an instantiation the size ladder reaches only at some sizes."""
+    w = _flavoured(_contig(call, "forced", 3, 40, 32, 8, 128, 128, NEOX if call != "packed"
+                           else GPTJ, 9800), flavour, 9800)
+    _forced([w], flavour)
+
+
+@pytest.mark.parametrize("flavour", ["fp16", "fp8"])
+@pytest.mark.parametrize("gather", [False, True], ids=["table_rows", "gather_fused"])
+def test_paged_forced_shapes_and_load_plans(gather, flavour):
+    """Both load plans (early, late) under every forced row-group count, on
+    a workload with padding rows and unmapped pages."""
+    seed = 9900 + gather
+    args = (300, 7, 8, 128, 128, 7 * 9, 9, NEOX, seed)
+    w = W.paged_gather(*args, rope_states=2, width=43, pad_frac=0.2, bad_frac=0.2,
+                       name="paged_gather_forced") if gather else \
+        W.paged(*args, width=43, pad_frac=0.2, bad_frac=0.2, name="paged_forced")
+    _forced([_flavoured(w, flavour, seed)], flavour, plans=(1, 2))
