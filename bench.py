@@ -614,66 +614,77 @@ def _paged_floors(steps, flush):
     live, rows_log2 = 115, 7
     n_live = sum(min(live, 128) for _ in range(4096 // 128))
     floor_bytes = n_live * (8 * 128 * 2 * 4 + 128 * 4)
-    for scatter in (0, 1):
-        for plan in (0, 1):
-            def run(t, scatter=scatter, plan=plan):
-                C.paged_floor(t["k_delta"], t["v_delta"], t["pool"], t["cos_sin"],
-                              x.num_pages, rows_log2, live, scatter, 2, plan)
-            r = _four_ways(run, tx, floor_bytes, flush, steps)
-            r.update(bytes=floor_bytes, **{"GB/s": floor_bytes / (r["kernel_us"] * 1e-6) / 1e9})
-            name = (f"paged_floor_{'scatter' if scatter else 'contiguous'}_"
-                    f"{'streaming' if plan else 'early_loads'}")
-            out[name] = r
-            log(f"[bench] {name}: {r['kernel_us']:.2f} us rotated ({r['GB/s']:.0f} GB/s), "
-                f"{r['cold_us']:.2f} us cold, {r['marginal_us']:.2f} us marginal, "
-                f"{r['hot_kernel_us']:.2f} us back to back")
+    for scatter, plan, g in [(sc, pl, g) for sc in (0, 1) for pl in (0, 1) for g in (2, 4)]:
+        def run(t, scatter=scatter, plan=plan, g=g):
+            C.paged_floor(t["k_delta"], t["v_delta"], t["pool"], t["cos_sin"],
+                          x.num_pages, rows_log2, live, scatter, g, plan)
+        r = _four_ways(run, tx, floor_bytes, flush, steps)
+        r.update(bytes=floor_bytes, **{"GB/s": floor_bytes / (r["kernel_us"] * 1e-6) / 1e9})
+        name = (f"paged_floor_{'scatter' if scatter else 'contiguous'}_"
+                f"{'nt_policy' if plan else 'default_policy'}_g{g}")
+        out[name] = r
+        log(f"[bench] {name}: {r['kernel_us']:.2f} us rotated ({r['GB/s']:.0f} GB/s), "
+            f"{r['cold_us']:.2f} us cold, {r['marginal_us']:.2f} us marginal, "
+            f"{r['hot_kernel_us']:.2f} us back to back")
     del tx, x
     torch.cuda.empty_cache()
     return out
 
 
 def _prefill_lds(steps):
+    """Call 1 on the headline shape with one workgroup per token: the cos/sin
+    row staged in LDS (lds_*) or fetched per wave as the library does
+    (wave_*), and, on the same shape in NeoX style, the NeoX partners
+    exchanged by ds_bpermute (the library's) or by DPP (wave_*_dpp).  Each
+    variant back to back over four copies of the written tensors, two
+    interleaved series; the library's own launch beside them."""
     import torch
     import ceilings as C
     import workloads as W
     from harness import launch, upload
     out = {}
-    w = W.config(HEADLINE)
-    nbytes = algorithmic_bytes(w)
-    t = upload(w)
-    sets = rotated(w, t, ROTATIONS)
-    variants = [("library", None, None)] + [(f"lds_g{g}_xcd{c}", g, c)
-                                            for g in (2, 4) for c in (5, 0)]
-    for rep in range(2):
-        for name, g, c in variants:
-            k = [0]
+    for style_name in ("gptj", "neox"):
+        w = W.config(HEADLINE)
+        if style_name == "neox":
+            w = _styled(w, W.NEOX)
+        nbytes = algorithmic_bytes(w)
+        t = upload(w)
+        sets = rotated(w, t, ROTATIONS)
+        variants = [("library", None, None, True, False)]
+        variants += [(f"lds_g{g}_xcd{c}", g, c, True, False) for g in (2, 4) for c in (5, 0)]
+        variants += [(f"wave_g{g}_xcd5", g, 5, False, False) for g in (2, 4)]
+        if style_name == "neox":
+            variants += [(f"wave_g{g}_xcd5_dpp", g, 5, False, True) for g in (2, 4)]
+        for rep in range(2):
+            for name, g, c, lds, dpp in variants:
+                k = [0]
 
-            def run(g=g, c=c):
-                s = sets[k[0] % len(sets)]
-                k[0] += 1
-                if g is None:
-                    launch(w, s)
-                else:
-                    C.prefill_lds(s["cos_sin"], s["qkv"], s["cache"], w.style, g, c)
-            for _ in range(4):
-                run()
-            torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(steps):
-                run()
-            b.record()
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) / steps * 1e3
-            key = f"prefill_{name}"
-            prev = out.get(key, {}).get("kernel_us_series", [])
-            out[key] = {"kernel_us_series": prev + [us], "bytes": nbytes,
-                        "timing": "back to back over 4 copies of the written tensors; two "
-                                  "interleaved series"}
-            log(f"[bench] {key}: {us:.1f} us ({nbytes / (us * 1e-6) / 1e9:.0f} GB/s)")
-    del sets, t
-    torch.cuda.empty_cache()
+                def run(g=g, c=c, lds=lds, dpp=dpp):
+                    s = sets[k[0] % len(sets)]
+                    k[0] += 1
+                    if g is None:
+                        launch(w, s)
+                    else:
+                        C.prefill_lds(s["cos_sin"], s["qkv"], s["cache"], w.style, g, c, lds, dpp)
+                for _ in range(4):
+                    run()
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(steps):
+                    run()
+                b.record()
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) / steps * 1e3
+                key = f"prefill_{style_name}_{name}"
+                prev = out.get(key, {}).get("kernel_us_series", [])
+                out[key] = {"kernel_us_series": prev + [us], "bytes": nbytes,
+                            "timing": "back to back over 4 copies of the written tensors; two "
+                                      "interleaved series"}
+                log(f"[bench] {key}: {us:.1f} us ({nbytes / (us * 1e-6) / 1e9:.0f} GB/s)")
+        del sets, t
+        torch.cuda.empty_cache()
     return out
 
 

@@ -25,7 +25,7 @@ _L.rkvc_stream_copy.argtypes = [_P, _P, _LL, _I, _I, _P]
 _L.rkvc_stream_inplace.argtypes = [_P, _LL, _U, _I, _I, _P]
 _L.rkvc_empty.argtypes = [_I, _P]
 _L.rkvc_paged_floor.argtypes = [_P, _P, _P, _P] + [_I] * 9 + [_P]
-_L.rkvc_prefill_lds.argtypes = [_P, _I, _I, _P, _P] + [_I] * 9 + [_P]
+_L.rkvc_prefill_lds.argtypes = [_P, _I, _I, _P, _P] + [_I] * 11 + [_P]
 for _f in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_empty", "rkvc_paged_floor",
            "rkvc_prefill_lds"):
     getattr(_L, _f).restype = _I
@@ -70,14 +70,16 @@ def paged_floor(k_delta, v_delta, pool, cos_sin, num_pages: int, rows_per_seq_lo
                                _stream()), "paged_floor")
 
 
-def prefill_lds(cos_sin, qkv, cache, style: int, groups: int = 2, chunk_log2: int = 5):
-    """Call 1 with the cos/sin row staged in LDS: cos_sin fp32 [TB, TL, R],
-    qkv fp16 [B, S, Hq + 2 Hkv, 128] (rotated in place), cache fp16
-    [B, 2, Hkv, cap, 128]."""
+def prefill_lds(cos_sin, qkv, cache, style: int, groups: int = 2, chunk_log2: int = 5,
+                lds: bool = True, dpp: bool = False):
+    """Call 1 with one workgroup per token: cos_sin fp32 [TB, TL, R], qkv fp16
+    [B, S, Hq + 2 Hkv, 128] (rotated in place), cache fp16 [B, 2, Hkv, cap,
+    128]; `lds` stages the cos/sin row in LDS, `dpp` exchanges NeoX partners
+    by DPP (NeoX, R = 128)."""
     TB, TL, R = cos_sin.shape
     B, S, H, D = qkv.shape
     Hkv, cap = cache.shape[2], cache.shape[3]
     assert D == 128 and cache.shape == (B, 2, Hkv, cap, D)
     _check(_L.rkvc_prefill_lds(cos_sin.data_ptr(), TB, TL, qkv.data_ptr(), cache.data_ptr(), B, S,
-                               H - 2 * Hkv, Hkv, cap, R, style, groups, chunk_log2, _stream()),
-           "prefill_lds")
+                               H - 2 * Hkv, Hkv, cap, R, style, groups, chunk_log2, int(lds),
+                               int(dpp), _stream()), "prefill_lds")

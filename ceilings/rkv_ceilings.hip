@@ -15,10 +15,11 @@
 //    NeoX rotation and stores for the same row shapes, with every address
 //    computed from the row number (no position, sequence or page-table
 //    loads), into contiguous rows or scattered over pool pages;
-//  * the packed prefill (call 1, fp16 cache, default arithmetic) with the
-//    token's cos/sin row staged in LDS once per workgroup and reused by all
-//    its waves: one workgroup per token, the alternative to each wave
-//    fetching the values its lanes need (the library's choice).
+//  * the packed prefill (call 1, fp16 cache, default arithmetic) with one
+//    workgroup per token, its cos/sin row staged in LDS once and reused by
+//    all its waves (the alternative to each wave fetching the values its
+//    lanes need, the library's choice), or fetched per wave with the NeoX
+//    partners exchanged by DPP instead of ds_bpermute.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -182,11 +183,31 @@ struct LdsParams {
   FastDiv div_seq;           // by S
 };
 
+// NeoX partner chunk of a lane (the lane R/16 away in its row): the
+// library's ds_bpermute, or, for R = D = 128 only, a DPP rotation by 8 inside
+// each row of 16 lanes (the partner of lane l is then l ^ 8).
+template <bool kDpp>
+__device__ __forceinline__ uint4 neox_partner(uint4 x, int lane, const ChunkRole& role) {
+  if constexpr (kDpp) {
+    constexpr int kRowRor8 = 0x128;
+    return make_uint4(__builtin_amdgcn_mov_dpp((int)x.x, kRowRor8, 0xf, 0xf, false),
+                      __builtin_amdgcn_mov_dpp((int)x.y, kRowRor8, 0xf, 0xf, false),
+                      __builtin_amdgcn_mov_dpp((int)x.z, kRowRor8, 0xf, 0xf, false),
+                      __builtin_amdgcn_mov_dpp((int)x.w, kRowRor8, 0xf, 0xf, false));
+  } else {
+    return lane_fetch(x, lane + role.partner);
+  }
+}
+
 // One workgroup per token, blockDim = 64 * ceil(row groups / G): the token's
 // table row (R floats) is loaded once into LDS by the first R/4 threads,
 // every wave waits at one barrier and reads its lanes' cos/sin values from
-// LDS.  Row loads, rotation and stores are the library's call-1 kernel's.
-template <int kStyle, int G>
+// LDS (kLds); or every wave fetches the values its lanes need, as the
+// library does (the lower half of the wave the cosines, the upper half the
+// sines, joined by v_permlane32_swap).  kDpp (NeoX, R = D = 128) exchanges
+// NeoX partners by DPP instead of ds_bpermute.  Row loads, rotation and
+// stores are the library's call-1 kernel's.
+template <int kStyle, int G, bool kLds, bool kDpp>
 __global__ __launch_bounds__(1024) void prefill_lds_kernel(LdsParams p) {
   __shared__ float4 table_row[kD / 4];
   const int token = block_id_xcd(p.chunk_log2, (int)gridDim.x);
@@ -210,21 +231,25 @@ __global__ __launch_bounds__(1024) void prefill_lds_kernel(LdsParams p) {
   }
   const int tb = (p.table_batch == 1) ? 0 : b;
   const float* trow = p.cos_sin + ((size_t)tb * p.table_len + s) * p.R;
-  if ((int)threadIdx.x < (p.R >> 2))
-    table_row[threadIdx.x] = reinterpret_cast<const float4*>(trow)[threadIdx.x];
-  __syncthreads();
   float cs[8] = {}, sn[8] = {};
-  if (role.rotary) {
-    const float* t = reinterpret_cast<const float*>(table_row);
-    const int half = p.R >> 1;
-    const int nf = kStyle == kNeox ? 8 : 4;
+  if constexpr (kLds) {
+    if ((int)threadIdx.x < (p.R >> 2))
+      table_row[threadIdx.x] = reinterpret_cast<const float4*>(trow)[threadIdx.x];
+    __syncthreads();
+    if (role.rotary) {
+      const float* t = reinterpret_cast<const float*>(table_row);
+      const int half = p.R >> 1;
+      const int nf = kStyle == kNeox ? 8 : 4;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k < nf) {
-        cs[k] = t[role.freq0 + k];
-        sn[k] = t[half + role.freq0 + k];
+      for (int k = 0; k < 8; ++k) {
+        if (k < nf) {
+          cs[k] = t[role.freq0 + k];
+          sn[k] = t[half + role.freq0 + k];
+        }
       }
     }
+  } else {
+    spread_cos_sin<kStyle>(load_cos_sin<kStyle>(trow, role.freq0, p.R, lane), cs, sn);
   }
   const size_t cache_b = (size_t)b * 2 * p.Hkv * p.cap * kD;
   const BufRes cache_buf = buffer_of(p.cache + cache_b, p.cache_b_bytes);
@@ -233,7 +258,13 @@ __global__ __launch_bounds__(1024) void prefill_lds_kernel(LdsParams p) {
     const int r = row[g];
     const bool is_q = r < p.Hq;
     const bool is_k = !is_q && r < p.Hq + p.Hkv;
-    const uint4 y = rotate_chunk<kStyle, false>(x[g], lane, role, is_q || is_k, cs, sn);
+    uint4 y;
+    if constexpr (kStyle == kNeox) {
+      const uint4 q = neox_partner<kDpp>(x[g], lane, role);
+      y = ((is_q || is_k) && role.rotary) ? rotate_neox<false>(x[g], q, cs, sn, role.first) : x[g];
+    } else {
+      y = rotate_chunk<kStyle, false>(x[g], lane, role, is_q || is_k, cs, sn);
+    }
     if (r >= H) continue;
     const uint32_t row_off = (uint32_t)(r * kD + 8 * c) * 2;
     if (is_q) {
@@ -343,19 +374,20 @@ int rkvc_paged_floor(const uint16_t* k_delta, const uint16_t* v_delta, uint16_t*
   return go(paged_floor_kernel<4, false>);
 }
 
-// Call 1 (packed prefill, fp16 cache, default arithmetic) on D = 128 with the
-// cos/sin row staged in LDS; style 0 NeoX, 1 GPT-J; G = 2 or 4 row groups
-// per wave; chunk_log2: tokens are taken by the XCDs in chunks of
-// 2^chunk_log2 (0: contiguous eighths).  Shapes as for
-// rkv_apply_rope_write_kv_packed_qkv; the host checks only what this
-// kernel's addressing needs.
+// Call 1 (packed prefill, fp16 cache, default arithmetic) on D = 128, one
+// workgroup per token; style 0 NeoX, 1 GPT-J; G = 2 or 4 row groups per
+// wave; chunk_log2: tokens are taken by the XCDs in chunks of 2^chunk_log2
+// (0: contiguous eighths); lds: the cos/sin row staged in LDS (else fetched
+// per wave); dpp: NeoX partners by DPP (NeoX, R = 128, per-wave fetch only).
+// Shapes as for rkv_apply_rope_write_kv_packed_qkv; the host checks only
+// what this kernel's addressing needs.
 int rkvc_prefill_lds(const float* cos_sin, int table_batch, int table_len, uint16_t* qkv,
                      uint16_t* cache, int B, int S, int Hq, int Hkv, int cap, int R, int style,
-                     int G, int chunk_log2, hipStream_t stream) {
+                     int G, int chunk_log2, int lds, int dpp, hipStream_t stream) {
   if (!cos_sin || !qkv || !cache || B <= 0 || S <= 0 || Hq < 0 || Hkv <= 0 || S > cap ||
       S > table_len || (table_batch != 1 && table_batch != B) || R <= 0 || R > kD || R % 16 ||
       (G != 2 && G != 4) || (style != kNeox && style != kGptj) || chunk_log2 < 0 ||
-      chunk_log2 > 16)
+      chunk_log2 > 16 || (dpp && (style != kNeox || R != kD || lds)))
     return err(hipErrorInvalidValue);
   const long long H = Hq + 2LL * Hkv;
   const long long groups = (H + kRowsPerGroup - 1) / kRowsPerGroup;
@@ -384,8 +416,18 @@ int rkvc_prefill_lds(const float* cos_sin, int table_batch, int table_len, uint1
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
     return err(hipGetLastError());
   };
-  if (style == kNeox) return G == 2 ? go(prefill_lds_kernel<kNeox, 2>) : go(prefill_lds_kernel<kNeox, 4>);
-  return G == 2 ? go(prefill_lds_kernel<kGptj, 2>) : go(prefill_lds_kernel<kGptj, 4>);
+  if (dpp) return G == 2 ? go(prefill_lds_kernel<kNeox, 2, false, true>)
+                        : go(prefill_lds_kernel<kNeox, 4, false, true>);
+  if (style == kNeox) {
+    if (lds) return G == 2 ? go(prefill_lds_kernel<kNeox, 2, true, false>)
+                           : go(prefill_lds_kernel<kNeox, 4, true, false>);
+    return G == 2 ? go(prefill_lds_kernel<kNeox, 2, false, false>)
+                  : go(prefill_lds_kernel<kNeox, 4, false, false>);
+  }
+  if (lds) return G == 2 ? go(prefill_lds_kernel<kGptj, 2, true, false>)
+                         : go(prefill_lds_kernel<kGptj, 4, true, false>);
+  return G == 2 ? go(prefill_lds_kernel<kGptj, 2, false, false>)
+                : go(prefill_lds_kernel<kGptj, 4, false, false>);
 }
 
 }  // extern "C"

@@ -93,18 +93,24 @@ def test_paged_floor_equals_library_update(scatter, plan, groups):
     assert torch.equal(a, b)
 
 
+_TABLE_MODES = [(True, False), (False, False), (False, True)]   # (lds, dpp)
+
+
 @pytest.mark.parametrize("style", [W.GPTJ, W.NEOX])
 @pytest.mark.parametrize("R", [128, 64])
 @pytest.mark.parametrize("groups", [2, 4])
 @pytest.mark.parametrize("chunk", [0, 5])
-def test_lds_prefill_equals_library_call1(style, R, groups, chunk):
+@pytest.mark.parametrize("lds,dpp", _TABLE_MODES, ids=["lds", "per_wave", "per_wave_dpp"])
+def test_lds_prefill_equals_library_call1(style, R, groups, chunk, lds, dpp):
+    if dpp and (style != W.NEOX or R != 128):
+        pytest.skip("the DPP exchange is the NeoX partner map for R = 128 only")
     C, rkv = _lib()
     from harness import upload
     w = W.packed(2, 96, 8, 2, 128, R, 128, style, 55 + R, table_batch=2, table_len=100,
                  offsets=np.array([0, 17]), name="lds")
     t_lib, t_lds = upload(w), upload(w)
     rkv.apply_rope_write_kv_packed_qkv(t_lib["cos_sin"], t_lib["qkv"], t_lib["cache"], style)
-    C.prefill_lds(t_lds["cos_sin"], t_lds["qkv"], t_lds["cache"], style, groups, chunk)
+    C.prefill_lds(t_lds["cos_sin"], t_lds["qkv"], t_lds["cache"], style, groups, chunk, lds, dpp)
     torch.cuda.synchronize()
     for key in ("qkv", "cache"):
         assert torch.equal(t_lds[key].view(torch.int16), t_lib[key].view(torch.int16)), key
