@@ -538,7 +538,7 @@ def _stream_ceilings(steps):
     for policy, pname in ((1, "library policy (nt loads, nt sc1 stores)"), (0, "plain")):
         for chunk in (7, 0):
             tag = f"{'lib' if policy else 'plain'}_xcd{'chunk128' if chunk else 'eighths'}"
-            for kind in ("copy", "inplace"):
+            for kind in ("copy", "narrow", "inplace"):
                 k = [0]
 
                 def run():
@@ -546,6 +546,8 @@ def _stream_ceilings(steps):
                     k[0] += 1
                     if kind == "copy":
                         C.stream_copy(bufs[i], bufs[4 + i], policy, chunk)
+                    elif kind == "narrow":
+                        C.stream_narrow(bufs[i], bufs[4 + i], policy, chunk)
                     else:
                         C.stream_inplace(bufs[i], policy, chunk)
                 for _ in range(4):
@@ -559,8 +561,9 @@ def _stream_ceilings(steps):
                 b.record()
                 torch.cuda.synchronize()
                 us = a.elapsed_time(b) / steps * 1e3
-                gbs = 2 * GiB / (us * 1e-6) / 1e9
-                out[f"stream_{kind}_{tag}"] = {"kernel_us": us, "bytes": 2 * GiB, "GB/s": gbs,
+                moved = GiB + GiB // 2 if kind == "narrow" else 2 * GiB
+                gbs = moved / (us * 1e-6) / 1e9
+                out[f"stream_{kind}_{tag}"] = {"kernel_us": us, "bytes": moved, "GB/s": gbs,
                                                "frac": gbs / PEAK_HBM_GBS, "policy": pname,
                                                "timing": "back to back over 4 buffers"}
                 log(f"[bench] ceiling stream_{kind}_{tag}: {us:.1f} us, {gbs:.0f} GB/s")

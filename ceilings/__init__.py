@@ -23,11 +23,12 @@ _L = ctypes.CDLL(LIB_PATH)
 _P, _I, _LL, _U = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_uint
 _L.rkvc_stream_copy.argtypes = [_P, _P, _LL, _I, _I, _P]
 _L.rkvc_stream_inplace.argtypes = [_P, _LL, _U, _I, _I, _P]
+_L.rkvc_stream_narrow.argtypes = [_P, _P, _LL, _I, _I, _P]
 _L.rkvc_empty.argtypes = [_I, _P]
 _L.rkvc_paged_floor.argtypes = [_P, _P, _P, _P] + [_I] * 9 + [_P]
 _L.rkvc_prefill_lds.argtypes = [_P, _I, _I, _P, _P] + [_I] * 11 + [_P]
-for _f in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_empty", "rkvc_paged_floor",
-           "rkvc_prefill_lds"):
+for _f in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_stream_narrow", "rkvc_empty",
+           "rkvc_paged_floor", "rkvc_prefill_lds"):
     getattr(_L, _f).restype = _I
 
 
@@ -45,6 +46,15 @@ def stream_copy(src: torch.Tensor, dst: torch.Tensor, policy: int = 1, chunk_log
     assert dst.numel() * dst.element_size() == n and src.is_contiguous() and dst.is_contiguous()
     _check(_L.rkvc_stream_copy(src.data_ptr(), dst.data_ptr(), n, policy, chunk_log2, _stream()),
            "stream_copy")
+
+
+def stream_narrow(src: torch.Tensor, dst: torch.Tensor, policy: int = 1, chunk_log2: int = 7):
+    """dst (int32 words) = src word 2i ^ src word 2i+1: reads all of src,
+    writes half as many bytes."""
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n // 2 and src.is_contiguous() and dst.is_contiguous()
+    _check(_L.rkvc_stream_narrow(src.data_ptr(), dst.data_ptr(), n, policy, chunk_log2, _stream()),
+           "stream_narrow")
 
 
 def stream_inplace(buf: torch.Tensor, policy: int = 1, chunk_log2: int = 7, key: int = 0):

@@ -8,8 +8,9 @@
 // rotate unit, from rkv_kernels.hpp, so a ceiling differs from the kernel it
 // bounds only in what it leaves out.
 //
-//  * streams: copy and in-place passes over a buffer, one 16-byte chunk per
-//    lane, with the library's load and store policy or with plain accesses;
+//  * streams: copy, narrowing (16 bytes read, 8 written per lane) and
+//    in-place passes over a buffer, one 16-byte chunk read per lane, with
+//    the library's load and store policy or with plain accesses;
 //  * an empty kernel of a given grid (the fixed cost of a launch);
 //  * a paged-update floor: the paged update's decomposition, cos/sin fetch,
 //    NeoX rotation and stores for the same row shapes, with every address
@@ -48,6 +49,25 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint8_t* src, uint8_t* 
   } else {
     const uint4 v = *reinterpret_cast<const uint4*>(src + base + off);
     *reinterpret_cast<uint4*>(dst + base + off) = v;
+  }
+}
+
+// Read 16 bytes, write 8 (the xor of each pair of dwords): the 2:1 read to
+// write mix of an update that narrows fp16 rows to one-byte cache entries.
+template <bool kLibPolicy>
+__global__ __launch_bounds__(256) void narrow_kernel(const uint8_t* src, uint8_t* dst,
+                                                     int chunk_log2) {
+  const int blk = block_id_xcd(chunk_log2, (int)gridDim.x);
+  const size_t base = (size_t)blk * kChunkBytes;
+  const uint32_t off = threadIdx.x * 16u;
+  if constexpr (kLibPolicy) {
+    const BufRes s = buffer_of(src + base, kChunkBytes);
+    const BufRes d = buffer_of(dst + base / 2, kChunkBytes / 2);
+    const uint4 v = ld16_buf(s, off);
+    st8_buf(d, off / 2, make_uint2(v.x ^ v.y, v.z ^ v.w));
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + base + off);
+    *reinterpret_cast<uint2*>(dst + base / 2 + off / 2) = make_uint2(v.x ^ v.y, v.z ^ v.w);
   }
 }
 
@@ -261,7 +281,9 @@ __global__ __launch_bounds__(1024) void prefill_lds_kernel(LdsParams p) {
     uint4 y;
     if constexpr (kStyle == kNeox) {
       const uint4 q = neox_partner<kDpp>(x[g], lane, role);
-      y = ((is_q || is_k) && role.rotary) ? rotate_neox<false>(x[g], q, cs, sn, role.first) : x[g];
+      y = ((is_q || is_k) && role.rotary)
+              ? rotate_neox<false>(x[g], q, cs, sn, role.first, role.neg_zero)
+              : x[g];
     } else {
       y = rotate_chunk<kStyle, false>(x[g], lane, role, is_q || is_k, cs, sn);
     }
@@ -301,6 +323,22 @@ int rkvc_stream_copy(const void* src, void* dst, long long bytes, int policy, in
                        (uint8_t*)dst, chunk_log2);
   else
     hipLaunchKernelGGL(copy_kernel<false>, grid, dim3(256), 0, stream, (const uint8_t*)src,
+                       (uint8_t*)dst, chunk_log2);
+  return err(hipGetLastError());
+}
+
+// dst[0:bytes/2) as 32-bit words: word i = src word 2i ^ src word 2i+1.
+int rkvc_stream_narrow(const void* src, void* dst, long long bytes, int policy, int chunk_log2,
+                       hipStream_t stream) {
+  if (!src || !dst || bytes <= 0 || bytes % kChunkBytes || bytes / kChunkBytes > INT32_MAX ||
+      chunk_log2 < 0 || chunk_log2 > 16)
+    return err(hipErrorInvalidValue);
+  const dim3 grid((unsigned)(bytes / kChunkBytes));
+  if (policy)
+    hipLaunchKernelGGL(narrow_kernel<true>, grid, dim3(256), 0, stream, (const uint8_t*)src,
+                       (uint8_t*)dst, chunk_log2);
+  else
+    hipLaunchKernelGGL(narrow_kernel<false>, grid, dim3(256), 0, stream, (const uint8_t*)src,
                        (uint8_t*)dst, chunk_log2);
   return err(hipGetLastError());
 }

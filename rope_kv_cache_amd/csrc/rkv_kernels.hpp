@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(
       if (is_q) {
         st16_buf(q_buf, row_off, narrow_chunk<kExact>(w, x[g], comp));
       } else if constexpr (kFp8) {
-        const uint2 e = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
+        const uint2 e = to_e4m3<kExact>(w, x[g], comp, is_k ? k_rcp : v_rcp, role.neg_zero);
         if (cache_buffered) st8_buf(cache_buf, (uint32_t)cache_el, e);
         else st8_stream(p.cache8 + cache_b + cache_el, e);
         if (kCall == kCallPacked && is_k)
@@ -542,8 +542,9 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(
     const uint32_t el_v = r >= Hkv && r < rows ? (uint32_t)((r - Hkv) * D + 8 * c) : kNowhere;
     if constexpr (kFp8) {
       WideT<kExact> w[8];
-      rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn, w);
-      const uint2 b = to_e4m3<kExact>(w, is_k ? k_rcp : v_rcp);
+      const bool comp =
+          rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, is_k && k_ok, cs, sn, w);
+      const uint2 b = to_e4m3<kExact>(w, x[g], comp, is_k ? k_rcp : v_rcp, role.neg_zero);
       if (g0 < Hkv) st8_buf(kp, el_k, b);
       if (g0 + kRowsPerGroup > Hkv) st8_buf(vp, el_v, b);
     } else {

@@ -32,8 +32,8 @@
 //
 // Q/K RMS norm.  A normalised row is n_d = x_d * r * w_d with
 // r = 1/sqrt(mean(x^2) + eps); the rotation then acts on n.  The row's sum
-// of squares is reduced over its D/8 lanes by a butterfly of lane moves.  Exact mode: every fp16 square is a multiple of 2^-48 below
-// 2^32; split into a multiple of 2^-13 and a remainder, both partial sums
+// of squares is reduced over its D/8 lanes by a butterfly of lane moves.
+// Exact mode: every fp16 square is a multiple of 2^-48 below 2^32; split into a multiple of 2^-13 and a remainder, both partial sums
 // are exact in binary64 in any order, so their sum is the correctly rounded
 // sum of squares (what the definition rounds once); sqrt and the division
 // are correctly rounded binary64 operations.  The rotation of normalised
@@ -98,6 +98,16 @@ __device__ __forceinline__ uint32_t narrow16(WideT<kExact> y) {
   else return f2h_bits(y);
 }
 
+// -0.0, hidden from the optimiser: fma(a, b, -0) equals RN(a*b) for every
+// a, b (signed zeros included), and with `a` widened from fp16 the compiler
+// emits it as one v_fma_mix_f32, which reads the fp16 operand directly,
+// where a product would take a conversion and a multiply.
+__device__ __forceinline__ float opaque_neg_zero() {
+  float z = -0.0f;
+  asm("" : "+v"(z));
+  return z;
+}
+
 // x*c + sign*(p*s), with sign = -1 (first pair member) or +1 (second),
 // before the rounding to fp16.
 //
@@ -109,7 +119,7 @@ __device__ __forceinline__ uint32_t narrow16(WideT<kExact> y) {
 // result is the correctly rounded one or its neighbour.
 template <bool kExact>
 __device__ __forceinline__ WideT<kExact> rot1_wide(uint32_t x_bits, uint32_t p_bits, float c,
-                                                   float s, bool first) {
+                                                   float s, bool first, float nz) {
   if constexpr (kExact) {
     double x = (double)h2f(x_bits), pv = (double)h2f(p_bits);
     double ps = pv * (double)s;               // exact
@@ -117,7 +127,7 @@ __device__ __forceinline__ WideT<kExact> rot1_wide(uint32_t x_bits, uint32_t p_b
   } else {
     const float x = h2f(x_bits), pv = h2f(p_bits);
     const float sv = first ? -s : s;
-    const float ps = pv * sv;
+    const float ps = __builtin_fmaf(pv, sv, nz);   // RN(pv*sv), nz = -0
     const float e = __builtin_fmaf(pv, sv, -ps);   // exact: pv*sv - ps
     return __builtin_fmaf(x, c, ps) + e;
   }
@@ -127,8 +137,8 @@ __device__ __forceinline__ WideT<kExact> rot1_wide(uint32_t x_bits, uint32_t p_b
 // the correctly rounded value or its neighbour.
 template <bool kExact>
 __device__ __forceinline__ uint32_t rot1(uint32_t x_bits, uint32_t p_bits, float c, float s,
-                                         bool first) {
-  return narrow16<kExact>(rot1_wide<kExact>(x_bits, p_bits, c, s, first));
+                                         bool first, float nz) {
+  return narrow16<kExact>(rot1_wide<kExact>(x_bits, p_bits, c, s, first, nz));
 }
 
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
@@ -139,14 +149,14 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo 
 // the cos/sin of element k's frequency; `first` for chunks c < R/16.
 template <bool kExact>
 __device__ __forceinline__ uint4 rotate_neox(uint4 x, uint4 p, const float (&c)[8],
-                                             const float (&s)[8], bool first) {
+                                             const float (&s)[8], bool first, float nz) {
   uint32_t xa[4] = {x.x, x.y, x.z, x.w};
   uint32_t pa[4] = {p.x, p.y, p.z, p.w};
   uint32_t y[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t y0 = rot1<kExact>(lo16(xa[w]), lo16(pa[w]), c[2 * w], s[2 * w], first);
-    uint32_t y1 = rot1<kExact>(hi16(xa[w]), hi16(pa[w]), c[2 * w + 1], s[2 * w + 1], first);
+    uint32_t y0 = rot1<kExact>(lo16(xa[w]), lo16(pa[w]), c[2 * w], s[2 * w], first, nz);
+    uint32_t y1 = rot1<kExact>(hi16(xa[w]), hi16(pa[w]), c[2 * w + 1], s[2 * w + 1], first, nz);
     y[w] = pack2(y0, y1);
   }
   return make_uint4(y[0], y[1], y[2], y[3]);
@@ -154,13 +164,14 @@ __device__ __forceinline__ uint4 rotate_neox(uint4 x, uint4 p, const float (&c)[
 
 // GPT-J: dword w of the chunk holds the pair (lo, hi) at frequency w.
 template <bool kExact>
-__device__ __forceinline__ uint4 rotate_gptj(uint4 x, const float (&c)[8], const float (&s)[8]) {
+__device__ __forceinline__ uint4 rotate_gptj(uint4 x, const float (&c)[8], const float (&s)[8],
+                                             float nz) {
   uint32_t xa[4] = {x.x, x.y, x.z, x.w};
   uint32_t y[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t y0 = rot1<kExact>(lo16(xa[w]), hi16(xa[w]), c[w], s[w], true);
-    uint32_t y1 = rot1<kExact>(hi16(xa[w]), lo16(xa[w]), c[w], s[w], false);
+    uint32_t y0 = rot1<kExact>(lo16(xa[w]), hi16(xa[w]), c[w], s[w], true, nz);
+    uint32_t y1 = rot1<kExact>(hi16(xa[w]), lo16(xa[w]), c[w], s[w], false, nz);
     y[w] = pack2(y0, y1);
   }
   return make_uint4(y[0], y[1], y[2], y[3]);
@@ -181,6 +192,7 @@ struct ChunkRole {
   bool first;      // NeoX: holds first pair members (c < R/16)
   int partner;     // NeoX: lane offset of the partner chunk (+R/16 or -R/16), else 0
   int freq0;       // index of the first frequency this lane uses
+  float neg_zero;  // -0.0, opaque to the optimiser (opaque_neg_zero), made once per wave
 };
 
 template <int kStyle>
@@ -189,6 +201,7 @@ __device__ __forceinline__ ChunkRole chunk_role(int c, int R) {
   const int half_chunks = R >> 4;   // R/16
   r.rotary = c < 2 * half_chunks;
   r.first = c < half_chunks;
+  r.neg_zero = opaque_neg_zero();
   if constexpr (kStyle == kNeox) {
     r.partner = r.rotary ? (r.first ? half_chunks : -half_chunks) : 0;
     r.freq0 = 8 * (r.first ? c : c - half_chunks);
@@ -208,10 +221,11 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 x, int lane, const ChunkRole
                                               const float (&s)[8]) {
   if constexpr (kStyle == kNeox) {
     const uint4 p = lane_fetch(x, lane + role.partner);
-    if (rotate_row && role.rotary) return rotate_neox<kExact>(x, p, c, s, role.first);
+    if (rotate_row && role.rotary)
+      return rotate_neox<kExact>(x, p, c, s, role.first, role.neg_zero);
     return x;
   } else {
-    if (rotate_row && role.rotary) return rotate_gptj<kExact>(x, c, s);
+    if (rotate_row && role.rotary) return rotate_gptj<kExact>(x, c, s, role.neg_zero);
     return x;
   }
 }
@@ -229,30 +243,33 @@ __device__ __forceinline__ bool rotate_chunk_wide(uint4 x, int lane, const Chunk
   if constexpr (kStyle == kNeox) {
     const uint4 p = lane_fetch(x, lane + role.partner);
     const uint32_t pa[4] = {p.x, p.y, p.z, p.w};
+    if (rot) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (rot) {
-        w[2 * k] = rot1_wide<kExact>(lo16(xa[k]), lo16(pa[k]), c[2 * k], s[2 * k], role.first);
-        w[2 * k + 1] =
-            rot1_wide<kExact>(hi16(xa[k]), hi16(pa[k]), c[2 * k + 1], s[2 * k + 1], role.first);
-      } else {
-        w[2 * k] = widen<kExact>(lo16(xa[k]));
-        w[2 * k + 1] = widen<kExact>(hi16(xa[k]));
+      for (int k = 0; k < 4; ++k) {
+        w[2 * k] = rot1_wide<kExact>(lo16(xa[k]), lo16(pa[k]), c[2 * k], s[2 * k], role.first,
+                                     role.neg_zero);
+        w[2 * k + 1] = rot1_wide<kExact>(hi16(xa[k]), hi16(pa[k]), c[2 * k + 1], s[2 * k + 1],
+                                         role.first, role.neg_zero);
       }
+      return true;
     }
   } else {
+    if (rot) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (rot) {
-        w[2 * k] = rot1_wide<kExact>(lo16(xa[k]), hi16(xa[k]), c[k], s[k], true);
-        w[2 * k + 1] = rot1_wide<kExact>(hi16(xa[k]), lo16(xa[k]), c[k], s[k], false);
-      } else {
-        w[2 * k] = widen<kExact>(lo16(xa[k]));
-        w[2 * k + 1] = widen<kExact>(hi16(xa[k]));
+      for (int k = 0; k < 4; ++k) {
+        w[2 * k] = rot1_wide<kExact>(lo16(xa[k]), hi16(xa[k]), c[k], s[k], true, role.neg_zero);
+        w[2 * k + 1] =
+            rot1_wide<kExact>(hi16(xa[k]), lo16(xa[k]), c[k], s[k], false, role.neg_zero);
       }
+      return true;
     }
   }
-  return rot;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    w[2 * k] = widen<kExact>(lo16(xa[k]));
+    w[2 * k + 1] = widen<kExact>(hi16(xa[k]));
+  }
+  return false;
 }
 
 // fp16 chunk from unrounded values; an unrotated chunk keeps its bits.
@@ -265,20 +282,38 @@ __device__ __forceinline__ uint4 narrow_chunk(const WideT<kExact> (&w)[8], uint4
                     pack2(narrow16<kExact>(w[6]), narrow16<kExact>(w[7])));
 }
 
-// Finite magnitudes beyond the largest E4M3 value saturate to it; NaN
-// fails both comparisons and passes through.
+// Magnitudes beyond the largest E4M3 value (infinities included) saturate
+// to it; NaN stays NaN.  IEEE 754-2019 maximum and minimum propagate NaN
+// (v_maximum3_f32 / v_minimum3_f32 on gfx950): two instructions where
+// comparisons and selects took four.  Checked on MI355X over all 2^32 fp32
+// inputs: the E4M3 bytes equal those of the compare-and-select form.
 __device__ __forceinline__ float saturate_e4m3(float v) {
-  return v > 448.f ? 448.f : (v < -448.f ? -448.f : v);
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.f), 448.f);
 }
 
-// Eight E4M3 bytes (element k in byte k) of w[k] * rcp.
+// Eight E4M3 bytes (element k in byte k) of the chunk's values times rcp:
+// the unrounded values w when `comp`, else the chunk's own fp16 values x
+// (which w then holds widened; the default mode reads x directly, so the
+// product is one v_fma_mix_f32 with the -0 addend nz).
 template <bool kExact>
-__device__ __forceinline__ uint2 to_e4m3(const WideT<kExact> (&w)[8], float rcp) {
+__device__ __forceinline__ uint2 to_e4m3(const WideT<kExact> (&w)[8], uint4 x, bool comp,
+                                         float rcp, float nz) {
   float v[8];
+  if constexpr (kExact) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if constexpr (kExact) v[k] = saturate_e4m3(narrow_odd(w[k] * (double)rcp));
-    else v[k] = saturate_e4m3(w[k] * rcp);
+    for (int k = 0; k < 8; ++k) v[k] = saturate_e4m3(narrow_odd(w[k] * (double)rcp));
+  } else {
+    const uint32_t xa[4] = {x.x, x.y, x.z, x.w};
+    if (comp) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(w[k], rcp, nz);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = __builtin_fmaf(h2f(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1])), rcp, nz);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = saturate_e4m3(v[k]);
   }
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
@@ -516,15 +551,15 @@ __device__ __forceinline__ bool rotate_chunk_norm(uint4 x, int lane, const Chunk
     for (int k = 0; k < 8; ++k)
       w[k] = rot ? rot1_general<kExact>(n[k], np[k], c[k], s[k], role.first) : n[k];
   } else {
+    if (rot) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (rot) {
+      for (int k = 0; k < 4; ++k) {
         w[2 * k] = rot1_general<kExact>(n[2 * k], n[2 * k + 1], c[k], s[k], true);
         w[2 * k + 1] = rot1_general<kExact>(n[2 * k + 1], n[2 * k], c[k], s[k], false);
-      } else {
-        w[2 * k] = n[2 * k];
-        w[2 * k + 1] = n[2 * k + 1];
       }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = n[k];
     }
   }
   return rot || normed;

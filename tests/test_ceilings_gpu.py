@@ -37,6 +37,11 @@ def test_streams_move_every_byte():
             torch.cuda.synchronize()
             want = src.view(torch.int32) ^ 0x00010001
             assert torch.equal(buf.view(torch.int32), want)
+            half = torch.zeros(n // 2, dtype=torch.float16, device="cuda")
+            C.stream_narrow(src, half, policy, chunk)
+            torch.cuda.synchronize()
+            words = src.view(torch.int32)
+            assert torch.equal(half.view(torch.int32), words[0::2] ^ words[1::2])
 
 
 def _floor_as_paged(N, Hkv, num_pages, rows_log2, live, scatter, seed):
