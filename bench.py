@@ -27,7 +27,8 @@ library's kernels; both exist for rocprofv3 runs.
 Prints one JSON line on stdout; progress goes to stderr.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-                      [--calib] [--paged-large] [--workload NAME]... [--ceilings]
+                      [--calib] [--paged-large [fp16|fp8|both]] [--workload NAME]...
+                      [--ceilings [PARTS]]
 """
 from __future__ import annotations
 
@@ -903,8 +904,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--paged-large", action="store_true",
-                    help="time only the 65,536-row paged update (for counter runs)")
+    ap.add_argument("--paged-large", nargs="?", const="fp16", default=None,
+                    choices=("fp16", "fp8", "both"),
+                    help="time only the 65,536-row paged update into an fp16 pool, an E4M3 "
+                         "pool, or both (for counter runs; default fp16)")
     ap.add_argument("--workload", action="append", default=[], metavar="NAME",
                     help="time only this small workload (repeatable; for counter and trace "
                          "runs): " + ", ".join(small_cases()))
@@ -949,7 +952,11 @@ def main():
         print(json.dumps(res), flush=True)
         return
     if args.paged_large:
-        res = paged_large(args.steps, args.warmup)
+        res = {}
+        if args.paged_large in ("fp16", "both"):
+            res["paged_delta_large"] = paged_large(args.steps, args.warmup)
+        if args.paged_large in ("fp8", "both"):
+            res["paged_delta_large_fp8"] = paged_large(args.steps, args.warmup, fp8=True)
         if args.calib:
             calibration_copy()
         print(json.dumps(res), flush=True)
