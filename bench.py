@@ -454,6 +454,7 @@ def small_workload(label, make, steps):
     """One small workload: rotated (HBM steady state, the figure of record)
     and back-to-back warm times."""
     import torch
+    import workloads as W
     from harness import launch, upload
     log(f"[bench] generating {label}")
     x = make()
@@ -468,10 +469,18 @@ def small_workload(label, make, steps):
     log(f"[bench] {label}: {r_ms * 1e3:.2f} us rotated, {gbs:.0f} GB/s "
         f"({gbs / PEAK_HBM_GBS:.1%}); warm, back to back {h_ms * 1e3:.2f} us")
     name, tokens = x.name, x.tokens
+    extra = {}
+    if isinstance(x, W.Paged):
+        # call 4 counts its N physical rows as tokens; the rows it writes are
+        # those with a position, a sequence below the batch size and a page
+        p, q = x.positions.astype(np.int64), x.seq.astype(np.int64)
+        live = (p >= 0) & (q >= 0) & (q < x.batch) & (p < x.max_pages * W.TOKENS_PER_PAGE)
+        valid = int(live.sum())
+        extra = {"valid_rows": valid, "valid_rows_per_s": valid / (r_ms * 1e-3)}
     del tx, x
     torch.cuda.empty_cache()
     return {"workload": name, "kernel_us": r_ms * 1e3, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS,
-            "tokens_per_s": tokens / (r_ms * 1e-3), "algorithmic_bytes": xb,
+            "tokens_per_s": tokens / (r_ms * 1e-3), **extra, "algorithmic_bytes": xb,
             "protocol": ROTATED_PROTOCOL,
             "hot_kernel_us": h_ms * 1e3,
             "hot_note": "not flushed: launches queued ahead and run back to back on the same "
@@ -855,36 +864,40 @@ def _token_ranges(w, n_parts):
 
 
 def _time_parts(w, parts, threads, budget_s):
-    """Rounds of every part's oracle call (in place) on a pool of `threads`
-    host threads until the budget is spent; the oracle's C code runs outside
-    Python's interpreter lock.  Returns (tokens per second, rounds, seconds)."""
+    """One warm-up round of every part's oracle call (in place) on a pool of
+    `threads` host threads, then timed rounds until the budget is spent; the
+    oracle's C code runs outside Python's interpreter lock.  Returns (tokens
+    per second at the median round, rounds, seconds)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     oracle.lib()
     tokens = sum(p[1].shape[1] for p in parts)
-    n, t_total = 0, 0.0
+    rounds = []
     with ThreadPoolExecutor(max_workers=threads) as pool:
-        while t_total < budget_s:
+        list(pool.map(lambda p: oracle.packed_qkv_in_place(*p, w.style), parts))
+        while sum(rounds) < budget_s or len(rounds) < 3:
             t0 = time.perf_counter()
             list(pool.map(lambda p: oracle.packed_qkv_in_place(*p, w.style), parts))
-            t_total += time.perf_counter() - t0
-            n += 1
-    return n * tokens / t_total, n, t_total
+            rounds.append(time.perf_counter() - t0)
+    return tokens / float(np.median(rounds)), len(rounds), sum(rounds)
 
 
 def cpu_baseline(w, budget_s=15.0):
     """The oracle as it is (plain C, one call-1 evaluation per token range),
     partitioned over every CPU this process may use: all B x S tokens of the
     headline workload in contiguous token ranges, at least one per thread,
-    repeated until the budget is spent."""
+    repeated until the budget is spent; the rate of the median round, and
+    the same in GB/s of the call's algorithmic bytes."""
     use, host, allowed, model = host_cpus()
     parts = _oracle_parts(w, _token_ranges(w, use))
     rate, n, secs = _time_parts(w, parts, use, budget_s)
-    return {"value": rate, "unit": "tokens/s", "cores": use, "kind": "oracle",
+    gbs = rate * algorithmic_bytes(w) / w.tokens / 1e9
+    return {"value": rate, "unit": "tokens/s", "cores": use, "kind": "oracle", "GB/s": gbs,
             "host_logical_cpus": host, "cpus_allowed": allowed, "cpu_model": model,
             "sample": f"all {w.B * w.S} tokens of the workload in {len(parts)} token ranges on "
-                      f"{use} threads, {n} rounds of in-place oracle calls, {secs:.1f} s wall"}
+                      f"{use} threads, one warm-up round, then the median of {n} rounds of "
+                      f"in-place oracle calls ({secs:.1f} s)"}
 
 
 def cpu_baseline_single(w, budget_s=10.0):
@@ -893,8 +906,9 @@ def cpu_baseline_single(w, budget_s=10.0):
     parts = _oracle_parts(w, [(0, 0, min(w.S, 2048))])
     rate, n, secs = _time_parts(w, parts, 1, budget_s)
     return {"value": rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"tokens 0-{parts[0][1].shape[1] - 1} of sequence 0, {n} in-place oracle "
-                      f"calls, {secs:.1f} s"}
+            "GB/s": rate * algorithmic_bytes(w) / w.tokens / 1e9,
+            "sample": f"tokens 0-{parts[0][1].shape[1] - 1} of sequence 0, one warm-up call, "
+                      f"then the median of {n} in-place oracle calls ({secs:.1f} s)"}
 
 
 def main():

@@ -148,3 +148,18 @@ def test_ceilings_library_loads():
     for name in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_stream_narrow", "rkvc_empty",
                  "rkvc_paged_floor", "rkvc_prefill_lds"):
         assert hasattr(C._L, name)
+
+
+def test_cpu_baseline_reports_rate_bandwidth_and_cores():
+    """The CPU leg times every CPU this process may use, reports the median
+    round's rate and the same rate in GB/s of the call's algorithmic bytes."""
+    import workloads as W
+    w = W.config(1)
+    cb = bench.cpu_baseline(w, budget_s=0.2)
+    use, host, allowed, model = bench.host_cpus()
+    assert cb["cores"] == use and cb["host_logical_cpus"] == host and cb["cpu_model"] == model
+    assert cb["value"] > 0 and cb["kind"] == "oracle" and cb["unit"] == "tokens/s"
+    per_token = bench.algorithmic_bytes(w) / w.tokens
+    assert abs(cb["GB/s"] - cb["value"] * per_token / 1e9) < 1e-9 * max(1.0, cb["GB/s"])
+    single = bench.cpu_baseline_single(w, budget_s=0.1)
+    assert single["cores"] == 1 and single["value"] > 0
