@@ -455,17 +455,31 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(
   const ChunkRole role = chunk_role<kStyle>(c, R);
   const int rows = 2 * Hkv;
   const size_t delta_row = (size_t)i * Hkv;
+  // A row group whose rows are all K heads or all V heads (every group when
+  // Hkv is a multiple of 512/D) addresses its loads and stores as a
+  // wave-uniform base plus the lane's offset inside the group, computed
+  // once; a group straddling the K/V boundary or past the last V head takes
+  // per-lane addresses.  Measured on MI355X, launches back to back over full
+  // copies of their tensors: the 4096-row E4M3 update 6.80 -> 6.62 us, the
+  // 65,536-row fp16 update 76.8 -> 76.0 us (fewer VALU instructions per
+  // wave on the path between the loads and the stores).
+  const uint32_t lane_el = (uint32_t)(row_in_group * D + 8 * c);
 
   int row[G];
   uint4 x[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int r = (part * G + g) * kRowsPerGroup + row_in_group;
+    const int g0 = (part * G + g) * kRowsPerGroup;   // the group's first row (wave-uniform)
+    const int r = g0 + row_in_group;
     row[g] = r;
     x[g] = make_uint4(0, 0, 0, 0);
     // small launches: request every row now, with the index loads
     if constexpr (!kLateLoads) {
-      if (r < Hkv)
+      if (g0 + kRowsPerGroup <= Hkv)
+        x[g] = ld16_stream(k_delta + (delta_row + g0) * D + lane_el);
+      else if (g0 >= Hkv && g0 + kRowsPerGroup <= rows)
+        x[g] = ld16_stream(v_delta + (delta_row + (g0 - Hkv)) * D + lane_el);
+      else if (r < Hkv)
         x[g] = ld16_stream(k_delta + (delta_row + r) * D + 8 * c);
       else if (r < rows)
         x[g] = ld16_stream(v_delta + (delta_row + (r - Hkv)) * D + 8 * c);
@@ -504,8 +518,13 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(
   if constexpr (kLateLoads) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
+      const int g0 = (part * G + g) * kRowsPerGroup;
       const int r = row[g];
-      if (r < Hkv ? k_ok : (r < rows && v_ok)) {
+      if (g0 + kRowsPerGroup <= Hkv) {
+        if (k_ok) x[g] = ld16_stream(k_delta + (delta_row + g0) * D + lane_el);
+      } else if (g0 >= Hkv && g0 + kRowsPerGroup <= rows) {
+        if (v_ok) x[g] = ld16_stream(v_delta + (delta_row + (g0 - Hkv)) * D + lane_el);
+      } else if (r < Hkv ? k_ok : (r < rows && v_ok)) {
         const uint16_t* src =
             r < Hkv ? k_delta + (delta_row + r) * D : v_delta + (delta_row + (r - Hkv)) * D;
         x[g] = ld16_stream(src + 8 * c);
@@ -536,8 +555,36 @@ __global__ __launch_bounds__(kBlock) void paged_kernel(
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int r = row[g];
-    const bool is_k = r < Hkv;
     const int g0 = (part * G + g) * kRowsPerGroup;   // the group's first row (wave-uniform)
+    if (g0 + kRowsPerGroup <= Hkv) {                  // K heads only
+      const uint32_t el = lane_el + (uint32_t)(g0 * D);
+      if constexpr (kFp8) {
+        WideT<kExact> w[8];
+        const bool comp =
+            rotate_chunk_wide<kStyle, kExact>(x[g], lane, role, k_ok, cs, sn, w);
+        st8_buf(kp, el, to_e4m3<kExact>(w, x[g], comp, k_rcp, role.neg_zero));
+      } else {
+        st16_buf(kp, el * 2, rotate_chunk<kStyle, kExact>(x[g], lane, role, k_ok, cs, sn));
+      }
+      continue;
+    }
+    if (g0 >= Hkv && g0 + kRowsPerGroup <= rows) {    // V heads only: no rotation
+      const uint32_t el = lane_el + (uint32_t)((g0 - Hkv) * D);
+      if constexpr (kFp8) {
+        WideT<kExact> w[8];
+        if constexpr (kExact) {
+          const uint32_t xa[4] = {x[g].x, x[g].y, x[g].z, x[g].w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            w[k] = widen<kExact>(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1]));
+        }
+        st8_buf(vp, el, to_e4m3<kExact>(w, x[g], false, v_rcp, role.neg_zero));
+      } else {
+        st16_buf(vp, el * 2, x[g]);
+      }
+      continue;
+    }
+    const bool is_k = r < Hkv;
     const uint32_t el_k = r < Hkv ? (uint32_t)(r * D + 8 * c) : kNowhere;
     const uint32_t el_v = r >= Hkv && r < rows ? (uint32_t)((r - Hkv) * D + 8 * c) : kNowhere;
     if constexpr (kFp8) {
