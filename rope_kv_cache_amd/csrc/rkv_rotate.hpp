@@ -33,8 +33,9 @@
 // Q/K RMS norm.  A normalised row is n_d = x_d * r * w_d with
 // r = 1/sqrt(mean(x^2) + eps); the rotation then acts on n.  The row's sum
 // of squares is reduced over its D/8 lanes by a butterfly of lane moves.
-// Exact mode: every fp16 square is a multiple of 2^-48 below 2^32; split into a multiple of 2^-13 and a remainder, both partial sums
-// are exact in binary64 in any order, so their sum is the correctly rounded
+// Exact mode: every fp16 square is a multiple of 2^-48 below 2^32; split
+// into a multiple of 2^-13 and a remainder, both partial sums are exact in
+// binary64 in any order, so their sum is the correctly rounded
 // sum of squares (what the definition rounds once); sqrt and the division
 // are correctly rounded binary64 operations.  The rotation of normalised
 // values, no longer exact products, rounds each product and the sum
@@ -515,11 +516,15 @@ __device__ __forceinline__ bool rotate_chunk_norm(uint4 x, int lane, const Chunk
   const uint32_t xa[4] = {x.x, x.y, x.z, x.w};
   const bool rot = rotate_row && role.rotary;
   T n[8];
+  if (normed) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const T v = widen<kExact>(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1]));
-    const T t = v * r;
-    n[k] = normed ? t * (T)ws[k] : v;
+    for (int k = 0; k < 8; ++k) {
+      const T v = widen<kExact>(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1]));
+      n[k] = (v * r) * (T)ws[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) n[k] = widen<kExact>(k & 1 ? hi16(xa[k >> 1]) : lo16(xa[k >> 1]));
   }
   if constexpr (kStyle == kNeox) {
     T np[8];
@@ -529,8 +534,7 @@ __device__ __forceinline__ bool rotate_chunk_norm(uint4 x, int lane, const Chunk
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const T v = widen<kExact>(k & 1 ? hi16(pa[k >> 1]) : lo16(pa[k >> 1]));
-        const T t = v * r;
-        np[k] = normed ? t * (T)wp[k] : v;
+        np[k] = normed ? (v * r) * (T)wp[k] : v;
       }
     } else {
       const uint4 lo = lane_fetch(make_uint4(__builtin_bit_cast(uint32_t, n[0]),
@@ -547,9 +551,13 @@ __device__ __forceinline__ bool rotate_chunk_norm(uint4 x, int lane, const Chunk
 #pragma unroll
       for (int k = 0; k < 8; ++k) np[k] = __builtin_bit_cast(float, pa[k]);
     }
+    if (rot) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      w[k] = rot ? rot1_general<kExact>(n[k], np[k], c[k], s[k], role.first) : n[k];
+      for (int k = 0; k < 8; ++k) w[k] = rot1_general<kExact>(n[k], np[k], c[k], s[k], role.first);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = n[k];
+    }
   } else {
     if (rot) {
 #pragma unroll
