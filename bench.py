@@ -314,6 +314,39 @@ def time_rotated(launch_set, sets, steps, warmup=None):
     return a.elapsed_time(b) / steps
 
 
+def time_graph(launch_k, n, reps=5):
+    """`launch_k(k)` for k < n captured as one HIP graph (torch's CUDAGraph
+    drives hipStreamBeginCapture), replayed after a GPU spin: event span of
+    one replay / n, the median over `reps` replays (ms).  The per-launch cost
+    a step captured in a graph pays."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm up on the capture stream
+        for k in range(n):
+            launch_k(k)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(n):
+            launch_k(k)
+    g.replay()
+    torch.cuda.synchronize()
+    spans = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        gpu_busy_wait(3000)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        spans.append(a.elapsed_time(b) / n)
+    del g
+    return float(np.median(spans))
+
+
 def time_queued(launch, steps, warmup=3):
     """Back to back: the GPU first spins long enough for the host to queue
     every launch, then the launches run; event span / count (ms)."""
@@ -356,6 +389,9 @@ COLD_PROTOCOL = ("cold: every launch follows a 1 GiB read that evicts its inputs
                  "recorded the same way (an estimate from below: part of the pair's own cost "
                  "overlaps the launch; rocprofv3's trace of such launches reads up to about "
                  "2 us more)")
+GRAPH_PROTOCOL = ("graph: the same launches (the same copies, in the same order) captured as "
+                  "one HIP graph and replayed behind a GPU spin; event span of a replay / "
+                  "launches, median of 5 replays")
 MARGINAL_PROTOCOL = ("marginal: span of K x (1 GiB read, launch) minus span of K x (1 GiB "
                      "read), / K: the time one launch adds to a stream of HBM-bound work, its "
                      "dispatch and the write-back of the lines it leaves dirty included")
@@ -500,7 +536,7 @@ def _device_paged(x):
     return t
 
 
-CEILING_PARTS = ("streams", "empty", "paged", "prefill", "shapes")
+CEILING_PARTS = ("streams", "empty", "paged", "prefill", "shapes", "graph")
 
 
 def ceilings_leg(steps, parts=CEILING_PARTS):
@@ -523,7 +559,9 @@ def ceilings_leg(steps, parts=CEILING_PARTS):
       token, 2 or 4 row groups per wave) beside the library's kernel;
     * launch shapes: each workload under every forced number of row groups
       per wave (and both load plans of the paged update), timed as its figure
-      of record is."""
+      of record is;
+    * graph: the empty kernel and the small workloads launched back to back
+      on the stream and the same launches captured in one HIP graph."""
     out = {}
     flush = make_flush()
     if "streams" in parts:
@@ -536,6 +574,44 @@ def ceilings_leg(steps, parts=CEILING_PARTS):
         out.update(_prefill_lds(steps))
     if "shapes" in parts:
         out["launch_shapes"] = _launch_shapes(steps)
+    if "graph" in parts:
+        out["graph_launches"] = _graph_launches(steps)
+    return out
+
+
+def _graph_launches(steps):
+    """Per-launch cost on the stream and inside a HIP graph: the empty kernel
+    (1 and 2048 workgroups) back to back, and every small workload over full
+    copies of its tensors (the rotated protocol), each also captured as one
+    graph of the same launches in the same order (time_graph).  Three
+    rounds, stream and graph alternating; medians.  Returns {name: {...}}."""
+    import torch
+    import ceilings as C
+    from harness import launch, upload
+    out = {}
+
+    def both(name, run_k, n, stream_ms):
+        e, g = [], []
+        for _ in range(3):
+            e.append(stream_ms())
+            g.append(time_graph(run_k, n))
+        out[name] = {"stream_us": float(np.median(e)) * 1e3, "graph_us": float(np.median(g)) * 1e3,
+                     "launches": n, "graph_protocol": GRAPH_PROTOCOL}
+        log(f"[bench] {name}: {out[name]['stream_us']:.2f} us per launch on the stream, "
+            f"{out[name]['graph_us']:.2f} us in a graph")
+
+    for wg in (1, 2048):
+        both(f"empty_kernel_{wg}wg", lambda k, wg=wg: C.empty(wg), steps,
+             lambda wg=wg: time_queued(lambda: C.empty(wg), steps))
+    for name, make in small_cases().items():
+        w = make()
+        t = upload(w)
+        sets = full_copies(t, algorithmic_bytes(w))
+        n = len(sets) * max(1, steps // len(sets))
+        both(name, lambda k: launch(w, sets[k % len(sets)]), n,
+             lambda: time_rotated(lambda s_: launch(w, s_), sets, n))
+        del sets, t, w
+        torch.cuda.empty_cache()
     return out
 
 
