@@ -41,22 +41,24 @@ void clear_error() {
 // tensors, small ones back to back over full copies of all their tensors
 // (medians, us):
 //  - large prefill (1.43 GB): two row groups per wave for every flavour
-//    (GPT-J 217.7, one 219.0, four 227.6; E4M3 205.2 against 210.2 / 218.8;
-//    Q/K norm 218.7, NeoX Q/K norm 214.7 against 224.8 at four, Q/K norm
-//    into E4M3 204.1 against 213.0) except the exact mode of the NeoX layout
-//    and of the E4M3 cache, whose binary64 arithmetic per byte is highest
-//    and which take four (NeoX 227.4 against 231.4, E4M3 219.6 against
-//    233.4; the exact GPT-J kernel takes two, 220.8 against 228.4);
+//    (GPT-J 217.3, one 219.0, four 227.2; E4M3 205.2 against 205.6 / 214.7;
+//    Q/K norm 219.2 against 223.4 / 227.0, NeoX Q/K norm 219.0 against 224.2
+//    at four, Q/K norm into E4M3 201.0 against 212.7) except the exact mode
+//    of the NeoX layout and of the E4M3 cache, whose binary64 arithmetic per
+//    byte is highest and which take four (NeoX 228.6 against 238.0, E4M3
+//    213.4 against 218.9; the exact GPT-J kernel takes two, 221.8 against
+//    228.3);
 //  - small launches are latency-bound: every wave is resident at once
 //    (256 CUs x 4 SIMDs x 8 waves), so a small launch doubles G while its
 //    waves would not all fit; the continuous and tree calls run alike at two
-//    and four (5.3-5.5), the Q/K-norm kernel starts from four;
+//    and four (5.3-5.4), the Q/K-norm kernel starts from four (5.9 against
+//    6.0 at two);
 //  - the paged update's small fp16 launches take four, one wave per delta
 //    row, which then resolves its index chain once (NeoX 6.5 against 8.2 at
-//    two, GPT-J 6.9 against 7.8, exact 7.1 against 8.3, fused gather 6.5
-//    against 7.3); small E4M3 ones take two with late loads (7.1); large
-//    ones take two for NeoX and the exact mode, one for GPT-J, four for E4M3
-//    (65,536 rows: 77.0 at two against 81.5 / 84.1).
+//    two, GPT-J 7.2 against 7.9, exact 7.4 against 8.3, fused gather 6.5
+//    against 7.8); small E4M3 ones take two with late loads (6.6, against 7.3
+//    at four); large ones take two for NeoX and the exact mode, one for
+//    GPT-J, four for E4M3 (65,536 rows: 76.0 at two against 80.6 / 85.4).
 constexpr long long kResidentWaves = 8192;
 constexpr long long kStreamingGroups = 65536;
 

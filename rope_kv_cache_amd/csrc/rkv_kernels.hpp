@@ -474,10 +474,12 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(
 // Both read non-temporally and store through buffers over the slot's K and
 // V page rows with nt sc1.  Measured on MI355X, launches back to back over
 // full copies of the paged workload's tensors (every byte from and back to
-// HBM), with preloaded arguments: early loads with ordinary accesses 9.2 us,
-// late loads 8.1 us, early loads non-temporal 8.2 us (the fused gather:
-// 8.4 and 7.5 us for the last two).  A 65,536-row update takes 78 us with
-// late loads (98 us with early ordinary ones).
+// HBM): the 4096-row fp16 update 6.5 us with early loads against 6.9 us
+// with late ones (the fused gather 6.5 against 8.0), the same rows into an
+// E4M3 pool 6.8 against 6.6, a 65,536-row fp16 update 83.4 against 76.0.
+// Requesting the rows once the position and sequence are known (before the
+// page ids) took the 4096-row update to 6.8 us: the round trip ahead of the
+// reads costs more than the padding rows' reads it saves.
 //
 // kGather fuses the page's cos/sin gather (launchDFlashGatherDeltaRope)
 // into the update: the row's cos/sin values come from the rope table row of
