@@ -536,7 +536,7 @@ def _device_paged(x):
     return t
 
 
-CEILING_PARTS = ("streams", "empty", "paged", "prefill", "shapes", "graph")
+CEILING_PARTS = ("streams", "persistent", "empty", "paged", "prefill", "shapes", "graph")
 
 
 def ceilings_leg(steps, parts=CEILING_PARTS):
@@ -548,6 +548,10 @@ def ceilings_leg(steps, parts=CEILING_PARTS):
       the library's load and store policy (buffer loads nt, buffer stores nt
       sc1) and with plain accesses, XCDs taking 128-workgroup chunks in turn
       or contiguous eighths;
+    * the in-place stream in persistent form (a fixed grid of workgroups
+      looping over the buffer, 1, 2 or 4 chunks per step, with and without
+      the next step's loads issued before the current stores, in plain or
+      XCD-region order) beside the one-workgroup-per-chunk stream;
     * an empty kernel of 1 and of 2048 workgroups (the paged workload's
       grid), flushed and back to back;
     * the paged workload's shape (4096 delta rows, 8 KV heads, D = R = 128,
@@ -566,6 +570,8 @@ def ceilings_leg(steps, parts=CEILING_PARTS):
     flush = make_flush()
     if "streams" in parts:
         out.update(_stream_ceilings(steps))
+    if "persistent" in parts:
+        out["persistent_streams"] = _persistent_streams(steps)
     if "empty" in parts:
         out.update(_empty_kernels(steps, flush))
     if "paged" in parts:
@@ -653,6 +659,56 @@ def _stream_ceilings(steps):
                                                "frac": gbs / PEAK_HBM_GBS, "policy": pname,
                                                "timing": "back to back over 4 buffers"}
                 log(f"[bench] ceiling stream_{kind}_{tag}: {us:.1f} us, {gbs:.0f} GB/s")
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+PERSISTENT_FORMS = [  # (chunks per step, next loads before stores, XCD regions, workgroups per CU)
+    (1, 0, 0, 8), (2, 0, 0, 4), (4, 0, 0, 2), (1, 1, 0, 4), (4, 1, 0, 2),
+    (1, 0, 1, 4), (4, 0, 1, 2), (2, 1, 1, 2), (4, 1, 1, 2)]
+
+
+def _persistent_streams(steps):
+    """The in-place stream with the library's policy over 1 GiB, four
+    buffers cycled, as the one-workgroup-per-chunk kernel (128-workgroup XCD
+    chunks) and in each persistent form of PERSISTENT_FORMS; two rounds,
+    interleaved; per form the round with the lower time."""
+    import torch
+    import ceilings as C
+    GiB = 1 << 30
+    bufs = [torch.ones(GiB // 2, dtype=torch.float16, device="cuda") for _ in range(4)]
+    n = max(8, steps // 5)
+
+    def timed(launch):
+        for i in range(4):
+            launch(bufs[i])
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            launch(bufs[i % 4])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    forms = {"one_workgroup_per_chunk": lambda buf: C.stream_inplace(buf, 1, 7)}
+    for u, pipe, xcd, wpc in PERSISTENT_FORMS:
+        forms[f"persistent_u{u}_pipe{pipe}_{'xcd' if xcd else 'plain'}_wg{wpc}"] = (
+            lambda buf, u=u, pipe=pipe, xcd=xcd, wpc=wpc:
+                C.stream_persistent(buf, u, pipe, xcd, 256 * wpc))
+    times = {k: [] for k in forms}
+    for _ in range(2):
+        for k, launch in forms.items():
+            times[k].append(timed(launch))
+    out = {}
+    for k, v in times.items():
+        us = min(v)
+        gbs = 2 * GiB / (us * 1e-6) / 1e9
+        out[k] = {"kernel_us": us, "rounds_us": v, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS,
+                  "launches": n}
+        log(f"[bench] {k}: {us:.1f} us, {gbs:.0f} GB/s")
     del bufs
     torch.cuda.empty_cache()
     return out

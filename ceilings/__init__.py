@@ -1,6 +1,6 @@
 """Measurement kernels timed by ``bench.py --ceilings`` beside the library.
 
-Streams with the library's memory policy, an empty kernel, an index-free
+Streams with the library's memory policy (also in persistent form), an empty kernel, an index-free
 floor of the paged update and the packed prefill with its cos/sin row staged
 in LDS (``rkv_ceilings.hip`` says what each one bounds).  Argument
 marshalling from torch tensors and torch's current stream only; importing
@@ -24,10 +24,12 @@ _P, _I, _LL, _U = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_uin
 _L.rkvc_stream_copy.argtypes = [_P, _P, _LL, _I, _I, _P]
 _L.rkvc_stream_inplace.argtypes = [_P, _LL, _U, _I, _I, _P]
 _L.rkvc_stream_narrow.argtypes = [_P, _P, _LL, _I, _I, _P]
+_L.rkvc_stream_persistent.argtypes = [_P, _LL, _U, _I, _I, _I, _I, _P]
 _L.rkvc_empty.argtypes = [_I, _P]
 _L.rkvc_paged_floor.argtypes = [_P, _P, _P, _P] + [_I] * 9 + [_P]
 _L.rkvc_prefill_lds.argtypes = [_P, _I, _I, _P, _P] + [_I] * 11 + [_P]
-for _f in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_stream_narrow", "rkvc_empty",
+for _f in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_stream_narrow",
+           "rkvc_stream_persistent", "rkvc_empty",
            "rkvc_paged_floor", "rkvc_prefill_lds"):
     getattr(_L, _f).restype = _I
 
@@ -61,6 +63,16 @@ def stream_inplace(buf: torch.Tensor, policy: int = 1, chunk_log2: int = 7, key:
     assert buf.is_contiguous()
     _check(_L.rkvc_stream_inplace(buf.data_ptr(), buf.numel() * buf.element_size(), key, policy,
                                   chunk_log2, _stream()), "stream_inplace")
+
+
+def stream_persistent(buf: torch.Tensor, unroll: int, pipe: int, xcd: int, workgroups: int,
+                      key: int = 0):
+    """buf ^= key (per 32-bit word) by a fixed grid of `workgroups` that loop
+    over it, `unroll` 4 KB chunks per step (see rkv_ceilings.hip)."""
+    assert buf.is_contiguous()
+    _check(_L.rkvc_stream_persistent(buf.data_ptr(), buf.numel() * buf.element_size(), key,
+                                     unroll, pipe, xcd, workgroups, _stream()),
+           "stream_persistent")
 
 
 def empty(workgroups: int):

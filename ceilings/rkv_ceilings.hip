@@ -11,6 +11,10 @@
 //  * streams: copy, narrowing (16 bytes read, 8 written per lane) and
 //    in-place passes over a buffer, one 16-byte chunk read per lane, with
 //    the library's load and store policy or with plain accesses;
+//  * the in-place stream in persistent form: a fixed grid whose workgroups
+//    loop over the buffer, U chunks per step, optionally loading the next
+//    step before storing the current one (the alternative to one short-lived
+//    workgroup per chunk, the library's choice);
 //  * an empty kernel of a given grid (the fixed cost of a launch);
 //  * a paged-update floor: the paged update's decomposition, cos/sin fetch,
 //    NeoX rotation and stores for the same row shapes, with every address
@@ -86,6 +90,59 @@ __global__ __launch_bounds__(256) void inplace_kernel(uint8_t* buf, uint32_t key
     uint4 v = *reinterpret_cast<const uint4*>(buf + base + off);
     v.x ^= key; v.y ^= key; v.z ^= key; v.w ^= key;
     *reinterpret_cast<uint4*>(buf + base + off) = v;
+  }
+}
+
+// Persistent in-place stream: every workgroup loops over the buffer, U
+// consecutive 4 KB chunks per step.  kXcd: workgroup b (on XCD b mod 8)
+// walks its XCD's own contiguous regions of 128 chunks, as the 128-workgroup
+// chunk order does; otherwise step i of workgroup b takes chunks
+// (i * grid + b) * U ...  kPipe: the next step's loads are issued before the
+// current step's stores.  The host checks that the chunk count is a
+// multiple of 8 * 128 and the grid a multiple of 8, so every chunk is
+// visited exactly once.
+template <int U, bool kPipe, bool kXcd>
+__global__ __launch_bounds__(256) void persistent_inplace_kernel(uint8_t* buf, uint32_t bytes,
+                                                                 uint32_t key) {
+  const BufRes r = buffer_of(buf, bytes);
+  const uint32_t nchunks = bytes / kChunkBytes;
+  constexpr uint32_t kGroups = 128 / U;          // U-chunk steps per XCD region
+  const uint32_t xcd = blockIdx.x & 7u, per_xcd = gridDim.x >> 3;
+  const uint32_t lane_off = threadIdx.x * 16u;
+  auto first_chunk = [&](uint32_t j) {
+    if constexpr (kXcd) return (xcd * kGroups + (j % kGroups) + (j / kGroups) * 8u * kGroups) * U;
+    else return j * U;
+  };
+  uint32_t j = kXcd ? blockIdx.x >> 3 : blockIdx.x;
+  const uint32_t j_step = kXcd ? per_xcd : gridDim.x;
+  uint32_t c0 = first_chunk(j);
+  uint4 cur[U];
+  if constexpr (kPipe) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      cur[u] = c0 < nchunks ? ld16_buf(r, (c0 + u) * kChunkBytes + lane_off) : make_uint4(0, 0, 0, 0);
+  }
+  while (c0 < nchunks) {
+    j += j_step;
+    const uint32_t c1 = first_chunk(j);
+    uint4 nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (kPipe)
+        nxt[u] = c1 < nchunks ? ld16_buf(r, (c1 + u) * kChunkBytes + lane_off) : make_uint4(0, 0, 0, 0);
+      else
+        cur[u] = ld16_buf(r, (c0 + u) * kChunkBytes + lane_off);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cur[u].x ^= key; cur[u].y ^= key; cur[u].z ^= key; cur[u].w ^= key;
+      st16_buf(r, (c0 + u) * kChunkBytes + lane_off, cur[u]);
+    }
+    if constexpr (kPipe) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+    c0 = c1;
   }
 }
 
@@ -356,6 +413,30 @@ int rkvc_stream_inplace(void* buf, long long bytes, unsigned key, int policy, in
   else
     hipLaunchKernelGGL(inplace_kernel<false>, grid, dim3(256), 0, stream, (uint8_t*)buf, key,
                        chunk_log2);
+  return err(hipGetLastError());
+}
+
+// buf[0:bytes) ^= key by persistent_inplace_kernel<unroll, pipe, xcd> on
+// `workgroups` workgroups of 256 threads.
+int rkvc_stream_persistent(void* buf, long long bytes, unsigned key, int unroll, int pipe,
+                           int xcd, int workgroups, hipStream_t stream) {
+  if (!buf || bytes <= 0 || bytes % (kChunkBytes * 8LL * 128) || bytes >= (1LL << 31) ||
+      workgroups <= 0 || workgroups % 8 || (unroll != 1 && unroll != 2 && unroll != 4))
+    return err(hipErrorInvalidValue);
+  const dim3 grid((unsigned)workgroups);
+  const uint32_t n = (uint32_t)bytes;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, (uint8_t*)buf, n, key);
+  };
+#define RKVC_PERSISTENT(U)                                                             \
+  if (unroll == U) {                                                                  \
+    if (pipe && xcd) go(persistent_inplace_kernel<U, true, true>);                    \
+    else if (pipe) go(persistent_inplace_kernel<U, true, false>);                     \
+    else if (xcd) go(persistent_inplace_kernel<U, false, true>);                      \
+    else go(persistent_inplace_kernel<U, false, false>);                              \
+  }
+  RKVC_PERSISTENT(1) RKVC_PERSISTENT(2) RKVC_PERSISTENT(4)
+#undef RKVC_PERSISTENT
   return err(hipGetLastError());
 }
 

@@ -44,6 +44,23 @@ def test_streams_move_every_byte():
             assert torch.equal(half.view(torch.int32), words[0::2] ^ words[1::2])
 
 
+def test_persistent_stream_visits_every_chunk_once():
+    """Every persistent form xors each 32-bit word exactly once: a chunk
+    visited twice would come back unchanged, one never visited too."""
+    C, _ = _lib()
+    n = 1 << 22   # 8 MiB of fp16: 2048 chunks of 4 KB, two rounds of 8 x 128
+    src = torch.from_numpy(W.normal_f16(W.rng(4), (n,)).view(np.float16)).cuda()
+    want = src.view(torch.int32) ^ 0x00FF00FF
+    for unroll in (1, 2, 4):
+        for pipe in (0, 1):
+            for xcd in (0, 1):
+                for grid in (8, 64, 512):
+                    buf = src.clone()
+                    C.stream_persistent(buf, unroll, pipe, xcd, grid, key=0x00FF00FF)
+                    torch.cuda.synchronize()
+                    assert torch.equal(buf.view(torch.int32), want), (unroll, pipe, xcd, grid)
+
+
 def _floor_as_paged(N, Hkv, num_pages, rows_log2, live, scatter, seed):
     """Delta rows, cos/sin rows, and the positions, sequences and page table
     under which the library's paged update writes what the floor writes."""
