@@ -25,11 +25,12 @@ _L.rkvc_stream_copy.argtypes = [_P, _P, _LL, _I, _I, _P]
 _L.rkvc_stream_inplace.argtypes = [_P, _LL, _U, _I, _I, _P]
 _L.rkvc_stream_narrow.argtypes = [_P, _P, _LL, _I, _I, _P]
 _L.rkvc_stream_persistent.argtypes = [_P, _LL, _U, _I, _I, _I, _I, _P]
+_L.rkvc_check_reciprocal.argtypes = [_P, _I, _P]
 _L.rkvc_empty.argtypes = [_I, _P]
 _L.rkvc_paged_floor.argtypes = [_P, _P, _P, _P] + [_I] * 9 + [_P]
 _L.rkvc_prefill_lds.argtypes = [_P, _I, _I, _P, _P] + [_I] * 11 + [_P]
 for _f in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_stream_narrow",
-           "rkvc_stream_persistent", "rkvc_empty",
+           "rkvc_stream_persistent", "rkvc_check_reciprocal", "rkvc_empty",
            "rkvc_paged_floor", "rkvc_prefill_lds"):
     getattr(_L, _f).restype = _I
 
@@ -73,6 +74,16 @@ def stream_persistent(buf: torch.Tensor, unroll: int, pipe: int, xcd: int, workg
     _check(_L.rkvc_stream_persistent(buf.data_ptr(), buf.numel() * buf.element_size(), key,
                                      unroll, pipe, xcd, workgroups, _stream()),
            "stream_persistent")
+
+
+def check_reciprocal(counts: torch.Tensor):
+    """The library's fp32 reciprocal of a scale against the rounded binary64
+    quotient for every fp32 pattern; `counts` (int32, even length 2t with t a
+    power of two >= 256) receives per thread its mismatch count and first
+    mismatching pattern."""
+    assert counts.dtype == torch.int32 and counts.is_contiguous() and counts.numel() % 2 == 0
+    _check(_L.rkvc_check_reciprocal(counts.data_ptr(), counts.numel() // 2, _stream()),
+           "check_reciprocal")
 
 
 def empty(workgroups: int):

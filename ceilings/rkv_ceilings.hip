@@ -16,6 +16,7 @@
 //    step before storing the current one (the alternative to one short-lived
 //    workgroup per chunk, the library's choice);
 //  * an empty kernel of a given grid (the fixed cost of a launch);
+//  * an exhaustive check of the library's fp32 reciprocal of a scale;
 //  * a paged-update floor: the paged update's decomposition, cos/sin fetch,
 //    NeoX rotation and stores for the same row shapes, with every address
 //    computed from the row number (no position, sequence or page-table
@@ -144,6 +145,31 @@ __global__ __launch_bounds__(256) void persistent_inplace_kernel(uint8_t* buf, u
     }
     c0 = c1;
   }
+}
+
+// Exhaustive check of the library's reciprocal() (rkv_rotate.hpp): for
+// every fp32 pattern b, reciprocal(b) against the binary64 quotient 1/b
+// rounded to binary32 (any NaN equals any NaN).  Thread t covers patterns
+// [t * per_thread, (t + 1) * per_thread); counts[2t] is its number of
+// mismatches, counts[2t + 1] its first mismatching pattern (or all ones).
+__global__ __launch_bounds__(256) void reciprocal_check_kernel(uint32_t* counts,
+                                                               uint32_t per_thread) {
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t n = 0, first = 0xffffffffu;
+  for (uint32_t j = 0; j < per_thread; ++j) {
+    const uint32_t u = tid * per_thread + j;
+    const float b = __builtin_bit_cast(float, u);
+    const float got = reciprocal(b);
+    const float want = (float)(1.0 / (double)b);
+    const bool same = __builtin_bit_cast(uint32_t, got) == __builtin_bit_cast(uint32_t, want) ||
+                      (got != got && want != want);
+    if (!same) {
+      if (n == 0) first = u;
+      ++n;
+    }
+  }
+  counts[2 * tid] = n;
+  counts[2 * tid + 1] = first;
 }
 
 __global__ __launch_bounds__(256) void empty_kernel() {}
@@ -437,6 +463,17 @@ int rkvc_stream_persistent(void* buf, long long bytes, unsigned key, int unroll,
   }
   RKVC_PERSISTENT(1) RKVC_PERSISTENT(2) RKVC_PERSISTENT(4)
 #undef RKVC_PERSISTENT
+  return err(hipGetLastError());
+}
+
+// reciprocal_check_kernel over all 2^32 fp32 patterns on `threads` threads
+// (a power of two from 256 to 2^24); counts holds 2 * threads words.
+int rkvc_check_reciprocal(uint32_t* counts, int threads, hipStream_t stream) {
+  if (!counts || threads < 256 || threads > (1 << 24) || (threads & (threads - 1)))
+    return err(hipErrorInvalidValue);
+  const uint32_t per = (uint32_t)((1ULL << 32) / (unsigned long long)threads);
+  hipLaunchKernelGGL(reciprocal_check_kernel, dim3((unsigned)threads / 256), dim3(256), 0, stream,
+                     counts, per);
   return err(hipGetLastError());
 }
 

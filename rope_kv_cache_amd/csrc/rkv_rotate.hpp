@@ -328,14 +328,38 @@ __device__ __forceinline__ uint2 to_e4m3(const WideT<kExact> (&w)[8], uint4 x, b
 // are in flight together.
 static __device__ float kUnitScale = 1.0f;   // global memory, never written
 
+// The scale is read through the constant address space: no kernel writes
+// it, and a wave-uniform load from there is a scalar load, whose wait does
+// not include the row loads issued before it (vector loads complete in
+// order; as a vector load the scale, and with it the reciprocal, waited for
+// every row of the wave).
+typedef __attribute__((address_space(4))) const float ConstFloat;
+
 __device__ __forceinline__ float load_scale(const float* scale) {
-  return *(scale ? scale : &kUnitScale);
+  return *(ConstFloat*)(scale ? scale : &kUnitScale);
 }
 
 // The fp32 reciprocal of a scale, correctly rounded: the binary64 quotient
 // rounded to binary32 (binary64 has more than 2*24+2 bits, so the double
-// rounding is innocuous).
+// rounding is innocuous).  For 2^-120 <= |scale| < 2^121 the same value
+// comes from binary32 arithmetic: the hardware estimate y (v_rcp_f32), the
+// residual e = 1 - scale*y by one fused multiply-add (exact for an estimate
+// this close), and y + e*y by another -- one Newton step, equal to the
+// rounded binary64 quotient for every such input (an exhaustive comparison,
+// ceilings/ reciprocal_check_kernel).  Zeros, subnormals, huge values,
+// infinities and NaN take the division.  The scale is wave-uniform, so the
+// branch is too.  With the scalar scale loads above, measured on MI355X
+// (launches back to back over full copies of their tensors): the continuous
+// call into an E4M3 cache 5.58 -> 5.49 us, the large prefill into an E4M3
+// cache 205.2 -> 203.6 us, the paged updates unchanged; bytes identical.
+// (The compiler turns the binary64 quotient into a correctly rounded
+// binary32 division, about ten instructions.)
 __device__ __forceinline__ float reciprocal(float scale) {
+  const uint32_t biased = (__builtin_bit_cast(uint32_t, scale) >> 23) & 0xffu;
+  if (biased >= 127u - 120u && biased <= 127u + 120u) {
+    const float y = __builtin_amdgcn_rcpf(scale);
+    return __builtin_fmaf(__builtin_fmaf(-scale, y, 1.0f), y, y);
+  }
   return (float)(1.0 / (double)scale);
 }
 

@@ -44,6 +44,22 @@ def test_streams_move_every_byte():
             assert torch.equal(half.view(torch.int32), words[0::2] ^ words[1::2])
 
 
+def test_reciprocal_is_the_rounded_binary64_quotient_for_every_fp32():
+    """The fp32 reciprocal the fp8 kernels take of a scale (a binary32
+    Newton step over the hardware estimate in the middle range, the binary64
+    division elsewhere) equals 1/scale in binary64 rounded to binary32, for
+    all 2^32 patterns."""
+    C, _ = _lib()
+    threads = 1 << 20
+    counts = torch.zeros(2 * threads, dtype=torch.int32, device="cuda")
+    C.check_reciprocal(counts)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy().view(np.uint32)
+    bad = int(c[0::2].astype(np.uint64).sum())
+    firsts = [hex(int(v)) for v in c[1::2][c[0::2] > 0][:8]]
+    assert bad == 0, (bad, firsts)
+
+
 def test_persistent_stream_visits_every_chunk_once():
     """Every persistent form xors each 32-bit word exactly once: a chunk
     visited twice would come back unchanged, one never visited too."""

@@ -78,11 +78,17 @@ def test_small_shapes_fp8(call, D, R, style):
 
 
 @pytest.mark.parametrize("k_scale,v_scale", [(None, None), (1.0, 0.5), (1e-3, 3e-3),
-                                             (64.0, 0.0123), (0.0123, None)],
-                         ids=["no_scale", "unit_half", "saturating", "subnormal", "k_only"])
+                                             (64.0, 0.0123), (0.0123, None),
+                                             (2.0 ** -124, 2.0 ** -125), (2.0 ** 122, 2.0 ** 125),
+                                             (0.0123, 2.0 ** -124)],
+                         ids=["no_scale", "unit_half", "saturating", "subnormal", "k_only",
+                              "tiny", "huge", "mixed_range"])
 def test_scales(k_scale, v_scale):
     """Scales that leave values unscaled, saturate most of them (|x|/1e-3
-    beyond 448) or push them into the E4M3 subnormals."""
+    beyond 448) or push them into the E4M3 subnormals; scales outside
+    [2^-120, 2^121), whose reciprocal the kernels take by binary64 division
+    instead of the binary32 Newton step (every value saturates, or
+    underflows to zero)."""
     w = W.continuous(4, 33, 6, 2, 128, 128, 64, GPTJ, 7300, 33, 64, name="continuous_scales")
     check(fp8(w, 7301, k_scale, v_scale))
     w = W.paged(200, 5, 3, 64, 48, 20, 4, NEOX, 7302, width=40, name="paged_scales")
