@@ -21,7 +21,7 @@ from harness import compare, exact_diffs, expected, run_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 2000
+N_CASES = 10000
 
 
 def _rotary_dim(r, D):
