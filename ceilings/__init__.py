@@ -26,11 +26,12 @@ _L.rkvc_stream_inplace.argtypes = [_P, _LL, _U, _I, _I, _P]
 _L.rkvc_stream_narrow.argtypes = [_P, _P, _LL, _I, _I, _P]
 _L.rkvc_stream_persistent.argtypes = [_P, _LL, _U, _I, _I, _I, _I, _P]
 _L.rkvc_check_reciprocal.argtypes = [_P, _I, _P]
+_L.rkvc_check_f16_pair.argtypes = [_P, _I, _P]
 _L.rkvc_empty.argtypes = [_I, _P]
 _L.rkvc_paged_floor.argtypes = [_P, _P, _P, _P] + [_I] * 9 + [_P]
 _L.rkvc_prefill_lds.argtypes = [_P, _I, _I, _P, _P] + [_I] * 11 + [_P]
 for _f in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_stream_narrow",
-           "rkvc_stream_persistent", "rkvc_check_reciprocal", "rkvc_empty",
+           "rkvc_stream_persistent", "rkvc_check_reciprocal", "rkvc_check_f16_pair", "rkvc_empty",
            "rkvc_paged_floor", "rkvc_prefill_lds"):
     getattr(_L, _f).restype = _I
 
@@ -84,6 +85,14 @@ def check_reciprocal(counts: torch.Tensor):
     assert counts.dtype == torch.int32 and counts.is_contiguous() and counts.numel() % 2 == 0
     _check(_L.rkvc_check_reciprocal(counts.data_ptr(), counts.numel() // 2, _stream()),
            "check_reciprocal")
+
+
+def check_f16_pair(counts: torch.Tensor):
+    """The library's packed fp16 conversion against two scalar conversions
+    for every fp32 pattern; `counts` as for check_reciprocal."""
+    assert counts.dtype == torch.int32 and counts.is_contiguous() and counts.numel() % 2 == 0
+    _check(_L.rkvc_check_f16_pair(counts.data_ptr(), counts.numel() // 2, _stream()),
+           "check_f16_pair")
 
 
 def empty(workgroups: int):

@@ -16,7 +16,8 @@
 //    step before storing the current one (the alternative to one short-lived
 //    workgroup per chunk, the library's choice);
 //  * an empty kernel of a given grid (the fixed cost of a launch);
-//  * an exhaustive check of the library's fp32 reciprocal of a scale;
+//  * exhaustive checks of the library's fp32 reciprocal of a scale and of
+//    its packed fp16 conversion;
 //  * a paged-update floor: the paged update's decomposition, cos/sin fetch,
 //    NeoX rotation and stores for the same row shapes, with every address
 //    computed from the row number (no position, sequence or page-table
@@ -164,6 +165,27 @@ __global__ __launch_bounds__(256) void reciprocal_check_kernel(uint32_t* counts,
     const bool same = __builtin_bit_cast(uint32_t, got) == __builtin_bit_cast(uint32_t, want) ||
                       (got != got && want != want);
     if (!same) {
+      if (n == 0) first = u;
+      ++n;
+    }
+  }
+  counts[2 * tid] = n;
+  counts[2 * tid + 1] = first;
+}
+
+// Exhaustive check of the library's packed fp16 conversion (f2h_pair in
+// rkv_rotate.hpp) against two scalar conversions (f2h_bits): every fp32
+// pattern u in the low half, with an unrelated pattern in the high half.
+// Same output layout as reciprocal_check_kernel.
+__global__ __launch_bounds__(256) void f16_pair_check_kernel(uint32_t* counts,
+                                                             uint32_t per_thread) {
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t n = 0, first = 0xffffffffu;
+  for (uint32_t j = 0; j < per_thread; ++j) {
+    const uint32_t u = tid * per_thread + j;
+    const uint32_t u2 = u * 2654435761u + 12345u;
+    const float lo = __builtin_bit_cast(float, u), hi = __builtin_bit_cast(float, u2);
+    if (f2h_pair(lo, hi) != (f2h_bits(lo) | (f2h_bits(hi) << 16))) {
       if (n == 0) first = u;
       ++n;
     }
@@ -473,6 +495,16 @@ int rkvc_check_reciprocal(uint32_t* counts, int threads, hipStream_t stream) {
     return err(hipErrorInvalidValue);
   const uint32_t per = (uint32_t)((1ULL << 32) / (unsigned long long)threads);
   hipLaunchKernelGGL(reciprocal_check_kernel, dim3((unsigned)threads / 256), dim3(256), 0, stream,
+                     counts, per);
+  return err(hipGetLastError());
+}
+
+// f16_pair_check_kernel over all 2^32 patterns, as rkvc_check_reciprocal.
+int rkvc_check_f16_pair(uint32_t* counts, int threads, hipStream_t stream) {
+  if (!counts || threads < 256 || threads > (1 << 24) || (threads & (threads - 1)))
+    return err(hipErrorInvalidValue);
+  const uint32_t per = (uint32_t)((1ULL << 32) / (unsigned long long)threads);
+  hipLaunchKernelGGL(f16_pair_check_kernel, dim3((unsigned)threads / 256), dim3(256), 0, stream,
                      counts, per);
   return err(hipGetLastError());
 }

@@ -81,9 +81,6 @@ __device__ __forceinline__ float narrow_odd(double y) {
   return __builtin_bit_cast(float, bits);
 }
 
-// binary64 -> binary16, round to nearest even, via round-to-odd binary32.
-__device__ __forceinline__ uint32_t narrow_exact(double y) { return f2h_bits(narrow_odd(y)); }
-
 // The unrounded rotated value: binary64 in the exact mode, else binary32.
 template <bool kExact>
 using WideT = typename std::conditional<kExact, double, float>::type;
@@ -93,10 +90,24 @@ __device__ __forceinline__ WideT<kExact> widen(uint32_t bits16) {
   return (WideT<kExact>)h2f(bits16);       // exact either way
 }
 
+// Two binary32 values rounded to fp16 (nearest even) and packed, `lo` in
+// the low half: one v_cvt_pk_f16_f32, where two conversions and a pack took
+// two instructions; bit for bit the two scalar conversions (an exhaustive
+// comparison over all 2^32 patterns, ceilings/ f16_pair_check_kernel).
+__device__ __forceinline__ uint32_t f2h_pair(float lo, float hi) {
+  typedef float F2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 H2 __attribute__((ext_vector_type(2)));
+  const F2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, H2));
+}
+
+// Two unrounded values rounded to fp16 and packed: binary64 values are
+// narrowed to binary32 with round-to-odd first, so the rounding to fp16 is
+// again the direct one (correctly rounded in the exact mode).
 template <bool kExact>
-__device__ __forceinline__ uint32_t narrow16(WideT<kExact> y) {
-  if constexpr (kExact) return narrow_exact(y);
-  else return f2h_bits(y);
+__device__ __forceinline__ uint32_t narrow_pair(WideT<kExact> lo, WideT<kExact> hi) {
+  if constexpr (kExact) return f2h_pair(narrow_odd(lo), narrow_odd(hi));
+  else return f2h_pair(lo, hi);
 }
 
 // -0.0, hidden from the optimiser: fma(a, b, -0) equals RN(a*b) for every
@@ -134,20 +145,13 @@ __device__ __forceinline__ WideT<kExact> rot1_wide(uint32_t x_bits, uint32_t p_b
   }
 }
 
-// The rotated element rounded to fp16: correctly rounded with kExact, else
-// the correctly rounded value or its neighbour.
-template <bool kExact>
-__device__ __forceinline__ uint32_t rot1(uint32_t x_bits, uint32_t p_bits, float c, float s,
-                                         bool first, float nz) {
-  return narrow16<kExact>(rot1_wide<kExact>(x_bits, p_bits, c, s, first, nz));
-}
-
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
-__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
 // NeoX: the lane's 8 elements x with the partner chunk p; c[k], s[k] are
-// the cos/sin of element k's frequency; `first` for chunks c < R/16.
+// the cos/sin of element k's frequency; `first` for chunks c < R/16.  Each
+// rotated element is rounded to fp16: correctly rounded with kExact, else
+// the correctly rounded value or its neighbour.
 template <bool kExact>
 __device__ __forceinline__ uint4 rotate_neox(uint4 x, uint4 p, const float (&c)[8],
                                              const float (&s)[8], bool first, float nz) {
@@ -156,9 +160,9 @@ __device__ __forceinline__ uint4 rotate_neox(uint4 x, uint4 p, const float (&c)[
   uint32_t y[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t y0 = rot1<kExact>(lo16(xa[w]), lo16(pa[w]), c[2 * w], s[2 * w], first, nz);
-    uint32_t y1 = rot1<kExact>(hi16(xa[w]), hi16(pa[w]), c[2 * w + 1], s[2 * w + 1], first, nz);
-    y[w] = pack2(y0, y1);
+    y[w] = narrow_pair<kExact>(
+        rot1_wide<kExact>(lo16(xa[w]), lo16(pa[w]), c[2 * w], s[2 * w], first, nz),
+        rot1_wide<kExact>(hi16(xa[w]), hi16(pa[w]), c[2 * w + 1], s[2 * w + 1], first, nz));
   }
   return make_uint4(y[0], y[1], y[2], y[3]);
 }
@@ -171,9 +175,8 @@ __device__ __forceinline__ uint4 rotate_gptj(uint4 x, const float (&c)[8], const
   uint32_t y[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t y0 = rot1<kExact>(lo16(xa[w]), hi16(xa[w]), c[w], s[w], true, nz);
-    uint32_t y1 = rot1<kExact>(hi16(xa[w]), lo16(xa[w]), c[w], s[w], false, nz);
-    y[w] = pack2(y0, y1);
+    y[w] = narrow_pair<kExact>(rot1_wide<kExact>(lo16(xa[w]), hi16(xa[w]), c[w], s[w], true, nz),
+                               rot1_wide<kExact>(hi16(xa[w]), lo16(xa[w]), c[w], s[w], false, nz));
   }
   return make_uint4(y[0], y[1], y[2], y[3]);
 }
@@ -277,10 +280,8 @@ __device__ __forceinline__ bool rotate_chunk_wide(uint4 x, int lane, const Chunk
 template <bool kExact>
 __device__ __forceinline__ uint4 narrow_chunk(const WideT<kExact> (&w)[8], uint4 x, bool rot) {
   if (!rot) return x;
-  return make_uint4(pack2(narrow16<kExact>(w[0]), narrow16<kExact>(w[1])),
-                    pack2(narrow16<kExact>(w[2]), narrow16<kExact>(w[3])),
-                    pack2(narrow16<kExact>(w[4]), narrow16<kExact>(w[5])),
-                    pack2(narrow16<kExact>(w[6]), narrow16<kExact>(w[7])));
+  return make_uint4(narrow_pair<kExact>(w[0], w[1]), narrow_pair<kExact>(w[2], w[3]),
+                    narrow_pair<kExact>(w[4], w[5]), narrow_pair<kExact>(w[6], w[7]));
 }
 
 // Magnitudes beyond the largest E4M3 value (infinities included) saturate

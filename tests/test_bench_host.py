@@ -146,7 +146,8 @@ def test_ceilings_library_loads():
     (no kernel is launched here)."""
     import ceilings as C
     for name in ("rkvc_stream_copy", "rkvc_stream_inplace", "rkvc_stream_narrow",
-                 "rkvc_stream_persistent", "rkvc_check_reciprocal", "rkvc_empty",
+                 "rkvc_stream_persistent", "rkvc_check_reciprocal", "rkvc_check_f16_pair",
+                 "rkvc_empty",
                  "rkvc_paged_floor", "rkvc_prefill_lds"):
         assert hasattr(C._L, name)
 

@@ -60,6 +60,21 @@ def test_reciprocal_is_the_rounded_binary64_quotient_for_every_fp32():
     assert bad == 0, (bad, firsts)
 
 
+def test_packed_fp16_conversion_equals_two_scalar_ones_for_every_fp32():
+    """v_cvt_pk_f16_f32, which the kernels round their fp16 outputs with,
+    gives bit for bit the two scalar conversions, for all 2^32 patterns in
+    the low half (NaN payloads included)."""
+    C, _ = _lib()
+    threads = 1 << 20
+    counts = torch.zeros(2 * threads, dtype=torch.int32, device="cuda")
+    C.check_f16_pair(counts)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy().view(np.uint32)
+    bad = int(c[0::2].astype(np.uint64).sum())
+    firsts = [hex(int(v)) for v in c[1::2][c[0::2] > 0][:8]]
+    assert bad == 0, (bad, firsts)
+
+
 def test_persistent_stream_visits_every_chunk_once():
     """Every persistent form xors each 32-bit word exactly once: a chunk
     visited twice would come back unchanged, one never visited too."""
