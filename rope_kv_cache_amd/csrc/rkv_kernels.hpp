@@ -255,6 +255,19 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerGroup = kWave / kLanesPerRow;
 
+  // Call 1 (the prefill, a streaming launch) issues its row loads at the
+  // highest wave priority and drops back once they are issued: instruction
+  // issue is otherwise oldest wave first, so a newly launched wave's loads
+  // waited behind older waves' arithmetic and stores.  Measured on MI355X,
+  // launches back to back over copies of their tensors: the large prefill
+  // 217.7 -> 214.8 us, NeoX 219.4 -> 214.5, into E4M3 203.4 -> 201.4, with
+  // Q/K norm 219.4 -> 215.9, its TP=8 shard 29.70 -> 29.27.  Calls 2 and 3
+  // do without: the 16 x 1024-token continuous write gained 0.4%, while the
+  // small (one-generation) launches were 1-1.5% slower with the priority,
+  // and as slow with a run-time test that raised it for large launches only
+  // (the test sits before every wave's first load); the paged update was
+  // 4% slower with it.
+  if constexpr (kCall == kCallPacked) __builtin_amdgcn_s_setprio(3);
   const int wave = wave_id_uniform((int)((shifts >> 16) & 0xffu), total_waves);
   if (wave >= total_waves) return;
   const FastDiv div_waves{(uint32_t)waves_per_token, waves_div_m, shifts & 0xffu};
@@ -296,6 +309,7 @@ __global__ __launch_bounds__(kBlock) void contig_kernel(
     x[g] = ld16_buf(tok_buf, (uint32_t)(row[g] * D + 8 * c) * 2);
   }
   if constexpr (kCall != kCallPacked) asm volatile("" ::: "memory");
+  if constexpr (kCall == kCallPacked) __builtin_amdgcn_s_setprio(0);
 
   int slot = s, pos = s;
   if constexpr (kCall != kCallPacked) {
