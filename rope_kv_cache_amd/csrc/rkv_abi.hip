@@ -40,14 +40,13 @@ void clear_error() {
 // rounds each, large launches back to back over four copies of the written
 // tensors, small ones back to back over full copies of all their tensors
 // (medians, us):
-//  - large prefill (1.43 GB): two row groups per wave for every flavour
-//    (GPT-J 217.3, one 219.0, four 227.2; E4M3 205.2 against 205.6 / 214.7;
-//    Q/K norm 219.2 against 223.4 / 227.0, NeoX Q/K norm 219.0 against 224.2
-//    at four, Q/K norm into E4M3 201.0 against 212.7) except the exact mode
-//    of the NeoX layout and of the E4M3 cache, whose binary64 arithmetic per
-//    byte is highest and which take four (NeoX 228.6 against 238.0, E4M3
-//    213.4 against 218.9; the exact GPT-J kernel takes two, 221.8 against
-//    228.3);
+//  - large prefill (1.43 GB, call 1): two row groups per wave for every
+//    flavour (GPT-J 217.3, one 222.1, four 236.2; E4M3 203.7 against 212.0 /
+//    223.5; Q/K norm 218.7 against 225.7 / 234.0; exact NeoX 223.5 against
+//    234.3 at four, exact E4M3 206.1 against 214.9); large launches of calls
+//    2 and 3 in the exact mode of the NeoX layout or of the E4M3 cache, whose
+//    binary64 arithmetic per byte is highest, take four (they do not raise
+//    their wave priority; call 1 took four too before it did);
 //  - small launches are latency-bound: every wave is resident at once
 //    (256 CUs x 4 SIMDs x 8 waves), so a small launch doubles G while its
 //    waves would not all fit; the continuous and tree calls run alike at two
@@ -55,10 +54,10 @@ void clear_error() {
 //    6.0 at two);
 //  - the paged update's small fp16 launches take four, one wave per delta
 //    row, which then resolves its index chain once (NeoX 6.5 against 8.2 at
-//    two, GPT-J 7.2 against 7.9, exact 7.4 against 8.3, fused gather 6.5
-//    against 7.8); small E4M3 ones take two with late loads (6.6, against 7.3
+//    two, GPT-J 7.2 against 7.8, exact 7.3 against 8.3, fused gather 6.5
+//    against 7.5); small E4M3 ones take two with late loads (6.6, against 7.3
 //    at four); large ones take two for NeoX and the exact mode, one for
-//    GPT-J, four for E4M3 (65,536 rows: 76.0 at two against 80.6 / 85.4).
+//    GPT-J, four for E4M3 (65,536 rows: 79.3 at two against 84.2 / 85.1).
 constexpr long long kResidentWaves = 8192;
 constexpr long long kStreamingGroups = 65536;
 
@@ -310,7 +309,9 @@ rkv_status contig(int call, const rkv_tensor* cos_sin, const rkv_tensor* end_len
   const bool heavy = exact_of(style) || fp8 || norm != nullptr;
   const bool neox = layout_of(style) == RKV_ROPE_NEOX;
   const bool exact = exact_of(style);
-  const int g_large = (exact && (neox || fp8)) ? 4 : 2;
+  // (call 1, which raises its wave priority while issuing its row loads,
+  // runs its exact modes fastest at two as well; calls 2 and 3 keep four)
+  const int g_large = (exact && (neox || fp8) && call != rkv::kCallPacked) ? 4 : 2;
   const Split sp = pick_split(tokens, (H + rows_per_group - 1) / rows_per_group, g_large,
                               norm ? 4 : (heavy ? 2 : 1));
   if (!sp.groups_per_wave) return fail(RKV_ERR_UNSUPPORTED, "too many rows for one launch");
