@@ -532,7 +532,8 @@ def _device_paged(x):
     from harness import upload
     t = upload(x)
     t["pool"] = torch.zeros((2, x.num_pages, W.TOKENS_PER_PAGE, x.Hkv, x.D),
-                            dtype=torch.float16, device="cuda")
+                            dtype=torch.uint8 if x.extra.get("fp8") else torch.float16,
+                            device="cuda")
     return t
 
 
@@ -888,7 +889,16 @@ def _launch_shapes(steps):
             ("prefill_qknorm_fp8_cache_neox", lambda: _styled(W.with_fp8_cache(W.with_qk_norm(W.config(HEADLINE), 7105), 7005, fill="sentinel"), W.NEOX), True, (0,)),
             ("paged_delta_n65536", lambda: W.paged(65536, 64, 8, 128, 128, 8192, 128, W.NEOX, 1044,
                                                    pool_fill="none", name="paged_delta_n65536_p8192"),
-             True, (1, 2))):
+             True, (1, 2)),
+            ("paged_delta_n65536_gptj", lambda: W.paged(65536, 64, 8, 128, 128, 8192, 128, W.GPTJ, 1045,
+                                                        pool_fill="none", name="paged_delta_n65536_gptj"),
+             True, (2,)),
+            ("paged_delta_n65536_fp8", lambda: W.with_fp8_cache(
+                W.paged(65536, 64, 8, 128, 128, 8192, 128, W.NEOX, 1044, pool_fill="none",
+                        name="paged_delta_n65536_p8192"), 7044, fill="sentinel"), True, (2,)),
+            ("paged_delta_n65536_fp8_gptj", lambda: W.with_fp8_cache(
+                W.paged(65536, 64, 8, 128, 128, 8192, 128, W.GPTJ, 1046, pool_fill="none",
+                        name="paged_delta_n65536_gptj"), 7046, fill="sentinel"), True, (2,))):
         log(f"[bench] generating {label}")
         w = make()
         t = _device_paged(w) if isinstance(w, W.Paged) else upload(w)

@@ -56,8 +56,9 @@ void clear_error() {
 //    row, which then resolves its index chain once (NeoX 6.5 against 8.2 at
 //    two, GPT-J 7.2 against 7.8, exact 7.3 against 8.3, fused gather 6.5
 //    against 7.5); small E4M3 ones take two with late loads (6.6, against 7.3
-//    at four); large ones take two for NeoX and the exact mode, one for
-//    GPT-J, four for E4M3 (65,536 rows: 79.3 at two against 84.2 / 85.1).
+//    at four); large ones take two in every flavour (65,536 rows, NeoX: 75.7
+//    against 83.9 at one and 84.8 at four; GPT-J 78.9 against 83.6 / 82.9;
+//    E4M3 pools 60.4 against 63.1 at four, GPT-J 62.5 against 63.7).
 constexpr long long kResidentWaves = 8192;
 constexpr long long kStreamingGroups = 65536;
 
@@ -418,9 +419,8 @@ rkv_status paged(const uint16_t* kDelta, const uint16_t* vDelta, void* kvCache, 
   const long long rows_per_group = 512 / D;
   const long long groups_per_row = (2 * Hkv + rows_per_group - 1) / rows_per_group;
   // row groups per wave (see "Launch shape" above)
-  const bool neox = layout_of(ropeStyle) == RKV_ROPE_NEOX;
   const int g_small = fp8 ? 2 : 4;
-  const int g_large = fp8 ? 4 : ((exact_of(ropeStyle) || neox) ? 2 : 1);
+  const int g_large = 2;
   const Split sp = pick_split(N, groups_per_row, g_large, g_small);
   // large launches and E4M3 pools load a delta row once its page ids are
   // known (only rows that are written move bytes); small fp16 ones request
